@@ -1,0 +1,288 @@
+/*
+ * Plain sequential CPU oracle for the Mamba-2 mixer core.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file or the library built from it; only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark do.  It shares no
+ * code, header, table or helper with the HIP kernels.
+ *
+ * What it computes (sources):
+ *  - The model scored on page "Mamb2_8B_FP4_Recall_SQ3.25" is a pure Mamba-2
+ *    model (header paragraph and section "Provenance and license"); the method
+ *    is Mamba-2 / structured state-space duality (Dao and Gu 2024, listed under
+ *    "References" on that page).  Per head h of a layer, with a P x N state S,
+ *    one token t does
+ *        S   <- exp(dt_t * A_h) * S + dt_t * x_t (outer) B_t
+ *        y_t  = S . C_t + D_h * x_t
+ *    where x_t is the head's P-vector, B_t and C_t the N-vectors of the head's
+ *    group and D_h the skip ("post-D" point, section "Representation",
+ *    paragraph "Resurface").  y_t sees token t's own update.
+ *  - The recurrent state is reset at every 2048-token scoring window (section
+ *    "Measured quality", test protocol paragraph), so each sequence here starts
+ *    from a given initial state (zeros unless supplied).
+ *  - The convolution caches counted in section "Storage and runtime memory"
+ *    are the history of the causal depthwise conv1d that precedes the scan;
+ *    SiLU follows it.  The gated RMSNorm after the scan is the "pinned
+ *    RMSNorm configuration" of section "Compatible reference environment";
+ *    its contents are not on the page, the reading used here is
+ *    out = g / sqrt(mean(g^2) + eps) * w with g = y * silu(z).
+ *  - "A recurrent row is requantized each token" (section "Representation",
+ *    paragraph "State"): the decode oracle stores the state to binary16 after
+ *    every token and reloads it.  That rounding is a quantisation decision, so
+ *    the pre-rounding value is formed in binary32, the state precision, with a
+ *    fixed evaluation order:
+ *        a  = (float) exp((double) dt * (double) A)          (rounded once)
+ *        u  = dt * x                                          (exact in fp32)
+ *        v  = u * B                                           (one rounding)
+ *        S' = fmaf(a, S, v)                                   (one rounding)
+ *        S  <- f16_rne(S')
+ *    y is accumulated in fp64 from the binary32 S'.
+ * Everything else is computed in fp64 from the exact input values.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16, round to nearest even, subnormals kept, overflow -> inf */
+
+/* Rounds a finite or infinite double to the nearest binary16 value (ties to
+ * even) and returns it as a double.  Written from the definition of the
+ * format: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits, smallest
+ * subnormal 2^-24, largest finite 65504. */
+double oracle_f16_round(double v)
+{
+    if (isnan(v) || isinf(v) || v == 0.0) return v;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);          /* a = m * 2^e, m in [0.5, 1) -> a in [2^(e-1), 2^e) */
+    int ulp_exp = (e - 1) - 10;        /* 10 fraction bits below the leading bit */
+    if (ulp_exp < -24) ulp_exp = -24;  /* subnormal spacing */
+    double ulp = ldexp(1.0, ulp_exp);
+    double q = a / ulp;                /* exact: scaling by a power of two */
+    double fl = floor(q);
+    double rem = q - fl;               /* exact */
+    double r;
+    if (rem > 0.5) r = fl + 1.0;
+    else if (rem < 0.5) r = fl;
+    else r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+    double out = r * ulp;
+    /* The overflow threshold is the midpoint between 65504 and 65536 (=2^16,
+     * the next value with one more exponent step); ties there go to even,
+     * which is 2^16, i.e. infinity. */
+    if (out > 65504.0) out = INFINITY;
+    return v < 0 ? -out : out;
+}
+
+/* binary16 bit pattern -> double (exact). */
+double oracle_f16_bits_to_double(uint16_t h)
+{
+    int s = (h >> 15) & 1, ex = (h >> 10) & 0x1f, fr = h & 0x3ff;
+    double v;
+    if (ex == 0) v = ldexp((double)fr, -24);
+    else if (ex == 31) v = fr ? NAN : INFINITY;
+    else v = ldexp((double)(fr | 0x400), ex - 25);
+    return s ? -v : v;
+}
+
+/* double that is already a binary16 value -> bit pattern. */
+uint16_t oracle_double_to_f16_bits(double v)
+{
+    uint16_t s = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return 0x7e00;
+    if (isinf(a)) return s | 0x7c00;
+    if (a == 0.0) return s;
+    if (a < ldexp(1.0, -14)) return s | (uint16_t)(a * ldexp(1.0, 24));
+    int e;
+    double m = frexp(a, &e);            /* a = m 2^e, m in [0.5,1) */
+    uint16_t ex = (uint16_t)(e - 1 + 15);
+    uint16_t fr = (uint16_t)((m * 2.0 - 1.0) * 1024.0);
+    return s | (uint16_t)(ex << 10) | fr;
+}
+
+/* Vector helpers used by the Python side (rounding pins). */
+void oracle_f16_round_array(const double* in, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_round(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Causal depthwise conv1d + SiLU.
+ * xin (B, L, Cn) raw activations, w (Cn, W) taps, bias (Cn).
+ * History: token positions before 0 come from state_in (B, Cn, W-1), oldest
+ * first, or are zero when state_in is NULL (a window reset).
+ * Tap orientation: w[c][W-1] multiplies the current token, w[c][W-1-k] the
+ * token k steps back (cross-correlation over the causal window).
+ * out (B, L, Cn) = silu(bias + sum_k w[c][k] * xin[t-(W-1)+k]).
+ * Only t < len_b is written.  state_out (B, Cn, W-1) receives the last W-1 raw
+ * inputs before len_b (taken from the history where len_b < W-1). */
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+void oracle_conv_silu(int B, int L, int Cn, int W,
+                      const double* xin, const double* w, const double* bias,
+                      const double* state_in, const int32_t* seqlens,
+                      double* out, double* state_out)
+{
+    for (int b = 0; b < B; ++b) {
+        int len = seqlens ? seqlens[b] : L;
+        for (int c = 0; c < Cn; ++c) {
+            /* raw value at position tau (may be negative -> history) */
+            #define RAW(tau) ((tau) >= 0 ? xin[((size_t)b * L + (tau)) * Cn + c] \
+                              : (state_in ? state_in[((size_t)b * Cn + c) * (W - 1) + (W - 1) + (tau)] : 0.0))
+            for (int t = 0; t < len; ++t) {
+                double u = bias ? bias[c] : 0.0;
+                for (int k = 0; k < W; ++k) u += w[(size_t)c * W + k] * RAW(t - (W - 1) + k);
+                out[((size_t)b * L + t) * Cn + c] = silu(u);
+            }
+            if (state_out)
+                for (int k = 0; k < W - 1; ++k)
+                    state_out[((size_t)b * Cn + c) * (W - 1) + k] = RAW(len - (W - 1) + k);
+            #undef RAW
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sequential selective state-space recurrence (fp64).
+ * x (B, L, H, P); dt (B, L, H) (positive, used as given); A, D (H);
+ * Bm, Cm (B, L, G, N); head h reads group g = h / (H / G).
+ * h0 (B, H, P, N) or NULL (zeros).  seqlens (B) or NULL (all L).
+ * y (B, L, H, P): rows t >= len_b are not touched.
+ * hT (B, H, P, N) or NULL: state after the last real token. */
+void oracle_ssd_scan(int B, int L, int H, int P, int N, int G,
+                     const double* x, const double* dt, const double* A,
+                     const double* Bm, const double* Cm, const double* D,
+                     const double* h0, const int32_t* seqlens,
+                     double* y, double* hT, double* work, int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int hpg = H / G;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H, g = h / hpg;
+        const int len = seqlens ? seqlens[b] : L;
+        double* S = work + (size_t)bh * P * N;
+        for (int i = 0; i < P * N; ++i) S[i] = h0 ? h0[(size_t)bh * P * N + i] : 0.0;
+        for (int t = 0; t < len; ++t) {
+            const double d = dt[((size_t)b * L + t) * H + h];
+            const double a = exp(d * A[h]);
+            const double* xt = x + (((size_t)b * L + t) * H + h) * P;
+            const double* Bt = Bm + (((size_t)b * L + t) * G + g) * N;
+            const double* Ct = Cm + (((size_t)b * L + t) * G + g) * N;
+            double* yt = y + (((size_t)b * L + t) * H + h) * P;
+            for (int p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    double s = a * S[p * N + n] + d * xt[p] * Bt[n];
+                    S[p * N + n] = s;
+                    acc += s * Ct[n];
+                }
+                yt[p] = acc + D[h] * xt[p];
+            }
+        }
+        if (hT)
+            for (int i = 0; i < P * N; ++i) hT[(size_t)bh * P * N + i] = S[i];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gated RMSNorm over groups of `group` consecutive channels of each token:
+ * g = y * silu(z); out = g / sqrt(mean_group(g^2) + eps) * w. */
+void oracle_gated_rmsnorm(int64_t T, int Cn, int group,
+                          const double* y, const double* z, const double* w,
+                          double eps, double* out)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int c0 = 0; c0 < Cn; c0 += group) {
+            double ss = 0.0;
+            for (int c = c0; c < c0 + group; ++c) {
+                double g = y[t * Cn + c] * silu(z[t * Cn + c]);
+                ss += g * g;
+            }
+            double r = 1.0 / sqrt(ss / group + eps);
+            for (int c = c0; c < c0 + group; ++c) {
+                double g = y[t * Cn + c] * silu(z[t * Cn + c]);
+                out[t * Cn + c] = g * r * w[c];
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp32 -> binary16 RNE on a float, via the double routine (a float is exactly
+ * representable as a double, so one rounding happens). */
+static float f16_round_f(float v) { return (float)oracle_f16_round((double)v); }
+
+/* One or more single-token decode steps with a binary16 resident state.
+ * Inputs are per step: x (T, B, H, P), dt (T, B, H), Bm, Cm (T, B, G, N);
+ * A, D (H).  All values are binary32 (the binary16 inputs widened exactly).
+ * state (B, H, P, N) holds binary16 bit patterns, read and written in place.
+ * y (T, B, H, P) in fp64.  See the header for the binary32 step contract.
+ * Only the (b) in [b_lo, b_hi) are processed (for sampled checks). */
+void oracle_decode_f16state(int T, int B, int H, int P, int N, int G,
+                            const float* x, const float* dt, const float* A,
+                            const float* Bm, const float* Cm, const float* D,
+                            uint16_t* state, double* y, int b_lo, int b_hi,
+                            int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int hpg = H / G;
+    const int nbh = (b_hi - b_lo) * H;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nbh; ++i) {
+        const int b = b_lo + i / H, h = i % H, g = h / hpg;
+        uint16_t* St = state + ((size_t)b * H + h) * P * N;
+        for (int t = 0; t < T; ++t) {
+            const float d = dt[((size_t)t * B + b) * H + h];
+            const float a = (float)exp((double)d * (double)A[h]);
+            const float* xt = x + (((size_t)t * B + b) * H + h) * P;
+            const float* Bt = Bm + (((size_t)t * B + b) * G + g) * N;
+            const float* Ct = Cm + (((size_t)t * B + b) * G + g) * N;
+            double* yt = y + (((size_t)t * B + b) * H + h) * P;
+            for (int p = 0; p < P; ++p) {
+                const float u = d * xt[p];
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    const float s_old = (float)oracle_f16_bits_to_double(St[p * N + n]);
+                    const float v = u * Bt[n];
+                    const float s_new = fmaf(a, s_old, v);
+                    acc += (double)s_new * (double)Ct[n];
+                    St[p * N + n] = oracle_double_to_f16_bits((double)f16_round_f(s_new));
+                }
+                yt[p] = acc + (double)D[h] * (double)xt[p];
+            }
+        }
+    }
+}
+
+/* Threads actually used by an OpenMP parallel region with this request. */
+int oracle_threads_used(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    int used = 1;
+    #pragma omp parallel
+    {
+        #pragma omp single
+        used = omp_get_num_threads();
+    }
+    return used;
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
