@@ -1,0 +1,245 @@
+"""Benchmark of the Mamba-2 mixer core on one MI355X.
+
+Headline: the chunked (state-space-dual) window scan at the Mamba2-8B layer
+shape -- batch 1, L=2048, H=128, P=64, N=128, G=8, chunk 256, fp16 I/O, fp32
+state -- in tokens/s.  A "step" is one call of mamba2_conv_scan_window over
+one window.  Inputs are resident in HBM before timing starts; several buffer
+sets are rotated so that the working set exceeds the 256 MB Infinity Cache.
+The one-token decode step (64 sequences, binary16 resident state) is timed in
+the same run and reported in microseconds per step.  Parity against the CPU
+oracle is re-checked on the timed buffers before any number is printed.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+MFMA_F16_PEAK = 2500.0     # TFLOP/s dense f16
+
+
+def window_bytes(B, L, H, P, N, G, lens=None):
+    """Algorithmic HBM bytes of one window call: every input element read once,
+    every output written once, fp16 I/O, fp32 final state."""
+    toks = sum(lens) if lens else B * L
+    per_tok = 2 * H * P + 2 * H + 2 * 2 * G * N + 2 * H * P   # x, dt, B, C in; y out
+    return toks * per_tok + B * H * P * N * 4 + 2 * H * 4       # final state, A, D
+
+
+def decode_bytes(B, H, P, N, G):
+    """Algorithmic bytes of one decode step with a binary16 resident state."""
+    return B * H * P * N * 2 * 2 + B * H * P * 2 * 2 + B * G * N * 2 * 2 + B * H * 2 + 2 * H * 4
+
+
+def window_mfma_flops(L, H, P, N, Q=256, sub=64):
+    """f16 MFMA flops the kernel issues per window (B=1): per (chunk, head) the
+    64-token sub-chunk diagonal (C.B^T over the causal 16x16 tiles and the
+    masked product), the sub-chunk states and the carry-in readout."""
+    nsub = L // sub
+    tiles = sub // 16
+    cb = sum(t + 1 for t in range(tiles)) * 2 * 16 * 16 * max(N, 32)
+    diag = sum((t // 2 + 1) for t in range(tiles)) * P // 16 * 2 * 16 * 16 * 32
+    st = 2 * P * N * sub
+    ro = 2 * P * N * sub
+    return H * nsub * (cb + diag + st + ro)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=5, help="rotated input/output buffer sets")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the scan shards by sequence and head with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mamba_ssd_scan_amd as m2
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    s = synth.layer_window()
+    B, L, H, P, N, G, Q = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk
+
+    # ---- inputs resident in HBM, rotated sets ---------------------------------
+    sets = []
+    for k in range(args.sets):
+        inp = synth.window_inputs(s, 1001 + 100 * k)
+        t = {kk: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for kk, v in inp.items()}
+        t["y"] = torch.empty((B, L, H * P), dtype=torch.float16, device=dev)
+        t["hT"] = torch.empty((B, H, P, N), dtype=torch.float32, device=dev)
+        t["np"] = inp if k == 0 else None
+        sets.append(t)
+    dims = m2.make_dims(B, L, H, P, N, G, Q)
+    ws = m2.alloc_workspace(dims, dev)
+
+    def step(k):
+        t = sets[k % len(sets)]
+        m2.conv_scan_window(t["dt"], t["A"], t["D"], t["y"], ws, x=t["x"], B=t["B"], C=t["C"], state_out=t["hT"],
+                            chunk=Q, stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # ---- parity on the timed buffers (sampled heads, one per group) -----------
+    import oracle
+    t0 = sets[0]
+    inp = t0["np"]
+    y = t0["y"].cpu().numpy().reshape(B, L, H, P).astype(np.float64)
+    hT = t0["hT"].cpu().numpy()
+    heads = [g * (H // G) + (g * 5) % (H // G) for g in range(G)]
+    worst_y = worst_s = 0.0
+    for h in heads:
+        g = h // (H // G)
+        yr, hr = oracle.ssd_scan(inp["x"][:, :, h:h + 1], inp["dt"][:, :, h:h + 1], inp["A"][h:h + 1],
+                                 inp["B"][:, :, g:g + 1], inp["C"][:, :, g:g + 1], inp["D"][h:h + 1])
+        worst_y = max(worst_y, np.abs(y[:, :, h] - yr[:, :, 0]).max() / np.abs(yr).max())
+        worst_s = max(worst_s, np.abs(hT[:, h] - hr[:, 0]).max() / np.abs(hr).max())
+    if not (worst_y <= 2e-3 and worst_s <= 1e-3):
+        print(f"parity check failed before timing: y {worst_y:.3e} state {worst_s:.3e}", file=sys.stderr)
+        sys.exit(1)
+
+    # ---- timed region: K window calls ------------------------------------------
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tok_s = B * L / (ms * 1e-3)
+    wbytes = window_bytes(B, L, H, P, N, G)
+    achieved = wbytes / (ms * 1e-3) / 1e9
+
+    # single-call latency (one launch, synchronized)
+    lat = []
+    for k in range(20):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        step(k)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        lat.append(ev0.elapsed_time(ev1) * 1e3)
+    lat_us = float(np.median(lat))
+    del sets
+    torch.cuda.empty_cache()
+
+    # ---- decode: 64 sequences, binary16 resident state ------------------------
+    d = synth.DECODE
+    DB, DH, DP, DN, DG, T = d["batch"], d["nheads"], d["headdim"], d["dstate"], d["ngroups"], args.decode_steps
+    prm = synth.decode_params(1003, DB, DH, DP, DN)
+    nin = 8
+    steps_in = []
+    for k in range(nin):
+        si = synth.decode_step_inputs(1003, k, prm["dt0"], DB, DH, DP, DN, DG)
+        steps_in.append({kk: torch.from_numpy(v).to(dev) for kk, v in si.items()})
+    A, Dd = torch.from_numpy(prm["A"]).to(dev), torch.from_numpy(prm["D"]).to(dev)
+    nstate = 3
+    states = [torch.empty((DB, DH, DP, DN), dtype=torch.float16, device=dev) for _ in range(nstate)]
+    seed32 = torch.from_numpy(prm["state"]).to(dev)
+    for st_ in states:
+        m2.state_load(seed32, st_, stream=stream)
+    ydec = torch.empty((DB, DH, DP), dtype=torch.float16, device=dev)
+
+    def dstep(k, st_):
+        si = steps_in[k % nin]
+        m2.decode_step(si["x"], si["dt"], si["B"], si["C"], A, Dd, st_, ydec, stream=stream)
+
+    for k in range(10):
+        dstep(k, states[0])
+    torch.cuda.synchronize()
+    # as written: one resident state, T consecutive steps
+    ev0.record(stream)
+    for k in range(T):
+        dstep(k, states[0])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_us = ev0.elapsed_time(ev1) * 1e3 / T
+    # rotated: three resident states (384 MiB > Infinity Cache)
+    ev0.record(stream)
+    for k in range(T):
+        dstep(k, states[k % nstate])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_rot_us = ev0.elapsed_time(ev1) * 1e3 / T
+    dbytes = decode_bytes(DB, DH, DP, DN, DG)
+
+    # ---- CPU baseline: the oracle on a bounded sample of the window ------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        nth = len(os.sched_getaffinity(0))
+        used = oracle.threads_used(nth)
+        hs = 32
+        sub = {k: v for k, v in inp.items()}
+        t_start = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.ssd_scan(sub["x"][:, :, :hs], sub["dt"][:, :, :hs], sub["A"][:hs], sub["B"][:, :, :hs // 16],
+                            sub["C"][:, :, :hs // 16], sub["D"][:hs], nthreads=nth)
+            reps += 1
+            el = time.perf_counter() - t_start
+            if el > 10.0 or reps >= 20:
+                break
+        per_window = el / reps * (H / hs)
+        cpu = {"value": round(B * L / per_window, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+               "sample": f"{hs} of {H} heads of one L={L} window (fp64 sequential recurrence), {reps} runs, "
+                         f"scaled to all {H} heads"}
+
+    mflops = window_mfma_flops(L, H, P, N, Q)
+    out = {
+        "metric": "SSD window-scan tokens/s at 8B layer shape L=2048 + decode us/step; % HBM roofline",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "mamba2-8b layer window scan", "batch": B, "seq_len": L, "nheads": H,
+                   "headdim": P, "dstate": N, "ngroups": G, "chunk": Q, "io": "f16", "state": "f32",
+                   "buffer_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "window_us": round(ms * 1e3, 2),
+        "window_latency_us": round(lat_us, 2),
+        "window_algorithmic_bytes": wbytes,
+        "window_mfma_tflops": round(mflops / (ms * 1e-3) / 1e12, 1),
+        "window_mfma_frac": round(mflops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK, 4),
+        "parity": {"y": float(f"{worst_y:.3e}"), "state": float(f"{worst_s:.3e}")},
+        "decode": {"us_per_step": round(dec_us, 2), "us_per_step_rotated_states": round(dec_rot_us, 2),
+                   "algorithmic_bytes": dbytes, "achieved_GBs": round(dbytes / (dec_rot_us * 1e-6) / 1e9, 1),
+                   "frac": round(dbytes / (dec_rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "batch": DB, "steps": T, "state": "f16"},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * mamba2ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 mixer core.
+ *
+ * The operation (Mamba-2 / structured state-space duality, the method listed
+ * under "References" on page "Mamb2_8B_FP4_Recall_SQ3.25"; that page scores a
+ * pure Mamba-2 8B model on 2048-token windows with the state reset per window,
+ * section "Measured quality"):
+ *
+ *   per sequence b, head h (group g = h / (H/G)), P x N state S:
+ *     S   <- exp(dt_t * A_h) * S + dt_t * x_t (outer) B_t
+ *     y_t  = S . C_t + D_h * x_t                 (y_t sees token t's update)
+ *
+ * optionally preceded by a causal depthwise conv1d of width 4 + SiLU over the
+ * xBC channels (the "convolution caches" of section "Storage and runtime
+ * memory") and followed by a gated RMSNorm  out = g / sqrt(mean(g^2)+eps) * w,
+ * g = y * silu(z)  (the "pinned RMSNorm configuration" of section "Compatible
+ * reference environment").  The one-token decode step stores the state to
+ * binary16 after every token when the resident state is f16 ("A recurrent row
+ * is requantized each token", section "Representation", paragraph "State").
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to caller-owned memory, dense and
+ *    row-major in the layouts given below, 16-byte aligned.  The library
+ *    allocates nothing and keeps no per-call state outside the workspace.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *    asynchronous on that stream; results are ready when the stream is.
+ *  - Return value: MAMBA2_OK (0) or a negative MAMBA2_E* code.  Arguments are
+ *    validated on the host before anything is enqueued; on error nothing is
+ *    enqueued and no output is touched.  There is no fallback path: a shape
+ *    the kernels do not cover returns MAMBA2_EUNSUPPORTED.
+ *  - NaN/Inf in the inputs propagate to the outputs; they are not errors.
+ *  - Inputs and outputs must not overlap, except where stated (in place).
+ *  - Thread safety: calls on different streams may run concurrently if they
+ *    use different workspaces.
+ */
+#ifndef MAMBA2SSD_H
+#define MAMBA2SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA2_ABI_VERSION 1
+
+enum {
+    MAMBA2_OK = 0,
+    MAMBA2_EINVAL = -1,        /* bad pointer, dimension, length or aliasing   */
+    MAMBA2_EUNSUPPORTED = -2,  /* valid request with no kernel for it          */
+    MAMBA2_EALIGN = -3,        /* a pointer is not 16-byte aligned             */
+    MAMBA2_EWORKSPACE = -4,    /* workspace missing or too small               */
+    MAMBA2_EHIP = -5           /* the HIP runtime refused a launch             */
+};
+
+enum { MAMBA2_F32 = 0, MAMBA2_F16 = 1 };
+
+typedef struct mamba2_dims {
+    int32_t batch;       /* B  sequences                                        */
+    int32_t seqlen;      /* L  tokens per sequence (window); ignored by decode  */
+    int32_t nheads;      /* H                                                    */
+    int32_t headdim;     /* P  (kernels: 64)                                     */
+    int32_t dstate;      /* N  (kernels: 16, 64 or 128)                          */
+    int32_t ngroups;     /* G  (H % G == 0; head h uses group h / (H/G))         */
+    int32_t chunk;       /* Q  chunk length of the window scan: 64, 128 or 256   */
+    int32_t conv_width;  /* 0: x, B, C given; 4: fused conv1d(4)+SiLU over xBC  */
+    int32_t norm_group;  /* 0: output y; >0: gated RMSNorm over groups of this
+                            many consecutive channels (must divide H*P)         */
+    int32_t io_dtype;    /* MAMBA2_F16 or MAMBA2_F32 for x/dt/B/C/xBC/z/y       */
+    int32_t state_dtype; /* resident decode state: MAMBA2_F32 or MAMBA2_F16     */
+    float norm_eps;      /* epsilon inside the RMSNorm square root              */
+} mamba2_dims;
+
+/* ------------------------------------------------------------------------ */
+/* Whole-window chunked scan (the state-space-dual form).
+ *
+ * Layouts (io = io_dtype):
+ *   conv_width == 0:  x (B,L,H,P) io;  B, C (B,L,G,N) io
+ *   conv_width == 4:  xBC (B,L,H*P+2*G*N) io, raw pre-conv activations with
+ *                     channel order x | B | C (x channel h*P+p, B/C channel
+ *                     g*N+n); conv_w (H*P+2*G*N, 4) f32 with tap 3 applied to
+ *                     the current token and tap 3-k to the token k back;
+ *                     conv_b (H*P+2*G*N) f32 or NULL (zero);
+ *                     conv_state_in (B, H*P+2*G*N, 3) io or NULL (zero history,
+ *                     a window reset), the 3 raw tokens preceding the window,
+ *                     oldest first; conv_state_out same shape or NULL: the last
+ *                     3 raw tokens before seqlens[b].
+ *   dt (B,L,H) io, already positive (no bias, softplus or clamp is applied)
+ *   A, D (H) f32
+ *   state_in  (B,H,P,N) f32 or NULL (zero initial state)
+ *   state_out (B,H,P,N) f32 or NULL: state after token seqlens[b]-1
+ *   seqlens   device int32 (B) or NULL (all L); each value is clamped to
+ *             [0, L].  Rows t >= seqlens[b] of y are not written.
+ *   norm_group == 0: y (B,L,H*P) io receives y.
+ *   norm_group  > 0: z (B,L,H*P) io and norm_w (H*P) f32 are required and
+ *             y receives the gated RMSNorm output.
+ *   ws, ws_bytes: workspace of at least mamba2_window_workspace_bytes()
+ *             bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE.  The
+ *             library leaves it ready for the next call on the same stream; it
+ *             must not be shared by calls that may overlap.
+ */
+typedef struct mamba2_window_io {
+    const void* x;
+    const void* B;
+    const void* C;
+    const void* xBC;
+    const float* conv_w;
+    const float* conv_b;
+    const void* conv_state_in;
+    void* conv_state_out;
+    const void* dt;
+    const float* A;
+    const float* D;
+    const float* state_in;
+    float* state_out;
+    const int32_t* seqlens;
+    const void* z;
+    const float* norm_w;
+    void* y;
+} mamba2_window_io;
+
+/* Workspace size for a window call with these dims (host only, no GPU call).
+ * Errors: MAMBA2_EINVAL (NULL argument or invalid dims), MAMBA2_EUNSUPPORTED. */
+int32_t mamba2_window_workspace_bytes(const mamba2_dims* dims, size_t* bytes);
+
+/* Runs the window scan.  Errors: EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE,
+ * EHIP. */
+int32_t mamba2_conv_scan_window(const mamba2_dims* dims, const mamba2_window_io* io,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* One-token recurrent step for B sequences (dims.seqlen is ignored).
+ *   x (B,H,P) io; dt (B,H) io (positive); B, C (B,G,N) io; A, D (H) f32
+ *   state (B,H,P,N) in state_dtype, read and updated IN PLACE
+ *   y (B,H,P) io
+ * With an f16 resident state the step is evaluated in binary32 as
+ *   a = (float)exp((double)dt * (double)A);  u = dt*x;  v = u*B[n];
+ *   s = fmaf(a, S_old, v);  y accumulates s*C[n];  S_new = f16_rne(s)
+ * (y uses the pre-store value s).  With an f32 state S_new = s.
+ * Errors: EINVAL, EUNSUPPORTED, EALIGN, EHIP. */
+typedef struct mamba2_decode_io {
+    const void* x;
+    const void* dt;
+    const void* B;
+    const void* C;
+    const float* A;
+    const float* D;
+    void* state;
+    void* y;
+} mamba2_decode_io;
+
+int32_t mamba2_decode_step(const mamba2_dims* dims, const mamba2_decode_io* io, void* stream);
+
+/* State load/store between f32 (B,H,P,N) and the resident state_dtype
+ * (f16: round to nearest even, subnormals kept; f32: copy).  src and dst must
+ * not overlap.  Errors: EINVAL, EUNSUPPORTED, EALIGN, EHIP. */
+int32_t mamba2_state_load(const mamba2_dims* dims, const float* src_f32, void* dst_resident, void* stream);
+int32_t mamba2_state_store(const mamba2_dims* dims, const void* src_resident, float* dst_f32, void* stream);
+
+/* ------------------------------------------------------------------------ */
+int32_t mamba2_abi_version(void);
+/* Static string for a status code (never NULL). */
+const char* mamba2_status_str(int32_t status);
+/* The hipError_t of the last MAMBA2_EHIP returned on this thread (0 if none). */
+int32_t mamba2_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MAMBA2SSD_H */

@@ -1,0 +1,197 @@
+"""MI355X (gfx950) Mamba-2 mixer core: Python binding of libmamba2ssd.so.
+
+Argument marshalling only: every step of the scan, convolution, norm and
+decode runs in the HIP kernels behind the C ABI declared in
+``include/mamba2ssd.h``.  PyTorch provides device memory and the stream.
+There is no CPU or PyTorch fallback: if the library is missing, every entry
+point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "F16", "F32", "Dims", "Mamba2Error", "library_path", "load_library",
+    "window_workspace_bytes", "alloc_workspace", "conv_scan_window", "decode_step",
+    "state_load", "state_store", "abi_version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmamba2ssd.so")
+
+F32, F16 = 0, 1
+_STATUS = {0: "ok", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EALIGN", -4: "EWORKSPACE", -5: "EHIP"}
+
+
+class Mamba2Error(RuntimeError):
+    def __init__(self, fn, status, lib):
+        self.status = status
+        msg = lib.mamba2_status_str(status).decode()
+        if status == -5:
+            msg += f" (hipError {lib.mamba2_last_hip_error()})"
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {msg}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk",
+        "conv_width", "norm_group", "io_dtype", "state_dtype")] + [("norm_eps", ctypes.c_float)]
+
+
+class _WindowIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "B", "C", "xBC", "conv_w", "conv_b", "conv_state_in", "conv_state_out", "dt", "A", "D",
+        "state_in", "state_out", "seqlens", "z", "norm_w", "y")]
+
+
+class _DecodeIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x", "dt", "B", "C", "A", "D", "state", "y")]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmamba2ssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950); there is no fallback path")
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(Dims)
+        vp = ctypes.c_void_p
+        lib.mamba2_abi_version.restype = ctypes.c_int32
+        lib.mamba2_status_str.restype = ctypes.c_char_p
+        lib.mamba2_status_str.argtypes = [ctypes.c_int32]
+        lib.mamba2_last_hip_error.restype = ctypes.c_int32
+        lib.mamba2_window_workspace_bytes.restype = ctypes.c_int32
+        lib.mamba2_window_workspace_bytes.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
+        lib.mamba2_conv_scan_window.restype = ctypes.c_int32
+        lib.mamba2_conv_scan_window.argtypes = [dp, ctypes.POINTER(_WindowIO), vp, ctypes.c_size_t, vp]
+        lib.mamba2_decode_step.restype = ctypes.c_int32
+        lib.mamba2_decode_step.argtypes = [dp, ctypes.POINTER(_DecodeIO), vp]
+        lib.mamba2_state_load.restype = ctypes.c_int32
+        lib.mamba2_state_load.argtypes = [dp, vp, vp, vp]
+        lib.mamba2_state_store.restype = ctypes.c_int32
+        lib.mamba2_state_store.argtypes = [dp, vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return load_library().mamba2_abi_version()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Mamba2Error(fn, status, load_library())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _io_dtype(t):
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported I/O dtype {t.dtype}")
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=256, conv_width=0, norm_group=0,
+              io_dtype=F16, state_dtype=F32, norm_eps=1e-5) -> Dims:
+    return Dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, conv_width, norm_group, io_dtype,
+                state_dtype, norm_eps)
+
+
+def window_workspace_bytes(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mamba2_window_workspace_bytes", load_library().mamba2_window_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_workspace(dims: Dims, device) -> torch.Tensor:
+    """A zero-filled workspace for window calls with these dims (reusable
+    across calls on one stream)."""
+    return torch.zeros(window_workspace_bytes(dims), dtype=torch.uint8, device=device)
+
+
+def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None, conv_w=None, conv_b=None,
+                     conv_state_in=None, conv_state_out=None, state_in=None, state_out=None, seqlens=None,
+                     z=None, norm_w=None, chunk=256, norm_group=0, norm_eps=1e-5, ngroups=None, dstate=None,
+                     headdim=None, stream=None):
+    """Whole-window scan.  Shapes: x (B,L,H,P), B/C (B,L,G,N) -- or xBC
+    (B,L,H*P+2*G*N) with conv_w (H*P+2*G*N, 4) for the fused conv --, dt
+    (B,L,H), A/D (H) f32, y (B,L,H*P) (or (B,L,H,P)).  See include/mamba2ssd.h."""
+    Bsz, L, H = dt.shape
+    conv = xBC is not None
+    if conv:
+        if ngroups is None or dstate is None:
+            raise ValueError("the fused conv needs ngroups and dstate")
+        P = 64 if headdim is None else headdim
+        G, N = ngroups, dstate
+    else:
+        P = x.shape[3]
+        G, N = B.shape[2], B.shape[3]
+    dims = make_dims(Bsz, L, H, P, N, G, chunk, 4 if conv else 0, norm_group, _io_dtype(dt), F32, norm_eps)
+    io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), _ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in),
+                   _ptr(conv_state_out), _ptr(dt), _ptr(A), _ptr(D), _ptr(state_in), _ptr(state_out),
+                   _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y))
+    _check("mamba2_conv_scan_window",
+           load_library().mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
+                                                  workspace.numel(), _stream(dt, stream)))
+
+
+def decode_step(x, dt, B, C, A, D, state, y, stream=None):
+    """One token for each of B sequences: x (B,H,P), dt (B,H), B/C (B,G,N),
+    A/D (H) f32, state (B,H,P,N) f16 or f32 updated in place, y (B,H,P)."""
+    Bsz, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    sd = F16 if state.dtype == torch.float16 else F32
+    dims = make_dims(Bsz, 1, H, P, N, G, 256, 0, 0, _io_dtype(x), sd)
+    io = _DecodeIO(_ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(state), _ptr(y))
+    _check("mamba2_decode_step", load_library().mamba2_decode_step(ctypes.byref(dims), ctypes.byref(io),
+                                                                   _stream(x, stream)))
+
+
+def _state_dims(t, resident_dtype):
+    Bsz, H, P, N = t.shape
+    sd = F16 if resident_dtype == torch.float16 else F32
+    return make_dims(Bsz, 1, H, P, N, 1, 256, 0, 0, F16, sd)
+
+
+def state_load(src_f32, dst_resident, stream=None):
+    """f32 (B,H,P,N) -> resident state (f16: round to nearest even)."""
+    dims = _state_dims(src_f32, dst_resident.dtype)
+    _check("mamba2_state_load", load_library().mamba2_state_load(ctypes.byref(dims), _ptr(src_f32),
+                                                                 _ptr(dst_resident), _stream(src_f32, stream)))
+
+
+def state_store(src_resident, dst_f32, stream=None):
+    """Resident state -> f32 (B,H,P,N)."""
+    dims = _state_dims(dst_f32, src_resident.dtype)
+    _check("mamba2_state_store", load_library().mamba2_state_store(ctypes.byref(dims), _ptr(src_resident),
+                                                                   _ptr(dst_f32), _stream(dst_f32, stream)))

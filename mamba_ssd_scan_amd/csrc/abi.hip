@@ -1,0 +1,206 @@
+// C ABI of the Mamba-2 mixer core: host-side validation and dispatch.
+// Every request is checked here before anything is enqueued; a request the
+// kernels do not cover returns MAMBA2_EUNSUPPORTED (there is no fallback).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mamba2ssd.h"
+
+namespace m2 {
+hipError_t launch_decode(int io_f16, int state_f16, int N, const void* x, const void* dt, const void* Bm,
+                         const void* Cm, const float* A, const float* D, void* state, void* y, int Bsz,
+                         int H, int P, int G, hipStream_t st);
+hipError_t launch_state_convert(int to_resident, int state_f16, const void* src, void* dst, size_t n,
+                                hipStream_t st);
+size_t window_workspace_bytes(const mamba2_dims& d);
+hipError_t launch_window(const mamba2_dims& d, const mamba2_window_io& io, void* ws, hipStream_t st);
+}  // namespace m2
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MAMBA2_OK;
+  g_last_hip_error = (int32_t)e;
+  return MAMBA2_EHIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  const char* lo;
+  const char* hi;
+};
+Range rng(const void* p, size_t bytes) { return Range{(const char*)p, (const char*)p + bytes}; }
+bool overlap(Range a, Range b) {
+  if (!a.lo || !b.lo || a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+size_t esize(int32_t dtype) { return dtype == MAMBA2_F16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.
+int32_t check_common(const mamba2_dims* d) {
+  if (!d) return MAMBA2_EINVAL;
+  if (d->batch < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 || d->ngroups < 1)
+    return MAMBA2_EINVAL;
+  if (d->nheads % d->ngroups != 0) return MAMBA2_EINVAL;
+  if (d->io_dtype != MAMBA2_F16 && d->io_dtype != MAMBA2_F32) return MAMBA2_EINVAL;
+  if (d->state_dtype != MAMBA2_F16 && d->state_dtype != MAMBA2_F32) return MAMBA2_EINVAL;
+  if (d->dstate != 16 && d->dstate != 64 && d->dstate != 128) return MAMBA2_EUNSUPPORTED;
+  // Every tensor stays well inside 2^31 elements per sequence-head slice and
+  // 2^62 bytes overall.
+  if ((int64_t)d->headdim * d->dstate > (1 << 24)) return MAMBA2_EUNSUPPORTED;
+  return MAMBA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mamba2_abi_version(void) { return MAMBA2_ABI_VERSION; }
+
+const char* mamba2_status_str(int32_t s) {
+  switch (s) {
+    case MAMBA2_OK: return "ok";
+    case MAMBA2_EINVAL: return "invalid argument";
+    case MAMBA2_EUNSUPPORTED: return "unsupported configuration";
+    case MAMBA2_EALIGN: return "pointer not 16-byte aligned";
+    case MAMBA2_EWORKSPACE: return "workspace missing or too small";
+    case MAMBA2_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t mamba2_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t mamba2_decode_step(const mamba2_dims* d, const mamba2_decode_io* io, void* stream) {
+  int32_t s = check_common(d);
+  if (s != MAMBA2_OK) return s;
+  if (!io) return MAMBA2_EINVAL;
+  if (!io->x || !io->dt || !io->B || !io->C || !io->A || !io->D || !io->state || !io->y) return MAMBA2_EINVAL;
+  if (d->headdim % 8 != 0) return MAMBA2_EUNSUPPORTED;
+  if (!aligned16(io->x) || !aligned16(io->B) || !aligned16(io->C) || !aligned16(io->state) ||
+      !aligned16(io->y))
+    return MAMBA2_EALIGN;
+  if (((uintptr_t)io->dt % esize(d->io_dtype)) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3))
+    return MAMBA2_EALIGN;
+  const size_t es = esize(d->io_dtype);
+  const size_t BH = (size_t)d->batch * d->nheads;
+  const size_t BG = (size_t)d->batch * d->ngroups;
+  Range ry = rng(io->y, BH * d->headdim * es);
+  Range rs = rng(io->state, BH * d->headdim * d->dstate * esize(d->state_dtype));
+  Range ins[] = {rng(io->x, BH * d->headdim * es), rng(io->dt, BH * es), rng(io->B, BG * d->dstate * es),
+                 rng(io->C, BG * d->dstate * es), rng(io->A, d->nheads * 4), rng(io->D, d->nheads * 4)};
+  if (overlap(ry, rs)) return MAMBA2_EINVAL;
+  for (const Range& r : ins)
+    if (overlap(r, ry) || overlap(r, rs)) return MAMBA2_EINVAL;
+  return hip_status(m2::launch_decode(d->io_dtype == MAMBA2_F16, d->state_dtype == MAMBA2_F16, d->dstate,
+                                      io->x, io->dt, io->B, io->C, io->A, io->D, io->state, io->y, d->batch,
+                                      d->nheads, d->headdim, d->ngroups, (hipStream_t)stream));
+}
+
+static int32_t state_convert(const mamba2_dims* d, const void* src, void* dst, int to_resident, void* stream) {
+  int32_t s = check_common(d);
+  if (s != MAMBA2_OK) return s;
+  if (!src || !dst) return MAMBA2_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return MAMBA2_EALIGN;
+  const size_t n = (size_t)d->batch * d->nheads * d->headdim * d->dstate;
+  const size_t rb = n * esize(d->state_dtype);
+  Range a = rng(src, to_resident ? n * 4 : rb), b = rng(dst, to_resident ? rb : n * 4);
+  if (overlap(a, b)) return MAMBA2_EINVAL;
+  return hip_status(m2::launch_state_convert(to_resident, d->state_dtype == MAMBA2_F16, src, dst, n,
+                                             (hipStream_t)stream));
+}
+
+int32_t mamba2_state_load(const mamba2_dims* d, const float* src, void* dst, void* stream) {
+  return state_convert(d, src, dst, 1, stream);
+}
+
+int32_t mamba2_state_store(const mamba2_dims* d, const void* src, float* dst, void* stream) {
+  return state_convert(d, src, dst, 0, stream);
+}
+
+// Validation for the window scan.  Returns OK when the request is covered.
+static int32_t check_window(const mamba2_dims* d) {
+  int32_t s = check_common(d);
+  if (s != MAMBA2_OK) return s;
+  if (d->seqlen < 1) return MAMBA2_EINVAL;
+  if (d->conv_width != 0 && d->conv_width != 4) return MAMBA2_EUNSUPPORTED;
+  if (d->norm_group < 0) return MAMBA2_EINVAL;
+  if (d->norm_group > 0 && (d->nheads * d->headdim) % d->norm_group != 0) return MAMBA2_EINVAL;
+  // the norm epilogue reduces whole heads: a group must be a multiple of P
+  if (d->norm_group > 0 && d->norm_group % d->headdim != 0) return MAMBA2_EUNSUPPORTED;
+  if (d->norm_group > 0 && !(d->norm_eps >= 0.f)) return MAMBA2_EINVAL;
+  // the norm finish keeps one scale per group of a token in LDS (256 slots)
+  if (d->norm_group > 0 && (d->nheads * d->headdim) / d->norm_group > 256) return MAMBA2_EUNSUPPORTED;
+  if (d->headdim != 64) return MAMBA2_EUNSUPPORTED;
+  if (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) return MAMBA2_EUNSUPPORTED;
+  const int64_t nchunks = ((int64_t)d->seqlen + d->chunk - 1) / d->chunk;
+  const int64_t items = nchunks * d->batch * d->nheads;
+  if (items > (int64_t)1 << 30) return MAMBA2_EUNSUPPORTED;
+  return MAMBA2_OK;
+}
+
+int32_t mamba2_window_workspace_bytes(const mamba2_dims* d, size_t* bytes) {
+  if (!bytes) return MAMBA2_EINVAL;
+  int32_t s = check_window(d);
+  if (s != MAMBA2_OK) return s;
+  *bytes = m2::window_workspace_bytes(*d);
+  return MAMBA2_OK;
+}
+
+int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io, void* ws, size_t ws_bytes,
+                                void* stream) {
+  int32_t s = check_window(d);
+  if (s != MAMBA2_OK) return s;
+  if (!io) return MAMBA2_EINVAL;
+  const size_t es = esize(d->io_dtype);
+  const size_t Bsz = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+  const size_t conv_dim = H * P + 2 * G * N;
+  // required pointers
+  if (!io->dt || !io->A || !io->D || !io->y) return MAMBA2_EINVAL;
+  if (d->conv_width == 0 && (!io->x || !io->B || !io->C)) return MAMBA2_EINVAL;
+  if (d->conv_width == 4 && (!io->xBC || !io->conv_w)) return MAMBA2_EINVAL;
+  if (d->norm_group > 0 && (!io->z || !io->norm_w)) return MAMBA2_EINVAL;
+  // alignment
+  const void* vec[] = {io->x, io->B, io->C, io->xBC, io->z, io->y, io->state_in, io->state_out, io->conv_w,
+                       io->norm_w};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return MAMBA2_EALIGN;
+  if (((uintptr_t)io->dt % es) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3) ||
+      ((uintptr_t)io->seqlens & 3) || ((uintptr_t)io->conv_b & 3) || ((uintptr_t)io->conv_state_in % es) ||
+      ((uintptr_t)io->conv_state_out % es))
+    return MAMBA2_EALIGN;
+  // workspace
+  const size_t need = m2::window_workspace_bytes(*d);
+  if (!ws || ws_bytes < need) return MAMBA2_EWORKSPACE;
+  if ((uintptr_t)ws & 255) return MAMBA2_EALIGN;
+  // aliasing: outputs against inputs and against each other
+  const size_t tok = Bsz * L;
+  Range outs[] = {rng(io->y, tok * H * P * es), rng(io->state_out, Bsz * H * P * N * 4),
+                  rng(io->conv_state_out, d->conv_width ? Bsz * conv_dim * 3 * es : 0), rng(ws, need)};
+  Range ins[] = {rng(io->x, d->conv_width ? 0 : tok * H * P * es),
+                 rng(io->B, d->conv_width ? 0 : tok * G * N * es),
+                 rng(io->C, d->conv_width ? 0 : tok * G * N * es),
+                 rng(io->xBC, d->conv_width ? tok * conv_dim * es : 0),
+                 rng(io->conv_w, d->conv_width ? conv_dim * 4 * 4 : 0),
+                 rng(io->conv_b, d->conv_width ? conv_dim * 4 : 0),
+                 rng(io->conv_state_in, d->conv_width ? Bsz * conv_dim * 3 * es : 0),
+                 rng(io->dt, tok * H * es), rng(io->A, H * 4), rng(io->D, H * 4),
+                 rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4),
+                 rng(io->z, d->norm_group ? tok * H * P * es : 0),
+                 rng(io->norm_w, d->norm_group ? H * P * 4 : 0)};
+  const size_t nout = sizeof(outs) / sizeof(outs[0]);
+  for (size_t i = 0; i < nout; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return MAMBA2_EINVAL;
+    for (size_t j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return MAMBA2_EINVAL;
+  }
+  return hip_status(m2::launch_window(*d, *io, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

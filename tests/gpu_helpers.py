@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU tests and the benchmark: run the HIP path from
+numpy inputs and measure errors against the oracle.  No arithmetic of the
+method lives here."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mamba_ssd_scan_amd as m2
+
+DEV = torch.device("cuda:0")
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def slice_err(got, ref, nlead):
+    """max over slices of max|got-ref| / max|ref|; a slice is one index of the
+    first `nlead` axes (e.g. (b, h)).  NaN/Inf anywhere in got -> inf."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    lead = int(np.prod(got.shape[:nlead]))
+    g = got.reshape(lead, -1)
+    r = ref.reshape(lead, -1)
+    den = np.maximum(np.abs(r).max(axis=1), 1e-30)
+    return float((np.abs(g - r).max(axis=1) / den).max())
+
+
+def run_window(inp, chunk, seqlens=None, state_in=None, want_state=True, ws=None, y_fill=None):
+    """Run the window scan on the GPU from numpy inputs x, dt, B, C, A, D."""
+    x, dt, Bm, Cm = (to_dev(inp[k]) for k in ("x", "dt", "B", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    Bsz, L, H, P = inp["x"].shape
+    G, N = inp["B"].shape[2], inp["B"].shape[3]
+    y = torch.empty((Bsz, L, H * P), dtype=x.dtype, device=DEV)
+    if y_fill is not None:
+        y.fill_(y_fill)
+    hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=DEV) if want_state else None
+    sl = torch.tensor(seqlens, dtype=torch.int32, device=DEV) if seqlens is not None else None
+    h0 = to_dev(np.asarray(state_in, np.float32)) if state_in is not None else None
+    if ws is None:
+        dims = m2.make_dims(Bsz, L, H, P, N, G, chunk, io_dtype=m2.F16 if x.dtype == torch.float16 else m2.F32)
+        ws = m2.alloc_workspace(dims, DEV)
+    m2.conv_scan_window(dt, A, D, y, ws, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl, chunk=chunk)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().reshape(Bsz, L, H, P), (hT.cpu().numpy() if want_state else None)
+
+
+def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=None, state_in=None,
+              want_conv_state=True):
+    xBC = to_dev(inp["xBC"])
+    Bsz, L, Cn = inp["xBC"].shape
+    y = torch.empty((Bsz, L, H * P), dtype=xBC.dtype, device=DEV)
+    hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=DEV)
+    cso = torch.empty((Bsz, Cn, 3), dtype=xBC.dtype, device=DEV) if want_conv_state else None
+    csi = to_dev(conv_state_in) if conv_state_in is not None else None
+    h0 = to_dev(np.asarray(state_in, np.float32)) if state_in is not None else None
+    sl = torch.tensor(seqlens, dtype=torch.int32, device=DEV) if seqlens is not None else None
+    dims = m2.make_dims(Bsz, L, H, P, N, G, chunk, conv_width=4, norm_group=norm_group,
+                        io_dtype=m2.F16 if xBC.dtype == torch.float16 else m2.F32)
+    ws = m2.alloc_workspace(dims, DEV)
+    m2.conv_scan_window(to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xBC,
+                        conv_w=to_dev(inp["conv_w"]), conv_b=to_dev(inp["conv_b"]), conv_state_in=csi,
+                        conv_state_out=cso, state_in=h0, state_out=hT, seqlens=sl,
+                        z=to_dev(inp["z"]) if norm_group else None,
+                        norm_w=to_dev(inp["norm_w"]) if norm_group else None,
+                        chunk=chunk, norm_group=norm_group, ngroups=G, dstate=N, headdim=P)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), hT.cpu().numpy(), (cso.cpu().numpy() if want_conv_state else None)

@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every entry point the header declares, and validates arguments before
+enqueuing anything (the pointers below are never dereferenced: each case
+is refused on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_scan_amd as m2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "mamba2ssd.h")).read()
+    return sorted(set(re.findall(r"\b(mamba2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m2.load_library()
+    syms = header_symbols()
+    assert len(syms) >= 8
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_version_and_status_strings():
+    lib = m2.load_library()
+    assert m2.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.mamba2_status_str(code)
+    assert lib.mamba2_status_str(77) == b"unknown status"
+
+
+def layer_dims(**kw):
+    base = dict(batch=1, seqlen=2048, nheads=128, headdim=64, dstate=128, ngroups=8, chunk=256)
+    base.update(kw)
+    return m2.make_dims(**base)
+
+
+def test_workspace_size_formula():
+    # control block + one flag and one fp32 P x N hand-off state per (chunk, sequence, head)
+    n = m2.window_workspace_bytes(layer_dims())
+    items = 8 * 128
+    up = lambda v: (v + 255) // 256 * 256
+    assert n == up(up(256 + items * 4) + items * 64 * 128 * 4)
+    n2 = m2.window_workspace_bytes(layer_dims(batch=4, norm_group=8192, conv_width=4))
+    items = 8 * 4 * 128
+    assert n2 == up(up(up(256 + items * 4) + items * 64 * 128 * 4) + 4 * 2048 * 128 * 4)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(headdim=32), -2), (dict(dstate=96), -2), (dict(chunk=100), -2), (dict(conv_width=3), -2),
+    (dict(nheads=100, ngroups=8), -1), (dict(batch=0), -1), (dict(seqlen=0), -1),
+    (dict(norm_group=1000), -1), (dict(norm_group=32), -2), (dict(norm_group=-1), -1),
+    (dict(io_dtype=7), -1),
+])
+def test_workspace_query_rejects(kw, code):
+    lib = m2.load_library()
+    n = ctypes.c_size_t(0)
+    assert lib.mamba2_window_workspace_bytes(ctypes.byref(layer_dims(**kw)), ctypes.byref(n)) == code
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below is refused on the host
+
+
+def window_io(**over):
+    L, H, P, N, G = 2048, 128, 64, 128, 8
+    MB = 1 << 26
+    base = dict(x=FAKE, B=FAKE + MB, C=FAKE + 2 * MB, dt=FAKE + 3 * MB, A=FAKE + 4 * MB, D=FAKE + 4 * MB + 4096,
+                y=FAKE + 8 * MB)
+    base.update(over)
+    return m2._WindowIO(**base)
+
+
+def call_window(io, dims=None, ws=FAKE + (1 << 30), ws_bytes=None):
+    lib = m2.load_library()
+    dims = dims or layer_dims()
+    if ws_bytes is None:
+        ws_bytes = m2.window_workspace_bytes(dims)
+    return lib.mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_window_validation_codes():
+    assert call_window(window_io(x=None)) == -1
+    assert call_window(window_io(y=None)) == -1
+    assert call_window(window_io(x=FAKE + 2)) == -3
+    assert call_window(window_io(), ws=None) == -4
+    assert call_window(window_io(), ws_bytes=1024) == -4
+    assert call_window(window_io(), ws=FAKE + (1 << 30) + 16) == -3
+    # output overlapping an input
+    assert call_window(window_io(y=FAKE + 1024)) == -1
+    # workspace overlapping the output
+    assert call_window(window_io(), ws=FAKE + 8 * (1 << 26)) == -1
+    # fused conv needs xBC and conv weights; the norm needs z and its weight
+    assert call_window(window_io(), dims=layer_dims(conv_width=4)) == -1
+    assert call_window(window_io(), dims=layer_dims(norm_group=8192)) == -1
+
+
+def test_decode_and_state_validation_codes():
+    lib = m2.load_library()
+    d = m2.make_dims(64, 1, 128, 64, 128, 8, 256, state_dtype=m2.F16)
+    MB = 1 << 26
+    io = m2._DecodeIO(FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 3 * MB, FAKE + 4 * MB, FAKE + 5 * MB,
+                      FAKE + 6 * MB, FAKE + 20 * MB)
+    bad = m2._DecodeIO(FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 3 * MB, FAKE + 4 * MB, FAKE + 5 * MB,
+                       FAKE + 6 * MB, FAKE + 6 * MB + 64)
+    assert lib.mamba2_decode_step(ctypes.byref(d), ctypes.byref(bad), None) == -1   # y inside the state
+    null = m2._DecodeIO(FAKE, FAKE + MB, None, FAKE + 3 * MB, FAKE + 4 * MB, FAKE + 5 * MB, FAKE + 6 * MB,
+                        FAKE + 20 * MB)
+    assert lib.mamba2_decode_step(ctypes.byref(d), ctypes.byref(null), None) == -1
+    mis = m2._DecodeIO(FAKE + 8, FAKE + MB, FAKE + 2 * MB, FAKE + 3 * MB, FAKE + 4 * MB, FAKE + 5 * MB,
+                       FAKE + 6 * MB, FAKE + 20 * MB)
+    assert lib.mamba2_decode_step(ctypes.byref(d), ctypes.byref(mis), None) == -3
+    d2 = m2.make_dims(64, 1, 128, 64, 100, 8, 256)
+    assert lib.mamba2_decode_step(ctypes.byref(d2), ctypes.byref(io), None) == -2
+    assert lib.mamba2_state_load(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), None) == -1
+    assert lib.mamba2_state_load(ctypes.byref(d), None, ctypes.c_void_p(FAKE), None) == -1
+    assert lib.mamba2_state_store(ctypes.byref(d), ctypes.c_void_p(FAKE + 2), ctypes.c_void_p(FAKE + MB * 40),
+                                  None) == -3
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        m2._ptr(torch.zeros(4))

@@ -1,0 +1,309 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (fp16 I/O, fp32 accumulate): per-slice max error / slice max magnitude
+<= 2e-3 on y (and on the normed output) and <= 1e-3 on final states; a slice
+is one (sequence, head) -- for the normed output one (sequence, token).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import mamba_ssd_scan_amd as m2  # noqa: E402
+from tests.gpu_helpers import DEV, run_mixer, run_window, slice_err, to_dev  # noqa: E402
+
+Y_TOL, S_TOL = 2e-3, 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rand_window(seed, B, L, H, N, G, dtype=np.float16, dt_mode="wide", P=64):
+    s = synth.WindowShape(B, L, H, P, N, G, 256, dtype, dt_mode)
+    return synth.window_inputs(s, seed)
+
+
+def oracle_window(inp, seqlens=None, state_in=None, nthreads=0):
+    return oracle.ssd_scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], h0=state_in,
+                           seqlens=seqlens, nthreads=nthreads)
+
+
+def check_window(name, inp, chunk, seqlens=None, state_in=None):
+    say(f"[window] {name}: shape x{inp['x'].shape} chunk {chunk} seqlens {seqlens}")
+    y, hT = run_window(inp, chunk, seqlens=seqlens, state_in=state_in, y_fill=12345.0)
+    yr, hr = oracle_window(inp, seqlens, state_in)
+    Bsz = y.shape[0]
+    ey = 0.0
+    for b in range(Bsz):
+        n = seqlens[b] if seqlens is not None else y.shape[1]
+        if n > 0:
+            ey = max(ey, slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)),
+                                   np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2))
+        # rows past the sequence end are untouched
+        assert np.all(y[b, n:] == np.float16(12345.0) if y.dtype == np.float16 else y[b, n:] == 12345.0)
+    es = slice_err(hT, hr, 2)
+    say(f"[window] {name}: y err {ey:.3e}  state err {es:.3e}")
+    assert ey <= Y_TOL and es <= S_TOL
+    return y, hT
+
+
+# ---------------------------------------------------------------------------
+def test_tiny_fp32_scan():
+    s = synth.tiny_scan()
+    check_window("tiny fp32", synth.window_inputs(s, 1000), s.chunk)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("N", [16, 64, 128])
+def test_chunk_sizes_and_state_sizes(chunk, N):
+    inp = rand_window(11 + N + chunk, 1, 300, 8, N, 2)
+    check_window(f"N={N}", inp, chunk)
+
+
+def test_ragged_batch_with_initial_state():
+    inp = rand_window(21, 3, 700, 16, 128, 2)
+    h0 = np.random.default_rng(22).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
+    check_window("ragged+h0", inp, 256, seqlens=[700, 513, 1], state_in=h0)
+
+
+def test_zero_length_sequence_passes_state_through():
+    inp = rand_window(23, 2, 130, 8, 64, 1)
+    h0 = np.random.default_rng(24).standard_normal((2, 8, 64, 64)).astype(np.float32)
+    y, hT = run_window(inp, 64, seqlens=[0, 130], state_in=h0, y_fill=7.0)
+    assert np.all(y[0] == np.float16(7.0))
+    assert np.array_equal(hT[0], h0[0])
+
+
+def test_dt_zero_gives_skip_and_keeps_state():
+    inp = rand_window(25, 1, 512, 8, 128, 2)
+    inp["dt"][:] = 0
+    h0 = np.random.default_rng(26).standard_normal((1, 8, 64, 128)).astype(np.float32)
+    y, hT = run_window(inp, 256, state_in=None)
+    ref = (inp["D"][None, None, :, None].astype(np.float32) * inp["x"].astype(np.float32))
+    assert np.max(np.abs(y.astype(np.float64) - ref.astype(np.float16).astype(np.float64))
+                  / np.maximum(np.abs(ref.astype(np.float16).astype(np.float64)), 6e-5)) <= 2 ** -10
+    assert np.all(hT == 0)
+    _, hT2 = run_window(inp, 256, state_in=h0)
+    assert np.array_equal(hT2, h0)
+
+
+def test_split_window_carry_matches_unsplit():
+    inp = rand_window(27, 1, 1024, 16, 128, 2)
+    y, hT = run_window(inp, 256)
+    for m in (256, 300):
+        a = {k: (v[:, :m] if v.ndim > 1 else v) for k, v in inp.items()}
+        b = {k: (v[:, m:] if v.ndim > 1 else v) for k, v in inp.items()}
+        y1, h1 = run_window(a, 256)
+        y2, h2 = run_window(b, 256, state_in=h1)
+        ey = slice_err(np.transpose(np.concatenate([y1, y2], 1), (0, 2, 1, 3)), np.transpose(y, (0, 2, 1, 3)), 2)
+        es = slice_err(h2, hT, 2)
+        say(f"[split] m={m}: y {ey:.3e} state {es:.3e}")
+        assert ey <= Y_TOL and es <= S_TOL
+
+
+def test_layer_window_full_size():
+    s = synth.layer_window()
+    check_window("layer L=2048", synth.window_inputs(s, 1001), s.chunk)
+
+
+def test_batched_windows_full_size_sampled():
+    s = synth.batched_windows()
+    inp = synth.window_inputs(s, 1002)
+    say(f"[window] batched: x{inp['x'].shape} lengths {s.seqlens}")
+    y, hT = run_window(inp, s.chunk, seqlens=s.seqlens, y_fill=12345.0)
+    for b in (0, 7):      # a full window and the 1955-token partial window
+        sub = {k: (v[b:b + 1] if v.ndim > 1 else v) for k, v in inp.items()}
+        n = s.seqlens[b]
+        yr, hr = oracle_window(sub, [n])
+        ey = slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)), np.transpose(yr[:, :n], (0, 2, 1, 3)), 2)
+        es = slice_err(hT[b:b + 1], hr, 2)
+        say(f"[window] batched seq {b} (len {n}): y {ey:.3e} state {es:.3e}")
+        assert ey <= Y_TOL and es <= S_TOL
+        assert np.all(y[b, n:] == np.float16(12345.0))
+
+
+def test_sequence_alone_equals_sequence_in_batch():
+    inp = rand_window(31, 4, 600, 16, 128, 2)
+    y, hT = run_window(inp, 256, seqlens=[600, 600, 431, 600])
+    sub = {k: (v[2:3] if v.ndim > 1 else v) for k, v in inp.items()}
+    y1, h1 = run_window(sub, 256, seqlens=[431])
+    assert np.array_equal(y1[0, :431], y[2, :431]) and np.array_equal(h1[0], hT[2])
+
+
+def test_deterministic_and_workspace_reuse():
+    inp = rand_window(33, 2, 777, 16, 128, 2)
+    dims = m2.make_dims(2, 777, 16, 64, 128, 2, 256)
+    ws = m2.alloc_workspace(dims, DEV)
+    outs = [run_window(inp, 256, ws=ws) for _ in range(3)]
+    for y, h in outs[1:]:
+        assert np.array_equal(y, outs[0][0]) and np.array_equal(h, outs[0][1])
+    # a smaller problem through the same workspace, then the first again
+    small = {k: (v[:1, :100] if v.ndim > 1 else v) for k, v in inp.items()}
+    ys, hs = run_window(small, 256, ws=ws)
+    yr, hr = oracle_window(small)
+    assert slice_err(hs, hr, 2) <= S_TOL
+    y3, h3 = run_window(inp, 256, ws=ws)
+    assert np.array_equal(y3, outs[0][0]) and np.array_equal(h3, outs[0][1])
+
+
+# ---- fused conv + gated norm ----------------------------------------------------
+def small_mixer(seed, B, L, H, G, N):
+    s = synth.WindowShape(B, L, H, 64, N, G, 256, np.float16, "wide")
+    return synth.mixer_inputs(s, seed)
+
+
+@pytest.mark.parametrize("norm_group", [0, 1024, 512])
+def test_mixer_core_small(norm_group):
+    H, P, G, N, L, Bsz = 16, 64, 2, 128, 300, 2
+    inp = small_mixer(41, Bsz, L, H, G, N)
+    Cn = H * P + 2 * G * N
+    csi = (np.random.default_rng(42).standard_normal((Bsz, Cn, 3))).astype(np.float16)
+    lens = [300, 157]
+    say(f"[mixer] small norm_group={norm_group}")
+    y, hT, cso = run_mixer(inp, H, P, G, N, 256, norm_group, seqlens=lens, conv_state_in=csi)
+    out_r, h_r, cs_r = oracle.mixer_core(inp["xBC"], inp["conv_w"], inp["conv_b"], inp["dt"], inp["A"], inp["D"],
+                                         inp["z"], inp["norm_w"], H, P, G, N, norm_group or H * P,
+                                         conv_state=csi, seqlens=lens)
+    if norm_group == 0:
+        u, _ = oracle.conv_silu(inp["xBC"], inp["conv_w"], inp["conv_b"], csi, lens)
+        u = np.nan_to_num(u)
+        yr, _ = oracle.ssd_scan(u[..., :H * P].reshape(Bsz, L, H, P), inp["dt"], inp["A"],
+                                u[..., H * P:H * P + G * N].reshape(Bsz, L, G, N),
+                                u[..., H * P + G * N:].reshape(Bsz, L, G, N), inp["D"], seqlens=lens)
+        for b, n in enumerate(lens):
+            e = slice_err(np.transpose(y[b:b + 1, :n].reshape(1, n, H, P), (0, 2, 1, 3)),
+                          np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2)
+            say(f"[mixer] y seq {b}: {e:.3e}")
+            assert e <= Y_TOL
+    else:
+        for b, n in enumerate(lens):
+            # slice = (sequence, norm group) over all tokens of the sequence
+            got = y[b, :n].reshape(n, -1, norm_group).transpose(1, 0, 2)
+            ref = out_r[b, :n].reshape(n, -1, norm_group).transpose(1, 0, 2)
+            e = slice_err(got, ref, 1)
+            say(f"[mixer] out seq {b}: {e:.3e} (per token and group: {slice_err(got.transpose(1, 0, 2), ref.transpose(1, 0, 2), 2):.3e})")
+            assert e <= Y_TOL
+    es = slice_err(hT, h_r, 2)
+    assert es <= S_TOL, es
+    assert np.array_equal(cso.astype(np.float64), cs_r)
+
+
+def test_mixer_core_full_size_sampled():
+    s = synth.mixer_window()
+    inp = synth.mixer_inputs(s, 1004)
+    H, P, G, N = s.nheads, s.headdim, s.ngroups, s.dstate
+    say("[mixer] full size B=4 L=2048")
+    y, hT, _ = run_mixer(inp, H, P, G, N, s.chunk, H * P, want_conv_state=False)
+    for b in (0, 3):
+        sub = {k: (v[b:b + 1] if (v.ndim > 1 and k in ("xBC", "dt", "z")) else v) for k, v in inp.items()}
+        out_r, h_r, _ = oracle.mixer_core(sub["xBC"], inp["conv_w"], inp["conv_b"], sub["dt"], inp["A"], inp["D"],
+                                          sub["z"], inp["norm_w"], H, P, G, N, H * P)
+        e = slice_err(y[b][None], out_r[0][None], 1)
+        es = slice_err(hT[b:b + 1], h_r, 2)
+        say(f"[mixer] seq {b}: out {e:.3e} state {es:.3e}")
+        assert e <= Y_TOL and es <= S_TOL
+
+
+# ---- decode --------------------------------------------------------------------
+def decode_inputs(seed, T, Bsz, H, N, G, P=64):
+    prm = synth.decode_params(seed, Bsz, H, P, N)
+    steps = [synth.decode_step_inputs(seed, t, prm["dt0"], Bsz, H, P, N, G) for t in range(T)]
+    stack = {k: np.stack([s[k] for s in steps]) for k in ("x", "dt", "B", "C")}
+    return prm, stack
+
+
+@pytest.mark.parametrize("N", [16, 64, 128])
+def test_decode_f16_state_small(N):
+    T, Bsz, H, G = 8, 3, 16, 2
+    prm, st = decode_inputs(51 + N, T, Bsz, H, N, G)
+    s16 = torch.empty((Bsz, H, 64, N), dtype=torch.float16, device=DEV)
+    m2.state_load(to_dev(prm["state"]), s16)
+    bits = prm["state"].astype(np.float16).view(np.uint16).copy()
+    torch.cuda.synchronize()
+    assert np.array_equal(s16.cpu().numpy().view(np.uint16), bits)
+    yg = []
+    for t in range(T):
+        y = torch.empty((Bsz, H, 64), dtype=torch.float16, device=DEV)
+        m2.decode_step(to_dev(st["x"][t]), to_dev(st["dt"][t]), to_dev(st["B"][t]), to_dev(st["C"][t]),
+                       to_dev(prm["A"]), to_dev(prm["D"]), s16, y)
+        yg.append(y.cpu().numpy())
+    yr = oracle.decode_f16state(st["x"], st["dt"], prm["A"], st["B"], st["C"], prm["D"], bits)
+    sg = s16.cpu().numpy()
+    same = np.mean(sg.view(np.uint16) == bits)
+    ey = slice_err(np.stack(yg).transpose(1, 2, 0, 3), yr.transpose(1, 2, 0, 3), 2)
+    es = slice_err(sg.astype(np.float64), bits.view(np.float16).astype(np.float64), 2)
+    say(f"[decode] N={N}: state identical {same:.6f} state err {es:.2e} y err {ey:.2e}")
+    assert same >= 0.9999 and es <= S_TOL and ey <= Y_TOL
+
+
+def test_decode_f32_state_matches_fp64_recurrence():
+    T, Bsz, H, N, G = 12, 2, 8, 128, 2
+    prm, st = decode_inputs(61, T, Bsz, H, N, G)
+    s32 = to_dev(prm["state"]).clone()
+    yg = []
+    for t in range(T):
+        y = torch.empty((Bsz, H, 64), dtype=torch.float16, device=DEV)
+        m2.decode_step(to_dev(st["x"][t]), to_dev(st["dt"][t]), to_dev(st["B"][t]), to_dev(st["C"][t]),
+                       to_dev(prm["A"]), to_dev(prm["D"]), s32, y)
+        yg.append(y.cpu().numpy())
+    tr = lambda a: np.transpose(a, (1, 0) + tuple(range(2, a.ndim)))
+    yr, hr = oracle.ssd_scan(tr(st["x"]), tr(st["dt"]), prm["A"], tr(st["B"]), tr(st["C"]), prm["D"],
+                             h0=prm["state"].astype(np.float64))
+    ey = slice_err(np.stack(yg).transpose(1, 2, 0, 3), np.transpose(yr, (0, 2, 1, 3)), 2)
+    es = slice_err(s32.cpu().numpy(), hr, 2)
+    say(f"[decode f32] y {ey:.2e} state {es:.2e}")
+    assert ey <= Y_TOL and es <= S_TOL
+
+
+def test_state_store_roundtrip():
+    r = np.random.default_rng(71)
+    v = (r.standard_normal((2, 4, 64, 128)) * np.exp2(r.integers(-26, 17, (2, 4, 64, 128)))).astype(np.float32)
+    s16 = torch.empty(v.shape, dtype=torch.float16, device=DEV)
+    m2.state_load(to_dev(v), s16)
+    back = torch.empty(v.shape, dtype=torch.float32, device=DEV)
+    m2.state_store(s16, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(s16.cpu().numpy().view(np.uint16), v.astype(np.float16).view(np.uint16))
+    assert np.array_equal(back.cpu().numpy(), v.astype(np.float16).astype(np.float32))
+
+
+def test_decode_full_size_1024_steps_sampled():
+    d = synth.DECODE
+    Bsz, H, P, N, G, T = d["batch"], d["nheads"], d["headdim"], d["dstate"], d["ngroups"], d["steps"]
+    seed = 1003
+    prm = synth.decode_params(seed, Bsz, H, P, N)
+    s16 = torch.empty((Bsz, H, P, N), dtype=torch.float16, device=DEV)
+    m2.state_load(to_dev(prm["state"]), s16)
+    sample = (0, 37)
+    keep = {k: [] for k in ("x", "dt", "B", "C", "y")}
+    A, D = to_dev(prm["A"]), to_dev(prm["D"])
+    y = torch.empty((Bsz, H, P), dtype=torch.float16, device=DEV)
+    say(f"[decode] full: {T} steps, B={Bsz}")
+    for t in range(T):
+        st = synth.decode_step_inputs(seed, t, prm["dt0"], Bsz, H, P, N, G)
+        m2.decode_step(to_dev(st["x"]), to_dev(st["dt"]), to_dev(st["B"]), to_dev(st["C"]), A, D, s16, y)
+        for k in ("x", "dt", "B", "C"):
+            keep[k].append(st[k][list(sample)])
+        keep["y"].append(y[list(sample)].cpu().numpy())
+    torch.cuda.synchronize()
+    bits = prm["state"][list(sample)].astype(np.float16).view(np.uint16).copy()
+    yr = oracle.decode_f16state(*(np.stack(keep[k]) for k in ("x", "dt")), prm["A"],
+                                np.stack(keep["B"]), np.stack(keep["C"]), prm["D"], bits)
+    sg = s16.cpu().numpy()[list(sample)]
+    same = np.mean(sg.view(np.uint16) == bits)
+    es = slice_err(sg.astype(np.float64), bits.view(np.float16).astype(np.float64), 2)
+    ey = slice_err(np.stack(keep["y"]).transpose(1, 2, 0, 3), yr.transpose(1, 2, 0, 3), 2)
+    say(f"[decode] full sampled: identical {same:.6f} state err {es:.2e} y err {ey:.2e}")
+    assert es <= S_TOL and ey <= Y_TOL
