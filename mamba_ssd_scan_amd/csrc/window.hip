@@ -14,7 +14,7 @@
 // <= 1 and nothing overflows however long the chunk decays.
 //
 // Design for gfx950:
-//  * one 256-thread workgroup (4 waves) per (chunk, sequence, head) item, taken
+//  * one 512-thread workgroup (8 waves) per (chunk, sequence, head) item, taken
 //    in chunk-major order from an atomic ticket, so that an item only ever
 //    waits for an item that started before it (no deadlock whatever the
 //    dispatch order);
@@ -42,27 +42,56 @@ constexpr int kTS = 64;         // tokens per sub-chunk
 constexpr int kXP = kTS + 8;    // pitch (halfs) of [p][s] tiles
 constexpr int kXN = kP + 8;     // pitch (halfs) of [s][p] tiles
 constexpr unsigned kSpinLimit = 1u << 22;
+#ifndef M2_WAVES
+#define M2_WAVES 8
+#endif
+#ifndef M2_DEPTH
+#define M2_DEPTH 1
+#endif
+constexpr int kDepth = M2_DEPTH;  // sub-chunk steps the global loads run ahead (1 or 2)
+constexpr int kWaves = M2_WAVES;  // waves per workgroup (4 or 8)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kNormParts = kWaves / 4;   // partial sums of g^2 per (token, head)
 
 template <int N> struct Lay {
   static constexpr int NT = N / 16;          // n-tiles of the state
   static constexpr int KN = (N + 31) / 32;   // k-steps over n
   static constexpr int NP = N + 8;           // pitch of [s][n] and [p][n] tiles (halfs)
   static constexpr int BTP = kTS + 8;        // pitch of the [n][s] tile
-  // state tiles (n-tile x p-tile) owned by each wave in the chunk-state phase
-  static constexpr int NTW = N == 128 ? 2 : 1;
-  static constexpr int PTW = N == 16 ? 1 : 4;
+  // state tiles (n-tile x p-tile) owned by each wave: whole n-tiles x all four
+  // p-tiles when there are at least as many n-tiles as waves, else one n-tile
+  // x a share of the p-tiles (N=16 with 8 waves: one tile on waves 0..3)
+  static constexpr bool WIDE = NT >= kWaves;
+  static constexpr int NTW = WIDE ? NT / kWaves : 1;
+  static constexpr int PTW = WIDE ? 4 : (4 * NT >= kWaves ? 4 * NT / kWaves : 1);
   static constexpr int TILES = NTW * PTW;
+  static constexpr int STATE_FLOATS = kWaves * TILES * 256;   // private hand-off layout
+  static __device__ __forceinline__ int nt0(int w) { return WIDE ? w * NTW : w % NT; }
+  static __device__ __forceinline__ int pt0(int w) { return WIDE ? 0 : (w / NT) * PTW; }
+  static __device__ __forceinline__ bool owns(int w) { return WIDE || w < 4 * NT; }
 };
 
 template <int N, bool CONV> struct alignas(16) Smem {
   alignas(16) _Float16 xt[kP * kXP];                 // [p][s]: x (post-conv when fused), transposed
-  alignas(16) _Float16 bt[N * Lay<N>::BTP];          // [n][s]: dt- and decay-weighted B, transposed
+  union alignas(16) {
+    alignas(16) _Float16 bt[N * Lay<N>::BTP];        // [n][s]: dt- and decay-weighted B, transposed
+    alignas(16) _Float16 mt[kTS * kXN];              // [t][s]: decay-masked C.B^T (after the state update)
+  };
   alignas(16) _Float16 bn[kTS * Lay<N>::NP];         // [s][n]: B as read
   alignas(16) _Float16 cn[kTS * Lay<N>::NP];         // [t][n]: C as read
-  alignas(16) _Float16 r[kP * Lay<N>::NP];           // [p][n]: state entering the sub-chunk
+  union alignas(16) {
+    alignas(16) _Float16 r[kP * Lay<N>::NP];         // [p][n]: state entering the sub-chunk
+    struct {                                         // look-back list (carry-in phase only)
+      unsigned lb_item[65];
+      float lb_coef[65];
+      int lb_kind[65];   // 0 aggregate, 1 inclusive, 2 initial state
+      int lb_n;
+    };
+  };
+  alignas(16) float u[kTS];                          // dt_s e^{S_r - S_s}, r = last token of s's 16-token tile
   float S[256];                                      // running log2-decay from the chunk start (inclusive)
   _Float16 dts[256];                                 // dt per token (0 past the sequence end)
-  float wsum[4];
+  float wsum[kWaves];
   unsigned ticket, gen;
 };
 
@@ -86,10 +115,20 @@ template <typename IO> struct WinArgs {
   const IO* z;
   float* normsum;   // (B, L, H) per-head sum of g^2 (norm epilogue)
   IO* y;
-  unsigned* ctrl;   // [0] ticket [1] done [2] generation [3] error
-  unsigned* flags;  // per item
-  float* states;    // per item hand-off state (private layout)
+  unsigned* ctrl;     // per-partition claim counters, done counter, generation, error
+  unsigned* flags;    // per item: generation tag | 1 (aggregate) | 2 (inclusive)
+  float* agg;         // per item local chunk state (private layout)
+  float* incl;        // per item inclusive state after the chunk (private layout)
+  unsigned* aggdec;   // per item chunk decay e^{S_end} (float bits)
 };
+
+// control block: eight claim counters and the done counter / generation /
+// error word, each on its own 128-byte line
+constexpr int kCtrlStride = 32;
+constexpr int kCtrlDone = 8 * kCtrlStride;
+constexpr int kCtrlGen = 9 * kCtrlStride;
+constexpr int kCtrlErr = 10 * kCtrlStride;
+constexpr int kCtrlBytes = 11 * kCtrlStride * 4;
 
 // ---- input access: plain tensors, or conv1d(4)+SiLU over raw xBC ----------
 template <typename IO, bool CONV> struct Src {
@@ -113,29 +152,68 @@ template <typename IO, bool CONV> struct Src {
     for (int e = 0; e < 8; ++e) r[e] = (_Float16)v[e];
     return r;
   }
+  // NE (4 or 8) consecutive raw channels at token tau (< 0: history or zeros)
+  template <int NE>
+  static __device__ __forceinline__ void rawn(const WinArgs<IO>& a, int b, int tau, int ch0, float* r) {
+    if (tau >= 0) {
+      const IO* src = a.xBC + ((size_t)b * a.L + tau) * a.Cd + ch0;
+      if constexpr (NE == 8) io<IO>::load8(src, r);
+      else {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) r[e] = io<IO>::load1(src + e);
+      }
+    } else if (a.conv_in) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) r[e] = io<IO>::load1(a.conv_in + ((size_t)b * a.Cd + ch0 + e) * 3 + 3 + tau);
+    } else {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) r[e] = 0.f;
+    }
+  }
+  template <int NE = 8>
   static __device__ __forceinline__ void conv8f(const WinArgs<IO>& a, int b, int t, int ch0, float* v) {
-    float acc[8];
+    float acc[NE];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = a.conv_b ? a.conv_b[ch0 + e] : 0.f;
-    float w[8][4];
+    for (int e = 0; e < NE; ++e) acc[e] = a.conv_b ? a.conv_b[ch0 + e] : 0.f;
+    float w[NE][4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NE; ++e) {
       f4 ww = *reinterpret_cast<const f4*>(a.conv_w + (size_t)(ch0 + e) * 4);
       w[e][0] = ww[0]; w[e][1] = ww[1]; w[e][2] = ww[2]; w[e][3] = ww[3];
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float r[8];
-      raw8(a, b, t - 3 + k, ch0, r);
+      float r[NE];
+      rawn<NE>(a, b, t - 3 + k, ch0, r);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w[e][k], r[e], acc[e]);
+      for (int e = 0; e < NE; ++e) acc[e] = __builtin_fmaf(w[e][k], r[e], acc[e]);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = acc[e] / (1.f + __expf(-acc[e]));
+    for (int e = 0; e < NE; ++e) v[e] = acc[e] / (1.f + __expf(-acc[e]));
   }
-  static __device__ __forceinline__ h8 x8(const WinArgs<IO>& a, int b, int t, int h, int p0) {
-    if (CONV) return conv8(a, b, t, h * kP + p0);
-    return io<IO>::load8h(a.x + (((size_t)b * a.L + t) * a.H + h) * kP + p0);
+  // NE (4 or 8) consecutive channels of x as binary16
+  template <int NE, typename HV>
+  static __device__ __forceinline__ HV xv(const WinArgs<IO>& a, int b, int t, int h, int p0) {
+    HV r;
+    if constexpr (CONV) {
+      float v[NE];
+      conv8f<NE>(a, b, t, h * kP + p0, v);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) r[e] = (_Float16)v[e];
+    } else {
+      const IO* src = a.x + (((size_t)b * a.L + t) * a.H + h) * kP + p0;
+      if constexpr (sizeof(IO) == 2) {
+        r = *reinterpret_cast<const HV*>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < NE; e += 4) {
+          const f4 v = *reinterpret_cast<const f4*>(src + e);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) r[e + k] = (_Float16)v[k];
+        }
+      }
+    }
+    return r;
   }
   template <int N>
   static __device__ __forceinline__ h8 b8(const WinArgs<IO>& a, int b, int t, int g, int n0) {
@@ -160,39 +238,69 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ h8 cat(h4 lo, h4 hi) { return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
 
+// x channels per thread per token (two tokens per thread)
+constexpr int kXE = (kTS * kP) / (2 * kThreads);
+typedef _Float16 hx __attribute__((ext_vector_type(kXE)));
+
 // One thread's share of a 64-token sub-chunk, fetched ahead of its use.
-//   x: tokens sx, sx+1 at channels 8*px..8*px+7 of the head
+//   x: tokens sx, sx+1 at channels kXE*px .. kXE*px+kXE-1 of the head
 //   B, C: tokens sb..sb+TPT-1 at state columns 8*nb..8*nb+7 of the group
 //   bs (fused conv only): B weighted for the state contraction, formed from the
 //   fp32 conv output so that the weighted B is rounded to binary16 once
 template <int N, bool CONV> struct Pref {
   static constexpr int NCH = N / 8;
-  static constexpr int TPT = (kTS * NCH) / 256 > 0 ? (kTS * NCH) / 256 : 1;
-  h8 x[2];
+  static constexpr int TPT = (kTS * NCH) / kThreads > 0 ? (kTS * NCH) / kThreads : 1;
+  hx x[2];
   h8 b[TPT];
   h8 c[TPT];
   h8 bs[CONV ? TPT : 1];
 };
 
 template <typename IO, int N, bool CONV, bool NORM>
-__global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
+__global__ __launch_bounds__(kThreads, 2) void ssd_window_kernel(WinArgs<IO> a) {
   using Ly = Lay<N>;
   using SRC = Src<IO, CONV>;
   using PF = Pref<N, CONV>;
   __shared__ Smem<N, CONV> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, q = lane >> 4;
+  const int BH = a.B * a.H;
+  const int hpg = a.H / a.G;
 
-  // ---- take a ticket: item = (chunk, sequence, head), chunk-major ----------
+  // ---- claim an item ------------------------------------------------------
+  // Items are split into 8 partitions by (sequence, group) so that the heads
+  // sharing B/C, and the chunks of one head, run on one XCD and meet in its
+  // L2.  A workgroup claims from the partition of the XCD it runs on, and from
+  // the others once that one is used up.  Inside a partition items are handed
+  // out chunk-major, so an item only ever waits for an item claimed before it.
   if (tid == 0) {
-    sm.gen = __hip_atomic_load(&a.ctrl[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.ticket = __hip_atomic_fetch_add(&a.ctrl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.gen = __hip_atomic_load(&a.ctrl[kCtrlGen], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned x0 = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u;   // HW_REG_XCC_ID
+    const int BG = a.B * a.G;
+    unsigned px = 0, t = 0;
+    for (int k = 0; k < 8; ++k) {
+      px = (x0 + k) & 7u;
+      const int npairs = BG > (int)px ? (BG - (int)px + 7) / 8 : 0;
+      const unsigned n = (unsigned)(npairs * hpg * a.nchunks);
+      if (n == 0) continue;
+      unsigned* cnt = &a.ctrl[px * kCtrlStride];
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+      t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t < n) {
+        const int per_c = npairs * hpg;
+        const int cc = (int)t / per_c, rem = (int)t - cc * per_c;
+        const int gid = (int)px + 8 * (rem / hpg);
+        const int bb = gid / a.G, gg = gid - bb * a.G;
+        sm.ticket = (unsigned)(cc * BH + bb * a.H + gg * hpg + rem % hpg);
+        break;
+      }
+    }
   }
   __syncthreads();
   const unsigned item = sm.ticket, gen = sm.gen;
-  const int BH = a.B * a.H;
+  const unsigned tag = (gen & 0x3fffffffu) << 2;   // flag = tag | 1 (aggregate) or tag | 2 (inclusive)
   const int c = item / BH, bh = item - c * BH;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int g = h / (a.H / a.G);
+  const int g = h / hpg;
   int len = a.seqlens ? a.seqlens[b] : a.L;
   len = len < 0 ? 0 : (len > a.L ? a.L : len);
   const int t0 = c * a.Q;                      // first token of the chunk
@@ -202,25 +310,31 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
   const float Dh = a.D[h];
 
   // per-thread staging coordinates
-  const int px = tid & 7, sx = 2 * (tid >> 3);
+  const int px = tid % (kP / kXE), sx = 2 * (tid / (kP / kXE));
   const int nb = tid % PF::NCH, sb = (tid / PF::NCH) * PF::TPT;
   const bool bact = sb < kTS;
 
-  // issue the global loads of sub-chunk j (tokens past the end are fetched
-  // from a valid token and zeroed when written to LDS)
-  // Sref: reference of the state weights (fused conv only, which forms the
-  // weighted B here; it needs the phase-0 decays)
-  auto fetch = [&](PF& f, int j, bool withC, float Sref) {
+  // The work of an item is a sequence of 2*Jv steps over its 64-token
+  // sub-chunks: steps [0, Jv) accumulate the chunk state, steps [Jv, 2Jv)
+  // produce the outputs.  Global loads run two steps ahead of their use.
+  const int NS = 2 * Jv;
+  // issue the global loads of step k (tokens past the end are fetched from a
+  // valid token and zeroed when written to LDS)
+  auto fetch = [&](PF& f, int k) {
+    const bool out = k >= Jv;
+    const int j = out ? k - Jv : k;
     const int i0 = j * kTS;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int s = i0 + sx + k;
-      f.x[k] = SRC::x8(a, b, t0 + (s < nvalid ? s : i0), h, px * 8);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int s = i0 + sx + kk;
+      f.x[kk] = SRC::template xv<kXE, hx>(a, b, t0 + (s < nvalid ? s : i0), h, px * kXE);
     }
     if (bact) {
+      // fused conv only: weight reference of this step (chunk end, or sub-chunk end)
+      const float Sref = CONV ? (out ? sm.S[i0 + kTS - 1] : sm.S[a.Q - 1]) : 0.f;
 #pragma unroll
-      for (int k = 0; k < PF::TPT; ++k) {
-        const int s = i0 + sb + k;
+      for (int kk = 0; kk < PF::TPT; ++kk) {
+        const int s = i0 + sb + kk;
         const int t = t0 + (s < nvalid ? s : i0);
         if constexpr (CONV) {
           float v[8];
@@ -228,20 +342,24 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
           const float wgt = s < nvalid ? (float)sm.dts[s] * exp2f(Sref - sm.S[s]) : 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            f.b[k][e] = (_Float16)v[e];
-            f.bs[k][e] = (_Float16)(v[e] * wgt);
+            f.b[kk][e] = (_Float16)v[e];
+            f.bs[kk][e] = (_Float16)(v[e] * wgt);
           }
         } else {
-          f.b[k] = SRC::template b8<N>(a, b, t, g, nb * 8);
+          f.b[kk] = SRC::template b8<N>(a, b, t, g, nb * 8);
         }
-        if (withC) f.c[k] = SRC::template c8<N>(a, b, t, g, nb * 8);
+        if (out) f.c[kk] = SRC::template c8<N>(a, b, t, g, nb * 8);
       }
     }
   };
 
+  PF pa, pb;
+  if (!CONV) {
+    if (NS > 0) fetch(pa, 0);
+    if (kDepth == 2 && NS > 1) fetch(pb, 1);
+  }
+
   // ---- phase 0: dt and the inclusive running log2-decay over the chunk -----
-  PF pf;
-  if (!CONV && Jv > 0) fetch(pf, 0, false, 0.f);
   {
     float d = 0.f;
     if (tid < nvalid) d = io<IO>::load1(a.dt + ((size_t)b * a.L + t0 + tid) * a.H + h);
@@ -262,11 +380,14 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
     __syncthreads();
   }
   const float Send = sm.S[a.Q - 1];
-  if (CONV && Jv > 0) fetch(pf, 0, false, Send);
+  if (CONV) {
+    if (NS > 0) fetch(pa, 0);
+    if (kDepth == 2 && NS > 1) fetch(pb, 1);
+  }
 
   // state tiles of this wave: n-tile nt0+i, p-tile pt0+jj
-  const int nt0 = (N == 16) ? 0 : w * Ly::NTW;
-  const int pt0 = (N == 16) ? w : 0;
+  const int nt0 = Ly::nt0(w), pt0 = Ly::pt0(w);
+  const bool owner = Ly::owns(w);
 
   // write x (transposed, as read: no rounding for f16 inputs) and the
   // transposed B weighted by dt_s e^{Sref - S_s} of sub-chunk j
@@ -276,8 +397,8 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
       const bool ok0 = i0 + sx < nvalid, ok1 = i0 + sx + 1 < nvalid;
       const _Float16 zero = (_Float16)0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<h2*>(&sm.xt[(px * 8 + e) * kXP + sx]) = h2{ok0 ? f.x[0][e] : zero, ok1 ? f.x[1][e] : zero};
+      for (int e = 0; e < kXE; ++e)
+        *reinterpret_cast<h2*>(&sm.xt[(px * kXE + e) * kXP + sx]) = h2{ok0 ? f.x[0][e] : zero, ok1 ? f.x[1][e] : zero};
     }
     if (CONV && bact) {
 #pragma unroll
@@ -309,6 +430,7 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
   };
   // acc[i][jj] += (weighted B)^T . x  for this wave's state tiles
   auto state_mfma = [&](f4 (&acc)[Ly::NTW][Ly::PTW]) {
+    if (!owner) return;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       h8 bf[Ly::PTW];
@@ -323,100 +445,199 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
       }
     }
   };
+  // private layout of a hand-off state: [wave][tile][lane][4] floats
+  auto st_off = [&](unsigned it, int i, int jj) -> size_t {
+    return (size_t)it * Ly::STATE_FLOATS + ((size_t)w * Ly::TILES + (i * Ly::PTW + jj)) * 256 + lane * 4;
+  };
+  // device-coherent (write-through) store / load of this thread's state values
+  auto put_state = [&](float* base, unsigned it, const f4 (&v)[Ly::NTW][Ly::PTW]) {
+    if (!owner) return;
+#pragma unroll
+    for (int i = 0; i < Ly::NTW; ++i)
+#pragma unroll
+      for (int jj = 0; jj < Ly::PTW; ++jj) {
+        uint64_t* q2 = reinterpret_cast<uint64_t*>(base + st_off(it, i, jj));
+        const f4 x4 = v[i][jj];
+        __hip_atomic_store(q2, (uint64_t)__float_as_uint(x4[0]) | ((uint64_t)__float_as_uint(x4[1]) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q2 + 1, (uint64_t)__float_as_uint(x4[2]) | ((uint64_t)__float_as_uint(x4[3]) << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+  };
+  auto add_state = [&](const float* base, unsigned it, float coef, f4 (&v)[Ly::NTW][Ly::PTW]) {
+    if (!owner) return;
+#pragma unroll
+    for (int i = 0; i < Ly::NTW; ++i)
+#pragma unroll
+      for (int jj = 0; jj < Ly::PTW; ++jj) {
+        const uint64_t* q2 = reinterpret_cast<const uint64_t*>(base + st_off(it, i, jj));
+        const uint64_t lo = __hip_atomic_load(q2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t hi = __hip_atomic_load(q2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[i][jj] += coef * f4{__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)),
+                              __uint_as_float((unsigned)hi), __uint_as_float((unsigned)(hi >> 32))};
+      }
+  };
+  // raise this item's flag once every wave's stores have completed
+  auto raise_flag = [&](unsigned status) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&a.flags[item], tag | status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
 
-  // ---- phase 1: local chunk state  s_c = sum_s e^{S_end-S_s} dt_s x_s B_s^T --
-  f4 acc[Ly::NTW][Ly::PTW];
+  f4 acc[Ly::NTW][Ly::PTW];   // local chunk state, from zero at the chunk start
 #pragma unroll
   for (int i = 0; i < Ly::NTW; ++i)
 #pragma unroll
     for (int jj = 0; jj < Ly::PTW; ++jj) acc[i][jj] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < Jv; ++j) {
-    stage_state_operands(pf, j, Send);
-    lds_barrier();
-    if (j + 1 < Jv) fetch(pf, j + 1, false, Send);
-    else fetch(pf, 0, true, sm.S[kTS - 1]);   // first sub-chunk of the output phase
-    state_mfma(acc);
-    lds_barrier();
-  }
+  f4 R[Ly::NTW][Ly::PTW];     // state entering the current sub-chunk (fp32)
+  const float dec_chunk = exp2f(Send);
 
-  // ---- phase 2: carry-in state, hand-off to the next chunk -----------------
-  f4 R[Ly::NTW][Ly::PTW];   // state entering the current sub-chunk (fp32)
-  {
-    if (c == 0) {
+  // ---- phase 2: carry-in state and hand-off to later chunks -----------------
+  // Decoupled look-back: a chunk first publishes its local (aggregate) state,
+  // then starts from the nearest published inclusive state of an earlier chunk,
+  // applies the aggregates in between, and publishes its own inclusive state.
+  // No chunk waits for a chain of hand-offs to ripple through.
+  auto carry_in = [&]() {
+    const bool publish = c + 1 < a.nchunks;
+    if (c > 0 && publish) {
+      put_state(a.agg, item, acc);
+      if (tid == 0) __hip_atomic_store(&a.aggdec[item], __float_as_uint(dec_chunk), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      raise_flag(1u);
+    }
 #pragma unroll
-      for (int i = 0; i < Ly::NTW; ++i)
+    for (int i = 0; i < Ly::NTW; ++i)
 #pragma unroll
-        for (int jj = 0; jj < Ly::PTW; ++jj) {
-          if (a.state_in) {
-            const int p = 16 * (pt0 + jj) + lr, n = 16 * (nt0 + i) + 4 * q;
-            R[i][jj] = *reinterpret_cast<const f4*>(a.state_in + ((size_t)bh * kP + p) * N + n);
-          } else {
-            R[i][jj] = f4{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-    } else {
-      const unsigned pred = item - BH;
-      if (tid == 0) {
+      for (int jj = 0; jj < Ly::PTW; ++jj) R[i][jj] = f4{0.f, 0.f, 0.f, 0.f};
+    if (c > 0) {
+      if (w == 0) {
+        const int W = c < 64 ? c : 64;      // predecessors c-1 .. c-W, one per lane
+        const unsigned pred = (unsigned)((c - 1 - lane) * BH + bh);
         unsigned spins = 0;
-        while (__hip_atomic_load(&a.flags[pred], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gen + 1u) {
+        int need = 0, lstar = W;
+        while (true) {
+          unsigned st = 0;
+          if (lane < W) {
+            const unsigned f = __hip_atomic_load(&a.flags[pred], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            st = (f & ~3u) == tag ? (f & 3u) : 0u;
+          }
+          const unsigned long long incl = __ballot(st == 2u), ready = __ballot(st >= 1u);
+          lstar = incl ? (int)__builtin_ctzll(incl) : W;            // nearest inclusive
+          need = lstar;                                               // aggregates before it
+          const unsigned long long m = need >= 64 ? ~0ull : ((1ull << need) - 1ull);
+          bool ok = (ready & m) == m;
+          if (lstar == W && c > W) ok = false;                        // window too short: wait
+          if (ok) break;
           __builtin_amdgcn_s_sleep(1);
           if (++spins > kSpinLimit) {
-            __hip_atomic_fetch_or(&a.ctrl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_fetch_or(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            need = 0; lstar = W;
             break;
           }
         }
+        // The carry-in state is rebuilt from the nearest inclusive state (or the
+        // initial state) by applying the later chunks' hand-offs in order,
+        // H <- a_k H + s_k, with the same fused multiply-add the chain itself
+        // uses -- so the result is bitwise the same whichever predecessor
+        // happened to be published first.  List order: base, then aggregates
+        // of chunks c-need .. c-1.
+        if (lane < need) {
+          const int e = need - lane;                         // chunk c-1-lane at position e
+          sm.lb_item[e] = pred;
+          sm.lb_coef[e] = __uint_as_float(__hip_atomic_load(&a.aggdec[pred], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          sm.lb_kind[e] = 0;
+        }
+        if (lane == 0) {
+          if (lstar < W) {                       // an inclusive state of an earlier chunk
+            sm.lb_item[0] = (unsigned)((c - 1 - lstar) * BH + bh);
+            sm.lb_kind[0] = 1;
+          } else {
+            sm.lb_kind[0] = a.state_in ? 2 : 3;  // the initial state, or zeros
+          }
+          sm.lb_n = need + 1;
+        }
       }
       __syncthreads();
-      // device-coherent loads: they never hit a stale line of this XCD's L2
-      const uint64_t* src = reinterpret_cast<const uint64_t*>(a.states + ((size_t)pred * 4 + w) * Ly::TILES * 256);
+      const int n = sm.lb_n;
+      {
+        const int kind = sm.lb_kind[0];
+        if (owner) {
+          if (kind == 1) {
+            add_state(a.incl, sm.lb_item[0], 1.f, R);
+          } else if (kind == 2) {
+#pragma unroll
+            for (int i = 0; i < Ly::NTW; ++i)
+#pragma unroll
+              for (int jj = 0; jj < Ly::PTW; ++jj) {
+                const int p = 16 * (pt0 + jj) + lr, nn = 16 * (nt0 + i) + 4 * q;
+                R[i][jj] = *reinterpret_cast<const f4*>(a.state_in + ((size_t)bh * kP + p) * N + nn);
+              }
+          }
+        }
+      }
+      for (int e = 1; e < n; ++e) {
+        if (owner) {
+          f4 Ae[Ly::NTW][Ly::PTW];
+#pragma unroll
+          for (int i = 0; i < Ly::NTW; ++i)
+#pragma unroll
+            for (int jj = 0; jj < Ly::PTW; ++jj) Ae[i][jj] = f4{0.f, 0.f, 0.f, 0.f};
+          add_state(a.agg, sm.lb_item[e], 1.f, Ae);
+          const float ae = sm.lb_coef[e];
+#pragma unroll
+          for (int i = 0; i < Ly::NTW; ++i)
+#pragma unroll
+            for (int jj = 0; jj < Ly::PTW; ++jj)
+#pragma unroll
+              for (int k = 0; k < 4; ++k) R[i][jj][k] = __builtin_fmaf(ae, R[i][jj][k], Ae[i][jj][k]);
+        }
+      }
+    } else if (a.state_in && owner) {
 #pragma unroll
       for (int i = 0; i < Ly::NTW; ++i)
 #pragma unroll
         for (int jj = 0; jj < Ly::PTW; ++jj) {
-          const uint64_t* q2 = src + ((i * Ly::PTW + jj) * 256 + lane * 4) / 2;
-          const uint64_t lo = __hip_atomic_load(q2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint64_t hi = __hip_atomic_load(q2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          R[i][jj] = f4{__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)),
-                        __uint_as_float((unsigned)hi), __uint_as_float((unsigned)(hi >> 32))};
+          const int p = 16 * (pt0 + jj) + lr, nn = 16 * (nt0 + i) + 4 * q;
+          R[i][jj] = *reinterpret_cast<const f4*>(a.state_in + ((size_t)bh * kP + p) * N + nn);
         }
     }
-    const float dec = exp2f(Send);
-    if (c + 1 < a.nchunks) {
-      // device-coherent (write-through) stores, then wait until every wave's
-      // stores have completed before the flag is raised
-      uint64_t* dst = reinterpret_cast<uint64_t*>(a.states + ((size_t)item * 4 + w) * Ly::TILES * 256);
+    // inclusive state after this chunk, H_c = a_c H_{c-1} + s_c (in place: the
+    // local state is no longer needed)
+    f4 (&Hout)[Ly::NTW][Ly::PTW] = acc;
+#pragma unroll
+    for (int i = 0; i < Ly::NTW; ++i)
+#pragma unroll
+      for (int jj = 0; jj < Ly::PTW; ++jj)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) Hout[i][jj][k] = __builtin_fmaf(dec_chunk, R[i][jj][k], acc[i][jj][k]);
+    if (publish) {
+      put_state(a.incl, item, Hout);
+      raise_flag(2u);
+    } else if (a.state_out && owner) {
 #pragma unroll
       for (int i = 0; i < Ly::NTW; ++i)
 #pragma unroll
         for (int jj = 0; jj < Ly::PTW; ++jj) {
-          const f4 v = R[i][jj] * dec + acc[i][jj];
-          uint64_t* q2 = dst + ((i * Ly::PTW + jj) * 256 + lane * 4) / 2;
-          __hip_atomic_store(q2, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(q2 + 1, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) __hip_atomic_store(&a.flags[item], gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (a.state_out) {
-#pragma unroll
-      for (int i = 0; i < Ly::NTW; ++i)
-#pragma unroll
-        for (int jj = 0; jj < Ly::PTW; ++jj) {
-          const int p = 16 * (pt0 + jj) + lr, n = 16 * (nt0 + i) + 4 * q;
-          *reinterpret_cast<f4*>(a.state_out + ((size_t)bh * kP + p) * N + n) = R[i][jj] * dec + acc[i][jj];
+          const int p = 16 * (pt0 + jj) + lr, nn = 16 * (nt0 + i) + 4 * q;
+          *reinterpret_cast<f4*>(a.state_out + ((size_t)bh * kP + p) * N + nn) = Hout[i][jj];
         }
     }
-  }
+    // the look-back list shares LDS with the carried-state tile written next
+    lds_barrier();
+  };
 
-  // ---- phase 3: outputs, sub-chunk by sub-chunk ----------------------------
-  for (int j = 0; j < Jv; ++j) {
+  // ---- output step for sub-chunk j ------------------------------------------
+  auto output_step = [&](PF& f, int j, int knext) {
     const int i0 = j * kTS;
     const float Sj_start = j ? sm.S[i0 - 1] : 0.f;
     const float Sj_end = sm.S[i0 + kTS - 1];
-    // stage: R (f16), dt*x, weighted B^T for the running state, B, C as read
-    stage_state_operands(pf, j, Sj_end);
+    // stage: R (f16), x, weighted B^T for the running state, B, C as read
+    stage_state_operands(f, j, Sj_end);
+    if (tid < kTS) {
+      const int s = i0 + tid;
+      sm.u[tid] = s < nvalid ? (float)sm.dts[s] * exp2f(sm.S[i0 + (tid | 15)] - sm.S[s]) : 0.f;
+    }
+    if (owner)
 #pragma unroll
     for (int i = 0; i < Ly::NTW; ++i)
 #pragma unroll
@@ -430,12 +651,12 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
       for (int k = 0; k < PF::TPT; ++k) {
         const bool ok = i0 + sb + k < nvalid;
         const h8 z8 = {};
-        *reinterpret_cast<h8*>(&sm.bn[(sb + k) * Ly::NP + nb * 8]) = ok ? pf.b[k] : z8;
-        *reinterpret_cast<h8*>(&sm.cn[(sb + k) * Ly::NP + nb * 8]) = ok ? pf.c[k] : z8;
+        *reinterpret_cast<h8*>(&sm.bn[(sb + k) * Ly::NP + nb * 8]) = ok ? f.b[k] : z8;
+        *reinterpret_cast<h8*>(&sm.cn[(sb + k) * Ly::NP + nb * 8]) = ok ? f.c[k] : z8;
       }
     }
     lds_barrier();
-    if (j + 1 < Jv) fetch(pf, j + 1, true, sm.S[i0 + 2 * kTS - 1]);
+    if (knext < NS) fetch(f, knext);
     // running state for the next sub-chunk: R <- e^{S_end_j - S_start_j} R + s_j
     if (j + 1 < Jv) {
       const float dec = exp2f(Sj_end - Sj_start);
@@ -445,16 +666,22 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
         for (int jj = 0; jj < Ly::PTW; ++jj) R[i][jj] *= dec;
       state_mfma(R);
     }
+    lds_barrier();   // the weighted B^T tile is dead: its space takes the masked C.B^T
     {
-      const int T = w;                       // this wave's 16 tokens: i0 + 16T + lr
-      const int ti = i0 + 16 * T + lr;       // chunk-relative token of this lane's column
-      const float St = sm.S[ti];
-      // C.B^T for s-tiles 0..T, masked and decayed
-      f4 m[4];
+      // Decay-masked C.B^T, one causal 16x16 block (s-tile S <= t-tile T) per
+      // job; the 10 jobs of a sub-chunk are spread over the 8 waves and the
+      // blocks meet in LDS as M[t][s] = (C_t.B_s) dt_s e^{S_t - S_s}.  Off the
+      // diagonal the decay is split at the last token r of the s-tile,
+      // e^{S_t-S_r} e^{S_r-S_s}, both factors <= 1, so a lane needs one
+      // exponential per block.
 #pragma unroll
-      for (int S = 0; S < 4; ++S) {
-        m[S] = f4{0.f, 0.f, 0.f, 0.f};
-        if (S <= T) {
+      for (int jb = 0; jb < (10 + kWaves - 1) / kWaves; ++jb) {
+        const int job = w + kWaves * jb;
+        if (job < 10) {
+          // job -> (S, T): (0,0) (0,1) (1,1) (0,2) (1,2) (2,2) (0,3) (1,3) (2,3) (3,3)
+          const int T = job < 1 ? 0 : (job < 3 ? 1 : (job < 6 ? 2 : 3));
+          const int S = job - (T * (T + 1)) / 2;
+          f4 cb = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < Ly::KN; ++kk) {
             const int n0 = 32 * kk + 8 * q;
@@ -463,31 +690,51 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
               af = *reinterpret_cast<const h8*>(&sm.bn[(16 * S + lr) * Ly::NP + n0]);
               bf = *reinterpret_cast<const h8*>(&sm.cn[(16 * T + lr) * Ly::NP + n0]);
             }
-            m[S] = mfma16(af, bf, m[S]);
+            cb = mfma16(af, bf, cb);
           }
+          const int tl = 16 * T + lr;                 // token of this lane's column
+          const float St = sm.S[i0 + tl];
+          const int s0 = 16 * S + 4 * q;              // first of this lane's four s
+          f4 mv;
+          if (S < T) {
+            const float vt = exp2f(St - sm.S[i0 + 16 * S + 15]);
+            const f4 uu = *reinterpret_cast<const f4*>(&sm.u[s0]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int si = i0 + 16 * S + 4 * q + i;
-            m[S][i] = (si <= ti) ? m[S][i] * (float)sm.dts[si] * exp2f(St - sm.S[si]) : 0.f;
+            for (int i = 0; i < 4; ++i) mv[i] = cb[i] * uu[i] * vt;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int si = s0 + i;
+              mv[i] = si <= tl ? cb[i] * (float)sm.dts[i0 + si] * exp2f(St - sm.S[i0 + si]) : 0.f;
+            }
           }
+          *reinterpret_cast<h4*>(&sm.mt[tl * kXN + s0]) = h4{(_Float16)mv[0], (_Float16)mv[1], (_Float16)mv[2], (_Float16)mv[3]};
         }
       }
-      f4 yacc[4], racc[4];
+      lds_barrier();
+      constexpr int PTO = 16 / kWaves;       // p-tiles per wave in the output
+      const int T = w & 3;                   // this wave's 16 tokens: i0 + 16T + lr
+      const int tpb = PTO * (w >> 2);        // and its p-tiles tpb .. tpb+PTO-1
+      const int ti = i0 + 16 * T + lr;       // chunk-relative token of this lane's column
+      const float St = sm.S[ti];
+      f4 yacc[PTO], racc[PTO];
 #pragma unroll
-      for (int tp = 0; tp < 4; ++tp) { yacc[tp] = f4{0.f, 0.f, 0.f, 0.f}; racc[tp] = f4{0.f, 0.f, 0.f, 0.f}; }
-      // diagonal: Y^T[p, t] += sum_s x^T[p, s] M^T[s, t],  M = (C.B^T) dt_s e^{S_t-S_s} masked
+      for (int u = 0; u < PTO; ++u) { yacc[u] = f4{0.f, 0.f, 0.f, 0.f}; racc[u] = f4{0.f, 0.f, 0.f, 0.f}; }
+      // diagonal: Y^T[p, t] += sum_s x^T[p, s] M[t, s]
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         if (2 * pr <= T) {
           const int S0 = 2 * pr, S1 = 2 * pr + 1;
-          h8 bf = {(_Float16)m[S0][0], (_Float16)m[S0][1], (_Float16)m[S0][2], (_Float16)m[S0][3],
-                   (_Float16)m[S1][0], (_Float16)m[S1][1], (_Float16)m[S1][2], (_Float16)m[S1][3]};
+          const _Float16* mrow = &sm.mt[(16 * T + lr) * kXN];
+          const h4 lo = *reinterpret_cast<const h4*>(mrow + 16 * S0 + 4 * q);
+          const h4 hi = S1 <= T ? *reinterpret_cast<const h4*>(mrow + 16 * S1 + 4 * q) : h4{};
+          const h8 bf = cat(lo, hi);
 #pragma unroll
-          for (int tp = 0; tp < 4; ++tp) {
-            const _Float16* row = &sm.xt[(16 * tp + lr) * kXP];
+          for (int u = 0; u < PTO; ++u) {
+            const _Float16* row = &sm.xt[(16 * (tpb + u) + lr) * kXP];
             h8 af = cat(*reinterpret_cast<const h4*>(row + 16 * S0 + 4 * q),
                         *reinterpret_cast<const h4*>(row + 16 * S1 + 4 * q));
-            yacc[tp] = mfma16(af, bf, yacc[tp]);
+            yacc[u] = mfma16(af, bf, yacc[u]);
           }
         }
       }
@@ -498,10 +745,10 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
         h8 bf = {};
         if (n0 < N) bf = *reinterpret_cast<const h8*>(&sm.cn[(16 * T + lr) * Ly::NP + n0]);
 #pragma unroll
-        for (int tp = 0; tp < 4; ++tp) {
+        for (int u = 0; u < PTO; ++u) {
           h8 af = {};
-          if (n0 < N) af = *reinterpret_cast<const h8*>(&sm.r[(16 * tp + lr) * Ly::NP + n0]);
-          racc[tp] = mfma16(af, bf, racc[tp]);
+          if (n0 < N) af = *reinterpret_cast<const h8*>(&sm.r[(16 * (tpb + u) + lr) * Ly::NP + n0]);
+          racc[u] = mfma16(af, bf, racc[u]);
         }
       }
       const float sc = exp2f(St - Sj_start);
@@ -510,8 +757,8 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
         IO* yrow = a.y + (tok * a.H + h) * kP;
         float gsq = 0.f;
 #pragma unroll
-        for (int tp = 0; tp < 4; ++tp) {
-          const int p0 = 16 * tp + 4 * q;
+        for (int u = 0; u < PTO; ++u) {
+          const int p0 = 16 * (tpb + u) + 4 * q;
           float xv[4];
           if constexpr (CONV || sizeof(IO) == 2) {
 #pragma unroll
@@ -523,7 +770,7 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
           }
           f4 out;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) out[i] = yacc[tp][i] + sc * racc[tp][i] + Dh * xv[i];
+          for (int i = 0; i < 4; ++i) out[i] = yacc[u][i] + sc * racc[u][i] + Dh * xv[i];
           if (NORM) {
             const IO* zrow = a.z + (tok * a.H + h) * kP + p0;
 #pragma unroll
@@ -538,20 +785,44 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
         if (NORM) {
           gsq += __shfl_xor(gsq, 16, 64);
           gsq += __shfl_xor(gsq, 32, 64);
-          if (q == 0) a.normsum[tok * a.H + h] = gsq;
+          if (q == 0) a.normsum[(tok * a.H + h) * kNormParts + (w >> 2)] = gsq;   // this wave's share of the head
         }
       }
     }
     lds_barrier();
+  };
+  // chunk-state step for sub-chunk j (weights to the chunk end)
+  auto state_step = [&](PF& f, int j, int knext) {
+    stage_state_operands(f, j, Send);
+    lds_barrier();
+    if (knext < NS) fetch(f, knext);
+    state_mfma(acc);
+    lds_barrier();
+  };
+  auto run_step = [&](PF& f, int k) {
+    if (k < Jv) state_step(f, k, k + kDepth);
+    else output_step(f, k - Jv, k + kDepth);
+  };
+
+  // one inlined step body: pa always holds the data of step k; after the step
+  // it is refilled with step k+kDepth (and with depth 2 the buffers trade places)
+  for (int k = 0; k <= NS; ++k) {
+    if (k == Jv) carry_in();
+    if (k == NS) break;
+    run_step(pa, k);
+    if constexpr (kDepth == 2) {
+      const PF t = pa;
+      pa = pb;
+      pb = t;
+    }
   }
 
   // ---- conv state out: the 3 raw tokens before the sequence end -------------
   if (CONV && a.conv_out) {
     const int clast = len > 0 ? (len - 1) / a.Q : 0;
     if (c == clast) {
-      const int hpg = a.H / a.G;
       const int nch = kP + ((h % hpg) == 0 ? 2 * N : 0);
-      for (int k = tid; k < nch * 3; k += 256) {
+      for (int k = tid; k < nch * 3; k += kThreads) {
         const int ci = k / 3, kk = k % 3;
         const int ch = ci < kP ? h * kP + ci : (ci - kP < N ? a.H * kP + g * N + (ci - kP)
                                                              : a.H * kP + a.G * N + g * N + (ci - kP - N));
@@ -564,16 +835,16 @@ __global__ __launch_bounds__(256, 2) void ssd_window_kernel(WinArgs<IO> a) {
     }
   }
 
-  // ---- retire: the last item resets the ticket and bumps the generation -----
+  // ---- retire: the last item resets the counters and bumps the generation ---
   __syncthreads();
   if (tid == 0) {
     const unsigned total = (unsigned)(a.nchunks * BH);
     // Relaxed: the next call reads these only after this kernel has ended.
-    const unsigned done = __hip_atomic_fetch_add(&a.ctrl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned done = __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == total - 1) {
-      __hip_atomic_store(&a.ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctrl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctrl[2], gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int k = 0; k < 8; ++k) __hip_atomic_store(&a.ctrl[k * kCtrlStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl[kCtrlDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl[kCtrlGen], gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -592,7 +863,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
   const int C = H * kP, ngr = C / group, hpgr = group / kP;
   for (int gi = threadIdx.x; gi < ngr; gi += 256) {
     float s = 0.f;
-    for (int k = 0; k < hpgr; ++k) s += normsum[(size_t)tok * H + gi * hpgr + k];
+    for (int k = 0; k < kNormParts * hpgr; ++k) s += normsum[((size_t)tok * H + gi * hpgr) * kNormParts + k];
     rs[gi] = rsqrtf(s / (float)group + eps);
   }
   __syncthreads();
@@ -611,7 +882,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
 
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t ctrl, flags, states, normsum, total;
+  size_t ctrl, flags, aggdec, agg, incl, normsum, total;
 };
 static WsLayout ws_layout(const mamba2_dims& d) {
   const size_t nchunks = ((size_t)d.seqlen + d.chunk - 1) / d.chunk;
@@ -619,10 +890,14 @@ static WsLayout ws_layout(const mamba2_dims& d) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   WsLayout w;
   w.ctrl = 0;
-  w.flags = 256;
-  w.states = up(w.flags + items * 4);
-  w.normsum = up(w.states + items * (size_t)kP * d.dstate * 4);
-  w.total = up(w.normsum + (d.norm_group > 0 ? (size_t)d.batch * d.seqlen * d.nheads * 4 : 0));
+  w.flags = up(kCtrlBytes);
+  w.aggdec = up(w.flags + items * 4);
+  w.agg = up(w.aggdec + items * 4);
+  const size_t sf = d.dstate == 128 ? Lay<128>::STATE_FLOATS : (d.dstate == 64 ? Lay<64>::STATE_FLOATS
+                                                                                 : Lay<16>::STATE_FLOATS);
+  w.incl = up(w.agg + items * sf * 4);
+  w.normsum = up(w.incl + items * sf * 4);
+  w.total = up(w.normsum + (d.norm_group > 0 ? (size_t)d.batch * d.seqlen * d.nheads * kNormParts * 4 : 0));
   return w;
 }
 
@@ -631,7 +906,7 @@ size_t window_workspace_bytes(const mamba2_dims& d) { return ws_layout(d).total;
 template <typename IO, int N, bool CONV, bool NORM>
 static hipError_t launch_T(const WinArgs<IO>& a, hipStream_t st) {
   const unsigned items = (unsigned)(a.nchunks * a.B * a.H);
-  ssd_window_kernel<IO, N, CONV, NORM><<<items, 256, 0, st>>>(a);
+  ssd_window_kernel<IO, N, CONV, NORM><<<items, kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -660,7 +935,9 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   char* base = (char*)ws;
   a.ctrl = (unsigned*)(base + wl.ctrl);
   a.flags = (unsigned*)(base + wl.flags);
-  a.states = (float*)(base + wl.states);
+  a.aggdec = (unsigned*)(base + wl.aggdec);
+  a.agg = (float*)(base + wl.agg);
+  a.incl = (float*)(base + wl.incl);
   a.normsum = (float*)(base + wl.normsum);
   const bool conv = d.conv_width == 4, norm = d.norm_group > 0;
   hipError_t e;

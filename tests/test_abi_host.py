@@ -40,15 +40,25 @@ def layer_dims(**kw):
     return m2.make_dims(**base)
 
 
-def test_workspace_size_formula():
-    # control block + one flag and one fp32 P x N hand-off state per (chunk, sequence, head)
-    n = m2.window_workspace_bytes(layer_dims())
-    items = 8 * 128
+def ws_formula(items, state_floats, norm_floats=0):
+    # control block, then per (chunk, sequence, head) item a flag, a decay and
+    # two fp32 hand-off states (aggregate and inclusive), then the norm partials
     up = lambda v: (v + 255) // 256 * 256
-    assert n == up(up(256 + items * 4) + items * 64 * 128 * 4)
+    off = up(11 * 32 * 4)
+    off = up(off + items * 4)
+    off = up(off + items * 4)
+    off = up(off + items * state_floats * 4)
+    off = up(off + items * state_floats * 4)
+    return up(off + norm_floats * 4)
+
+
+def test_workspace_size_formula():
+    assert m2.window_workspace_bytes(layer_dims()) == ws_formula(8 * 128, 64 * 128)
     n2 = m2.window_workspace_bytes(layer_dims(batch=4, norm_group=8192, conv_width=4))
-    items = 8 * 4 * 128
-    assert n2 == up(up(up(256 + items * 4) + items * 64 * 128 * 4) + 4 * 2048 * 128 * 4)
+    assert n2 == ws_formula(8 * 4 * 128, 64 * 128, 4 * 2048 * 128 * 2)
+    # N=16 keeps an 8-wave private layout of 2048 floats per state
+    assert m2.window_workspace_bytes(layer_dims(dstate=16, ngroups=1, nheads=4, seqlen=256, chunk=64)) == \
+        ws_formula(4 * 4, 2048)
 
 
 @pytest.mark.parametrize("kw,code", [
