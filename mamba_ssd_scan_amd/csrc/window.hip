@@ -849,6 +849,554 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_window_kernel(WinArgs<IO> a) 
   }
 }
 
+// ===========================================================================
+// One wave per (chunk, sequence, head, half of the head dim) item, for plain
+// x, B, C inputs.
+//
+// The wave keeps its 32 x N share of the fp32 state in registers as MFMA
+// tiles of s^T[n, p], so the carry-in readout takes its A operand straight
+// from those registers.  Each half of a head is an independent scan (the
+// recurrence is separable over p); splitting heads this way keeps a wave
+// under 256 registers, so two waves share each SIMD.  C fragments go from HBM to registers and feed both C.B^T
+// and the readout; x and B of a 32-token step are staged in a small private
+// LDS tile (B as read, x as read, and x scaled by the per-token state weight)
+// and read back transposed (ds_read_b64_tr_b16) where tokens are the
+// contraction index.  No workgroup barriers: the 2048 items of a 2048-token
+// layer window fill the chip at two waves per SIMD.
+//
+// State columns are kept in a permuted order so that the n-slots a lane owns
+// in the state tiles are the slots it needs for the readout's contraction
+// over n, and so that a C fragment is one contiguous 16-byte read:
+//   tile nt, row 4j + e  <->  n = 32 (nt / 2) + 8 j + 4 (nt % 2) + e   (N >= 32)
+//   tile 0,  row 4j + e  <->  n = 4 j + e                              (N = 16)
+//
+// Inputs are read through buffer descriptors whose range ends at the
+// sequence's last token, so tokens at or past the sequence length read as
+// zero (dt = 0 keeps the state) and their outputs are dropped by the store.
+namespace wv {
+constexpr int TS = 32;                 // tokens per step
+constexpr int PH = 32;                 // head-dim columns per item
+constexpr int PT = PH / 16;            // p-tiles per item
+constexpr int XP = PH + 8;             // pitch (halfs) of the [s][p] x tiles
+constexpr int kSc1 = 16;               // cache policy: device-coherent access
+
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t mkr(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Transposed 64-bit LDS read: within each 16-lane group, lane i receives the
+// 16-bit elements at column (i % 4) of the 8-byte chunks addressed by lanes
+// 4k + i / 4, k = 0..3.
+__device__ __forceinline__ h4 tr4(const _Float16* p) {
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(__attribute__((address_space(3))) void*)(p));
+  return __builtin_bit_cast(h4, v);
+}
+
+// NV (4 or 8) consecutive elements at byte offset off, as binary16, zero-padded to 8
+template <typename IO, int NV> __device__ __forceinline__ h8 ldh(rsrc_t r, unsigned off) {
+  if constexpr (sizeof(IO) == 2) {
+    if constexpr (NV == 8) {
+      return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    } else {
+      const h4 v = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+      return h8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    }
+  } else {
+    const f4 lo = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    f4 hi = f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NV == 8) hi = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    return h8{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
+              (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
+  }
+}
+template <typename IO> __device__ __forceinline__ float ld1(rsrc_t r, unsigned off) {
+  if constexpr (sizeof(IO) == 2)
+    return (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <typename IO> __device__ __forceinline__ f4 ld4f(rsrc_t r, unsigned off) {
+  if constexpr (sizeof(IO) == 2) {
+    const h4 v = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return f4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  } else {
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+}
+template <typename IO> __device__ __forceinline__ void st4(rsrc_t r, unsigned off, f4 v) {
+  if constexpr (sizeof(IO) == 2) {
+    const h4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, hv), r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
+  }
+}
+
+template <int N> struct Sm {
+  static constexpr int NP = N + 8;     // pitch (halfs) of the [s][n] B tile
+  alignas(16) _Float16 x[TS * XP];     // [s][p] x as read
+  alignas(16) _Float16 xw[TS * XP];    // [s][p] x times the state weight of token s
+  alignas(16) _Float16 b[TS * NP];     // [s][n] B as read
+  alignas(16) float S[256];            // running log2-decay from the chunk start (inclusive)
+  alignas(16) _Float16 dts[256];
+  unsigned ticket, gen;
+};
+
+// first state column of the 4-row group j of state tile nt
+template <int N> __device__ __forceinline__ int ncol(int nt, int j) {
+  if constexpr (N >= 32) return 32 * (nt >> 1) + 8 * j + 4 * (nt & 1);
+  else return 4 * j;
+}
+}  // namespace wv
+
+static_assert(kNormParts >= 2, "one g^2 partial per head half");
+
+template <typename IO, int N, bool NORM>
+__global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
+  using namespace wv;
+  constexpr unsigned ES = sizeof(IO);
+  constexpr int NT = N / 16;                    // state tiles along n
+  constexpr int KM = N >= 32 ? N / 32 : 1;      // 32-wide k-steps over n
+  constexpr int NV = N >= 32 ? 8 : 4;           // real n per lane in a k-step
+  constexpr int NCH = N / 8;                    // 16-byte chunks per B row (f16)
+  constexpr int BPL = TS * NCH / 64;            // B chunks per lane per step
+  constexpr int XPL = TS * (PH / 8) / 64;       // x chunks per lane per step
+  constexpr int NP = Sm<N>::NP;
+  __shared__ Sm<N> sm;
+  const int lane = threadIdx.x, lr = lane & 15, q = lane >> 4;
+  // items run over virtual heads hv = 2 h + half
+  const int HV = 2 * a.H;
+  const int BH = a.B * HV;
+  const int hpg = HV / a.G;
+
+  // ---- claim an item: the XCD's own group pairs first, chunk-major --------------
+  if (lane == 0) {
+    sm.gen = __hip_atomic_load(&a.ctrl[kCtrlGen], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned x0 = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u;   // HW_REG_XCC_ID
+    const int BG = a.B * a.G;
+    for (int k = 0; k < 8; ++k) {
+      const unsigned px = (x0 + k) & 7u;
+      const int npairs = BG > (int)px ? (BG - (int)px + 7) / 8 : 0;
+      const unsigned n = (unsigned)(npairs * hpg * a.nchunks);
+      if (n == 0) continue;
+      unsigned* cnt = &a.ctrl[px * kCtrlStride];
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+      const unsigned t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t < n) {
+        const int per_c = npairs * hpg;
+        const int cc = (int)t / per_c, rem = (int)t - cc * per_c;
+        const int gid = (int)px + 8 * (rem / hpg);
+        const int bb = gid / a.G, gg = gid - bb * a.G;
+        sm.ticket = (unsigned)(cc * BH + bb * HV + gg * hpg + rem % hpg);
+        break;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  const unsigned item = sm.ticket, gen = sm.gen;
+  const unsigned tag = (gen & 0x3fffffffu) << 2;
+  const int c = item / BH, bh = item - c * BH;
+  const int b = bh / HV, hv = bh - b * HV;
+  const int h = hv >> 1, half = hv & 1;
+  const int g = hv / hpg;
+  const int hb = b * a.H + h;                   // (sequence, head) index
+  int len = a.seqlens ? a.seqlens[b] : a.L;
+  len = len < 0 ? 0 : (len > a.L ? a.L : len);
+  const int t0 = c * a.Q;
+  const int nvalid = min(max(len - t0, 0), a.Q);
+  const int Jv = (nvalid + TS - 1) / TS;        // steps holding real tokens
+  const float Ah = a.A[h] * kLog2e;
+  const float Dh = a.D[h];
+
+  // buffer views of this sequence (range ends at its last token)
+  const unsigned xrow = (unsigned)(a.H * kP) * ES;     // bytes between tokens in x, z, y
+  const unsigned grow = (unsigned)(a.G * N) * ES;      // in B, C
+  const unsigned xspan = len > 0 ? (unsigned)(len - 1) * xrow + PH * ES : 0u;
+  const unsigned gspan = len > 0 ? (unsigned)(len - 1) * grow + N * ES : 0u;
+  const size_t seq_x = ((size_t)b * a.L * a.H + h) * kP + PH * half;
+  const size_t seq_g = ((size_t)b * a.L * a.G + g) * N;
+  const rsrc_t rx = mkr(a.x + seq_x, xspan);
+  const rsrc_t rb = mkr(a.Bm + seq_g, gspan);
+  const rsrc_t rc = mkr(a.Cm + seq_g, gspan);
+  const rsrc_t ry = mkr(a.y + seq_x, xspan);
+  const rsrc_t rdt = mkr(a.dt + (size_t)b * a.L * a.H + h, len > 0 ? (unsigned)((len - 1) * a.H + 1) * ES : 0u);
+
+  // ---- phase 0: dt and the running log2-decay over the chunk (4 tokens/lane) --
+  {
+    float d[4], v[4];
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * lane + e;
+      d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((t0 + i) * a.H) * ES) : 0.f;
+      run += d[e] * Ah;
+      v[e] = run;
+    }
+    float pre = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float u = __shfl_up(pre, off, 64);
+      if (lane >= off) pre += u;
+    }
+    pre -= run;                                   // exclusive prefix of the lane totals
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * lane + e;
+      if (i < a.Q) {
+        sm.S[i] = v[e] + pre;
+        sm.dts[i] = (_Float16)d[e];
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  const float Send = sm.S[a.Q - 1];
+  const float dec_chunk = exp2f(Send);
+
+  // ---- per-step operands ---------------------------------------------------
+  // lane-constant byte offsets inside a step (the step adds i0 tokens)
+  struct XB { h8 x[XPL]; h8 b[BPL]; };
+  struct CF { h8 f[2][KM]; };                   // C fragments per t-tile and k-step
+  auto fetch_xb = [&](XB& r, int j) {
+    const unsigned tok = (unsigned)(t0 + j * TS);
+#pragma unroll
+    for (int k = 0; k < XPL; ++k) {
+      const int c8 = lane + 64 * k, s = c8 / (PH / 8), pc = c8 % (PH / 8);
+      r.x[k] = ldh<IO, 8>(rx, (tok + s) * xrow + (unsigned)(pc * 8) * ES);
+    }
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      const int c8 = lane + 64 * k, s = c8 / NCH, nc = c8 % NCH;
+      r.b[k] = ldh<IO, 8>(rb, (tok + s) * grow + (unsigned)(nc * 8) * ES);
+    }
+  };
+  auto fetch_c = [&](CF& r, int j) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const unsigned tok = (unsigned)(t0 + j * TS + 16 * T + lr);
+#pragma unroll
+      for (int m = 0; m < KM; ++m) r.f[T][m] = ldh<IO, NV>(rc, tok * grow + (unsigned)(32 * m + NV * q) * ES);
+    }
+  };
+  // stage step j: B as read, x as read (phase 3 only) and x weighted by
+  // dt_s e^{Sref - S_s} for the state contraction
+  auto stage = [&](const XB& r, int j, float Sref, bool natural_x) {
+    const int i0 = j * TS;
+#pragma unroll
+    for (int k = 0; k < XPL; ++k) {
+      const int c8 = lane + 64 * k, s = c8 / (PH / 8), pc = c8 % (PH / 8);
+      const float w = (float)sm.dts[i0 + s] * exp2f(Sref - sm.S[i0 + s]);
+      h8 xw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xw[e] = (_Float16)((float)r.x[k][e] * w);
+      *reinterpret_cast<h8*>(&sm.xw[s * XP + pc * 8]) = xw;
+      if (natural_x) *reinterpret_cast<h8*>(&sm.x[s * XP + pc * 8]) = r.x[k];
+    }
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      const int c8 = lane + 64 * k, s = c8 / NCH, nc = c8 % NCH;
+      *reinterpret_cast<h8*>(&sm.b[s * NP + nc * 8]) = r.b[k];
+    }
+  };
+  auto lds_sync = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  // acc[nt][pt] += sum_s B[s, n] (w_s x[s, p]) over the staged step (K = 32 tokens)
+  auto state_mfma = [&](f4 (&acc)[NT][PT]) {
+    h8 xf[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      const int col = 16 * pt + 4 * (lr & 3);
+      xf[pt] = cat(tr4(&sm.xw[(8 * q + (lr >> 2)) * XP + col]), tr4(&sm.xw[(8 * q + 4 + (lr >> 2)) * XP + col]));
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = ncol<N>(nt, lr & 3);
+      const h8 af = cat(tr4(&sm.b[(8 * q + (lr >> 2)) * NP + col]), tr4(&sm.b[(8 * q + 4 + (lr >> 2)) * NP + col]));
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(af, xf[pt], acc[nt][pt]);
+    }
+  };
+
+  f4 acc[NT][PT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- phase 1: local chunk state ------------------------------------------
+  XB xb;
+  CF cf;
+  if (Jv > 0) fetch_xb(xb, 0);
+  for (int j = 0; j < Jv; ++j) {
+    stage(xb, j, Send, false);
+    lds_sync();
+    if (j + 1 < Jv) fetch_xb(xb, j + 1);
+    else {
+      fetch_xb(xb, 0);                 // first step of the output phase
+      fetch_c(cf, 0);
+    }
+    state_mfma(acc);
+    lds_sync();
+  }
+
+  // ---- phase 2: carry-in state (decoupled look-back), hand-off -------------
+  // hand-off states: per item N*PH floats, tile-major, 16 contiguous bytes per lane
+  constexpr unsigned kStBytes = (unsigned)(N * PH) * 4u;
+  auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * 4u; };
+  auto put = [&](float* base, unsigned it, const f4 (&v)[NT][PT]) {
+    const rsrc_t r = mkr(base + (size_t)it * (N * PH), kStBytes);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v[nt][pt]), r, st_off(nt, pt), 0, kSc1);
+  };
+  auto raise = [&](unsigned status) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) __hip_atomic_store(&a.flags[item], tag | status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  f4 R[NT][PT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) R[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
+  auto load_initial = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const int p = PH * half + 16 * pt + lr, n = ncol<N>(nt, q);
+        R[nt][pt] = *reinterpret_cast<const f4*>(a.state_in + ((size_t)hb * kP + p) * N + n);
+      }
+  };
+  {
+    const bool publish = c + 1 < a.nchunks;
+    if (c > 0 && publish) {
+      put(a.agg, item, acc);
+      if (lane == 0) __hip_atomic_store(&a.aggdec[item], __float_as_uint(dec_chunk), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      raise(1u);
+    }
+    if (c > 0) {
+      // look back over up to 64 predecessors of the same (sequence, head):
+      // the nearest inclusive state, and aggregates of every chunk after it
+      const int W = c < 64 ? c : 64;
+      const unsigned pred = (unsigned)((c - 1 - lane) * BH + bh);
+      unsigned spins = 0;
+      int need = 0, lstar = W;
+      while (true) {
+        unsigned st = 0;
+        if (lane < W) {
+          const unsigned f = __hip_atomic_load(&a.flags[pred], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          st = (f & ~3u) == tag ? (f & 3u) : 0u;
+        }
+        const unsigned long long incl = __ballot(st == 2u), ready = __ballot(st >= 1u);
+        lstar = incl ? (int)__builtin_ctzll(incl) : W;
+        need = lstar;
+        const unsigned long long m = need >= 64 ? ~0ull : ((1ull << need) - 1ull);
+        bool ok = (ready & m) == m;
+        if (lstar == W && c > W) ok = false;
+        if (ok) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          if (lane == 0) __hip_atomic_fetch_or(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          need = 0; lstar = W;
+          break;
+        }
+      }
+      if (lstar < W) {
+        const unsigned it = (unsigned)((c - 1 - lstar) * BH + bh);
+        const rsrc_t r = mkr(a.incl + (size_t)it * (N * PH), kStBytes);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt)
+            R[nt][pt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
+      } else if (a.state_in) {
+        load_initial();
+      }
+      // aggregates of chunks c-need .. c-1 in order: bitwise the same result
+      // as the one-hop-at-a-time chain of inclusive states
+      for (int e = need - 1; e >= 0; --e) {
+        const unsigned it = (unsigned)((c - 1 - e) * BH + bh);
+        const float ae = __uint_as_float(__hip_atomic_load(&a.aggdec[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        const rsrc_t r = mkr(a.agg + (size_t)it * (N * PH), kStBytes);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) {
+            const f4 A4 = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) R[nt][pt][k] = __builtin_fmaf(ae, R[nt][pt][k], A4[k]);
+          }
+      }
+    } else if (a.state_in) {
+      load_initial();
+    }
+    // inclusive state after this chunk (in place of the local state)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[nt][pt][k] = __builtin_fmaf(dec_chunk, R[nt][pt][k], acc[nt][pt][k]);
+    if (publish) {
+      put(a.incl, item, acc);
+      raise(2u);
+    } else if (a.state_out) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const int p = PH * half + 16 * pt + lr, n = ncol<N>(nt, q);
+          *reinterpret_cast<f4*>(a.state_out + ((size_t)hb * kP + p) * N + n) = acc[nt][pt];
+        }
+    }
+  }
+
+  // ---- phase 3: outputs ------------------------------------------------------
+  rsrc_t rz = ry;
+  if constexpr (NORM) rz = mkr(a.z + seq_x, xspan);
+  for (int j = 0; j < Jv; ++j) {
+    const int i0 = j * TS;
+    const float Sj_start = j ? sm.S[i0 - 1] : 0.f;
+    const float Sj_end = sm.S[i0 + TS - 1];
+    stage(xb, j, Sj_end, true);
+    lds_sync();
+    const CF cur = cf;
+    if (j + 1 < Jv) {
+      fetch_xb(xb, j + 1);
+      fetch_c(cf, j + 1);
+    }
+    // decay-masked C.B^T, rows s (4 per lane) x column t (one per lane), per t-tile
+    h8 mf[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int tl = 16 * T + lr;
+      const float St = sm.S[i0 + tl];
+      f4 mb[2];
+#pragma unroll
+      for (int S = 0; S < 2; ++S) {
+        mb[S] = f4{0.f, 0.f, 0.f, 0.f};
+        if (S <= T) {
+          const _Float16* row = &sm.b[(16 * S + lr) * NP];
+#pragma unroll
+          for (int m = 0; m < KM; ++m) {
+            h8 bo;
+            if constexpr (NV == 8) bo = *reinterpret_cast<const h8*>(row + 32 * m + 8 * q);
+            else {
+              const h4 v = *reinterpret_cast<const h4*>(row + 4 * q);
+              bo = h8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+            }
+            mb[S] = mfma16(bo, cur.f[T][m], mb[S]);
+          }
+          const f4 Ss = *reinterpret_cast<const f4*>(&sm.S[i0 + 16 * S + 4 * q]);
+          const h4 ds = *reinterpret_cast<const h4*>(&sm.dts[i0 + 16 * S + 4 * q]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int si = 16 * S + 4 * q + i;
+            mb[S][i] = si <= tl ? mb[S][i] * (float)ds[i] * exp2f(St - Ss[i]) : 0.f;
+          }
+        }
+      }
+      mf[T] = h8{(_Float16)mb[0][0], (_Float16)mb[0][1], (_Float16)mb[0][2], (_Float16)mb[0][3],
+                 (_Float16)mb[1][0], (_Float16)mb[1][1], (_Float16)mb[1][2], (_Float16)mb[1][3]};
+    }
+    float sc[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) sc[T] = exp2f(sm.S[i0 + 16 * T + lr] - Sj_start);
+    float gsq[2] = {0.f, 0.f};
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      // diagonal: sum_s x[s, p] M[s, t]; x rows s = 4q..4q+3 and 16+4q..16+4q+3
+      const int col = 16 * pt + 4 * (lr & 3);
+      const h8 xa = cat(tr4(&sm.x[(4 * q + (lr >> 2)) * XP + col]), tr4(&sm.x[(16 + 4 * q + (lr >> 2)) * XP + col]));
+      // carry-in readout operand: the state rows p of this p-tile as binary16
+      h8 ra[KM];
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        const f4 r0 = R[N >= 32 ? 2 * m : 0][pt];
+        const f4 r1 = N >= 32 ? R[N >= 32 ? 2 * m + 1 : 0][pt] : f4{0.f, 0.f, 0.f, 0.f};
+        ra[m] = h8{(_Float16)r0[0], (_Float16)r0[1], (_Float16)r0[2], (_Float16)r0[3],
+                   (_Float16)r1[0], (_Float16)r1[1], (_Float16)r1[2], (_Float16)r1[3]};
+      }
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const int tl = 16 * T + lr;
+        const f4 yd = mfma16(xa, mf[T], f4{0.f, 0.f, 0.f, 0.f});
+        f4 yr = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KM; ++m) yr = mfma16(ra[m], cur.f[T][m], yr);
+        const int p0 = 16 * pt + 4 * q;
+        const h4 xr = *reinterpret_cast<const h4*>(&sm.x[tl * XP + p0]);
+        const unsigned off = (unsigned)(t0 + i0 + tl) * xrow + (unsigned)p0 * ES;
+        f4 out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = __builtin_fmaf(sc[T], yr[i], yd[i]) + Dh * (float)xr[i];
+        if constexpr (NORM) {
+          const f4 zz = ld4f<IO>(rz, off);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            out[i] = out[i] * (zz[i] / (1.f + __expf(-zz[i])));
+            gsq[T] += out[i] * out[i];
+          }
+        }
+        st4<IO>(ry, off, out);
+      }
+    }
+    if constexpr (NORM) {
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        float v = gsq[T];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        const int tl = 16 * T + lr;
+        if (q == 0 && t0 + i0 + tl < len) {
+          const size_t tok = (size_t)b * a.L + t0 + i0 + tl;
+          a.normsum[(tok * a.H + h) * kNormParts + half] = v;
+          if (half == 0) {
+#pragma unroll
+            for (int k = 2; k < kNormParts; ++k) a.normsum[(tok * a.H + h) * kNormParts + k] = 0.f;
+          }
+        }
+      }
+    }
+    // running state for the next step: R <- e^{S_end_j - S_start_j} R + sum_s w_s B_s x_s
+    if (j + 1 < Jv) {
+      const float dec = exp2f(Sj_end - Sj_start);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
+      state_mfma(R);
+    }
+    lds_sync();
+  }
+
+  // ---- retire -------------------------------------------------------------------
+  if (lane == 0) {
+    const unsigned total = (unsigned)(a.nchunks * BH);
+    const unsigned done = __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == total - 1) {
+      for (int k = 0; k < 8; ++k) __hip_atomic_store(&a.ctrl[k * kCtrlStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl[kCtrlDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl[kCtrlGen], gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Gated RMSNorm finish: out = g * rsqrt(mean_group(g^2) + eps) * w, with the
 // per-head sums of g^2 produced by the scan's epilogue.  One block per token.
 template <typename IO>
@@ -890,9 +1438,11 @@ static WsLayout ws_layout(const mamba2_dims& d) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   WsLayout w;
   w.ctrl = 0;
+  // flags and decays for up to two items per (chunk, sequence, head): the
+  // plain-input scan splits each head into two independent halves
   w.flags = up(kCtrlBytes);
-  w.aggdec = up(w.flags + items * 4);
-  w.agg = up(w.aggdec + items * 4);
+  w.aggdec = up(w.flags + 2 * items * 4);
+  w.agg = up(w.aggdec + 2 * items * 4);
   const size_t sf = d.dstate == 128 ? Lay<128>::STATE_FLOATS : (d.dstate == 64 ? Lay<64>::STATE_FLOATS
                                                                                  : Lay<16>::STATE_FLOATS);
   w.incl = up(w.agg + items * sf * 4);
@@ -906,7 +1456,8 @@ size_t window_workspace_bytes(const mamba2_dims& d) { return ws_layout(d).total;
 template <typename IO, int N, bool CONV, bool NORM>
 static hipError_t launch_T(const WinArgs<IO>& a, hipStream_t st) {
   const unsigned items = (unsigned)(a.nchunks * a.B * a.H);
-  ssd_window_kernel<IO, N, CONV, NORM><<<items, kThreads, 0, st>>>(a);
+  if constexpr (CONV) ssd_window_kernel<IO, N, CONV, NORM><<<items, kThreads, 0, st>>>(a);
+  else ssd_window_wave_kernel<IO, N, NORM><<<2 * items, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

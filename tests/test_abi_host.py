@@ -41,12 +41,14 @@ def layer_dims(**kw):
 
 
 def ws_formula(items, state_floats, norm_floats=0):
-    # control block, then per (chunk, sequence, head) item a flag, a decay and
-    # two fp32 hand-off states (aggregate and inclusive), then the norm partials
+    # control block, then two flags and two decays per (chunk, sequence, head)
+    # (the plain-input scan runs each head as two halves), two fp32 hand-off
+    # states per (chunk, sequence, head) (aggregate and inclusive), then the
+    # norm partials
     up = lambda v: (v + 255) // 256 * 256
     off = up(11 * 32 * 4)
-    off = up(off + items * 4)
-    off = up(off + items * 4)
+    off = up(off + 2 * items * 4)
+    off = up(off + 2 * items * 4)
     off = up(off + items * state_floats * 4)
     off = up(off + items * state_floats * 4)
     return up(off + norm_floats * 4)
