@@ -850,19 +850,20 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_window_kernel(WinArgs<IO> a) 
 }
 
 // ===========================================================================
-// One wave per (chunk, sequence, head, half of the head dim) item, for plain
-// x, B, C inputs.
+// Chunked scan for plain x, B, C inputs: one workgroup per (chunk, sequence,
+// group, block of KH heads of the group), one wave per (head, half of the
+// head dim).
 //
-// The wave keeps its 32 x N share of the fp32 state in registers as MFMA
-// tiles of s^T[n, p], so the carry-in readout takes its A operand straight
-// from those registers.  Each half of a head is an independent scan (the
-// recurrence is separable over p); splitting heads this way keeps a wave
-// under 256 registers, so two waves share each SIMD.  C fragments go from HBM to registers and feed both C.B^T
-// and the readout; x and B of a 32-token step are staged in a small private
-// LDS tile (B as read, x as read, and x scaled by the per-token state weight)
-// and read back transposed (ds_read_b64_tr_b16) where tokens are the
-// contraction index.  No workgroup barriers: the 2048 items of a 2048-token
-// layer window fill the chip at two waves per SIMD.
+// Each half of a head is an independent scan (the recurrence is separable
+// over p).  A wave keeps its 32 x N share of the fp32 state in registers as
+// MFMA tiles of s^T[n, p], so the carry-in readout takes its A operand
+// straight from those registers, and the wave stays within 256 registers so
+// that two waves share each SIMD.  The KH heads of a workgroup read the same
+// B and C rows: each 32-token step of B and C is loaded once per workgroup
+// into LDS tiles (as read, [token][n]) and every wave takes its operands from
+// there; x of a step goes into a per-wave LDS tile, once as read and once
+// scaled by the per-token state weight, and is read back transposed
+// (ds_read_b64_tr_b16) where tokens are the contraction index.
 //
 // State columns are kept in a permuted order so that the n-slots a lane owns
 // in the state tiles are the slots it needs for the readout's contraction
@@ -885,9 +886,21 @@ typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Buffer descriptor over [p, p + bytes).  p and bytes must be wave-uniform;
+// they are read from the first lane so that the descriptor is built in SGPRs
+// (a descriptor the compiler cannot prove uniform turns every access through
+// it into a loop over lanes).
 __device__ __forceinline__ rsrc_t mkr(const void* p, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  void* const pu = (void*)(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
+
+// 2^x with the hardware exponential (arguments here are <= 0; results below
+// the binary32 normal range are negligible against the terms they scale)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Transposed 64-bit LDS read: within each 16-lane group, lane i receives the
 // 16-bit elements at column (i % 4) of the 8-byte chunks addressed by lanes
@@ -938,13 +951,17 @@ template <typename IO> __device__ __forceinline__ void st4(rsrc_t r, unsigned of
   }
 }
 
-template <int N> struct Sm {
-  static constexpr int NP = N + 8;     // pitch (halfs) of the [s][n] B tile
-  alignas(16) _Float16 x[TS * XP];     // [s][p] x as read
-  alignas(16) _Float16 xw[TS * XP];    // [s][p] x times the state weight of token s
+constexpr int KH = 4;                  // heads per workgroup
+constexpr int NWV = 2 * KH;            // waves per workgroup
+
+template <int N> struct SmG {
+  static constexpr int NP = N + 8;     // pitch (halfs) of the [s][n] B and C tiles
   alignas(16) _Float16 b[TS * NP];     // [s][n] B as read
-  alignas(16) float S[256];            // running log2-decay from the chunk start (inclusive)
-  alignas(16) _Float16 dts[256];
+  alignas(16) _Float16 c[TS * NP];     // [t][n] C as read
+  alignas(16) _Float16 x[NWV][TS * XP];   // per wave: [s][p] x as read
+  alignas(16) _Float16 xw[NWV][TS * XP];  // per wave: x times the state weight of token s
+  alignas(16) float S[NWV][256];       // per wave: running log2-decay from the chunk start (inclusive)
+  alignas(16) _Float16 dts[NWV][256];
   unsigned ticket, gen;
 };
 
@@ -958,57 +975,66 @@ template <int N> __device__ __forceinline__ int ncol(int nt, int j) {
 static_assert(kNormParts >= 2, "one g^2 partial per head half");
 
 template <typename IO, int N, bool NORM>
-__global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
+__global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<IO> a) {
   using namespace wv;
   constexpr unsigned ES = sizeof(IO);
   constexpr int NT = N / 16;                    // state tiles along n
   constexpr int KM = N >= 32 ? N / 32 : 1;      // 32-wide k-steps over n
   constexpr int NV = N >= 32 ? 8 : 4;           // real n per lane in a k-step
-  constexpr int NCH = N / 8;                    // 16-byte chunks per B row (f16)
-  constexpr int BPL = TS * NCH / 64;            // B chunks per lane per step
+  constexpr int NCH = N / 8;                    // 8-element chunks per B or C row
+  constexpr int NTH = 64 * NWV;
+  constexpr int BK = (TS * NCH + NTH - 1) / NTH;   // B (and C) chunks per thread per step
   constexpr int XPL = TS * (PH / 8) / 64;       // x chunks per lane per step
-  constexpr int NP = Sm<N>::NP;
-  __shared__ Sm<N> sm;
-  const int lane = threadIdx.x, lr = lane & 15, q = lane >> 4;
-  // items run over virtual heads hv = 2 h + half
+  constexpr int NP = SmG<N>::NP;
+  __shared__ SmG<N> sm;
+  // wave-uniform values are pinned to scalar registers (readfirstlane): the
+  // buffer descriptors built from them must live in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, q = lane >> 4;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hpg = a.H / a.G;
+  const int nhb = (hpg + KH - 1) / KH;          // head blocks per group
+  const int BG = a.B * a.G;
+  // hand-off items run over virtual heads hv = 2 h + half
   const int HV = 2 * a.H;
-  const int BH = a.B * HV;
-  const int hpg = HV / a.G;
+  const int BHV = a.B * HV;
 
-  // ---- claim an item: the XCD's own group pairs first, chunk-major --------------
-  if (lane == 0) {
+  // ---- claim a workgroup item: the XCD's own group pairs first, chunk-major --
+  if (tid == 0) {
     sm.gen = __hip_atomic_load(&a.ctrl[kCtrlGen], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned x0 = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u;   // HW_REG_XCC_ID
-    const int BG = a.B * a.G;
     for (int k = 0; k < 8; ++k) {
       const unsigned px = (x0 + k) & 7u;
       const int npairs = BG > (int)px ? (BG - (int)px + 7) / 8 : 0;
-      const unsigned n = (unsigned)(npairs * hpg * a.nchunks);
+      const unsigned n = (unsigned)(npairs * nhb * a.nchunks);
       if (n == 0) continue;
       unsigned* cnt = &a.ctrl[px * kCtrlStride];
       if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
       const unsigned t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (t < n) {
-        const int per_c = npairs * hpg;
+        const int per_c = npairs * nhb;
         const int cc = (int)t / per_c, rem = (int)t - cc * per_c;
-        const int gid = (int)px + 8 * (rem / hpg);
-        const int bb = gid / a.G, gg = gid - bb * a.G;
-        sm.ticket = (unsigned)(cc * BH + bb * HV + gg * hpg + rem % hpg);
+        const int gid = (int)px + 8 * (rem / nhb);
+        sm.ticket = (unsigned)((cc * BG + gid) * nhb + rem % nhb);
         break;
       }
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  const unsigned item = sm.ticket, gen = sm.gen;
+  __syncthreads();
+  const unsigned ticket = __builtin_amdgcn_readfirstlane(sm.ticket);
+  const unsigned gen = __builtin_amdgcn_readfirstlane(sm.gen);
   const unsigned tag = (gen & 0x3fffffffu) << 2;
-  const int c = item / BH, bh = item - c * BH;
-  const int b = bh / HV, hv = bh - b * HV;
-  const int h = hv >> 1, half = hv & 1;
-  const int g = hv / hpg;
+  const int hblk = (int)(ticket % (unsigned)nhb);
+  const int c = (int)(ticket / (unsigned)nhb) / BG;
+  const int gid = (int)(ticket / (unsigned)nhb) - c * BG;
+  const int b = gid / a.G, g = gid - b * a.G;
+  const int hin = hblk * KH + (wid >> 1);       // head within the group
+  const bool live = hin < hpg;                  // waves past the group's last head only help load B, C
+  const int h = g * hpg + (live ? hin : 0);
+  const int half = wid & 1;
   const int hb = b * a.H + h;                   // (sequence, head) index
-  int len = a.seqlens ? a.seqlens[b] : a.L;
+  const int bhv = b * HV + 2 * h + half;
+  const unsigned item = (unsigned)(c * BHV + bhv);
+  int len = a.seqlens ? __builtin_amdgcn_readfirstlane(a.seqlens[b]) : a.L;
   len = len < 0 ? 0 : (len > a.L ? a.L : len);
   const int t0 = c * a.Q;
   const int nvalid = min(max(len - t0, 0), a.Q);
@@ -1019,7 +1045,7 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
   // buffer views of this sequence (range ends at its last token)
   const unsigned xrow = (unsigned)(a.H * kP) * ES;     // bytes between tokens in x, z, y
   const unsigned grow = (unsigned)(a.G * N) * ES;      // in B, C
-  const unsigned xspan = len > 0 ? (unsigned)(len - 1) * xrow + PH * ES : 0u;
+  const unsigned xspan = len > 0 && live ? (unsigned)(len - 1) * xrow + PH * ES : 0u;
   const unsigned gspan = len > 0 ? (unsigned)(len - 1) * grow + N * ES : 0u;
   const size_t seq_x = ((size_t)b * a.L * a.H + h) * kP + PH * half;
   const size_t seq_g = ((size_t)b * a.L * a.G + g) * N;
@@ -1027,7 +1053,11 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
   const rsrc_t rb = mkr(a.Bm + seq_g, gspan);
   const rsrc_t rc = mkr(a.Cm + seq_g, gspan);
   const rsrc_t ry = mkr(a.y + seq_x, xspan);
-  const rsrc_t rdt = mkr(a.dt + (size_t)b * a.L * a.H + h, len > 0 ? (unsigned)((len - 1) * a.H + 1) * ES : 0u);
+  const rsrc_t rdt = mkr(a.dt + (size_t)b * a.L * a.H + h, len > 0 && live ? (unsigned)((len - 1) * a.H + 1) * ES : 0u);
+  float* const Sw = sm.S[wid];
+  _Float16* const dtw = sm.dts[wid];
+  _Float16* const xs = sm.x[wid];
+  _Float16* const xws = sm.xw[wid];
 
   // ---- phase 0: dt and the running log2-decay over the chunk (4 tokens/lane) --
   {
@@ -1051,22 +1081,20 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * lane + e;
       if (i < a.Q) {
-        sm.S[i] = v[e] + pre;
-        sm.dts[i] = (_Float16)d[e];
+        Sw[i] = v[e] + pre;
+        dtw[i] = (_Float16)d[e];
       }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  const float Send = sm.S[a.Q - 1];
-  const float dec_chunk = exp2f(Send);
+  const float Send = Sw[a.Q - 1];
+  const float dec_chunk = ex2(Send);
 
   // ---- per-step operands ---------------------------------------------------
-  // lane-constant byte offsets inside a step (the step adds i0 tokens)
-  struct XB { h8 x[XPL]; h8 b[BPL]; };
-  struct CF { h8 f[2][KM]; };                   // C fragments per t-tile and k-step
-  auto fetch_xb = [&](XB& r, int j) {
+  struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; };
+  auto fetch = [&](XB& r, int j, bool with_c) {
     const unsigned tok = (unsigned)(t0 + j * TS);
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
@@ -1074,43 +1102,37 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
       r.x[k] = ldh<IO, 8>(rx, (tok + s) * xrow + (unsigned)(pc * 8) * ES);
     }
 #pragma unroll
-    for (int k = 0; k < BPL; ++k) {
-      const int c8 = lane + 64 * k, s = c8 / NCH, nc = c8 % NCH;
-      r.b[k] = ldh<IO, 8>(rb, (tok + s) * grow + (unsigned)(nc * 8) * ES);
+    for (int k = 0; k < BK; ++k) {
+      const int id = tid + NTH * k, s = id / NCH, nc = id % NCH;
+      if (id < TS * NCH) {
+        const unsigned off = (tok + s) * grow + (unsigned)(nc * 8) * ES;
+        r.b[k] = ldh<IO, 8>(rb, off);
+        if (with_c) r.c[k] = ldh<IO, 8>(rc, off);
+      }
     }
   };
-  auto fetch_c = [&](CF& r, int j) {
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const unsigned tok = (unsigned)(t0 + j * TS + 16 * T + lr);
-#pragma unroll
-      for (int m = 0; m < KM; ++m) r.f[T][m] = ldh<IO, NV>(rc, tok * grow + (unsigned)(32 * m + NV * q) * ES);
-    }
-  };
-  // stage step j: B as read, x as read (phase 3 only) and x weighted by
-  // dt_s e^{Sref - S_s} for the state contraction
-  auto stage = [&](const XB& r, int j, float Sref, bool natural_x) {
+  // stage step j: B (and C) as read, x as read (phase 3 only) and x weighted
+  // by dt_s e^{Sref - S_s} for the state contraction
+  auto stage = [&](const XB& r, int j, float Sref, bool with_c) {
     const int i0 = j * TS;
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
       const int c8 = lane + 64 * k, s = c8 / (PH / 8), pc = c8 % (PH / 8);
-      const float w = (float)sm.dts[i0 + s] * exp2f(Sref - sm.S[i0 + s]);
+      const float w = (float)dtw[i0 + s] * ex2(Sref - Sw[i0 + s]);
       h8 xw;
 #pragma unroll
       for (int e = 0; e < 8; ++e) xw[e] = (_Float16)((float)r.x[k][e] * w);
-      *reinterpret_cast<h8*>(&sm.xw[s * XP + pc * 8]) = xw;
-      if (natural_x) *reinterpret_cast<h8*>(&sm.x[s * XP + pc * 8]) = r.x[k];
+      *reinterpret_cast<h8*>(&xws[s * XP + pc * 8]) = xw;
+      if (with_c) *reinterpret_cast<h8*>(&xs[s * XP + pc * 8]) = r.x[k];
     }
 #pragma unroll
-    for (int k = 0; k < BPL; ++k) {
-      const int c8 = lane + 64 * k, s = c8 / NCH, nc = c8 % NCH;
-      *reinterpret_cast<h8*>(&sm.b[s * NP + nc * 8]) = r.b[k];
+    for (int k = 0; k < BK; ++k) {
+      const int id = tid + NTH * k, s = id / NCH, nc = id % NCH;
+      if (id < TS * NCH) {
+        *reinterpret_cast<h8*>(&sm.b[s * NP + nc * 8]) = r.b[k];
+        if (with_c) *reinterpret_cast<h8*>(&sm.c[s * NP + nc * 8]) = r.c[k];
+      }
     }
-  };
-  auto lds_sync = [&]() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
   // acc[nt][pt] += sum_s B[s, n] (w_s x[s, p]) over the staged step (K = 32 tokens)
   auto state_mfma = [&](f4 (&acc)[NT][PT]) {
@@ -1118,7 +1140,7 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
       const int col = 16 * pt + 4 * (lr & 3);
-      xf[pt] = cat(tr4(&sm.xw[(8 * q + (lr >> 2)) * XP + col]), tr4(&sm.xw[(8 * q + 4 + (lr >> 2)) * XP + col]));
+      xf[pt] = cat(tr4(&xws[(8 * q + (lr >> 2)) * XP + col]), tr4(&xws[(8 * q + 4 + (lr >> 2)) * XP + col]));
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1126,6 +1148,15 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
       const h8 af = cat(tr4(&sm.b[(8 * q + (lr >> 2)) * NP + col]), tr4(&sm.b[(8 * q + 4 + (lr >> 2)) * NP + col]));
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(af, xf[pt], acc[nt][pt]);
+    }
+  };
+  // 8 (or 4) n of row r of an LDS [s][n] tile at the n-slots of k-step m
+  auto row8 = [&](const _Float16* tile, int r, int m) -> h8 {
+    const _Float16* row = tile + r * NP;
+    if constexpr (NV == 8) return *reinterpret_cast<const h8*>(row + 32 * m + 8 * q);
+    else {
+      const h4 v = *reinterpret_cast<const h4*>(row + 4 * q);
+      return h8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
     }
   };
 
@@ -1137,18 +1168,13 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
 
   // ---- phase 1: local chunk state ------------------------------------------
   XB xb;
-  CF cf;
-  if (Jv > 0) fetch_xb(xb, 0);
+  if (Jv > 0) fetch(xb, 0, false);
   for (int j = 0; j < Jv; ++j) {
     stage(xb, j, Send, false);
-    lds_sync();
-    if (j + 1 < Jv) fetch_xb(xb, j + 1);
-    else {
-      fetch_xb(xb, 0);                 // first step of the output phase
-      fetch_c(cf, 0);
-    }
-    state_mfma(acc);
-    lds_sync();
+    lds_barrier();
+    fetch(xb, j + 1 < Jv ? j + 1 : 0, j + 1 == Jv);   // the last fetch is the output phase's first step
+    if (live) state_mfma(acc);
+    lds_barrier();
   }
 
   // ---- phase 2: carry-in state (decoupled look-back), hand-off -------------
@@ -1181,7 +1207,7 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
         R[nt][pt] = *reinterpret_cast<const f4*>(a.state_in + ((size_t)hb * kP + p) * N + n);
       }
   };
-  {
+  if (live) {
     const bool publish = c + 1 < a.nchunks;
     if (c > 0 && publish) {
       put(a.agg, item, acc);
@@ -1190,10 +1216,10 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
       raise(1u);
     }
     if (c > 0) {
-      // look back over up to 64 predecessors of the same (sequence, head):
+      // look back over up to 64 predecessors of the same (sequence, head, half):
       // the nearest inclusive state, and aggregates of every chunk after it
       const int W = c < 64 ? c : 64;
-      const unsigned pred = (unsigned)((c - 1 - lane) * BH + bh);
+      const unsigned pred = (unsigned)((c - 1 - lane) * BHV + bhv);
       unsigned spins = 0;
       int need = 0, lstar = W;
       while (true) {
@@ -1217,7 +1243,7 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
         }
       }
       if (lstar < W) {
-        const unsigned it = (unsigned)((c - 1 - lstar) * BH + bh);
+        const unsigned it = (unsigned)((c - 1 - lstar) * BHV + bhv);
         const rsrc_t r = mkr(a.incl + (size_t)it * (N * PH), kStBytes);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -1230,7 +1256,7 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
       // aggregates of chunks c-need .. c-1 in order: bitwise the same result
       // as the one-hop-at-a-time chain of inclusive states
       for (int e = need - 1; e >= 0; --e) {
-        const unsigned it = (unsigned)((c - 1 - e) * BH + bh);
+        const unsigned it = (unsigned)((c - 1 - e) * BHV + bhv);
         const float ae = __uint_as_float(__hip_atomic_load(&a.aggdec[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         const rsrc_t r = mkr(a.agg + (size_t)it * (N * PH), kStBytes);
 #pragma unroll
@@ -1271,123 +1297,118 @@ __global__ __launch_bounds__(64, 2) void ssd_window_wave_kernel(WinArgs<IO> a) {
   if constexpr (NORM) rz = mkr(a.z + seq_x, xspan);
   for (int j = 0; j < Jv; ++j) {
     const int i0 = j * TS;
-    const float Sj_start = j ? sm.S[i0 - 1] : 0.f;
-    const float Sj_end = sm.S[i0 + TS - 1];
+    const float Sj_start = j ? Sw[i0 - 1] : 0.f;
+    const float Sj_end = Sw[i0 + TS - 1];
     stage(xb, j, Sj_end, true);
-    lds_sync();
-    const CF cur = cf;
-    if (j + 1 < Jv) {
-      fetch_xb(xb, j + 1);
-      fetch_c(cf, j + 1);
-    }
-    // decay-masked C.B^T, rows s (4 per lane) x column t (one per lane), per t-tile
-    h8 mf[2];
+    lds_barrier();
+    if (j + 1 < Jv) fetch(xb, j + 1, true);
+    if (live) {
+      // C fragments: rows t = 16T + lr, n-slots of k-step m
+      h8 cf[2][KM];
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const int tl = 16 * T + lr;
-      const float St = sm.S[i0 + tl];
-      f4 mb[2];
+      for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int S = 0; S < 2; ++S) {
-        mb[S] = f4{0.f, 0.f, 0.f, 0.f};
-        if (S <= T) {
-          const _Float16* row = &sm.b[(16 * S + lr) * NP];
+        for (int m = 0; m < KM; ++m) cf[T][m] = row8(sm.c, 16 * T + lr, m);
+      // decay-masked C.B^T, rows s (4 per lane) x column t (one per lane), per t-tile
+      h8 mf[2];
 #pragma unroll
-          for (int m = 0; m < KM; ++m) {
-            h8 bo;
-            if constexpr (NV == 8) bo = *reinterpret_cast<const h8*>(row + 32 * m + 8 * q);
-            else {
-              const h4 v = *reinterpret_cast<const h4*>(row + 4 * q);
-              bo = h8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+      for (int T = 0; T < 2; ++T) {
+        const int tl = 16 * T + lr;
+        const float St = Sw[i0 + tl];
+        f4 mb[2];
+#pragma unroll
+        for (int S = 0; S < 2; ++S) {
+          mb[S] = f4{0.f, 0.f, 0.f, 0.f};
+          if (S <= T) {
+#pragma unroll
+            for (int m = 0; m < KM; ++m) mb[S] = mfma16(row8(sm.b, 16 * S + lr, m), cf[T][m], mb[S]);
+            const f4 Ss = *reinterpret_cast<const f4*>(&Sw[i0 + 16 * S + 4 * q]);
+            const h4 ds = *reinterpret_cast<const h4*>(&dtw[i0 + 16 * S + 4 * q]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int si = 16 * S + 4 * q + i;
+              mb[S][i] = si <= tl ? mb[S][i] * (float)ds[i] * ex2(St - Ss[i]) : 0.f;
             }
-            mb[S] = mfma16(bo, cur.f[T][m], mb[S]);
           }
-          const f4 Ss = *reinterpret_cast<const f4*>(&sm.S[i0 + 16 * S + 4 * q]);
-          const h4 ds = *reinterpret_cast<const h4*>(&sm.dts[i0 + 16 * S + 4 * q]);
+        }
+        mf[T] = h8{(_Float16)mb[0][0], (_Float16)mb[0][1], (_Float16)mb[0][2], (_Float16)mb[0][3],
+                   (_Float16)mb[1][0], (_Float16)mb[1][1], (_Float16)mb[1][2], (_Float16)mb[1][3]};
+      }
+      float sc[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int si = 16 * S + 4 * q + i;
-            mb[S][i] = si <= tl ? mb[S][i] * (float)ds[i] * exp2f(St - Ss[i]) : 0.f;
+      for (int T = 0; T < 2; ++T) sc[T] = ex2(Sw[i0 + 16 * T + lr] - Sj_start);
+      float gsq[2] = {0.f, 0.f};
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        // diagonal: sum_s x[s, p] M[s, t]; x rows s = 4q..4q+3 and 16+4q..16+4q+3
+        const int col = 16 * pt + 4 * (lr & 3);
+        const h8 xa = cat(tr4(&xs[(4 * q + (lr >> 2)) * XP + col]), tr4(&xs[(16 + 4 * q + (lr >> 2)) * XP + col]));
+        // carry-in readout operand: the state rows p of this p-tile as binary16
+        h8 ra[KM];
+#pragma unroll
+        for (int m = 0; m < KM; ++m) {
+          const f4 r0 = R[N >= 32 ? 2 * m : 0][pt];
+          const f4 r1 = N >= 32 ? R[N >= 32 ? 2 * m + 1 : 0][pt] : f4{0.f, 0.f, 0.f, 0.f};
+          ra[m] = h8{(_Float16)r0[0], (_Float16)r0[1], (_Float16)r0[2], (_Float16)r0[3],
+                     (_Float16)r1[0], (_Float16)r1[1], (_Float16)r1[2], (_Float16)r1[3]};
+        }
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+          const int tl = 16 * T + lr;
+          const f4 yd = mfma16(xa, mf[T], f4{0.f, 0.f, 0.f, 0.f});
+          f4 yr = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < KM; ++m) yr = mfma16(ra[m], cf[T][m], yr);
+          const int p0 = 16 * pt + 4 * q;
+          const h4 xr = *reinterpret_cast<const h4*>(&xs[tl * XP + p0]);
+          const unsigned off = (unsigned)(t0 + i0 + tl) * xrow + (unsigned)p0 * ES;
+          f4 out;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[i] = __builtin_fmaf(sc[T], yr[i], yd[i]) + Dh * (float)xr[i];
+          if constexpr (NORM) {
+            const f4 zz = ld4f<IO>(rz, off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              out[i] = out[i] * (zz[i] / (1.f + __expf(-zz[i])));
+              gsq[T] += out[i] * out[i];
+            }
+          }
+          st4<IO>(ry, off, out);
+        }
+      }
+      if constexpr (NORM) {
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+          float v = gsq[T];
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          const int tl = 16 * T + lr;
+          if (q == 0 && t0 + i0 + tl < len) {
+            const size_t tok = (size_t)b * a.L + t0 + i0 + tl;
+            a.normsum[(tok * a.H + h) * kNormParts + half] = v;
+            if (half == 0) {
+#pragma unroll
+              for (int k = 2; k < kNormParts; ++k) a.normsum[(tok * a.H + h) * kNormParts + k] = 0.f;
+            }
           }
         }
       }
-      mf[T] = h8{(_Float16)mb[0][0], (_Float16)mb[0][1], (_Float16)mb[0][2], (_Float16)mb[0][3],
-                 (_Float16)mb[1][0], (_Float16)mb[1][1], (_Float16)mb[1][2], (_Float16)mb[1][3]};
-    }
-    float sc[2];
+      // running state for the next step: R <- e^{S_end_j - S_start_j} R + sum_s w_s B_s x_s
+      if (j + 1 < Jv) {
+        const float dec = ex2(Sj_end - Sj_start);
 #pragma unroll
-    for (int T = 0; T < 2; ++T) sc[T] = exp2f(sm.S[i0 + 16 * T + lr] - Sj_start);
-    float gsq[2] = {0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-      // diagonal: sum_s x[s, p] M[s, t]; x rows s = 4q..4q+3 and 16+4q..16+4q+3
-      const int col = 16 * pt + 4 * (lr & 3);
-      const h8 xa = cat(tr4(&sm.x[(4 * q + (lr >> 2)) * XP + col]), tr4(&sm.x[(16 + 4 * q + (lr >> 2)) * XP + col]));
-      // carry-in readout operand: the state rows p of this p-tile as binary16
-      h8 ra[KM];
-#pragma unroll
-      for (int m = 0; m < KM; ++m) {
-        const f4 r0 = R[N >= 32 ? 2 * m : 0][pt];
-        const f4 r1 = N >= 32 ? R[N >= 32 ? 2 * m + 1 : 0][pt] : f4{0.f, 0.f, 0.f, 0.f};
-        ra[m] = h8{(_Float16)r0[0], (_Float16)r0[1], (_Float16)r0[2], (_Float16)r0[3],
-                   (_Float16)r1[0], (_Float16)r1[1], (_Float16)r1[2], (_Float16)r1[3]};
-      }
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        const int tl = 16 * T + lr;
-        const f4 yd = mfma16(xa, mf[T], f4{0.f, 0.f, 0.f, 0.f});
-        f4 yr = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < KM; ++m) yr = mfma16(ra[m], cur.f[T][m], yr);
-        const int p0 = 16 * pt + 4 * q;
-        const h4 xr = *reinterpret_cast<const h4*>(&sm.x[tl * XP + p0]);
-        const unsigned off = (unsigned)(t0 + i0 + tl) * xrow + (unsigned)p0 * ES;
-        f4 out;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = __builtin_fmaf(sc[T], yr[i], yd[i]) + Dh * (float)xr[i];
-        if constexpr (NORM) {
-          const f4 zz = ld4f<IO>(rz, off);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            out[i] = out[i] * (zz[i] / (1.f + __expf(-zz[i])));
-            gsq[T] += out[i] * out[i];
-          }
-        }
-        st4<IO>(ry, off, out);
+          for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
+        state_mfma(R);
       }
     }
-    if constexpr (NORM) {
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        float v = gsq[T];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        const int tl = 16 * T + lr;
-        if (q == 0 && t0 + i0 + tl < len) {
-          const size_t tok = (size_t)b * a.L + t0 + i0 + tl;
-          a.normsum[(tok * a.H + h) * kNormParts + half] = v;
-          if (half == 0) {
-#pragma unroll
-            for (int k = 2; k < kNormParts; ++k) a.normsum[(tok * a.H + h) * kNormParts + k] = 0.f;
-          }
-        }
-      }
-    }
-    // running state for the next step: R <- e^{S_end_j - S_start_j} R + sum_s w_s B_s x_s
-    if (j + 1 < Jv) {
-      const float dec = exp2f(Sj_end - Sj_start);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
-      state_mfma(R);
-    }
-    lds_sync();
+    lds_barrier();
   }
 
   // ---- retire -------------------------------------------------------------------
-  if (lane == 0) {
-    const unsigned total = (unsigned)(a.nchunks * BH);
+  if (tid == 0) {
+    const unsigned total = (unsigned)(a.nchunks * BG * nhb);
     const unsigned done = __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == total - 1) {
       for (int k = 0; k < 8; ++k) __hip_atomic_store(&a.ctrl[k * kCtrlStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1457,7 +1478,11 @@ template <typename IO, int N, bool CONV, bool NORM>
 static hipError_t launch_T(const WinArgs<IO>& a, hipStream_t st) {
   const unsigned items = (unsigned)(a.nchunks * a.B * a.H);
   if constexpr (CONV) ssd_window_kernel<IO, N, CONV, NORM><<<items, kThreads, 0, st>>>(a);
-  else ssd_window_wave_kernel<IO, N, NORM><<<2 * items, 64, 0, st>>>(a);
+  else {
+    const int hpg = a.H / a.G;
+    const unsigned wgs = (unsigned)(a.nchunks * a.B * a.G * ((hpg + wv::KH - 1) / wv::KH));
+    ssd_window_group_kernel<IO, N, NORM><<<wgs, 64 * wv::NWV, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
