@@ -1177,117 +1177,106 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     lds_barrier();
   }
 
-  // ---- phase 2: carry-in state (decoupled look-back), hand-off -------------
+  // ---- phase 2: carry-in state over a binary-indexed tree of chunks ---------
+  // With i = c + 1, chunk c publishes the aggregate of chunks (i - lowbit(i), i]
+  // (1-based), and its carry-in is the initial state advanced through the
+  // aggregates that tile [1, i-1].  Those aggregates are taken newest first,
+  // n_1 = i-1, n_{k+1} = n_k - lowbit(n_k):
+  //   carry = F(n_1) + D(n_1) F(n_2) + D(n_1) D(n_2) F(n_3) + ... + (prod D) h0
+  // (F: aggregate state, D: its decay), so the aggregates that are ready first
+  // are folded in first.  The first ctz(i) of them cover (i - lowbit(i), i-1]:
+  // once they are folded in, the running sum combined with the local state is
+  // this chunk's own aggregate, published for later chunks.  A chunk waits
+  // only on earlier chunks (claimed before it), on at most log2(#chunks) of
+  // them, and the order of the sums is fixed, so results do not depend on
+  // timing.
   // hand-off states: per item N*PH floats, tile-major, 16 contiguous bytes per lane
   constexpr unsigned kStBytes = (unsigned)(N * PH) * 4u;
   auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * 4u; };
-  auto put = [&](float* base, unsigned it, const f4 (&v)[NT][PT]) {
-    const rsrc_t r = mkr(base + (size_t)it * (N * PH), kStBytes);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v[nt][pt]), r, st_off(nt, pt), 0, kSc1);
-  };
-  auto raise = [&](unsigned status) {
-    __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) __hip_atomic_store(&a.flags[item], tag | status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto node_item = [&](int j) -> unsigned { return (unsigned)((j - 1) * BHV + bhv); };   // j: 1-based chunk
+  auto wait_node = [&](unsigned it) {
+    unsigned spins = 0;
+    while (true) {
+      const unsigned f = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&a.flags[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (f == (tag | 1u)) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        if (lane == 0) __hip_atomic_fetch_or(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
   };
   f4 R[NT][PT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) R[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
-  auto load_initial = [&]() {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        const int p = PH * half + 16 * pt + lr, n = ncol<N>(nt, q);
-        R[nt][pt] = *reinterpret_cast<const f4*>(a.state_in + ((size_t)hb * kP + p) * N + n);
-      }
-  };
   if (live) {
-    const bool publish = c + 1 < a.nchunks;
-    if (c > 0 && publish) {
-      put(a.agg, item, acc);
-      if (lane == 0) __hip_atomic_store(&a.aggdec[item], __float_as_uint(dec_chunk), __ATOMIC_RELAXED,
+    const int i = c + 1;
+    const bool last = c + 1 == a.nchunks;
+    const int t = __builtin_ctz((unsigned)i);
+    float scale = 1.f;                                     // product of the decays folded in so far
+    auto publish = [&]() {                                 // own aggregate: (dec_chunk R + local, dec_chunk scale)
+      const rsrc_t r = mkr(a.agg + (size_t)item * (N * PH), kStBytes);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          f4 v = acc[nt][pt];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(dec_chunk, R[nt][pt][k], v[k]);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
+        }
+      if (lane == 0) __hip_atomic_store(&a.aggdec[item], __float_as_uint(dec_chunk * scale), __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
-      raise(1u);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (lane == 0) __hip_atomic_store(&a.flags[item], tag | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    int k = 0;
+    for (int n = i - 1; n > 0; n -= n & -n, ++k) {
+      if (k == t && !last) publish();
+      const unsigned it = node_item(n);
+      wait_node(it);
+      const float Dn = __uint_as_float(__builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&a.aggdec[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+      const rsrc_t r = mkr(a.agg + (size_t)it * (N * PH), kStBytes);
+      f4 F[NT][PT];                                        // all loads in flight at once
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+          F[nt][pt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, F[nt][pt][e], R[nt][pt][e]);
+      scale *= Dn;
     }
-    if (c > 0) {
-      // look back over up to 64 predecessors of the same (sequence, head, half):
-      // the nearest inclusive state, and aggregates of every chunk after it
-      const int W = c < 64 ? c : 64;
-      const unsigned pred = (unsigned)((c - 1 - lane) * BHV + bhv);
-      unsigned spins = 0;
-      int need = 0, lstar = W;
-      while (true) {
-        unsigned st = 0;
-        if (lane < W) {
-          const unsigned f = __hip_atomic_load(&a.flags[pred], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          st = (f & ~3u) == tag ? (f & 3u) : 0u;
-        }
-        const unsigned long long incl = __ballot(st == 2u), ready = __ballot(st >= 1u);
-        lstar = incl ? (int)__builtin_ctzll(incl) : W;
-        need = lstar;
-        const unsigned long long m = need >= 64 ? ~0ull : ((1ull << need) - 1ull);
-        bool ok = (ready & m) == m;
-        if (lstar == W && c > W) ok = false;
-        if (ok) break;
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
-          if (lane == 0) __hip_atomic_fetch_or(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          need = 0; lstar = W;
-          break;
-        }
-      }
-      if (lstar < W) {
-        const unsigned it = (unsigned)((c - 1 - lstar) * BHV + bhv);
-        const rsrc_t r = mkr(a.incl + (size_t)it * (N * PH), kStBytes);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt)
-            R[nt][pt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
-      } else if (a.state_in) {
-        load_initial();
-      }
-      // aggregates of chunks c-need .. c-1 in order: bitwise the same result
-      // as the one-hop-at-a-time chain of inclusive states
-      for (int e = need - 1; e >= 0; --e) {
-        const unsigned it = (unsigned)((c - 1 - e) * BHV + bhv);
-        const float ae = __uint_as_float(__hip_atomic_load(&a.aggdec[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        const rsrc_t r = mkr(a.agg + (size_t)it * (N * PH), kStBytes);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt) {
-            const f4 A4 = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
-#pragma unroll
-            for (int k = 0; k < 4; ++k) R[nt][pt][k] = __builtin_fmaf(ae, R[nt][pt][k], A4[k]);
-          }
-      }
-    } else if (a.state_in) {
-      load_initial();
-    }
-    // inclusive state after this chunk (in place of the local state)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[nt][pt][k] = __builtin_fmaf(dec_chunk, R[nt][pt][k], acc[nt][pt][k]);
-    if (publish) {
-      put(a.incl, item, acc);
-      raise(2u);
-    } else if (a.state_out) {
+    if (k <= t && !last) publish();                        // fewer than ctz(i) aggregates before it: i is a power of 2
+    if (a.state_in) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
           const int p = PH * half + 16 * pt + lr, n = ncol<N>(nt, q);
-          *reinterpret_cast<f4*>(a.state_out + ((size_t)hb * kP + p) * N + n) = acc[nt][pt];
+          const f4 h0 = *reinterpret_cast<const f4*>(a.state_in + ((size_t)hb * kP + p) * N + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, h0[e], R[nt][pt][e]);
+        }
+    }
+    if (last && a.state_out) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const int p = PH * half + 16 * pt + lr, n = ncol<N>(nt, q);
+          f4 v = acc[nt][pt];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(dec_chunk, R[nt][pt][e], v[e]);
+          *reinterpret_cast<f4*>(a.state_out + ((size_t)hb * kP + p) * N + n) = v;
         }
     }
   }
