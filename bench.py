@@ -11,10 +11,15 @@ oracle is re-checked on the timed buffers before any number is printed.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line.
+
+  --copy-probe MIB   copy MIB of device memory a few times and exit; the HBM
+                     counters of this plain copy calibrate the counters of the
+                     scan kernel (profiles/window_layer_traffic.txt)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +33,43 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_F16_PEAK = 2500.0     # TFLOP/s dense f16
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_layer_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "mamba_ssd_scan_amd", "csrc", "window.hip")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the scan kernel from the committed counter
+    summary, or None when the summary is missing or was taken on a different
+    kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    """Plain device copies of known size (counter calibration)."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch_read": n, "copy_bytes_per_launch_write": n, "launches": 5}), flush=True)
 
 
 def window_bytes(B, L, H, P, N, G, lens=None):
@@ -43,17 +85,17 @@ def decode_bytes(B, H, P, N, G):
     return B * H * P * N * 2 * 2 + B * H * P * 2 * 2 + B * G * N * 2 * 2 + B * H * 2 + 2 * H * 4
 
 
-def window_mfma_flops(L, H, P, N, Q=256, sub=64):
-    """f16 MFMA flops the kernel issues per window (B=1): per (chunk, head) the
-    64-token sub-chunk diagonal (C.B^T over the causal 16x16 tiles and the
-    masked product), the sub-chunk states and the carry-in readout."""
-    nsub = L // sub
-    tiles = sub // 16
-    cb = sum(t + 1 for t in range(tiles)) * 2 * 16 * 16 * max(N, 32)
-    diag = sum((t // 2 + 1) for t in range(tiles)) * P // 16 * 2 * 16 * 16 * 32
-    st = 2 * P * N * sub
-    ro = 2 * P * N * sub
-    return H * nsub * (cb + diag + st + ro)
+def window_mfma_flops(L, H, P, N, Q=256, step=32, half=32):
+    """f16 MFMA flops the window kernel issues for one sequence (16x16x32
+    instructions, 16384 flops each).  Per (chunk, half of a head) and 32-token
+    step: the chunk-state pass takes N/16 x half/16 instructions; the output
+    pass takes the causal C.B^T blocks (3 blocks x N/32), the masked product
+    (2 x half/16), the carry readout (2 x half/16 x N/32) and, except on the
+    last step, the running-state update (N/16 x half/16)."""
+    J = Q // step
+    nt, pt, km = N // 16, half // 16, max(N // 32, 1)
+    per = nt * pt * J + (3 * km + 2 * pt + 2 * pt * km) * J + nt * pt * (J - 1)
+    return (L // Q) * H * (P // half) * per * 16384
 
 
 def main():
@@ -64,7 +106,11 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=5, help="rotated input/output buffer sets")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the scan shards by sequence and head with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -225,7 +271,7 @@ def main():
                    "headdim": P, "dstate": N, "ngroups": G, "chunk": Q, "io": "f16", "state": "f32",
                    "buffer_sets": args.sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "window_us": round(ms * 1e3, 2),
         "window_latency_us": round(lat_us, 2),
