@@ -120,6 +120,7 @@ template <typename IO> struct WinArgs {
   float* agg;         // per item local chunk state (private layout)
   float* incl;        // per item inclusive state after the chunk (private layout)
   unsigned* aggdec;   // per item chunk decay e^{S_end} (float bits)
+  int tree_lg;        // log2 of the radix of the chunk tree (plain-input scan)
 };
 
 // control block: eight claim counters and the done counter / generation /
@@ -867,9 +868,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_window_kernel(WinArgs<IO> a) 
 //
 // State columns are kept in a permuted order so that the n-slots a lane owns
 // in the state tiles are the slots it needs for the readout's contraction
-// over n, and so that a C fragment is one contiguous 16-byte read:
-//   tile nt, row 4j + e  <->  n = 32 (nt / 2) + 8 j + 4 (nt % 2) + e   (N >= 32)
-//   tile 0,  row 4j + e  <->  n = 4 j + e                              (N = 16)
+// over n, so that a C fragment is one contiguous 16-byte read, and so that
+// the four column groups of a transposed read of the B tile fall N/4 columns
+// apart (in different LDS banks):
+//   tile nt, row 4j + e  <->  n = (N/4) j + 8 (nt / 2) + 4 (nt % 2) + e   (N >= 32)
+//   tile 0,  row 4j + e  <->  n = 4 j + e                                 (N = 16)
 //
 // Inputs are read through buffer descriptors whose range ends at the
 // sequence's last token, so tokens at or past the sequence length read as
@@ -967,7 +970,7 @@ template <int N> struct SmG {
 
 // first state column of the 4-row group j of state tile nt
 template <int N> __device__ __forceinline__ int ncol(int nt, int j) {
-  if constexpr (N >= 32) return 32 * (nt >> 1) + 8 * j + 4 * (nt & 1);
+  if constexpr (N >= 32) return (N / 4) * j + 8 * (nt >> 1) + 4 * (nt & 1);
   else return 4 * j;
 }
 }  // namespace wv
@@ -1153,7 +1156,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   // 8 (or 4) n of row r of an LDS [s][n] tile at the n-slots of k-step m
   auto row8 = [&](const _Float16* tile, int r, int m) -> h8 {
     const _Float16* row = tile + r * NP;
-    if constexpr (NV == 8) return *reinterpret_cast<const h8*>(row + 32 * m + 8 * q);
+    if constexpr (NV == 8) return *reinterpret_cast<const h8*>(row + (N / 4) * q + 8 * m);
     else {
       const h4 v = *reinterpret_cast<const h4*>(row + 4 * q);
       return h8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
@@ -1177,36 +1180,26 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     lds_barrier();
   }
 
-  // ---- phase 2: carry-in state over a binary-indexed tree of chunks ---------
-  // With i = c + 1, chunk c publishes the aggregate of chunks (i - lowbit(i), i]
-  // (1-based), and its carry-in is the initial state advanced through the
-  // aggregates that tile [1, i-1].  Those aggregates are taken newest first,
-  // n_1 = i-1, n_{k+1} = n_k - lowbit(n_k):
+  // ---- phase 2: carry-in state over an indexed tree of chunks (radix r = 2^lg)
+  // With i = c + 1 and block(i) = r^(number of trailing zero base-r digits of i),
+  // chunk c publishes the aggregate of chunks (i - block(i), i] (1-based), and
+  // its carry-in is the initial state advanced through the aggregates that
+  // tile [1, i-1].  Those aggregates are taken newest first,
+  // n_1 = i-1, n_{k+1} = n_k - block(n_k):
   //   carry = F(n_1) + D(n_1) F(n_2) + D(n_1) D(n_2) F(n_3) + ... + (prod D) h0
   // (F: aggregate state, D: its decay), so the aggregates that are ready first
-  // are folded in first.  The first ctz(i) of them cover (i - lowbit(i), i-1]:
-  // once they are folded in, the running sum combined with the local state is
-  // this chunk's own aggregate, published for later chunks.  A chunk waits
-  // only on earlier chunks (claimed before it), on at most log2(#chunks) of
-  // them, and the order of the sums is fixed, so results do not depend on
-  // timing.
+  // are folded in first.  The first (r-1) log_r(block(i)) of them cover
+  // (i - block(i), i-1]: once they are folded in, the running sum combined
+  // with the local state is this chunk's own aggregate, published for later
+  // chunks.  A chunk waits only on earlier chunks (claimed before it), and the
+  // order of the sums is fixed, so results do not depend on timing.  A larger
+  // radix means fewer dependent publishes (shorter latency chain) and more
+  // aggregate loads (more traffic).
   // hand-off states: per item N*PH floats, tile-major, 16 contiguous bytes per lane
   constexpr unsigned kStBytes = (unsigned)(N * PH) * 4u;
   auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * 4u; };
   auto node_item = [&](int j) -> unsigned { return (unsigned)((j - 1) * BHV + bhv); };   // j: 1-based chunk
-  auto wait_node = [&](unsigned it) {
-    unsigned spins = 0;
-    while (true) {
-      const unsigned f = __builtin_amdgcn_readfirstlane(
-          __hip_atomic_load(&a.flags[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      if (f == (tag | 1u)) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        if (lane == 0) __hip_atomic_fetch_or(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  };
+
   f4 R[NT][PT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -1215,7 +1208,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   if (live) {
     const int i = c + 1;
     const bool last = c + 1 == a.nchunks;
-    const int t = __builtin_ctz((unsigned)i);
+    const int lg = a.tree_lg;                             // tree radix 2^lg
+    const int t = ((1 << lg) - 1) * (__builtin_ctz((unsigned)i) / lg);   // aggregates inside this chunk's block
     float scale = 1.f;                                     // product of the decays folded in so far
     auto publish = [&]() {                                 // own aggregate: (dec_chunk R + local, dec_chunk scale)
       const rsrc_t r = mkr(a.agg + (size_t)item * (N * PH), kStBytes);
@@ -1233,14 +1227,33 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       __builtin_amdgcn_s_waitcnt(0);
       if (lane == 0) __hip_atomic_store(&a.flags[item], tag | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    int k = 0;
-    for (int n = i - 1; n > 0; n -= n & -n, ++k) {
-      if (k == t && !last) publish();
-      const unsigned it = node_item(n);
-      wait_node(it);
-      const float Dn = __uint_as_float(__builtin_amdgcn_readfirstlane(
-          __hip_atomic_load(&a.aggdec[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
-      const rsrc_t r = mkr(a.agg + (size_t)it * (N * PH), kStBytes);
+    // the aggregates to fold, newest first: lane k holds the k-th (1-based chunk)
+    int nodes = 0, my_node = 0;
+    for (int n = i - 1; n > 0; n -= 1 << (lg * (__builtin_ctz((unsigned)n) / lg)), ++nodes)
+      if (lane == nodes) my_node = n;
+    // wait until aggregates k0 .. k1-1 are published (one flag per lane, all
+    // polled together), then read their decays
+    float my_dec = 1.f;
+    auto wait_group = [&](int k0, int k1) {
+      const bool mine = lane >= k0 && lane < k1;
+      const unsigned it = mine ? node_item(my_node) : 0u;
+      unsigned spins = 0;
+      while (true) {
+        bool ready = true;
+        if (mine) ready = __hip_atomic_load(&a.flags[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (tag | 1u);
+        if (__ballot(!ready) == 0) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          if (lane == 0) __hip_atomic_fetch_or(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      if (mine) my_dec = __uint_as_float(__hip_atomic_load(&a.aggdec[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    };
+    auto fold = [&](int k) {
+      const int n = __builtin_amdgcn_readlane(my_node, k);
+      const float Dn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
+      const rsrc_t r = mkr(a.agg + (size_t)node_item(n) * (N * PH), kStBytes);
       f4 F[NT][PT];                                        // all loads in flight at once
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -1254,8 +1267,18 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 #pragma unroll
           for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, F[nt][pt][e], R[nt][pt][e]);
       scale *= Dn;
+    };
+    // the first t aggregates are this chunk's block: fold them, publish, then the rest
+    const int tb = t < nodes ? t : nodes;
+    if (tb > 0) {
+      wait_group(0, tb);
+      for (int k = 0; k < tb; ++k) fold(k);
     }
-    if (k <= t && !last) publish();                        // fewer than ctz(i) aggregates before it: i is a power of 2
+    if (!last) publish();
+    if (nodes > tb) {
+      wait_group(tb, nodes);
+      for (int k = tb; k < nodes; ++k) fold(k);
+    }
     if (a.state_in) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -1463,6 +1486,18 @@ static WsLayout ws_layout(const mamba2_dims& d) {
 
 size_t window_workspace_bytes(const mamba2_dims& d) { return ws_layout(d).total; }
 
+// compute units of the current device (cached per device)
+static int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev] = n;
+  return n;
+}
+
 template <typename IO, int N, bool CONV, bool NORM>
 static hipError_t launch_T(const WinArgs<IO>& a, hipStream_t st) {
   const unsigned items = (unsigned)(a.nchunks * a.B * a.H);
@@ -1470,7 +1505,13 @@ static hipError_t launch_T(const WinArgs<IO>& a, hipStream_t st) {
   else {
     const int hpg = a.H / a.G;
     const unsigned wgs = (unsigned)(a.nchunks * a.B * a.G * ((hpg + wv::KH - 1) / wv::KH));
-    ssd_window_group_kernel<IO, N, NORM><<<wgs, 64 * wv::NWV, 0, st>>>(a);
+    // When every workgroup is resident at once (one per CU), all chunks reach
+    // the hand-off together and the chain of dependent publishes is the
+    // critical path: a radix-8 tree.  Otherwise chunk levels are staggered in
+    // time and aggregate traffic matters more: radix 4.
+    WinArgs<IO> b = a;
+    b.tree_lg = wgs <= (unsigned)device_cus() ? 3 : 2;
+    ssd_window_group_kernel<IO, N, NORM><<<wgs, 64 * wv::NWV, 0, st>>>(b);
   }
   return hipGetLastError();
 }

@@ -72,6 +72,16 @@ def test_chunk_sizes_and_state_sizes(chunk, N):
     check_window(f"N={N}", inp, chunk)
 
 
+@pytest.mark.parametrize("B", [1, 8])
+def test_many_chunks_carry_tree(B):
+    # 64 chunks per sequence: a deep carry tree.  One sequence fits the chip in
+    # one pass of workgroups (radix-8 tree); eight do not (radix-4 tree).
+    inp = rand_window(31 + B, B, 4096, 4, 16, 1)
+    lens = [4096] * B if B == 1 else [4096, 4000, 3, 64, 65, 2048, 4095, 1000]
+    h0 = np.random.default_rng(32).standard_normal((B, 4, 64, 16)).astype(np.float32) * 0.3
+    check_window(f"64 chunks B={B}", inp, 64, seqlens=lens, state_in=h0)
+
+
 def test_ragged_batch_with_initial_state():
     inp = rand_window(21, 3, 700, 16, 128, 2)
     h0 = np.random.default_rng(22).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
