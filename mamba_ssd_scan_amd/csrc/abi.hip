@@ -140,7 +140,13 @@ static int32_t check_window(const mamba2_dims* d) {
   if (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) return MAMBA2_EUNSUPPORTED;
   const int64_t nchunks = ((int64_t)d->seqlen + d->chunk - 1) / d->chunk;
   const int64_t items = nchunks * d->batch * d->nheads;
-  if (items > (int64_t)1 << 30) return MAMBA2_EUNSUPPORTED;
+  if (items > (int64_t)1 << 29) return MAMBA2_EUNSUPPORTED;
+  // one sequence's rows of x, B, C, y, z (or of xBC) are addressed with 32-bit
+  // byte offsets
+  const int64_t es = d->io_dtype == MAMBA2_F16 ? 2 : 4;
+  const int64_t row = d->conv_width == 4 ? (int64_t)d->nheads * d->headdim + 2 * (int64_t)d->ngroups * d->dstate
+                                         : (int64_t)d->nheads * d->headdim;
+  if ((int64_t)d->seqlen * row * es >= ((int64_t)1 << 31)) return MAMBA2_EUNSUPPORTED;
   return MAMBA2_OK;
 }
 

@@ -18,9 +18,16 @@
 
 namespace m2 {
 
+// The resident state is streamed once per step and not reused before the
+// next step touches the rest of the batch: its loads and stores are marked
+// non-temporal so that they do not evict the other operands from the caches.
 template <int N> struct StateF16 {
   using T = _Float16;
-  static __device__ __forceinline__ void load(const T* p, float* v) { io<_Float16>::load8(p, v); }
+  static __device__ __forceinline__ void load(const T* p, float* v) {
+    const h8 h = __builtin_nontemporal_load(reinterpret_cast<const h8*>(p));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+  }
   static __device__ __forceinline__ void store(T* p, const float* v) {
     h8 h;
 #pragma unroll
@@ -34,7 +41,7 @@ template <int N> struct StateF16 {
       asm volatile("" : "+v"(t));
       h[i] = (_Float16)t;
     }
-    *reinterpret_cast<h8*>(p) = h;
+    __builtin_nontemporal_store(h, reinterpret_cast<h8*>(p));
   }
 };
 template <int N> struct StateF32 {

@@ -40,27 +40,33 @@ def layer_dims(**kw):
     return m2.make_dims(**base)
 
 
-def ws_formula(items, state_floats, norm_floats=0):
-    # control block, then two flags and two decays per (chunk, sequence, head)
-    # (the plain-input scan runs each head as two halves), two fp32 hand-off
-    # states per (chunk, sequence, head) (aggregate and inclusive), then the
-    # norm partials
+def ws_formula(chunk_items, N, norm_floats=0, conv_bytes=0):
+    # control block; per (chunk, sequence, head, half) item a flag, a decay
+    # and an fp32 aggregate of N x 32; the norm partials; the conv output
     up = lambda v: (v + 255) // 256 * 256
+    items = 2 * chunk_items
     off = up(11 * 32 * 4)
-    off = up(off + 2 * items * 4)
-    off = up(off + 2 * items * 4)
-    off = up(off + items * state_floats * 4)
-    off = up(off + items * state_floats * 4)
-    return up(off + norm_floats * 4)
+    off = up(off + items * 4)
+    off = up(off + items * 4)
+    off = up(off + items * N * 32 * 4)
+    off = up(off + norm_floats * 4)
+    return up(off + conv_bytes)
 
 
 def test_workspace_size_formula():
-    assert m2.window_workspace_bytes(layer_dims()) == ws_formula(8 * 128, 64 * 128)
+    assert m2.window_workspace_bytes(layer_dims()) == ws_formula(8 * 128, 128)
     n2 = m2.window_workspace_bytes(layer_dims(batch=4, norm_group=8192, conv_width=4))
-    assert n2 == ws_formula(8 * 4 * 128, 64 * 128, 4 * 2048 * 128 * 2)
-    # N=16 keeps an 8-wave private layout of 2048 floats per state
+    assert n2 == ws_formula(8 * 4 * 128, 128, 4 * 2048 * 128 * 2, 4 * 2048 * 10240 * 2)
     assert m2.window_workspace_bytes(layer_dims(dstate=16, ngroups=1, nheads=4, seqlen=256, chunk=64)) == \
-        ws_formula(4 * 4, 2048)
+        ws_formula(4 * 4, 16)
+
+
+def test_long_sequences_beyond_32_bit_rows_are_refused():
+    # 2^31 bytes of one sequence's x rows: 131072 tokens x 8192 channels x 2 bytes
+    n = ctypes.c_size_t(0)
+    lib = m2.load_library()
+    assert lib.mamba2_window_workspace_bytes(ctypes.byref(layer_dims(seqlen=131072)), ctypes.byref(n)) == -2
+    assert lib.mamba2_window_workspace_bytes(ctypes.byref(layer_dims(seqlen=131071)), ctypes.byref(n)) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
