@@ -80,6 +80,14 @@ def window_bytes(B, L, H, P, N, G, lens=None):
     return toks * per_tok + B * H * P * N * 4 + 2 * H * 4       # final state, A, D
 
 
+def mixer_bytes(B, L, H, P, N, G):
+    """Algorithmic bytes of one mixer-core call (f16 I/O, no conv state in):
+    raw xBC, dt and z read, the normed output written, the final states and
+    the conv states written, the conv weights and bias read."""
+    Cd = H * P + 2 * G * N
+    return B * L * (2 * Cd + 2 * H + 2 * H * P + 2 * H * P) + B * H * P * N * 4 + B * Cd * 3 * 2 + Cd * 5 * 4
+
+
 def decode_bytes(B, H, P, N, G):
     """Algorithmic bytes of one decode step with a binary16 resident state."""
     return B * H * P * N * 2 * 2 + B * H * P * 2 * 2 + B * G * N * 2 * 2 + B * H * 2 + 2 * H * 4
@@ -192,6 +200,47 @@ def main():
     del sets
     torch.cuda.empty_cache()
 
+    # ---- mixer core: conv1d+SiLU, scan, gated RMSNorm (batch 4, L=2048) --------
+    # timing only (parity of this path is covered by the GPU tests); inputs are
+    # drawn on the device with the mixer workload's distributions
+    ms_ = synth.mixer_window()
+    MB_, ML_, MH_, MN_, MG_ = ms_.batch, ms_.seqlen, ms_.nheads, ms_.dstate, ms_.ngroups
+    Cd_ = MH_ * P + 2 * MG_ * MN_
+    gen = torch.Generator(device=dev).manual_seed(1004)
+    mx = {
+        "xBC": torch.randn(MB_, ML_, Cd_, device=dev, generator=gen).half(),
+        "conv_w": torch.randn(Cd_, 4, device=dev, generator=gen) * 0.5,
+        "conv_b": torch.zeros(Cd_, device=dev),
+        "dt": torch.nn.functional.softplus(torch.randn(MB_, ML_, MH_, device=dev, generator=gen) - 3.0).half(),
+        "z": torch.randn(MB_, ML_, MH_ * P, device=dev, generator=gen).half(),
+        "norm_w": torch.ones(MH_ * P, device=dev),
+    }
+    mA = -torch.exp(torch.rand(MH_, device=dev, generator=gen) * float(np.log(16.0)))
+    mD = torch.randn(MH_, device=dev, generator=gen)
+    my = torch.empty(MB_, ML_, MH_ * P, dtype=torch.float16, device=dev)
+    mh = torch.empty(MB_, MH_, P, MN_, dtype=torch.float32, device=dev)
+    mcs = torch.empty(MB_, Cd_, 3, dtype=torch.float16, device=dev)
+    mdims = m2.make_dims(MB_, ML_, MH_, P, MN_, MG_, Q, conv_width=4, norm_group=MH_ * P)
+    mws = m2.alloc_workspace(mdims, dev)
+
+    def mstep():
+        m2.conv_scan_window(mx["dt"], mA, mD, my, mws, xBC=mx["xBC"], conv_w=mx["conv_w"], conv_b=mx["conv_b"],
+                            conv_state_out=mcs, state_out=mh, z=mx["z"], norm_w=mx["norm_w"], chunk=Q,
+                            norm_group=MH_ * P, ngroups=MG_, dstate=MN_, headdim=P, stream=stream)
+
+    for _ in range(3):
+        mstep()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(20):
+        mstep()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    mix_us = ev0.elapsed_time(ev1) * 1e3 / 20
+    mbytes = mixer_bytes(MB_, ML_, MH_, P, MN_, MG_)
+    del mx, my, mh, mcs, mws
+    torch.cuda.empty_cache()
+
     # ---- decode: 64 sequences, binary16 resident state ------------------------
     d = synth.DECODE
     DB, DH, DP, DN, DG, T = d["batch"], d["nheads"], d["headdim"], d["dstate"], d["ngroups"], args.decode_steps
@@ -279,6 +328,10 @@ def main():
         "window_mfma_tflops": round(mflops / (ms * 1e-3) / 1e12, 1),
         "window_mfma_frac": round(mflops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK, 4),
         "parity": {"y": float(f"{worst_y:.3e}"), "state": float(f"{worst_s:.3e}")},
+        "mixer": {"workload": "conv1d(4)+SiLU, scan, gated RMSNorm over 8192 channels", "batch": MB_,
+                  "seq_len": ML_, "us": round(mix_us, 2), "tokens_per_s": round(MB_ * ML_ / (mix_us * 1e-6), 1),
+                  "algorithmic_bytes": mbytes, "achieved_GBs": round(mbytes / (mix_us * 1e-6) / 1e9, 1),
+                  "frac": round(mbytes / (mix_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "decode": {"us_per_step": round(dec_us, 2), "us_per_step_rotated_states": round(dec_rot_us, 2),
                    "algorithmic_bytes": dbytes, "achieved_GBs": round(dbytes / (dec_rot_us * 1e-6) / 1e9, 1),
                    "frac": round(dbytes / (dec_rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

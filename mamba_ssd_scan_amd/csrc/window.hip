@@ -373,6 +373,29 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   _Float16* const xs = sm.x[wid];
   _Float16* const xws = sm.xw[wid];
 
+  // ---- per-step operands ---------------------------------------------------
+  struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; };
+  auto fetch = [&](XB& r, int j, bool with_c) {
+    const unsigned tok = (unsigned)(t0 + j * TS);
+#pragma unroll
+    for (int k = 0; k < XPL; ++k) {
+      const int c8 = lane + 64 * k, s = c8 / (PH / 8), pc = c8 % (PH / 8);
+      r.x[k] = ldh<IO, 8>(rx, (tok + s) * xrow + (unsigned)(pc * 8) * ES);
+    }
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+      const int id = tid + NTH * k, s = id / NCH, nc = id % NCH;
+      if (id < TS * NCH) {
+        const unsigned off = (tok + s) * grow + (unsigned)(nc * 8) * ES;
+        r.b[k] = ldh<IO, 8>(rb, off);
+        if (with_c) r.c[k] = ldh<IO, 8>(rc, off);
+      }
+    }
+  };
+  // the first step's loads go out before the dt scan, so both latencies overlap
+  XB xb;
+  if (Jv > 0) fetch(xb, 0, false);
+
   // ---- phase 0: dt and the running log2-decay over the chunk (4 tokens/lane) --
   {
     float d[4], v[4];
@@ -406,25 +429,6 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   const float Send = Sw[a.Q - 1];
   const float dec_chunk = ex2(Send);
 
-  // ---- per-step operands ---------------------------------------------------
-  struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; };
-  auto fetch = [&](XB& r, int j, bool with_c) {
-    const unsigned tok = (unsigned)(t0 + j * TS);
-#pragma unroll
-    for (int k = 0; k < XPL; ++k) {
-      const int c8 = lane + 64 * k, s = c8 / (PH / 8), pc = c8 % (PH / 8);
-      r.x[k] = ldh<IO, 8>(rx, (tok + s) * xrow + (unsigned)(pc * 8) * ES);
-    }
-#pragma unroll
-    for (int k = 0; k < BK; ++k) {
-      const int id = tid + NTH * k, s = id / NCH, nc = id % NCH;
-      if (id < TS * NCH) {
-        const unsigned off = (tok + s) * grow + (unsigned)(nc * 8) * ES;
-        r.b[k] = ldh<IO, 8>(rb, off);
-        if (with_c) r.c[k] = ldh<IO, 8>(rc, off);
-      }
-    }
-  };
   // stage step j: B (and C) as read, x as read (phase 3 only) and x weighted
   // by dt_s e^{Sref - S_s} for the state contraction
   auto stage = [&](const XB& r, int j, float Sref, bool with_c) {
@@ -481,8 +485,6 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
 
   // ---- phase 1: local chunk state ------------------------------------------
-  XB xb;
-  if (Jv > 0) fetch(xb, 0, false);
   for (int j = 0; j < Jv; ++j) {
     stage(xb, j, Send, false);
     lds_barrier();
