@@ -20,6 +20,8 @@
 //    state out;
 //  * ssd_window_group_kernel: the chunked scan (see the comment above it);
 //  * gated_norm_kernel: the RMS finish of the gated norm.
+#include <type_traits>
+
 #include "common.h"
 #include "../../include/mamba2ssd.h"
 
@@ -80,7 +82,36 @@ __device__ __forceinline__ h8 cat(h4 lo, h4 hi) { return h8{lo[0], lo[1], lo[2],
 // registers, so every raw row is read once (plus a 3-row halo per tile).
 // Rows at or past a sequence's length read as zero; the thread that sees a
 // sequence's last token writes the last 3 raw tokens as the conv state out.
-constexpr int kConvTT = 32;
+constexpr int kConvTT = 32;  // tokens per thread
+constexpr int kConvRB = 8;   // raw rows per batch; batch k+1 is loaded while batch k is computed
+
+// 8 raw channels of one token in the input's own type (packed: 4 registers for f16).
+template <typename IO> struct Raw8;
+template <> struct Raw8<_Float16> {
+  h8 v;
+  __device__ __forceinline__ void load(const _Float16* p) { v = *reinterpret_cast<const h8*>(p); }
+  __device__ __forceinline__ void zero() { v = h8{}; }
+  __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
+  __device__ __forceinline__ void set(int e, float x) { v[e] = (_Float16)x; }
+};
+template <> struct Raw8<float> {
+  f4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f4*>(p);
+    b = *reinterpret_cast<const f4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = f4{}; b = f4{}; }
+  __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
+  __device__ __forceinline__ void set(int e, float x) { if (e < 4) a[e] = x; else b[e - 4] = x; }
+};
+template <typename IO> __device__ __forceinline__ void store_raw8(IO* p, const Raw8<IO>& r);
+template <> __device__ __forceinline__ void store_raw8(_Float16* p, const Raw8<_Float16>& r) {
+  *reinterpret_cast<h8*>(p) = r.v;
+}
+template <> __device__ __forceinline__ void store_raw8(float* p, const Raw8<float>& r) {
+  *reinterpret_cast<f4*>(p) = r.a;
+  *reinterpret_cast<f4*>(p + 4) = r.b;
+}
 
 template <typename IO>
 __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ xBC, const float* __restrict__ w,
@@ -96,6 +127,32 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
   const int c0 = cc * 8, t0 = tt * kConvTT;
   int len = seqlens ? seqlens[b] : L;
   len = len < 0 ? 0 : (len > L ? L : len);
+  const IO* src = xBC + (size_t)b * L * Cd + c0;
+  // Row t >= 0 of these channels, zero at or past the length.  The address is
+  // clamped into the sequence and the zero applied by a select, so the loads
+  // carry no branch and a whole batch is in flight at once.
+  const int tmax = len > 0 ? len - 1 : 0;
+  auto row = [&](int t, Raw8<IO>& v) {
+    v.load(src + (size_t)min(t, tmax) * Cd);
+    if (t >= len) v.zero();
+  };
+  Raw8<IO> h[3], cur[kConvRB], nxt[kConvRB];              // h: the 3 raw rows before the batch
+  if (tt > 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) row(t0 - 3 + k, h[k]);
+  } else {                                                // tokens before the window: the conv state
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      if (cs_in) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[k].set(e, io<IO>::load1(cs_in + ((size_t)b * Cd + c0 + e) * 3 + k));
+      } else {
+        h[k].zero();
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kConvRB; ++k) row(t0 + k, cur[k]);
   float wk[4][8], bs[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -103,57 +160,50 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
     wk[0][e] = v[0]; wk[1][e] = v[1]; wk[2][e] = v[2]; wk[3][e] = v[3];
     bs[e] = bias ? bias[c0 + e] : 0.f;
   }
-  const IO* src = xBC + (size_t)b * L * Cd + c0;
-  auto raw = [&](int t, float* v) {                       // raw row t of these channels (zero past the length)
-    if (t >= 0) {
-      if (t < len) io<IO>::load8(src + (size_t)t * Cd, v);
-      else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
-      }
-    } else if (cs_in) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = io<IO>::load1(cs_in + ((size_t)b * Cd + c0 + e) * 3 + 3 + t);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-  };
-  float h0[8], h1[8], h2[8];                              // raw rows t-3, t-2, t-1
-  raw(t0 - 3, h0);
-  raw(t0 - 2, h1);
-  raw(t0 - 1, h2);
-  auto put_state = [&]() {                                // the last 3 raw tokens, oldest first
+  auto put_state = [&](const Raw8<IO>& r0, const Raw8<IO>& r1, const Raw8<IO>& r2) {  // oldest first
     if (!cs_out) return;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       IO* d = cs_out + ((size_t)b * Cd + c0 + e) * 3;
-      io<IO>::store1(d + 0, h0[e]);
-      io<IO>::store1(d + 1, h1[e]);
-      io<IO>::store1(d + 2, h2[e]);
+      io<IO>::store1(d + 0, r0[e]);
+      io<IO>::store1(d + 1, r1[e]);
+      io<IO>::store1(d + 2, r2[e]);
     }
   };
-  if (len == 0 && tt == 0) put_state();
+  if (len == 0 && tt == 0) put_state(h[0], h[1], h[2]);
   IO* dst = out + (size_t)b * L * Cd + c0;
-  const int tend = min(t0 + kConvTT, L);
-  for (int t = t0; t < tend; ++t) {
-    float r[8];
-    raw(t, r);
-    f4 lo, hi;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float u = bs[e];
-      u = __builtin_fmaf(wk[0][e], h0[e], u);
-      u = __builtin_fmaf(wk[1][e], h1[e], u);
-      u = __builtin_fmaf(wk[2][e], h2[e], u);
-      u = __builtin_fmaf(wk[3][e], r[e], u);
-      const float v = u / (1.f + __expf(-u));
-      if (e < 4) lo[e] = v; else hi[e - 4] = v;
-      h0[e] = h1[e]; h1[e] = h2[e]; h2[e] = r[e];
+  for (int kb = 0; kb < kConvTT / kConvRB; ++kb) {
+    const int tb = t0 + kb * kConvRB;
+    if (tb >= L) break;
+    if (kb + 1 < kConvTT / kConvRB) {
+#pragma unroll
+      for (int k = 0; k < kConvRB; ++k) row(tb + kConvRB + k, nxt[k]);
     }
-    io<IO>::store4(dst + (size_t)t * Cd, lo);
-    io<IO>::store4(dst + (size_t)t * Cd + 4, hi);
-    if (t == len - 1) put_state();
+#pragma unroll
+    for (int k = 0; k < kConvRB; ++k) {
+      const int t = tb + k;
+      if (t >= L) break;
+      const Raw8<IO>& r0 = k >= 3 ? cur[k - 3] : h[k];
+      const Raw8<IO>& r1 = k >= 2 ? cur[k - 2] : h[k + 1];
+      const Raw8<IO>& r2 = k >= 1 ? cur[k - 1] : h[2];
+      Raw8<IO> o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float u = bs[e];
+        u = __builtin_fmaf(wk[0][e], r0[e], u);
+        u = __builtin_fmaf(wk[1][e], r1[e], u);
+        u = __builtin_fmaf(wk[2][e], r2[e], u);
+        u = __builtin_fmaf(wk[3][e], cur[k][e], u);
+        o.set(e, u * __builtin_amdgcn_rcpf(1.f + __expf(-u)));
+      }
+      store_raw8(dst + (size_t)t * Cd, o);
+      if (t == len - 1) put_state(r1, r2, cur[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) h[k] = cur[kConvRB - 3 + k];
+#pragma unroll
+    for (int k = 0; k < kConvRB; ++k) cur[k] = nxt[k];
   }
 }
 
@@ -374,9 +424,27 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   _Float16* const xws = sm.xw[wid];
 
   // ---- per-step operands ---------------------------------------------------
-  struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; };
+  // the norm gate's z rows of this wave (output pass only): 4 values per
+  // (p-tile, t-tile), raw I/O bits
+  typedef typename std::conditional<sizeof(IO) == 2, u2, u4>::type zraw_t;
+  constexpr int ZN = NORM ? 1 : 0;
+  struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; zraw_t z[ZN ? PT : 1][2]; };
+  rsrc_t rz = ry;
+  if constexpr (NORM) rz = mkr(a.z + seq_y, yspan);
   auto fetch = [&](XB& r, int j, bool with_c) {
     const unsigned tok = (unsigned)(t0 + j * TS);
+    if constexpr (NORM) {
+      if (with_c) {
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+          for (int T = 0; T < 2; ++T) {
+            const unsigned off = (tok + 16 * T + lr) * yrow + (unsigned)(16 * pt + 4 * q) * ES;
+            if constexpr (sizeof(IO) == 2) r.z[pt][T] = __builtin_amdgcn_raw_buffer_load_b64(rz, off, 0, 0);
+            else r.z[pt][T] = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
+          }
+      }
+    }
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
       const int c8 = lane + 64 * k, s = c8 / (PH / 8), pc = c8 % (PH / 8);
@@ -618,13 +686,18 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   }
 
   // ---- phase 3: outputs ------------------------------------------------------
-  rsrc_t rz = ry;
-  if constexpr (NORM) rz = mkr(a.z + seq_y, yspan);
   for (int j = 0; j < Jv; ++j) {
     const int i0 = j * TS;
     const float Sj_start = j ? Sw[i0 - 1] : 0.f;
     const float Sj_end = Sw[i0 + TS - 1];
     stage(xb, j, Sj_end, true);
+    zraw_t zc[ZN ? PT : 1][2];                            // this step's z, before the prefetch reuses xb
+    if constexpr (NORM) {
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int T = 0; T < 2; ++T) zc[pt][T] = xb.z[pt][T];
+    }
     lds_barrier();
     if (j + 1 < Jv) fetch(xb, j + 1, true);
     if (live) {
@@ -691,7 +764,13 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 #pragma unroll
           for (int i = 0; i < 4; ++i) out[i] = __builtin_fmaf(sc[T], yr[i], yd[i]) + Dh * (float)xr[i];
           if constexpr (NORM) {
-            const f4 zz = ld4f<IO>(rz, off);
+            f4 zz;
+            if constexpr (sizeof(IO) == 2) {
+              const h4 zh = __builtin_bit_cast(h4, zc[pt][T]);
+              zz = f4{(float)zh[0], (float)zh[1], (float)zh[2], (float)zh[3]};
+            } else {
+              zz = __builtin_bit_cast(f4, zc[pt][T]);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               out[i] = out[i] * (zz[i] / (1.f + __expf(-zz[i])));
