@@ -460,9 +460,12 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       }
     }
   };
+  // The last chunk publishes nothing, so it skips the local-state pass: its
+  // final state is the running state of the output pass.
+  const bool last = c + 1 == a.nchunks;
   // the first step's loads go out before the dt scan, so both latencies overlap
   XB xb;
-  if (Jv > 0) fetch(xb, 0, false);
+  if (Jv > 0) fetch(xb, 0, last);
 
   // ---- phase 0: dt and the running log2-decay over the chunk (4 tokens/lane) --
   {
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       const float w = (float)dtw[i0 + s] * ex2(Sref - Sw[i0 + s]);
       h8 xw;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xw[e] = (_Float16)((float)r.x[k][e] * w);
+      for (int e = 0; e < 8; ++e) xw[e] = (_Float16)__builtin_fmaf((float)r.x[k][e], w, 0.f);   // one mixed-precision op
       *reinterpret_cast<h8*>(&xws[s * XP + pc * 8]) = xw;
       if (with_c) *reinterpret_cast<h8*>(&xs[s * XP + pc * 8]) = r.x[k];
     }
@@ -553,7 +556,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
 
   // ---- phase 1: local chunk state ------------------------------------------
-  for (int j = 0; j < Jv; ++j) {
+  for (int j = 0; j < (last ? 0 : Jv); ++j) {
     stage(xb, j, Send, false);
     lds_barrier();
     fetch(xb, j + 1 < Jv ? j + 1 : 0, j + 1 == Jv);   // the last fetch is the output phase's first step
@@ -588,7 +591,6 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     for (int pt = 0; pt < PT; ++pt) R[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
   if (live) {
     const int i = c + 1;
-    const bool last = c + 1 == a.nchunks;
     const int lg = a.tree_lg;                             // tree radix 2^lg
     const int t = ((1 << lg) - 1) * (__builtin_ctz((unsigned)i) / lg);   // aggregates inside this chunk's block
     float scale = 1.f;                                     // product of the decays folded in so far
@@ -631,16 +633,17 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       }
       if (mine) my_dec = __uint_as_float(__hip_atomic_load(&a.aggdec[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     };
-    auto fold = [&](int k) {
+    auto load_node = [&](f4 (&F)[NT][PT], int k) {         // all 16 loads in flight at once
       const int n = __builtin_amdgcn_readlane(my_node, k);
-      const float Dn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
       const rsrc_t r = mkr(a.agg + (size_t)node_item(n) * (N * PH), kStBytes);
-      f4 F[NT][PT];                                        // all loads in flight at once
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
           F[nt][pt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
+    };
+    auto add_node = [&](const f4 (&F)[NT][PT], int k) {
+      const float Dn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -653,12 +656,20 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     const int tb = t < nodes ? t : nodes;
     if (tb > 0) {
       wait_group(0, tb);
-      for (int k = 0; k < tb; ++k) fold(k);
+      for (int k = 0; k < tb; ++k) {
+        f4 F[NT][PT];
+        load_node(F, k);
+        add_node(F, k);
+      }
     }
     if (!last) publish();
     if (nodes > tb) {
       wait_group(tb, nodes);
-      for (int k = tb; k < nodes; ++k) fold(k);
+      for (int k = tb; k < nodes; ++k) {
+        f4 F[NT][PT];
+        load_node(F, k);
+        add_node(F, k);
+      }
     }
     if (a.state_in) {
 #pragma unroll
@@ -669,18 +680,6 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           const f4 h0 = *reinterpret_cast<const f4*>(a.state_in + ((size_t)hb * kP + p) * N + n);
 #pragma unroll
           for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, h0[e], R[nt][pt][e]);
-        }
-    }
-    if (last && a.state_out) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const int p = PH * half + 16 * pt + lr, n = ncol<N>(nt, q);
-          f4 v = acc[nt][pt];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(dec_chunk, R[nt][pt][e], v[e]);
-          *reinterpret_cast<f4*>(a.state_out + ((size_t)hb * kP + p) * N + n) = v;
         }
     }
   }
@@ -724,8 +723,10 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
             const h4 ds = *reinterpret_cast<const h4*>(&dtw[i0 + 16 * S + 4 * q]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int si = 16 * S + 4 * q + i;
-              mb[S][i] = si <= tl ? mb[S][i] * (float)ds[i] * ex2(St - Ss[i]) : 0.f;
+              // the exponent is clamped so that the masked entries (s > t) stay finite;
+              // off-diagonal tiles (S < T) hold only s < t and need no mask
+              const float v = mb[S][i] * (float)ds[i] * ex2(fminf(St - Ss[i], 0.f));
+              mb[S][i] = (S < T || 4 * q + i <= lr) ? v : 0.f;
             }
           }
         }
@@ -798,7 +799,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
         }
       }
       // running state for the next step: R <- e^{S_end_j - S_start_j} R + sum_s w_s B_s x_s
-      if (j + 1 < Jv) {
+      // (after the last step of the last chunk it is the window's final state)
+      if (j + 1 < Jv || (last && a.state_out)) {
         const float dec = ex2(Sj_end - Sj_start);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -808,6 +810,15 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       }
     }
     lds_barrier();
+  }
+  if (last && a.state_out && live) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const int p = PH * half + 16 * pt + lr, n = ncol<N>(nt, q);
+        *reinterpret_cast<f4*>(a.state_out + ((size_t)hb * kP + p) * N + n) = R[nt][pt];
+      }
   }
 
   // ---- retire -------------------------------------------------------------------
