@@ -70,6 +70,12 @@ typedef struct mamba2_dims {
     int32_t io_dtype;    /* MAMBA2_F16 or MAMBA2_F32 for x/dt/B/C/xBC/z/y       */
     int32_t state_dtype; /* resident decode state: MAMBA2_F32 or MAMBA2_F16     */
     float norm_eps;      /* epsilon inside the RMSNorm square root              */
+    int32_t segments;    /* window scan work split: 0 lets the library choose;
+                            k > 0 splits each sequence into min(k, chunks)
+                            runs of consecutive chunks.  Chunks inside a run
+                            pass the state on in registers; runs hand it over
+                            through the workspace.  Results agree up to
+                            rounding for every k.                              */
 } mamba2_dims;
 
 /* ------------------------------------------------------------------------ */

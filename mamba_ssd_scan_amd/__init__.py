@@ -38,7 +38,8 @@ class Mamba2Error(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk",
-        "conv_width", "norm_group", "io_dtype", "state_dtype")] + [("norm_eps", ctypes.c_float)]
+        "conv_width", "norm_group", "io_dtype", "state_dtype")] + [("norm_eps", ctypes.c_float),
+                                                                   ("segments", ctypes.c_int32)]
 
 
 class _WindowIO(ctypes.Structure):
@@ -122,9 +123,9 @@ def _io_dtype(t):
 
 
 def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=256, conv_width=0, norm_group=0,
-              io_dtype=F16, state_dtype=F32, norm_eps=1e-5) -> Dims:
+              io_dtype=F16, state_dtype=F32, norm_eps=1e-5, segments=0) -> Dims:
     return Dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, conv_width, norm_group, io_dtype,
-                state_dtype, norm_eps)
+                state_dtype, norm_eps, segments)
 
 
 def window_workspace_bytes(dims: Dims) -> int:
@@ -142,7 +143,7 @@ def alloc_workspace(dims: Dims, device) -> torch.Tensor:
 def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None, conv_w=None, conv_b=None,
                      conv_state_in=None, conv_state_out=None, state_in=None, state_out=None, seqlens=None,
                      z=None, norm_w=None, chunk=256, norm_group=0, norm_eps=1e-5, ngroups=None, dstate=None,
-                     headdim=None, stream=None):
+                     headdim=None, segments=0, stream=None):
     """Whole-window scan.  Shapes: x (B,L,H,P), B/C (B,L,G,N) -- or xBC
     (B,L,H*P+2*G*N) with conv_w (H*P+2*G*N, 4) for the fused conv --, dt
     (B,L,H), A/D (H) f32, y (B,L,H*P) (or (B,L,H,P)).  See include/mamba2ssd.h."""
@@ -156,7 +157,8 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
     else:
         P = x.shape[3]
         G, N = B.shape[2], B.shape[3]
-    dims = make_dims(Bsz, L, H, P, N, G, chunk, 4 if conv else 0, norm_group, _io_dtype(dt), F32, norm_eps)
+    dims = make_dims(Bsz, L, H, P, N, G, chunk, 4 if conv else 0, norm_group, _io_dtype(dt), F32, norm_eps,
+                     segments)
     io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), _ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in),
                    _ptr(conv_state_out), _ptr(dt), _ptr(A), _ptr(D), _ptr(state_in), _ptr(state_out),
                    _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y))

@@ -138,6 +138,7 @@ static int32_t check_window(const mamba2_dims* d) {
   if (d->norm_group > 0 && (d->nheads * d->headdim) / d->norm_group > 256) return MAMBA2_EUNSUPPORTED;
   if (d->headdim != 64) return MAMBA2_EUNSUPPORTED;
   if (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) return MAMBA2_EUNSUPPORTED;
+  if (d->segments < 0) return MAMBA2_EINVAL;
   const int64_t nchunks = ((int64_t)d->seqlen + d->chunk - 1) / d->chunk;
   const int64_t items = nchunks * d->batch * d->nheads;
   if (items > (int64_t)1 << 29) return MAMBA2_EUNSUPPORTED;

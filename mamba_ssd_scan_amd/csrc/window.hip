@@ -50,7 +50,9 @@ template <typename IO> struct WinArgs {
   unsigned* flags;    // per item: generation tag | 1 once its chunk aggregate is published
   float* agg;         // per item chunk aggregate state (private layout)
   unsigned* aggdec;   // per item aggregate decay (float bits)
-  int tree_lg;        // log2 of the radix of the chunk tree
+  int tree_lg;        // log2 of the radix of the segment tree
+  int cps;            // chunks per segment: one workgroup runs a segment's chunks in order
+  int nseg;           // segments per sequence
 };
 
 // control block: eight claim counters and the done counter / generation /
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     for (int k = 0; k < 8; ++k) {
       const unsigned px = (x0 + k) & 7u;
       const int npairs = BG > (int)px ? (BG - (int)px + 7) / 8 : 0;
-      const unsigned n = (unsigned)(npairs * nhb * a.nchunks);
+      const unsigned n = (unsigned)(npairs * nhb * a.nseg);
       if (n == 0) continue;
       unsigned* cnt = &a.ctrl[px * kCtrlStride];
       if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
@@ -385,8 +387,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   const unsigned gen = __builtin_amdgcn_readfirstlane(sm.gen);
   const unsigned tag = (gen & 0x3fffffffu) << 2;
   const int hblk = (int)(ticket % (unsigned)nhb);
-  const int c = (int)(ticket / (unsigned)nhb) / BG;
-  const int gid = (int)(ticket / (unsigned)nhb) - c * BG;
+  const int sg = (int)(ticket / (unsigned)nhb) / BG;   // segment
+  const int gid = (int)(ticket / (unsigned)nhb) - sg * BG;
   const int b = gid / a.G, g = gid - b * a.G;
   const int hin = hblk * KH + (wid >> 1);       // head within the group
   const bool live = hin < hpg;                  // waves past the group's last head only help load B, C
@@ -394,12 +396,13 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   const int half = wid & 1;
   const int hb = b * a.H + h;                   // (sequence, head) index
   const int bhv = b * HV + 2 * h + half;
-  const unsigned item = (unsigned)(c * BHV + bhv);
+  const unsigned item = (unsigned)(sg * BHV + bhv);
   int len = a.seqlens ? __builtin_amdgcn_readfirstlane(a.seqlens[b]) : a.L;
   len = len < 0 ? 0 : (len > a.L ? a.L : len);
-  const int t0 = c * a.Q;
-  const int nvalid = min(max(len - t0, 0), a.Q);
-  const int Jv = (nvalid + TS - 1) / TS;        // steps holding real tokens
+  const int cb = sg * a.cps;                    // the segment's first chunk
+  // chunks of the segment that hold tokens of this sequence, and the steps of each
+  const int ncv = min(max((len - cb * a.Q + a.Q - 1) / a.Q, 0), min(a.cps, a.nchunks - cb));
+  auto steps_of = [&](int ci) { return (min(max(len - (cb + ci) * a.Q, 0), a.Q) + TS - 1) / TS; };
   const float Ah = a.A[h] * kLog2e;
   const float Dh = a.D[h];
 
@@ -431,8 +434,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; zraw_t z[ZN ? PT : 1][2]; };
   rsrc_t rz = ry;
   if constexpr (NORM) rz = mkr(a.z + seq_y, yspan);
-  auto fetch = [&](XB& r, int j, bool with_c) {
-    const unsigned tok = (unsigned)(t0 + j * TS);
+  auto fetch = [&](XB& r, int tok0, bool with_c) {   // the step starting at token tok0
+    const unsigned tok = (unsigned)tok0;
     if constexpr (NORM) {
       if (with_c) {
 #pragma unroll
@@ -460,21 +463,27 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       }
     }
   };
-  // The last chunk publishes nothing, so it skips the local-state pass: its
+  // The last segment publishes nothing, so it skips the local-state pass: its
   // final state is the running state of the output pass.
-  const bool last = c + 1 == a.nchunks;
+  const bool last = sg + 1 == a.nseg;
   // the first step's loads go out before the dt scan, so both latencies overlap
   XB xb;
-  if (Jv > 0) fetch(xb, 0, last);
+  if (ncv > 0) fetch(xb, cb * a.Q, last);
 
-  // ---- phase 0: dt and the running log2-decay over the chunk (4 tokens/lane) --
-  {
-    float d[4], v[4];
-    float run = 0.f;
+  // ---- phase 0 (per chunk): dt and the running log2-decay over the chunk --
+  // (4 tokens per lane); the dt of the next chunk is loaded while a chunk runs
+  auto load_dt = [&](int cc, float (&d)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * lane + e;
-      d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((t0 + i) * a.H) * ES) : 0.f;
+      d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((cc * a.Q + i) * a.H) * ES) : 0.f;
+    }
+  };
+  auto scan_dt = [&](const float (&d)[4]) {
+    float v[4];
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
       run += d[e] * Ah;
       v[e] = run;
     }
@@ -493,12 +502,12 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
         dtw[i] = (_Float16)d[e];
       }
     }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  const float Send = Sw[a.Q - 1];
-  const float dec_chunk = ex2(Send);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  float dtv[4];
+  if (ncv > 0) load_dt(cb, dtv);
 
   // stage step j: B (and C) as read, x as read (phase 3 only) and x weighted
   // by dt_s e^{Sref - S_s} for the state contraction
@@ -554,19 +563,42 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
+  float segdec = 1.f;                             // decay over the segment
 
-  // ---- phase 1: local chunk state ------------------------------------------
-  for (int j = 0; j < (last ? 0 : Jv); ++j) {
-    stage(xb, j, Send, false);
-    lds_barrier();
-    fetch(xb, j + 1 < Jv ? j + 1 : 0, j + 1 == Jv);   // the last fetch is the output phase's first step
-    if (live) state_mfma(acc);
-    lds_barrier();
+  // ---- phase 1: local segment state ----------------------------------------
+  // acc is kept relative to the end of the current chunk: it is decayed over
+  // each new chunk before that chunk's tokens are added.
+  if (!last) {
+    for (int ci = 0; ci < ncv; ++ci) {
+      const int cc = cb + ci;
+      scan_dt(dtv);
+      load_dt(ci + 1 < ncv ? cc + 1 : cb, dtv);   // the output pass starts over at the first chunk
+      const float Send = Sw[a.Q - 1];
+      const float dec = ex2(Send);
+      segdec *= dec;
+      if (ci > 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) acc[nt][pt] *= dec;
+      }
+      const int Jc = steps_of(ci);
+      for (int j = 0; j < Jc; ++j) {
+        stage(xb, j, Send, false);
+        lds_barrier();
+        // next: this chunk's next step, the next chunk's first, or the output pass's first
+        if (j + 1 < Jc) fetch(xb, cc * a.Q + (j + 1) * TS, false);
+        else if (ci + 1 < ncv) fetch(xb, (cc + 1) * a.Q, false);
+        else fetch(xb, cb * a.Q, true);
+        if (live) state_mfma(acc);
+        lds_barrier();
+      }
+    }
   }
 
-  // ---- phase 2: carry-in state over an indexed tree of chunks (radix r = 2^lg)
-  // With i = c + 1 and block(i) = r^(number of trailing zero base-r digits of i),
-  // chunk c publishes the aggregate of chunks (i - block(i), i] (1-based), and
+  // ---- phase 2: carry-in state over an indexed tree of segments (radix r = 2^lg)
+  // With i = sg + 1 and block(i) = r^(number of trailing zero base-r digits of i),
+  // segment sg publishes the aggregate of segments (i - block(i), i] (1-based), and
   // its carry-in is the initial state advanced through the aggregates that
   // tile [1, i-1].  Those aggregates are taken newest first,
   // n_1 = i-1, n_{k+1} = n_k - block(n_k):
@@ -574,15 +606,15 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   // (F: aggregate state, D: its decay), so the aggregates that are ready first
   // are folded in first.  The first (r-1) log_r(block(i)) of them cover
   // (i - block(i), i-1]: once they are folded in, the running sum combined
-  // with the local state is this chunk's own aggregate, published for later
-  // chunks.  A chunk waits only on earlier chunks (claimed before it), and the
+  // with the local state is this segment's own aggregate, published for later
+  // segments.  A segment waits only on earlier ones (claimed before it), and the
   // order of the sums is fixed, so results do not depend on timing.  A larger
   // radix means fewer dependent publishes (shorter latency chain) and more
   // aggregate loads (more traffic).
   // hand-off states: per item N*PH floats, tile-major, 16 contiguous bytes per lane
   constexpr unsigned kStBytes = (unsigned)(N * PH) * 4u;
   auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * 4u; };
-  auto node_item = [&](int j) -> unsigned { return (unsigned)((j - 1) * BHV + bhv); };   // j: 1-based chunk
+  auto node_item = [&](int j) -> unsigned { return (unsigned)((j - 1) * BHV + bhv); };   // j: 1-based segment
 
   f4 R[NT][PT];
 #pragma unroll
@@ -590,11 +622,11 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) R[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
   if (live) {
-    const int i = c + 1;
+    const int i = sg + 1;
     const int lg = a.tree_lg;                             // tree radix 2^lg
-    const int t = ((1 << lg) - 1) * (__builtin_ctz((unsigned)i) / lg);   // aggregates inside this chunk's block
+    const int t = ((1 << lg) - 1) * (__builtin_ctz((unsigned)i) / lg);   // aggregates inside this segment's block
     float scale = 1.f;                                     // product of the decays folded in so far
-    auto publish = [&]() {                                 // own aggregate: (dec_chunk R + local, dec_chunk scale)
+    auto publish = [&]() {                                 // own aggregate: (segdec R + local, segdec scale)
       const rsrc_t r = mkr(a.agg + (size_t)item * (N * PH), kStBytes);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -602,10 +634,10 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
         for (int pt = 0; pt < PT; ++pt) {
           f4 v = acc[nt][pt];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(dec_chunk, R[nt][pt][k], v[k]);
+          for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(segdec, R[nt][pt][k], v[k]);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
         }
-      if (lane == 0) __hip_atomic_store(&a.aggdec[item], __float_as_uint(dec_chunk * scale), __ATOMIC_RELAXED,
+      if (lane == 0) __hip_atomic_store(&a.aggdec[item], __float_as_uint(segdec * scale), __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_s_waitcnt(0);
       if (lane == 0) __hip_atomic_store(&a.flags[item], tag | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -652,7 +684,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, F[nt][pt][e], R[nt][pt][e]);
       scale *= Dn;
     };
-    // the first t aggregates are this chunk's block: fold them, publish, then the rest
+    // the first t aggregates are this segment's block: fold them, publish, then the rest
     const int tb = t < nodes ? t : nodes;
     if (tb > 0) {
       wait_group(0, tb);
@@ -685,6 +717,13 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   }
 
   // ---- phase 3: outputs ------------------------------------------------------
+  // R runs from the carry-in through every chunk of the segment
+  for (int ci = 0; ci < ncv; ++ci) {
+  const int t0 = (cb + ci) * a.Q;
+  scan_dt(dtv);
+  if (ci + 1 < ncv) load_dt(cb + ci + 1, dtv);
+  const int Jv = steps_of(ci);
+  const bool more = ci + 1 < ncv;                 // the state carries into the next chunk
   for (int j = 0; j < Jv; ++j) {
     const int i0 = j * TS;
     const float Sj_start = j ? Sw[i0 - 1] : 0.f;
@@ -698,7 +737,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
         for (int T = 0; T < 2; ++T) zc[pt][T] = xb.z[pt][T];
     }
     lds_barrier();
-    if (j + 1 < Jv) fetch(xb, j + 1, true);
+    if (j + 1 < Jv) fetch(xb, t0 + (j + 1) * TS, true);
+    else if (more) fetch(xb, t0 + a.Q, true);
     if (live) {
       // C fragments: rows t = 16T + lr, n-slots of k-step m
       h8 cf[2][KM];
@@ -799,8 +839,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
         }
       }
       // running state for the next step: R <- e^{S_end_j - S_start_j} R + sum_s w_s B_s x_s
-      // (after the last step of the last chunk it is the window's final state)
-      if (j + 1 < Jv || (last && a.state_out)) {
+      // (after the last step of the last segment it is the window's final state)
+      if (j + 1 < Jv || more || (last && a.state_out)) {
         const float dec = ex2(Sj_end - Sj_start);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -810,6 +850,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       }
     }
     lds_barrier();
+  }
   }
   if (last && a.state_out && live) {
 #pragma unroll
@@ -823,7 +864,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 
   // ---- retire -------------------------------------------------------------------
   if (tid == 0) {
-    const unsigned total = (unsigned)(a.nchunks * BG * nhb);
+    const unsigned total = (unsigned)(a.nseg * BG * nhb);
     const unsigned done = __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == total - 1) {
       for (int k = 0; k < 8; ++k) __hip_atomic_store(&a.ctrl[k * kCtrlStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -918,13 +959,31 @@ static int device_cus() {
 template <typename IO, int N, bool NORM>
 static hipError_t launch_scan(const WinArgs<IO>& a, hipStream_t st) {
   const int hpg = a.H / a.G;
-  const unsigned wgs = (unsigned)(a.nchunks * a.B * a.G * ((hpg + wv::KH - 1) / wv::KH));
-  // When every workgroup is resident at once (one per CU), all chunks reach
-  // the hand-off together and the chain of dependent publishes is the
-  // critical path: a radix-8 tree.  Otherwise chunk levels are staggered in
-  // time and aggregate traffic matters more: radix 4.
+  const long long slots = (long long)a.B * a.G * ((hpg + wv::KH - 1) / wv::KH);   // workgroups per segment index
+  // Resident workgroups per CU (the state lives in registers, so usually one).
+  static int per_cu = 0;
+  if (per_cu <= 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ssd_window_group_kernel<IO, N, NORM>, 64 * wv::NWV, 0) !=
+            hipSuccess || n <= 0)
+      n = 1;
+    per_cu = n;
+  }
+  const long long resident = (long long)device_cus() * per_cu;
+  // Segments: as many consecutive-chunk runs per sequence as keep every
+  // resident slot busy.  Chunks inside a segment pass the state in registers;
+  // only segment boundaries go through the hand-off.
   WinArgs<IO> b = a;
-  b.tree_lg = wgs <= (unsigned)device_cus() ? 3 : 2;
+  int nseg = a.nseg > 0 ? a.nseg : (int)(resident / slots);
+  nseg = nseg < 1 ? 1 : (nseg > a.nchunks ? a.nchunks : nseg);
+  b.cps = (a.nchunks + nseg - 1) / nseg;
+  b.nseg = (a.nchunks + b.cps - 1) / b.cps;
+  const unsigned wgs = (unsigned)(b.nseg * slots);
+  // When every workgroup is resident at once, all segments reach the hand-off
+  // together and the chain of dependent publishes is the critical path: a
+  // radix-8 tree.  Otherwise segment levels are staggered in time and
+  // aggregate traffic matters more: radix 4.
+  b.tree_lg = wgs <= resident ? 3 : 2;
   ssd_window_group_kernel<IO, N, NORM><<<wgs, 64 * wv::NWV, 0, st>>>(b);
   return hipGetLastError();
 }
@@ -936,6 +995,7 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   WinArgs<IO> a;
   a.B = d.batch; a.L = d.seqlen; a.H = d.nheads; a.G = d.ngroups; a.Q = d.chunk;
   a.nchunks = (d.seqlen + d.chunk - 1) / d.chunk;
+  a.nseg = d.segments;                           // 0: chosen at launch
   a.dt = (const IO*)io_.dt; a.A = io_.A; a.D = io_.D;
   a.state_in = io_.state_in; a.state_out = io_.state_out; a.seqlens = io_.seqlens;
   a.z = (const IO*)io_.z; a.y = (IO*)io_.y;

@@ -30,7 +30,7 @@ def slice_err(got, ref, nlead):
     return float((np.abs(g - r).max(axis=1) / den).max())
 
 
-def run_window(inp, chunk, seqlens=None, state_in=None, want_state=True, ws=None, y_fill=None):
+def run_window(inp, chunk, seqlens=None, state_in=None, want_state=True, ws=None, y_fill=None, segments=0):
     """Run the window scan on the GPU from numpy inputs x, dt, B, C, A, D."""
     x, dt, Bm, Cm = (to_dev(inp[k]) for k in ("x", "dt", "B", "C"))
     A, D = to_dev(inp["A"]), to_dev(inp["D"])
@@ -45,13 +45,14 @@ def run_window(inp, chunk, seqlens=None, state_in=None, want_state=True, ws=None
     if ws is None:
         dims = m2.make_dims(Bsz, L, H, P, N, G, chunk, io_dtype=m2.F16 if x.dtype == torch.float16 else m2.F32)
         ws = m2.alloc_workspace(dims, DEV)
-    m2.conv_scan_window(dt, A, D, y, ws, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl, chunk=chunk)
+    m2.conv_scan_window(dt, A, D, y, ws, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl, chunk=chunk,
+                        segments=segments)
     torch.cuda.synchronize()
     return y.cpu().numpy().reshape(Bsz, L, H, P), (hT.cpu().numpy() if want_state else None)
 
 
 def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=None, state_in=None,
-              want_conv_state=True):
+              want_conv_state=True, segments=0):
     xBC = to_dev(inp["xBC"])
     Bsz, L, Cn = inp["xBC"].shape
     y = torch.empty((Bsz, L, H * P), dtype=xBC.dtype, device=DEV)
@@ -68,6 +69,6 @@ def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=No
                         conv_state_out=cso, state_in=h0, state_out=hT, seqlens=sl,
                         z=to_dev(inp["z"]) if norm_group else None,
                         norm_w=to_dev(inp["norm_w"]) if norm_group else None,
-                        chunk=chunk, norm_group=norm_group, ngroups=G, dstate=N, headdim=P)
+                        chunk=chunk, norm_group=norm_group, ngroups=G, dstate=N, headdim=P, segments=segments)
     torch.cuda.synchronize()
     return y.cpu().numpy(), hT.cpu().numpy(), (cso.cpu().numpy() if want_conv_state else None)

@@ -61,6 +61,12 @@ def test_workspace_size_formula():
         ws_formula(4 * 4, 16)
 
 
+def test_segment_count_does_not_change_the_workspace():
+    # the hand-off area is sized for one segment per chunk, the most there can be
+    for k in (0, 1, 3, 8, 100):
+        assert m2.window_workspace_bytes(layer_dims(segments=k)) == ws_formula(8 * 128, 128)
+
+
 def test_long_sequences_beyond_32_bit_rows_are_refused():
     # 2^31 bytes of one sequence's x rows: 131072 tokens x 8192 channels x 2 bytes
     n = ctypes.c_size_t(0)
@@ -73,7 +79,7 @@ def test_long_sequences_beyond_32_bit_rows_are_refused():
     (dict(headdim=32), -2), (dict(dstate=96), -2), (dict(chunk=100), -2), (dict(conv_width=3), -2),
     (dict(nheads=100, ngroups=8), -1), (dict(batch=0), -1), (dict(seqlen=0), -1),
     (dict(norm_group=1000), -1), (dict(norm_group=32), -2), (dict(norm_group=-1), -1),
-    (dict(io_dtype=7), -1),
+    (dict(io_dtype=7), -1), (dict(segments=-1), -1),
 ])
 def test_workspace_query_rejects(kw, code):
     lib = m2.load_library()

@@ -40,9 +40,9 @@ def oracle_window(inp, seqlens=None, state_in=None, nthreads=0):
                            seqlens=seqlens, nthreads=nthreads)
 
 
-def check_window(name, inp, chunk, seqlens=None, state_in=None):
-    say(f"[window] {name}: shape x{inp['x'].shape} chunk {chunk} seqlens {seqlens}")
-    y, hT = run_window(inp, chunk, seqlens=seqlens, state_in=state_in, y_fill=12345.0)
+def check_window(name, inp, chunk, seqlens=None, state_in=None, segments=0):
+    say(f"[window] {name}: shape x{inp['x'].shape} chunk {chunk} seqlens {seqlens} segments {segments}")
+    y, hT = run_window(inp, chunk, seqlens=seqlens, state_in=state_in, y_fill=12345.0, segments=segments)
     yr, hr = oracle_window(inp, seqlens, state_in)
     Bsz = y.shape[0]
     ey = 0.0
@@ -80,6 +80,16 @@ def test_many_chunks_carry_tree(B):
     lens = [4096] * B if B == 1 else [4096, 4000, 3, 64, 65, 2048, 4095, 1000]
     h0 = np.random.default_rng(32).standard_normal((B, 4, 64, 16)).astype(np.float32) * 0.3
     check_window(f"64 chunks B={B}", inp, 64, seqlens=lens, state_in=h0)
+
+
+@pytest.mark.parametrize("segments", [1, 2, 3, 9])
+def test_segments_of_consecutive_chunks(segments):
+    # 9 chunks of 128 tokens run as 1, 2, 3 or 9 segments (runs of 9, 5, 3 or 1
+    # chunks passing the state in registers); the lengths end inside the first
+    # chunk, inside a middle segment and at the window end
+    inp = rand_window(51 + segments, 3, 1100, 16, 128, 2)
+    h0 = np.random.default_rng(52).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
+    check_window(f"segments={segments}", inp, 128, seqlens=[1100, 700, 100], state_in=h0, segments=segments)
 
 
 def test_ragged_batch_with_initial_state():
@@ -174,15 +184,15 @@ def small_mixer(seed, B, L, H, G, N):
     return synth.mixer_inputs(s, seed)
 
 
-@pytest.mark.parametrize("norm_group", [0, 1024, 512])
-def test_mixer_core_small(norm_group):
+@pytest.mark.parametrize("norm_group,segments", [(0, 0), (1024, 0), (512, 0), (1024, 1), (512, 2)])
+def test_mixer_core_small(norm_group, segments):
     H, P, G, N, L, Bsz = 16, 64, 2, 128, 300, 2
     inp = small_mixer(41, Bsz, L, H, G, N)
     Cn = H * P + 2 * G * N
     csi = (np.random.default_rng(42).standard_normal((Bsz, Cn, 3))).astype(np.float16)
     lens = [300, 157]
-    say(f"[mixer] small norm_group={norm_group}")
-    y, hT, cso = run_mixer(inp, H, P, G, N, 256, norm_group, seqlens=lens, conv_state_in=csi)
+    say(f"[mixer] small norm_group={norm_group} segments={segments}")
+    y, hT, cso = run_mixer(inp, H, P, G, N, 256, norm_group, seqlens=lens, conv_state_in=csi, segments=segments)
     out_r, h_r, cs_r = oracle.mixer_core(inp["xBC"], inp["conv_w"], inp["conv_b"], inp["dt"], inp["A"], inp["D"],
                                          inp["z"], inp["norm_w"], H, P, G, N, norm_group or H * P,
                                          conv_state=csi, seqlens=lens)
