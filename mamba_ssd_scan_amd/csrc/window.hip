@@ -243,6 +243,7 @@ constexpr int PH = 32;                 // head-dim columns per item
 constexpr int PT = PH / 16;            // p-tiles per item
 constexpr int XP = PH + 8;             // pitch (halfs) of the [s][p] x tiles
 constexpr int kSc1 = 16;               // cache policy: device-coherent access
+static_assert(TS == 32 && PH == 32, "the x tiles are moved as 16 tokens x 4 chunks of 16 bytes per wave access");
 
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
@@ -318,7 +319,9 @@ constexpr int KH = 4;                  // heads per workgroup
 constexpr int NWV = 2 * KH;            // waves per workgroup
 
 template <int N> struct SmG {
-  static constexpr int NP = N + 8;     // pitch (halfs) of the [s][n] B and C tiles
+  // pitch (halfs) of the [s][n] B and C tiles, chosen so that the row reads
+  // of 8 consecutive n per lane hit distinct LDS banks
+  static constexpr int NP = N == 128 ? N + 16 : N + 8;
   alignas(16) _Float16 b[TS * NP];     // [s][n] B as read
   alignas(16) _Float16 c[TS * NP];     // [t][n] C as read
   alignas(16) _Float16 x[NWV][TS * XP];   // per wave: [s][p] x as read
@@ -328,9 +331,10 @@ template <int N> struct SmG {
   unsigned ticket, gen;
 };
 
-// first state column of the 4-row group j of state tile nt
+// first state column of the 4-row group j of state tile nt: lane group j of
+// k-step m reads n = 8 j + 32 m .. + 7, tiles 2m and 2m+1 hold its two halves
 template <int N> __device__ __forceinline__ int ncol(int nt, int j) {
-  if constexpr (N >= 32) return (N / 4) * j + 8 * (nt >> 1) + 4 * (nt & 1);
+  if constexpr (N >= 32) return 8 * j + 32 * (nt >> 1) + 4 * (nt & 1);
   else return 4 * j;
 }
 }  // namespace wv
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     }
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
-      const int c8 = lane + 64 * k, s = c8 / (PH / 8), pc = c8 % (PH / 8);
+      const int s = (lane & 15) + 16 * k, pc = lane >> 4;   // token, 16-byte column chunk
       r.x[k] = ldh<IO, 8>(rx, (tok + s) * xrow + (unsigned)(pc * 8) * ES);
     }
 #pragma unroll
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     const int i0 = j * TS;
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
-      const int c8 = lane + 64 * k, s = c8 / (PH / 8), pc = c8 % (PH / 8);
+      const int s = (lane & 15) + 16 * k, pc = lane >> 4;   // token, 16-byte column chunk
       const float w = (float)dtw[i0 + s] * ex2(Sref - Sw[i0 + s]);
       h8 xw;
 #pragma unroll
@@ -532,18 +536,19 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       }
     }
   };
-  // acc[nt][pt] += sum_s B[s, n] (w_s x[s, p]) over the staged step (K = 32 tokens)
+  // acc[nt][pt] += sum_s B[s, n] (w_s x[s, p]) over the staged step (K = 32
+  // tokens; lane group q takes tokens 4q..4q+3 and 16+4q..16+4q+3)
   auto state_mfma = [&](f4 (&acc)[NT][PT]) {
     h8 xf[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
       const int col = 16 * pt + 4 * (lr & 3);
-      xf[pt] = cat(tr4(&xws[(8 * q + (lr >> 2)) * XP + col]), tr4(&xws[(8 * q + 4 + (lr >> 2)) * XP + col]));
+      xf[pt] = cat(tr4(&xws[(4 * q + (lr >> 2)) * XP + col]), tr4(&xws[(16 + 4 * q + (lr >> 2)) * XP + col]));
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int col = ncol<N>(nt, lr & 3);
-      const h8 af = cat(tr4(&sm.b[(8 * q + (lr >> 2)) * NP + col]), tr4(&sm.b[(8 * q + 4 + (lr >> 2)) * NP + col]));
+      const h8 af = cat(tr4(&sm.b[(4 * q + (lr >> 2)) * NP + col]), tr4(&sm.b[(16 + 4 * q + (lr >> 2)) * NP + col]));
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(af, xf[pt], acc[nt][pt]);
     }
@@ -551,7 +556,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   // 8 (or 4) n of row r of an LDS [s][n] tile at the n-slots of k-step m
   auto row8 = [&](const _Float16* tile, int r, int m) -> h8 {
     const _Float16* row = tile + r * NP;
-    if constexpr (NV == 8) return *reinterpret_cast<const h8*>(row + (N / 4) * q + 8 * m);
+    if constexpr (NV == 8) return *reinterpret_cast<const h8*>(row + 8 * q + 32 * m);
     else {
       const h4 v = *reinterpret_cast<const h4*>(row + 4 * q);
       return h8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
