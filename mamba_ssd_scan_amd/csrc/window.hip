@@ -47,9 +47,8 @@ template <typename IO> struct WinArgs {
   float* normsum;     // (B, L, H, kNormParts) partial sums of g^2 (norm epilogue)
   IO* y;
   unsigned* ctrl;     // per-partition claim counters, done counter, generation, error
-  unsigned* flags;    // per item: generation tag | 1 once its chunk aggregate is published
-  float* agg;         // per item chunk aggregate state (private layout)
-  unsigned* aggdec;   // per item aggregate decay (float bits)
+  unsigned long long* flags;   // per item: decay bits << 32 | generation tag | 1 once its aggregate is published
+  float* agg;         // per item segment aggregate state (private layout)
   int tree_lg;        // log2 of the radix of the segment tree
   int cps;            // chunks per segment: one workgroup runs a segment's chunks in order
   int nseg;           // segments per sequence
@@ -244,6 +243,8 @@ constexpr int PT = PH / 16;            // p-tiles per item
 constexpr int XP = PH + 8;             // pitch (halfs) of the [s][p] x tiles
 constexpr int kSc1 = 16;               // cache policy: device-coherent access
 static_assert(TS == 32 && PH == 32, "the x tiles are moved as 16 tokens x 4 chunks of 16 bytes per wave access");
+// (four neighbouring lanes load one token's 64 contiguous bytes: global
+//  coalescing outweighs the LDS bank conflicts of the matching tile writes)
 
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
@@ -306,6 +307,11 @@ template <typename IO> __device__ __forceinline__ f4 ld4f(rsrc_t r, unsigned off
     return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   }
 }
+// 16 bytes per lane from a buffer straight into LDS: lane i's data lands at
+// dst + 16 i (device-coherent read)
+__device__ __forceinline__ void ld16_to_lds(rsrc_t r, void* dst, unsigned off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, kSc1);
+}
 template <typename IO> __device__ __forceinline__ void st4(rsrc_t r, unsigned off, f4 v) {
   if constexpr (sizeof(IO) == 2) {
     const h4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
@@ -322,10 +328,18 @@ template <int N> struct SmG {
   // pitch (halfs) of the [s][n] B and C tiles, chosen so that the row reads
   // of 8 consecutive n per lane hit distinct LDS banks
   static constexpr int NP = N == 128 ? N + 16 : N + 8;
-  alignas(16) _Float16 b[TS * NP];     // [s][n] B as read
-  alignas(16) _Float16 c[TS * NP];     // [t][n] C as read
-  alignas(16) _Float16 x[NWV][TS * XP];   // per wave: [s][p] x as read
-  alignas(16) _Float16 xw[NWV][TS * XP];  // per wave: x times the state weight of token s
+  struct Tiles {
+    alignas(16) _Float16 b[TS * NP];     // [s][n] B as read
+    alignas(16) _Float16 c[TS * NP];     // [t][n] C as read
+    alignas(16) _Float16 x[NWV][TS * XP];   // per wave: [s][p] x as read
+    alignas(16) _Float16 xw[NWV][TS * XP];  // per wave: x times the state weight of token s
+  };
+  // the step tiles are idle during the hand-off, where each wave lands one
+  // aggregate state in LDS while another one is in flight to its registers
+  union {
+    Tiles t;
+    alignas(16) float land[NWV][N * PH];
+  } u;
   alignas(16) float S[NWV][256];       // per wave: running log2-decay from the chunk start (inclusive)
   alignas(16) _Float16 dts[NWV][256];
   unsigned ticket, gen;
@@ -427,8 +441,10 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   const rsrc_t rdt = mkr(a.dt + (size_t)b * a.L * a.H + h, len > 0 && live ? (unsigned)((len - 1) * a.H + 1) * ES : 0u);
   float* const Sw = sm.S[wid];
   _Float16* const dtw = sm.dts[wid];
-  _Float16* const xs = sm.x[wid];
-  _Float16* const xws = sm.xw[wid];
+  _Float16* const xs = sm.u.t.x[wid];
+  _Float16* const xws = sm.u.t.xw[wid];
+  _Float16* const smb = sm.u.t.b;
+  _Float16* const smc = sm.u.t.c;
 
   // ---- per-step operands ---------------------------------------------------
   // the norm gate's z rows of this wave (output pass only): 4 values per
@@ -454,7 +470,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     }
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
-      const int s = (lane & 15) + 16 * k, pc = lane >> 4;   // token, 16-byte column chunk
+      const int s = (lane >> 2) + 16 * k, pc = lane & 3;   // token, 16-byte column chunk
       r.x[k] = ldh<IO, 8>(rx, (tok + s) * xrow + (unsigned)(pc * 8) * ES);
     }
 #pragma unroll
@@ -519,7 +535,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     const int i0 = j * TS;
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
-      const int s = (lane & 15) + 16 * k, pc = lane >> 4;   // token, 16-byte column chunk
+      const int s = (lane >> 2) + 16 * k, pc = lane & 3;   // token, 16-byte column chunk
       const float w = (float)dtw[i0 + s] * ex2(Sref - Sw[i0 + s]);
       h8 xw;
 #pragma unroll
@@ -531,8 +547,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     for (int k = 0; k < BK; ++k) {
       const int id = tid + NTH * k, s = id / NCH, nc = id % NCH;
       if (id < TS * NCH) {
-        *reinterpret_cast<h8*>(&sm.b[s * NP + nc * 8]) = r.b[k];
-        if (with_c) *reinterpret_cast<h8*>(&sm.c[s * NP + nc * 8]) = r.c[k];
+        *reinterpret_cast<h8*>(&smb[s * NP + nc * 8]) = r.b[k];
+        if (with_c) *reinterpret_cast<h8*>(&smc[s * NP + nc * 8]) = r.c[k];
       }
     }
   };
@@ -548,7 +564,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int col = ncol<N>(nt, lr & 3);
-      const h8 af = cat(tr4(&sm.b[(4 * q + (lr >> 2)) * NP + col]), tr4(&sm.b[(16 + 4 * q + (lr >> 2)) * NP + col]));
+      const h8 af = cat(tr4(&smb[(4 * q + (lr >> 2)) * NP + col]), tr4(&smb[(16 + 4 * q + (lr >> 2)) * NP + col]));
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(af, xf[pt], acc[nt][pt]);
     }
@@ -642,17 +658,18 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(segdec, R[nt][pt][k], v[k]);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
         }
-      if (lane == 0) __hip_atomic_store(&a.aggdec[item], __float_as_uint(segdec * scale), __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_s_waitcnt(0);
-      if (lane == 0) __hip_atomic_store(&a.flags[item], tag | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // one 64-bit word carries the aggregate's decay and the ready tag
+      const unsigned long long f =
+          ((unsigned long long)__float_as_uint(segdec * scale) << 32) | (unsigned long long)(tag | 1u);
+      if (lane == 0) __hip_atomic_store(&a.flags[item], f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     // the aggregates to fold, newest first: lane k holds the k-th (1-based chunk)
     int nodes = 0, my_node = 0;
     for (int n = i - 1; n > 0; n -= 1 << (lg * (__builtin_ctz((unsigned)n) / lg)), ++nodes)
       if (lane == nodes) my_node = n;
     // wait until aggregates k0 .. k1-1 are published (one flag per lane, all
-    // polled together), then read their decays
+    // polled together); the flag word also holds the aggregate's decay
     float my_dec = 1.f;
     auto wait_group = [&](int k0, int k1) {
       const bool mine = lane >= k0 && lane < k1;
@@ -660,7 +677,11 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       unsigned spins = 0;
       while (true) {
         bool ready = true;
-        if (mine) ready = __hip_atomic_load(&a.flags[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (tag | 1u);
+        if (mine) {
+          const unsigned long long f = __hip_atomic_load(&a.flags[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ready = (unsigned)f == (tag | 1u);
+          my_dec = __uint_as_float((unsigned)(f >> 32));
+        }
         if (__ballot(!ready) == 0) break;
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) {
@@ -668,44 +689,81 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           break;
         }
       }
-      if (mine) my_dec = __uint_as_float(__hip_atomic_load(&a.aggdec[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     };
-    auto load_node = [&](f4 (&F)[NT][PT], int k) {         // all 16 loads in flight at once
+    // Aggregates k0 .. k1-1 are folded with two in flight: even positions land
+    // in registers, odd ones in this wave's LDS area (direct loads, 1 KB per
+    // instruction in the same lane order as the state tiles).
+    float* const land = sm.u.land[wid];
+    auto node_rsrc = [&](int k) {
       const int n = __builtin_amdgcn_readlane(my_node, k);
-      const rsrc_t r = mkr(a.agg + (size_t)node_item(n) * (N * PH), kStBytes);
+      return mkr(a.agg + (size_t)node_item(n) * (N * PH), kStBytes);
+    };
+    auto to_regs = [&](f4 (&F)[NT][PT], int k) {
+      const rsrc_t r = node_rsrc(k);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
           F[nt][pt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
     };
-    auto add_node = [&](const f4 (&F)[NT][PT], int k) {
-      const float Dn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
+    auto to_lds = [&](int k) {
+      const rsrc_t r = node_rsrc(k);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+          ld16_to_lds(r, land + (nt * PT + pt) * 256, st_off(nt, pt));
+    };
+    auto dec_of = [&](int k) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
+    };
+    auto add_regs = [&](const f4 (&F)[NT][PT], int k) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, F[nt][pt][e], R[nt][pt][e]);
-      scale *= Dn;
+      scale *= dec_of(k);
     };
-    // the first t aggregates are this segment's block: fold them, publish, then the rest
+    auto add_lds = [&](int k) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const f4 v = *reinterpret_cast<const f4*>(land + (nt * PT + pt) * 256 + lane * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, v[e], R[nt][pt][e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // a few LDS reads at a time: no register peak
+      }
+      scale *= dec_of(k);
+    };
+    // the first t aggregates are this segment's block (the local state is still
+    // live there: one at a time), then the own aggregate is published and the
+    // rest are folded two in flight
     const int tb = t < nodes ? t : nodes;
     if (tb > 0) {
       wait_group(0, tb);
       for (int k = 0; k < tb; ++k) {
         f4 F[NT][PT];
-        load_node(F, k);
-        add_node(F, k);
+        to_regs(F, k);
+        add_regs(F, k);
       }
     }
     if (!last) publish();
     if (nodes > tb) {
       wait_group(tb, nodes);
-      for (int k = tb; k < nodes; ++k) {
-        f4 F[NT][PT];
-        load_node(F, k);
-        add_node(F, k);
+      f4 F[NT][PT];
+      to_regs(F, tb);
+      if (tb + 1 < nodes) to_lds(tb + 1);
+      for (int k = tb; k < nodes; k += 2) {
+        add_regs(F, k);
+        if (k + 2 < nodes) to_regs(F, k + 2);
+        if (k + 1 < nodes) {
+          add_lds(k + 1);
+          if (k + 3 < nodes) to_lds(k + 3);
+        }
       }
     }
     if (a.state_in) {
@@ -720,6 +778,9 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
         }
     }
   }
+
+  // the hand-off's landing areas overlay the step tiles
+  lds_barrier();
 
   // ---- phase 3: outputs ------------------------------------------------------
   // R runs from the carry-in through every chunk of the segment
@@ -750,7 +811,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int m = 0; m < KM; ++m) cf[T][m] = row8(sm.c, 16 * T + lr, m);
+        for (int m = 0; m < KM; ++m) cf[T][m] = row8(smc, 16 * T + lr, m);
       // decay-masked C.B^T, rows s (4 per lane) x column t (one per lane), per t-tile
       h8 mf[2];
 #pragma unroll
@@ -763,7 +824,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           mb[S] = f4{0.f, 0.f, 0.f, 0.f};
           if (S <= T) {
 #pragma unroll
-            for (int m = 0; m < KM; ++m) mb[S] = mfma16(row8(sm.b, 16 * S + lr, m), cf[T][m], mb[S]);
+            for (int m = 0; m < KM; ++m) mb[S] = mfma16(row8(smb, 16 * S + lr, m), cf[T][m], mb[S]);
             const f4 Ss = *reinterpret_cast<const f4*>(&Sw[i0 + 16 * S + 4 * q]);
             const h4 ds = *reinterpret_cast<const h4*>(&dtw[i0 + 16 * S + 4 * q]);
 #pragma unroll
@@ -928,7 +989,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
 
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t ctrl, flags, aggdec, agg, normsum, convx, total;
+  size_t ctrl, flags, agg, normsum, convx, total;
 };
 static WsLayout ws_layout(const mamba2_dims& d) {
   const size_t nchunks = ((size_t)d.seqlen + d.chunk - 1) / d.chunk;
@@ -938,8 +999,7 @@ static WsLayout ws_layout(const mamba2_dims& d) {
   WsLayout w;
   w.ctrl = 0;
   w.flags = up(kCtrlBytes);
-  w.aggdec = up(w.flags + items * 4);
-  w.agg = up(w.aggdec + items * 4);
+  w.agg = up(w.flags + items * 8);
   w.normsum = up(w.agg + items * (size_t)d.dstate * (kP / 2) * 4);
   w.convx = up(w.normsum + (d.norm_group > 0 ? (size_t)d.batch * d.seqlen * d.nheads * kNormParts * 4 : 0));
   const size_t cd = (size_t)d.nheads * kP + 2 * (size_t)d.ngroups * d.dstate;
@@ -1005,8 +1065,7 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   a.state_in = io_.state_in; a.state_out = io_.state_out; a.seqlens = io_.seqlens;
   a.z = (const IO*)io_.z; a.y = (IO*)io_.y;
   a.ctrl = (unsigned*)(base + wl.ctrl);
-  a.flags = (unsigned*)(base + wl.flags);
-  a.aggdec = (unsigned*)(base + wl.aggdec);
+  a.flags = (unsigned long long*)(base + wl.flags);
   a.agg = (float*)(base + wl.agg);
   a.normsum = (float*)(base + wl.normsum);
   if (d.conv_width == 4) {

@@ -41,13 +41,12 @@ def layer_dims(**kw):
 
 
 def ws_formula(chunk_items, N, norm_floats=0, conv_bytes=0):
-    # control block; per (chunk, sequence, head, half) item a flag, a decay
+    # control block; per (chunk, sequence, head, half) item a 64-bit flag word
     # and an fp32 aggregate of N x 32; the norm partials; the conv output
     up = lambda v: (v + 255) // 256 * 256
     items = 2 * chunk_items
     off = up(11 * 32 * 4)
-    off = up(off + items * 4)
-    off = up(off + items * 4)
+    off = up(off + items * 8)
     off = up(off + items * N * 32 * 4)
     off = up(off + norm_floats * 4)
     return up(off + conv_bytes)
