@@ -15,7 +15,7 @@
 //
 // Kernels:
 //  * conv_silu_kernel (mixer input only): conv1d(4) + SiLU over the raw xBC
-//    channels, streamed token by token with the 3-token history in registers,
+//    channels, streamed in prefetched batches of token rows per thread,
 //    written to a workspace copy in the xBC layout; it also writes the conv
 //    state out;
 //  * ssd_window_group_kernel: the chunked scan (see the comment above it);
@@ -209,10 +209,12 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
 }
 
 // ===========================================================================
-// Chunked scan: one workgroup per (chunk, sequence, group, block of KH heads
-// of the group), one wave per (head, half of the head dim).  x, B and C are
-// token rows with a given token stride: the caller's tensors, or the conv
-// prologue's output in the xBC layout.
+// Chunked scan: one workgroup per (segment, sequence, group, block of KH heads
+// of the group), one wave per (head, half of the head dim).  A segment is a
+// run of consecutive chunks: inside it the state passes from chunk to chunk
+// in registers, and only segment boundaries go through the hand-off tree.
+// x, B and C are token rows with a given token stride: the caller's tensors,
+// or the conv kernel's output in the xBC layout.
 //
 // Each half of a head is an independent scan (the recurrence is separable
 // over p).  A wave keeps its 32 x N share of the fp32 state in registers as
@@ -227,10 +229,9 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
 //
 // State columns are kept in a permuted order so that the n-slots a lane owns
 // in the state tiles are the slots it needs for the readout's contraction
-// over n, so that a C fragment is one contiguous 16-byte read, and so that
-// the four column groups of a transposed read of the B tile fall N/4 columns
-// apart (in different LDS banks):
-//   tile nt, row 4j + e  <->  n = (N/4) j + 8 (nt / 2) + 4 (nt % 2) + e   (N >= 32)
+// over n, and so that a C fragment is one contiguous 16-byte read that hits
+// distinct LDS banks across the wave:
+//   tile nt, row 4j + e  <->  n = 8 j + 32 (nt / 2) + 4 (nt % 2) + e      (N >= 32)
 //   tile 0,  row 4j + e  <->  n = 4 j + e                                 (N = 16)
 //
 // Inputs are read through buffer descriptors whose range ends at the
