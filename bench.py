@@ -93,17 +93,25 @@ def decode_bytes(B, H, P, N, G):
     return B * H * P * N * 2 * 2 + B * H * P * 2 * 2 + B * G * N * 2 * 2 + B * H * 2 + 2 * H * 4
 
 
-def window_mfma_flops(L, H, P, N, Q=256, step=32, half=32):
-    """f16 MFMA flops the window kernel issues for one sequence (16x16x32
-    instructions, 16384 flops each).  Per (chunk, half of a head) and 32-token
-    step: the chunk-state pass takes N/16 x half/16 instructions; the output
-    pass takes the causal C.B^T blocks (3 blocks x N/32), the masked product
-    (2 x half/16), the carry readout (2 x half/16 x N/32) and, except on the
-    last step, the running-state update (N/16 x half/16)."""
+def window_mfma_flops(L, H, P, N, Q=256, segments=8, step=32, half=32):
+    """f16 MFMA flops the window kernel issues for one sequence with a final
+    state (16x16x32 instructions, 16384 flops each), for the chunks split into
+    `segments` runs of consecutive chunks (the split the library picks for
+    one layer window).  Per (half of a head) and 32-token step: the local-state
+    pass, run on every segment but the last, takes N/16 x half/16
+    instructions; the output pass takes the causal C.B^T blocks (3 blocks x
+    N/32), the masked product (2 x half/16), the carry readout (2 x half/16 x
+    N/32) and the running-state update (N/16 x half/16) on every step but the
+    last step of each non-final segment."""
     J = Q // step
+    C = L // Q
+    cps = -(-C // segments)
+    nseg = -(-C // cps)
     nt, pt, km = N // 16, half // 16, max(N // 32, 1)
-    per = nt * pt * J + (3 * km + 2 * pt + 2 * pt * km) * J + nt * pt * (J - 1)
-    return (L // Q) * H * (P // half) * per * 16384
+    local = nt * pt * J * (C - cps)                      # all chunks outside the last segment
+    out = (3 * km + 2 * pt + 2 * pt * km) * J * C
+    upd = nt * pt * (J * C - (nseg - 1))
+    return H * (P // half) * (local + out + upd) * 16384
 
 
 def main():
@@ -281,6 +289,47 @@ def main():
     dec_rot_us = ev0.elapsed_time(ev1) * 1e3 / T
     dbytes = decode_bytes(DB, DH, DP, DN, DG)
 
+    # ---- batched windows: 8 sequences, seven of 2048 tokens and one of 1955 ----
+    # timing only (parity of this workload is covered by the GPU tests); inputs
+    # are drawn on the device with the layer window's distributions
+    BB, blens = 8, [L] * 7 + [1955]
+    gen = torch.Generator(device=dev).manual_seed(1005)
+    bsets = []
+    for k in range(2):
+        dt0 = torch.exp(torch.rand(H, device=dev, generator=gen) * float(np.log(100.0)) + float(np.log(1e-3)))
+        bsets.append({
+            "x": torch.randn(BB, L, H, P, device=dev, generator=gen).half(),
+            "dt": torch.nn.functional.softplus(torch.randn(BB, L, H, device=dev, generator=gen)
+                                               + torch.log(torch.expm1(dt0))).half(),
+            "B": (torch.randn(BB, L, G, N, device=dev, generator=gen) / N ** 0.5).half(),
+            "C": (torch.randn(BB, L, G, N, device=dev, generator=gen) / N ** 0.5).half(),
+            "y": torch.empty(BB, L, H * P, dtype=torch.float16, device=dev),
+            "hT": torch.empty(BB, H, P, N, dtype=torch.float32, device=dev),
+        })
+    bA = -torch.exp(torch.rand(H, device=dev, generator=gen) * float(np.log(16.0)))
+    bD = torch.randn(H, device=dev, generator=gen)
+    bsl = torch.tensor(blens, dtype=torch.int32, device=dev)
+    bdims = m2.make_dims(BB, L, H, P, N, G, Q)
+    bws = m2.alloc_workspace(bdims, dev)
+
+    def bstep(k):
+        t = bsets[k % len(bsets)]
+        m2.conv_scan_window(t["dt"], bA, bD, t["y"], bws, x=t["x"], B=t["B"], C=t["C"], state_out=t["hT"],
+                            seqlens=bsl, chunk=Q, stream=stream)
+
+    for k in range(3):
+        bstep(k)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(20):
+        bstep(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    bat_us = ev0.elapsed_time(ev1) * 1e3 / 20
+    bbytes = window_bytes(BB, L, H, P, N, G, lens=blens)
+    del bsets, bws
+    torch.cuda.empty_cache()
+
     # ---- CPU baseline: the oracle on a bounded sample of the window ------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -332,6 +381,10 @@ def main():
                   "seq_len": ML_, "us": round(mix_us, 2), "tokens_per_s": round(MB_ * ML_ / (mix_us * 1e-6), 1),
                   "algorithmic_bytes": mbytes, "achieved_GBs": round(mbytes / (mix_us * 1e-6) / 1e9, 1),
                   "frac": round(mbytes / (mix_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "batched": {"workload": "8 layer windows, 7 x 2048 + 1955 tokens, final states", "us": round(bat_us, 2),
+                    "tokens_per_s": round(sum(blens) / (bat_us * 1e-6), 1), "algorithmic_bytes": bbytes,
+                    "achieved_GBs": round(bbytes / (bat_us * 1e-6) / 1e9, 1),
+                    "frac": round(bbytes / (bat_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "decode": {"us_per_step": round(dec_us, 2), "us_per_step_rotated_states": round(dec_rot_us, 2),
                    "algorithmic_bytes": dbytes, "achieved_GBs": round(dbytes / (dec_rot_us * 1e-6) / 1e9, 1),
                    "frac": round(dbytes / (dec_rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
