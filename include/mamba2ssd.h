@@ -136,6 +136,29 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* dims, const mamba2_window_io*
                                 void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Whole window with the recurrent state requantized to binary16 after every
+ * token, the way page "Mamb2_8B_FP4_Recall_SQ3.25" scores its windows (carry
+ * requantized each token, section "Representation", paragraph "State"; state
+ * reset per window, section "Measured quality").  Each token is the
+ * one-token step of mamba2_decode_step with a binary16 state (same binary32
+ * contract), run over the window's tokens with the state kept on chip, so
+ * the final state equals that many decode steps bit for bit.
+ *   dims: conv_width 0 and norm_group 0 (EUNSUPPORTED otherwise); headdim 64;
+ *         dstate 16, 64 or 128; chunk, segments and state_dtype are ignored.
+ *   io:   x, B, C, dt, A, D, y as for mamba2_conv_scan_window (x and y need
+ *         only element alignment, B and C 16 bytes); xBC, conv_*, z, norm_w
+ *         are ignored.
+ *         state_in  (B,H,P,N) f32 or NULL (zeros): rounded once to binary16
+ *                   (nearest even) before the first token;
+ *         state_out (B,H,P,N) f32 or NULL: the binary16 state after the
+ *                   sequence's last token, widened exactly;
+ *         seqlens   device int32 (B) or NULL: tokens at or past a sequence's
+ *                   length are not processed and their y rows not written.
+ * No workspace.  Outputs must not overlap inputs or each other.
+ * Errors: EINVAL, EUNSUPPORTED, EALIGN, EHIP. */
+int32_t mamba2_requant_window(const mamba2_dims* dims, const mamba2_window_io* io, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* One-token recurrent step for B sequences (dims.seqlen is ignored).
  *   x (B,H,P) io; dt (B,H) io (positive); B, C (B,G,N) io; A, D (H) f32
  *   state (B,H,P,N) in state_dtype, read and updated IN PLACE

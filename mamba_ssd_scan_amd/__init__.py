@@ -77,6 +77,8 @@ def load_library():
         lib.mamba2_window_workspace_bytes.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
         lib.mamba2_conv_scan_window.restype = ctypes.c_int32
         lib.mamba2_conv_scan_window.argtypes = [dp, ctypes.POINTER(_WindowIO), vp, ctypes.c_size_t, vp]
+        lib.mamba2_requant_window.restype = ctypes.c_int32
+        lib.mamba2_requant_window.argtypes = [dp, ctypes.POINTER(_WindowIO), vp]
         lib.mamba2_decode_step.restype = ctypes.c_int32
         lib.mamba2_decode_step.argtypes = [dp, ctypes.POINTER(_DecodeIO), vp]
         lib.mamba2_state_load.restype = ctypes.c_int32
@@ -165,6 +167,20 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
     _check("mamba2_conv_scan_window",
            load_library().mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
                                                   workspace.numel(), _stream(dt, stream)))
+
+
+def requant_window(dt, A, D, y, *, x, B, C, state_in=None, state_out=None, seqlens=None, stream=None):
+    """Whole window with the state requantized to binary16 after every token.
+    Shapes: x (B,L,H,P), B/C (B,L,G,N), dt (B,L,H), A/D (H) f32, y (B,L,H*P)
+    (or (B,L,H,P)); state_in/state_out (B,H,P,N) f32.  See include/mamba2ssd.h."""
+    Bsz, L, H = dt.shape
+    P = x.shape[3]
+    G, N = B.shape[2], B.shape[3]
+    dims = make_dims(Bsz, L, H, P, N, G, 256, 0, 0, _io_dtype(dt), F16)
+    io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), None, None, None, None, None, _ptr(dt), _ptr(A), _ptr(D),
+                   _ptr(state_in), _ptr(state_out), _ptr(seqlens), None, None, _ptr(y))
+    _check("mamba2_requant_window", load_library().mamba2_requant_window(ctypes.byref(dims), ctypes.byref(io),
+                                                                         _stream(dt, stream)))
 
 
 def decode_step(x, dt, B, C, A, D, state, y, stream=None):

@@ -15,6 +15,7 @@ hipError_t launch_state_convert(int to_resident, int state_f16, const void* src,
                                 hipStream_t st);
 size_t window_workspace_bytes(const mamba2_dims& d);
 hipError_t launch_window(const mamba2_dims& d, const mamba2_window_io& io, void* ws, hipStream_t st);
+hipError_t launch_requant_window(const mamba2_dims& d, const mamba2_window_io& io, hipStream_t st);
 }  // namespace m2
 
 namespace {
@@ -208,6 +209,35 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
       if (overlap(outs[i], outs[j])) return MAMBA2_EINVAL;
   }
   return hip_status(m2::launch_window(*d, *io, ws, (hipStream_t)stream));
+}
+
+int32_t mamba2_requant_window(const mamba2_dims* d, const mamba2_window_io* io, void* stream) {
+  int32_t s = check_common(d);
+  if (s != MAMBA2_OK) return s;
+  if (d->seqlen < 1) return MAMBA2_EINVAL;
+  if (!io) return MAMBA2_EINVAL;
+  // plain x, B, C only: no fused conv, no norm
+  if (d->conv_width != 0 || d->norm_group != 0) return MAMBA2_EUNSUPPORTED;
+  if (d->headdim != 64) return MAMBA2_EUNSUPPORTED;
+  const size_t es = esize(d->io_dtype);
+  const size_t Bsz = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+  if (!io->x || !io->B || !io->C || !io->dt || !io->A || !io->D || !io->y) return MAMBA2_EINVAL;
+  const void* vec[] = {io->B, io->C, io->state_in, io->state_out};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return MAMBA2_EALIGN;
+  if (((uintptr_t)io->x % es) || ((uintptr_t)io->y % es) || ((uintptr_t)io->dt % es) || ((uintptr_t)io->A & 3) ||
+      ((uintptr_t)io->D & 3) || ((uintptr_t)io->seqlens & 3))
+    return MAMBA2_EALIGN;
+  const size_t tok = Bsz * L;
+  Range outs[] = {rng(io->y, tok * H * P * es), rng(io->state_out, Bsz * H * P * N * 4)};
+  Range ins[] = {rng(io->x, tok * H * P * es), rng(io->B, tok * G * N * es), rng(io->C, tok * G * N * es),
+                 rng(io->dt, tok * H * es),    rng(io->A, H * 4),            rng(io->D, H * 4),
+                 rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4)};
+  for (const Range& o : outs)
+    for (const Range& r : ins)
+      if (overlap(o, r)) return MAMBA2_EINVAL;
+  if (overlap(outs[0], outs[1])) return MAMBA2_EINVAL;
+  return hip_status(m2::launch_requant_window(*d, *io, (hipStream_t)stream));
 }
 
 }  // extern "C"

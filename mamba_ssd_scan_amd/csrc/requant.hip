@@ -1,0 +1,265 @@
+// Whole window with the recurrent state requantized to binary16 after every
+// token: the one-token step of the decode path, run token by token over a
+// window with the state kept on chip.
+//
+// Page "Mamb2_8B_FP4_Recall_SQ3.25" scores each 2048-token window with the
+// recurrent row requantized every token (section "Representation", paragraph
+// "State"; reset per window, section "Measured quality").  Per token and head
+// the step is the decode step's binary32 contract:
+//   a  = (float) exp((double) dt * A_h)         (rounded once)
+//   u  = dt * x_p,  v = u * B_n                 (one rounding each)
+//   s  = fma(a, S, v)                           (binary32)
+//   y_p = sum_n s C_n  (binary32 fma chain) + D_h x_p
+//   S  <- binary16_rne(s)
+// so the stored state after any number of tokens is reproducible bit for bit.
+//
+// Work split: a workgroup owns one (sequence, head, block of ROWS state rows
+// p) for the whole window; each thread keeps RPT rows x 8 consecutive n of
+// the state in registers (binary16 values held as binary32).  Tokens are
+// staged 32 at a time into LDS (B and C rows, x of the block's rows, the
+// decays), double-buffered so that the next block's loads are in flight while
+// the current block runs; y of a block is gathered in LDS and stored as 64
+// contiguous bytes per token.  The work is fp32 VALU-bound: per state element
+// and token one multiply, two fmas and a binary16 rounding.
+#include "common.h"
+#include "../../include/mamba2ssd.h"
+
+namespace m2 {
+
+template <int N> struct RqShape;
+template <> struct RqShape<128> { static constexpr int ROWS = 32, RPT = 2, NTH = 256; };
+template <> struct RqShape<64> { static constexpr int ROWS = 32, RPT = 1, NTH = 256; };
+template <> struct RqShape<16> { static constexpr int ROWS = 64, RPT = 1, NTH = 128; };
+
+constexpr int kRqTB = 32;   // tokens per staged block
+
+// 8 consecutive elements in the I/O type (the B and C rows are staged in LDS
+// as given, so that binary32 inputs stay exact)
+template <typename IO> struct Raw8;
+template <> struct Raw8<_Float16> {
+  h8 v;
+  __device__ __forceinline__ void load(const _Float16* p) { v = *reinterpret_cast<const h8*>(p); }
+  __device__ __forceinline__ void put(_Float16* p) const { *reinterpret_cast<h8*>(p) = v; }
+  static __device__ __forceinline__ void get(const _Float16* p, float* f) {
+    const h8 h = *reinterpret_cast<const h8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
+  }
+};
+template <> struct Raw8<float> {
+  f4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f4*>(p);
+    b = *reinterpret_cast<const f4*>(p + 4);
+  }
+  __device__ __forceinline__ void put(float* p) const {
+    *reinterpret_cast<f4*>(p) = a;
+    *reinterpret_cast<f4*>(p + 4) = b;
+  }
+  static __device__ __forceinline__ void get(const float* p, float* f) {
+    const f4 x = *reinterpret_cast<const f4*>(p), y = *reinterpret_cast<const f4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = x[i];
+      f[4 + i] = y[i];
+    }
+  }
+};
+
+template <typename IO, int N>
+__global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
+    const IO* __restrict__ x, const IO* __restrict__ dt, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
+    const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ state_in,
+    float* __restrict__ state_out, const int* __restrict__ seqlens, IO* __restrict__ y, int L, int H, int G) {
+  constexpr int P = 64;
+  constexpr int ROWS = RqShape<N>::ROWS, RPT = RqShape<N>::RPT, NTH = RqShape<N>::NTH;
+  constexpr int LPR = N / 8;                 // lanes per state row
+  static_assert(ROWS == (NTH / LPR) * RPT, "rows per workgroup");
+  constexpr int NBLK = P / ROWS;
+  __shared__ alignas(16) IO sB[2][kRqTB][N];
+  __shared__ alignas(16) IO sC[2][kRqTB][N];
+  __shared__ alignas(16) float sX[2][kRqTB][ROWS];
+  __shared__ float sA[2][kRqTB], sD[2][kRqTB];
+  __shared__ float sY[kRqTB][ROWS];
+
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x % NBLK;
+  const int bh = blockIdx.x / NBLK;
+  const int b = bh / H, h = bh - b * H;
+  const int g = h / (H / G);
+  const int nc = (tid % LPR) * 8;            // first n of this thread
+  const int r0 = tid / LPR;                  // first of its rows (stride NTH / LPR)
+  constexpr int RSTRIDE = NTH / LPR;
+  const int p0 = blk * ROWS;
+  int len = seqlens ? seqlens[b] : L;
+  len = len < 0 ? 0 : (len > L ? L : len);
+  const float Ah = A[h], Dh = D[h];
+
+  // state: binary16 values, held as binary32
+  float S[RPT][8];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int p = p0 + r0 + k * RSTRIDE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S[k][i] = 0.f;
+    if (state_in) {
+      float v[8];
+      io<float>::load8(state_in + (((size_t)bh * P + p) * N + nc), v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float t = v[i];
+        asm volatile("" : "+v"(t));
+        S[k][i] = (float)(_Float16)t;
+      }
+    }
+  }
+
+  // ---- staging of one 32-token block --------------------------------------
+  // B and C: NTH threads x 16 bytes cover kRqTB * N halfs per matrix when N
+  // is 128; the loops below stride by NTH for the smaller N.
+  constexpr int BC8 = kRqTB * N / 8;         // 8-element chunks per matrix
+  constexpr int XC = kRqTB * ROWS;           // x elements per block
+  struct Pre {
+    Raw8<IO> b[(BC8 + NTH - 1) / NTH], c[(BC8 + NTH - 1) / NTH];
+    float xv[(XC + NTH - 1) / NTH];
+    float d;
+  };
+  const size_t seqtok = (size_t)b * L;
+  auto fetch = [&](Pre& r, int t0) {
+#pragma unroll
+    for (int k = 0; k < (BC8 + NTH - 1) / NTH; ++k) {
+      const int id = tid + k * NTH;
+      if (id < BC8) {
+        const int t = id / (N / 8), c8 = id % (N / 8);
+        const int tt = min(t0 + t, len - 1);
+        const size_t off = ((seqtok + tt) * G + g) * N + c8 * 8;
+        r.b[k].load(Bm + off);
+        r.c[k].load(Cm + off);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < (XC + NTH - 1) / NTH; ++k) {
+      const int id = tid + k * NTH;
+      if (id < XC) {
+        const int t = id / ROWS, rr = id % ROWS;
+        const int tt = min(t0 + t, len - 1);
+        r.xv[k] = io<IO>::load1(x + ((seqtok + tt) * H + h) * P + p0 + rr);
+      }
+    }
+    r.d = 0.f;
+    if (tid < kRqTB) {
+      const int tt = min(t0 + tid, len - 1);
+      r.d = io<IO>::load1(dt + (seqtok + tt) * H + h);
+    }
+  };
+  auto stage = [&](const Pre& r, int buf) {
+#pragma unroll
+    for (int k = 0; k < (BC8 + NTH - 1) / NTH; ++k) {
+      const int id = tid + k * NTH;
+      if (id < BC8) {
+        const int t = id / (N / 8), c8 = id % (N / 8);
+        r.b[k].put(&sB[buf][t][c8 * 8]);
+        r.c[k].put(&sC[buf][t][c8 * 8]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < (XC + NTH - 1) / NTH; ++k) {
+      const int id = tid + k * NTH;
+      if (id < XC) sX[buf][id / ROWS][id % ROWS] = r.xv[k];
+    }
+    if (tid < kRqTB) {
+      sD[buf][tid] = r.d;
+      sA[buf][tid] = (float)exp((double)r.d * (double)Ah);   // the decay, rounded once from double
+    }
+  };
+  // y of a block: gathered in LDS, then 4 bytes (f16 pairs) or 8 per thread
+  auto store_y = [&](int t0, int nt) {
+    constexpr int PAIRS = kRqTB * ROWS / 2;
+    for (int id = tid; id < PAIRS; id += NTH) {
+      const int t = id / (ROWS / 2), c2 = (id % (ROWS / 2)) * 2;
+      if (t < nt) {
+        IO* dst = y + ((seqtok + t0 + t) * H + h) * P + p0 + c2;
+        io<IO>::store1(dst, sY[t][c2]);
+        io<IO>::store1(dst + 1, sY[t][c2 + 1]);
+      }
+    }
+  };
+
+  const int nblocks = (len + kRqTB - 1) / kRqTB;
+  Pre pre;
+  if (nblocks > 0) {
+    fetch(pre, 0);
+    stage(pre, 0);
+  }
+  __syncthreads();
+  for (int kb = 0; kb < nblocks; ++kb) {
+    const int buf = kb & 1;
+    const int t0 = kb * kRqTB;
+    const int nt = min(kRqTB, len - t0);
+    if (kb + 1 < nblocks) fetch(pre, t0 + kRqTB);   // next block in flight
+    for (int t = 0; t < nt; ++t) {
+      const float d = sD[buf][t], a = sA[buf][t];
+      float bv[8], cv[8];
+      Raw8<IO>::get(&sB[buf][t][nc], bv);
+      Raw8<IO>::get(&sC[buf][t][nc], cv);
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int rr = r0 + k * RSTRIDE;
+        const float xp = sX[buf][t][rr];
+        float acc = 0.f;
+        {
+#pragma clang fp contract(off)
+          const float u = d * xp;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float v = u * bv[i];
+            float sn = __builtin_fmaf(a, S[k][i], v);
+            acc = __builtin_fmaf(sn, cv[i], acc);
+            // binary32 first, then binary16 (the empty asm keeps the two
+            // roundings apart: a fused fma-to-binary16 would round once)
+            asm volatile("" : "+v"(sn));
+            S[k][i] = (float)(_Float16)sn;
+          }
+        }
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if ((tid % LPR) == 0) sY[t][rr] = acc + Dh * xp;
+      }
+    }
+    __syncthreads();                           // sY complete; buffer buf free
+    store_y(t0, nt);
+    if (kb + 1 < nblocks) stage(pre, buf ^ 1);
+    __syncthreads();
+  }
+
+  if (state_out) {
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int p = p0 + r0 + k * RSTRIDE;
+      float* dst = state_out + (((size_t)bh * P + p) * N + nc);
+      *reinterpret_cast<f4*>(dst) = f4{S[k][0], S[k][1], S[k][2], S[k][3]};
+      *reinterpret_cast<f4*>(dst + 4) = f4{S[k][4], S[k][5], S[k][6], S[k][7]};
+    }
+  }
+}
+
+template <typename IO, int N>
+static hipError_t launch_rq(const mamba2_dims& d, const mamba2_window_io& io_, hipStream_t st) {
+  constexpr int ROWS = RqShape<N>::ROWS, NTH = RqShape<N>::NTH;
+  const unsigned grid = (unsigned)(d.batch * d.nheads * (64 / ROWS));
+  requant_window_kernel<IO, N><<<grid, NTH, 0, st>>>(
+      (const IO*)io_.x, (const IO*)io_.dt, (const IO*)io_.B, (const IO*)io_.C, io_.A, io_.D, io_.state_in,
+      io_.state_out, io_.seqlens, (IO*)io_.y, d.seqlen, d.nheads, d.ngroups);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_window(const mamba2_dims& d, const mamba2_window_io& io_, hipStream_t st) {
+  const bool f16 = d.io_dtype == MAMBA2_F16;
+  switch (d.dstate) {
+    case 16: return f16 ? launch_rq<_Float16, 16>(d, io_, st) : launch_rq<float, 16>(d, io_, st);
+    case 64: return f16 ? launch_rq<_Float16, 64>(d, io_, st) : launch_rq<float, 64>(d, io_, st);
+    default: return f16 ? launch_rq<_Float16, 128>(d, io_, st) : launch_rq<float, 128>(d, io_, st);
+  }
+}
+
+}  // namespace m2

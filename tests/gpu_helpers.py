@@ -51,6 +51,23 @@ def run_window(inp, chunk, seqlens=None, state_in=None, want_state=True, ws=None
     return y.cpu().numpy().reshape(Bsz, L, H, P), (hT.cpu().numpy() if want_state else None)
 
 
+def run_requant(inp, seqlens=None, state_in=None, y_fill=None):
+    """Run the per-token-requantized window on the GPU from numpy inputs."""
+    x, dt, Bm, Cm = (to_dev(inp[k]) for k in ("x", "dt", "B", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    Bsz, L, H, P = inp["x"].shape
+    N = inp["B"].shape[3]
+    y = torch.empty((Bsz, L, H * P), dtype=x.dtype, device=DEV)
+    if y_fill is not None:
+        y.fill_(y_fill)
+    hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=DEV)
+    sl = torch.tensor(seqlens, dtype=torch.int32, device=DEV) if seqlens is not None else None
+    h0 = to_dev(np.asarray(state_in, np.float32)) if state_in is not None else None
+    m2.requant_window(dt, A, D, y, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().reshape(Bsz, L, H, P), hT.cpu().numpy()
+
+
 def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=None, state_in=None,
               want_conv_state=True, segments=0):
     xBC = to_dev(inp["xBC"])

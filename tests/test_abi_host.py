@@ -122,6 +122,25 @@ def test_window_validation_codes():
     assert call_window(window_io(), dims=layer_dims(norm_group=8192)) == -1
 
 
+def call_requant(io, dims=None):
+    lib = m2.load_library()
+    dims = dims or layer_dims()
+    return lib.mamba2_requant_window(ctypes.byref(dims), ctypes.byref(io), None)
+
+
+def test_requant_window_validation_codes():
+    # plain x, B, C only; every refusal happens on the host
+    assert call_requant(window_io(), dims=layer_dims(conv_width=4)) == -2
+    assert call_requant(window_io(), dims=layer_dims(norm_group=8192)) == -2
+    assert call_requant(window_io(), dims=layer_dims(headdim=32)) == -2
+    assert call_requant(window_io(), dims=layer_dims(seqlen=0)) == -1
+    assert call_requant(window_io(x=None)) == -1
+    assert call_requant(window_io(y=None)) == -1
+    assert call_requant(window_io(B=FAKE + (1 << 26) + 8)) == -3
+    # y overlapping x
+    assert call_requant(window_io(y=FAKE + 1024)) == -1
+
+
 def test_decode_and_state_validation_codes():
     lib = m2.load_library()
     d = m2.make_dims(64, 1, 128, 64, 128, 8, 256, state_dtype=m2.F16)

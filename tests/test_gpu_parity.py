@@ -20,7 +20,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
 import mamba_ssd_scan_amd as m2  # noqa: E402
-from tests.gpu_helpers import DEV, run_mixer, run_window, slice_err, to_dev  # noqa: E402
+from tests.gpu_helpers import DEV, run_mixer, run_requant, run_window, slice_err, to_dev  # noqa: E402
 
 Y_TOL, S_TOL = 2e-3, 1e-3
 
@@ -176,6 +176,83 @@ def test_deterministic_and_workspace_reuse():
     assert slice_err(hs, hr, 2) <= S_TOL
     y3, h3 = run_window(inp, 256, ws=ws)
     assert np.array_equal(y3, outs[0][0]) and np.array_equal(h3, outs[0][1])
+
+
+# ---- window with the state requantized every token ------------------------------
+def oracle_requant(inp, seqlens=None, state_in=None, heads=None):
+    """The oracle's decode steps run over each sequence's tokens (binary16
+    state after every token).  heads: optional slice of heads sharing one
+    group, checked on their own."""
+    x, dt, Bm, Cm, A, D = (inp[k] for k in ("x", "dt", "B", "C", "A", "D"))
+    Bsz, L, H, P = x.shape
+    N = Bm.shape[3]
+    if heads is not None:
+        g = heads.start // (H // Bm.shape[2])
+        x, dt, A, D = x[:, :, heads], dt[:, :, heads], A[heads], D[heads]
+        Bm, Cm = Bm[:, :, g:g + 1], Cm[:, :, g:g + 1]
+        H = x.shape[2]
+        if state_in is not None:
+            state_in = state_in[:, heads]
+    h0 = np.zeros((Bsz, H, P, N), np.float32) if state_in is None else np.asarray(state_in, np.float32)
+    bits = np.ascontiguousarray(h0.astype(np.float16)).view(np.uint16)
+    y = np.full((Bsz, L, H, P), np.nan)
+    for b in range(Bsz):
+        n = L if seqlens is None else seqlens[b]
+        if n == 0:
+            continue
+        sb = np.ascontiguousarray(bits[b:b + 1])
+        yt = oracle.decode_f16state(np.ascontiguousarray(x[b:b + 1, :n].transpose(1, 0, 2, 3)),
+                                    np.ascontiguousarray(dt[b:b + 1, :n].transpose(1, 0, 2)), A,
+                                    np.ascontiguousarray(Bm[b:b + 1, :n].transpose(1, 0, 2, 3)),
+                                    np.ascontiguousarray(Cm[b:b + 1, :n].transpose(1, 0, 2, 3)), D, sb)
+        bits[b] = sb[0]
+        y[b, :n] = yt[:, 0]
+    return y, bits
+
+
+def check_requant(name, inp, seqlens=None, state_in=None):
+    say(f"[requant] {name}: shape x{inp['x'].shape} seqlens {seqlens}")
+    y, hT = run_requant(inp, seqlens=seqlens, state_in=state_in, y_fill=12345.0)
+    yr, bits = oracle_requant(inp, seqlens, state_in)
+    got_bits = np.ascontiguousarray(hT.astype(np.float16)).view(np.uint16)
+    # the state holds binary16 values: widening back is exact
+    assert np.array_equal(got_bits.view(np.float16).astype(np.float32), hT)
+    same = float(np.mean(got_bits == bits))
+    ey = 0.0
+    for b in range(y.shape[0]):
+        n = seqlens[b] if seqlens is not None else y.shape[1]
+        if n > 0:
+            ey = max(ey, slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)),
+                                   np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2))
+        assert np.all(y[b, n:] == np.float16(12345.0) if y.dtype == np.float16 else y[b, n:] == 12345.0)
+    say(f"[requant] {name}: state identical {same:.6f}  y err {ey:.3e}")
+    assert same == 1.0 and ey <= Y_TOL
+
+
+@pytest.mark.parametrize("N", [16, 64, 128])
+def test_requant_window_small(N):
+    inp = rand_window(61 + N, 2, 300, 8, N, 2)
+    h0 = np.random.default_rng(62).standard_normal((2, 8, 64, N)).astype(np.float32) * 0.3
+    check_requant(f"N={N}", inp, seqlens=[300, 177], state_in=h0)
+
+
+def test_requant_window_fp32_io_and_zero_length():
+    inp = synth.window_inputs(synth.WindowShape(2, 256, 4, 64, 16, 1, 64, np.float32, "narrow"), 1010)
+    check_requant("fp32 tiny", inp, seqlens=[256, 0])
+
+
+def test_requant_window_layer_shape_sampled():
+    # the layer window's shape, checked on the 16 heads of group 3
+    s = synth.layer_window()
+    inp = synth.window_inputs(s, 1011)
+    y, hT = run_requant(inp)
+    heads = slice(48, 64)
+    yr, bits = oracle_requant(inp, heads=heads)
+    got = np.ascontiguousarray(hT[:, heads].astype(np.float16)).view(np.uint16)
+    same = float(np.mean(got == bits))
+    ey = slice_err(np.transpose(y[:, :, heads], (0, 2, 1, 3)), np.transpose(yr, (0, 2, 1, 3)), 2)
+    say(f"[requant] layer shape, heads 48..63: state identical {same:.6f}  y err {ey:.3e}")
+    assert same == 1.0 and ey <= Y_TOL
 
 
 # ---- fused conv + gated norm ----------------------------------------------------
