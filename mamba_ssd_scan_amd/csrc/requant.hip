@@ -27,11 +27,25 @@
 namespace m2 {
 
 template <int N> struct RqShape;
-template <> struct RqShape<128> { static constexpr int ROWS = 32, RPT = 2, NTH = 256; };
+template <> struct RqShape<128> { static constexpr int ROWS = 16, RPT = 1, NTH = 256; };
 template <> struct RqShape<64> { static constexpr int ROWS = 32, RPT = 1, NTH = 256; };
 template <> struct RqShape<16> { static constexpr int ROWS = 64, RPT = 1, NTH = 128; };
 
 constexpr int kRqTB = 32;   // tokens per staged block
+
+// Sum over groups of W consecutive lanes (W = 2, 8 or 16), left in every lane
+// of the group: cross-lane DPP moves inside a row (swap neighbours, swap
+// pairs, mirror within 8, mirror within 16) instead of LDS permutes.
+template <int W> __device__ __forceinline__ float row_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  if constexpr (W >= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if constexpr (W >= 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  if constexpr (W >= 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
+}
 
 // 8 consecutive elements in the I/O type (the B and C rows are staged in LDS
 // as given, so that binary32 inputs stay exact)
@@ -79,7 +93,8 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
   __shared__ alignas(16) IO sB[2][kRqTB][N];
   __shared__ alignas(16) IO sC[2][kRqTB][N];
   __shared__ alignas(16) float sX[2][kRqTB][ROWS];
-  __shared__ float sA[2][kRqTB], sD[2][kRqTB];
+  __shared__ alignas(16) float sA[2][kRqTB];
+  __shared__ alignas(16) float sD[2][kRqTB];
   __shared__ float sY[kRqTB][ROWS];
 
   const int tid = threadIdx.x;
@@ -95,22 +110,18 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
   len = len < 0 ? 0 : (len > L ? L : len);
   const float Ah = A[h], Dh = D[h];
 
-  // state: binary16 values, held as binary32
-  float S[RPT][8];
+  // state: binary16 in registers (the mixed-precision fmas read it directly)
+  _Float16 S[RPT][8];
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     const int p = p0 + r0 + k * RSTRIDE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S[k][i] = 0.f;
+    for (int i = 0; i < 8; ++i) S[k][i] = (_Float16)0.f;
     if (state_in) {
       float v[8];
       io<float>::load8(state_in + (((size_t)bh * P + p) * N + nc), v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float t = v[i];
-        asm volatile("" : "+v"(t));
-        S[k][i] = (float)(_Float16)t;
-      }
+      for (int i = 0; i < 8; ++i) S[k][i] = (_Float16)v[i];
     }
   }
 
@@ -197,34 +208,56 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     const int t0 = kb * kRqTB;
     const int nt = min(kRqTB, len - t0);
     if (kb + 1 < nblocks) fetch(pre, t0 + kRqTB);   // next block in flight
-    for (int t = 0; t < nt; ++t) {
-      const float d = sD[buf][t], a = sA[buf][t];
-      float bv[8], cv[8];
-      Raw8<IO>::get(&sB[buf][t][nc], bv);
-      Raw8<IO>::get(&sC[buf][t][nc], cv);
+    // one token: the state update of this thread's rows and y of each row
+    // (every lane of a row ends with the row's sum and writes the same value)
+    // -0 as an opaque register value: fma(u, B, -0) is exactly u * B, and
+    // kept as an fma it takes a binary16 B without a separate conversion
+    float mzero = -0.f;
+    asm volatile("" : "+v"(mzero));
+    auto token = [&](int t, float d, float a, const float (&bv)[8], const float (&cv)[8], const float (&xr)[RPT]) {
 #pragma unroll
       for (int k = 0; k < RPT; ++k) {
-        const int rr = r0 + k * RSTRIDE;
-        const float xp = sX[buf][t][rr];
         float acc = 0.f;
         {
 #pragma clang fp contract(off)
-          const float u = d * xp;
+          const float u = d * xr[k];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float v = u * bv[i];
-            float sn = __builtin_fmaf(a, S[k][i], v);
+            const float v = __builtin_fmaf(u, bv[i], mzero);   // exactly u * B
+            float sn = __builtin_fmaf(a, (float)S[k][i], v);
             acc = __builtin_fmaf(sn, cv[i], acc);
             // binary32 first, then binary16 (the empty asm keeps the two
             // roundings apart: a fused fma-to-binary16 would round once)
             asm volatile("" : "+v"(sn));
-            S[k][i] = (float)(_Float16)sn;
+            S[k][i] = (_Float16)sn;
           }
         }
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        if ((tid % LPR) == 0) sY[t][rr] = acc + Dh * xp;
+        acc = row_sum<LPR>(acc);
+        sY[t][r0 + k * RSTRIDE] = acc + Dh * xr[k];
       }
+    };
+    auto operands = [&](int t, float (&bv)[8], float (&cv)[8], float (&xr)[RPT]) {
+      Raw8<IO>::get(&sB[buf][t][nc], bv);
+      Raw8<IO>::get(&sC[buf][t][nc], cv);
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) xr[k] = sX[buf][t][r0 + k * RSTRIDE];
+    };
+    // four tokens at a time: all their LDS operands are read before the
+    // first update, so the reads' latency is paid once per four tokens
+    int t = 0;
+    for (; t + 4 <= nt; t += 4) {
+      const f4 dq = *reinterpret_cast<const f4*>(&sD[buf][t]);
+      const f4 aq = *reinterpret_cast<const f4*>(&sA[buf][t]);
+      float bv[4][8], cv[4][8], xr[4][RPT];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) operands(t + u, bv[u], cv[u], xr[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) token(t + u, dq[u], aq[u], bv[u], cv[u], xr[u]);
+    }
+    for (; t < nt; ++t) {
+      float bv[8], cv[8], xr[RPT];
+      operands(t, bv, cv, xr);
+      token(t, sD[buf][t], sA[buf][t], bv, cv, xr);
     }
     __syncthreads();                           // sY complete; buffer buf free
     store_y(t0, nt);
@@ -237,8 +270,8 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     for (int k = 0; k < RPT; ++k) {
       const int p = p0 + r0 + k * RSTRIDE;
       float* dst = state_out + (((size_t)bh * P + p) * N + nc);
-      *reinterpret_cast<f4*>(dst) = f4{S[k][0], S[k][1], S[k][2], S[k][3]};
-      *reinterpret_cast<f4*>(dst + 4) = f4{S[k][4], S[k][5], S[k][6], S[k][7]};
+      *reinterpret_cast<f4*>(dst) = f4{(float)S[k][0], (float)S[k][1], (float)S[k][2], (float)S[k][3]};
+      *reinterpret_cast<f4*>(dst + 4) = f4{(float)S[k][4], (float)S[k][5], (float)S[k][6], (float)S[k][7]};
     }
   }
 }
