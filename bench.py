@@ -33,6 +33,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_F16_PEAK = 2500.0     # TFLOP/s dense f16
+# fp32 VALU issue without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_layer_traffic.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "mamba_ssd_scan_amd", "csrc", "window.hip")
 
@@ -205,6 +207,25 @@ def main():
         torch.cuda.synchronize()
         lat.append(ev0.elapsed_time(ev1) * 1e3)
     lat_us = float(np.median(lat))
+
+    # ---- the same window with the state requantized to binary16 every token ----
+    # (the pages' scoring semantics; VALU-bound: per state element and token a
+    # product, an fma, a binary16 rounding and an fma into y)
+    def rqstep(k):
+        t = sets[k % len(sets)]
+        m2.requant_window(t["dt"], t["A"], t["D"], t["y"], x=t["x"], B=t["B"], C=t["C"], state_out=t["hT"],
+                          stream=stream)
+
+    for k in range(2):
+        rqstep(k)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(10):
+        rqstep(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    rq_us = ev0.elapsed_time(ev1) * 1e3 / 10
+    rq_updates = B * L * H * P * N
     del sets
     torch.cuda.empty_cache()
 
@@ -385,6 +406,13 @@ def main():
                     "tokens_per_s": round(sum(blens) / (bat_us * 1e-6), 1), "algorithmic_bytes": bbytes,
                     "achieved_GBs": round(bbytes / (bat_us * 1e-6) / 1e9, 1),
                     "frac": round(bbytes / (bat_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "requant_window": {"workload": "layer window, state requantized to binary16 after every token",
+                           "us": round(rq_us, 2), "tokens_per_s": round(B * L / (rq_us * 1e-6), 1),
+                           "state_updates_per_s": round(rq_updates / (rq_us * 1e-6), 1),
+                           "roofline": {"bound": "alu", "ops_per_update": 4,
+                                        "achieved": round(4 * rq_updates / (rq_us * 1e-6) / 1e12, 2),
+                                        "peak": VALU_PEAK_TOPS, "unit": "T lane-ops/s",
+                                        "frac": round(4 * rq_updates / (rq_us * 1e-6) / 1e12 / VALU_PEAK_TOPS, 4)}},
         "decode": {"us_per_step": round(dec_us, 2), "us_per_step_rotated_states": round(dec_rot_us, 2),
                    "algorithmic_bytes": dbytes, "achieved_GBs": round(dbytes / (dec_rot_us * 1e-6) / 1e9, 1),
                    "frac": round(dbytes / (dec_rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
