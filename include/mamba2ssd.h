@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 1
+#define MAMBA2_ABI_VERSION 2
 
 enum {
     MAMBA2_OK = 0,
@@ -76,6 +76,11 @@ typedef struct mamba2_dims {
                             pass the state on in registers; runs hand it over
                             through the workspace.  Results agree up to
                             rounding for every k.                              */
+    int32_t dt_softplus; /* 0: dt is given positive and used as is;
+                            1: dt is the raw pre-activation and every kernel
+                            uses dt_eff = (float) sp((double) dt +
+                            (double) dt_bias[h]), sp(v) = v for v > 20 and
+                            log1p(exp(v)) otherwise (no clamp)              */
 } mamba2_dims;
 
 /* ------------------------------------------------------------------------ */
@@ -92,7 +97,8 @@ typedef struct mamba2_dims {
  *                     a window reset), the 3 raw tokens preceding the window,
  *                     oldest first; conv_state_out same shape or NULL: the last
  *                     3 raw tokens before seqlens[b].
- *   dt (B,L,H) io, already positive (no bias, softplus or clamp is applied)
+ *   dt (B,L,H) io: positive, or raw when dims.dt_softplus == 1 (then
+ *             dt_bias (H) f32 or NULL (zero) is added before the softplus)
  *   A, D (H) f32
  *   state_in  (B,H,P,N) f32 or NULL (zero initial state)
  *   state_out (B,H,P,N) f32 or NULL: state after token seqlens[b]-1
@@ -124,6 +130,7 @@ typedef struct mamba2_window_io {
     const void* z;
     const float* norm_w;
     void* y;
+    const float* dt_bias;
 } mamba2_window_io;
 
 /* Workspace size for a window call with these dims (host only, no GPU call).
@@ -160,7 +167,8 @@ int32_t mamba2_requant_window(const mamba2_dims* dims, const mamba2_window_io* i
 
 /* ------------------------------------------------------------------------ */
 /* One-token recurrent step for B sequences (dims.seqlen is ignored).
- *   x (B,H,P) io; dt (B,H) io (positive); B, C (B,G,N) io; A, D (H) f32
+ *   x (B,H,P) io; dt (B,H) io (positive, or raw with dims.dt_softplus);
+ *   B, C (B,G,N) io; A, D (H) f32
  *   state (B,H,P,N) in state_dtype, read and updated IN PLACE
  *   y (B,H,P) io
  * With an f16 resident state the step is evaluated in binary32 as
@@ -177,6 +185,7 @@ typedef struct mamba2_decode_io {
     const float* D;
     void* state;
     void* y;
+    const float* dt_bias;   /* (H) f32 or NULL, used when dims.dt_softplus == 1 */
 } mamba2_decode_io;
 
 int32_t mamba2_decode_step(const mamba2_dims* dims, const mamba2_decode_io* io, void* stream);

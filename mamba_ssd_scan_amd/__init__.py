@@ -39,17 +39,18 @@ class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk",
         "conv_width", "norm_group", "io_dtype", "state_dtype")] + [("norm_eps", ctypes.c_float),
-                                                                   ("segments", ctypes.c_int32)]
+                                                                   ("segments", ctypes.c_int32),
+                                                                   ("dt_softplus", ctypes.c_int32)]
 
 
 class _WindowIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "B", "C", "xBC", "conv_w", "conv_b", "conv_state_in", "conv_state_out", "dt", "A", "D",
-        "state_in", "state_out", "seqlens", "z", "norm_w", "y")]
+        "state_in", "state_out", "seqlens", "z", "norm_w", "y", "dt_bias")]
 
 
 class _DecodeIO(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("x", "dt", "B", "C", "A", "D", "state", "y")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x", "dt", "B", "C", "A", "D", "state", "y", "dt_bias")]
 
 
 _lib = None
@@ -125,9 +126,9 @@ def _io_dtype(t):
 
 
 def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=256, conv_width=0, norm_group=0,
-              io_dtype=F16, state_dtype=F32, norm_eps=1e-5, segments=0) -> Dims:
+              io_dtype=F16, state_dtype=F32, norm_eps=1e-5, segments=0, dt_softplus=0) -> Dims:
     return Dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, conv_width, norm_group, io_dtype,
-                state_dtype, norm_eps, segments)
+                state_dtype, norm_eps, segments, dt_softplus)
 
 
 def window_workspace_bytes(dims: Dims) -> int:
@@ -145,7 +146,7 @@ def alloc_workspace(dims: Dims, device) -> torch.Tensor:
 def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None, conv_w=None, conv_b=None,
                      conv_state_in=None, conv_state_out=None, state_in=None, state_out=None, seqlens=None,
                      z=None, norm_w=None, chunk=256, norm_group=0, norm_eps=1e-5, ngroups=None, dstate=None,
-                     headdim=None, segments=0, stream=None):
+                     headdim=None, segments=0, dt_softplus=False, dt_bias=None, stream=None):
     """Whole-window scan.  Shapes: x (B,L,H,P), B/C (B,L,G,N) -- or xBC
     (B,L,H*P+2*G*N) with conv_w (H*P+2*G*N, 4) for the fused conv --, dt
     (B,L,H), A/D (H) f32, y (B,L,H*P) (or (B,L,H,P)).  See include/mamba2ssd.h."""
@@ -160,37 +161,38 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
         P = x.shape[3]
         G, N = B.shape[2], B.shape[3]
     dims = make_dims(Bsz, L, H, P, N, G, chunk, 4 if conv else 0, norm_group, _io_dtype(dt), F32, norm_eps,
-                     segments)
+                     segments, int(bool(dt_softplus)))
     io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), _ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in),
                    _ptr(conv_state_out), _ptr(dt), _ptr(A), _ptr(D), _ptr(state_in), _ptr(state_out),
-                   _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y))
+                   _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y), _ptr(dt_bias))
     _check("mamba2_conv_scan_window",
            load_library().mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
                                                   workspace.numel(), _stream(dt, stream)))
 
 
-def requant_window(dt, A, D, y, *, x, B, C, state_in=None, state_out=None, seqlens=None, stream=None):
+def requant_window(dt, A, D, y, *, x, B, C, state_in=None, state_out=None, seqlens=None, dt_softplus=False,
+                   dt_bias=None, stream=None):
     """Whole window with the state requantized to binary16 after every token.
     Shapes: x (B,L,H,P), B/C (B,L,G,N), dt (B,L,H), A/D (H) f32, y (B,L,H*P)
     (or (B,L,H,P)); state_in/state_out (B,H,P,N) f32.  See include/mamba2ssd.h."""
     Bsz, L, H = dt.shape
     P = x.shape[3]
     G, N = B.shape[2], B.shape[3]
-    dims = make_dims(Bsz, L, H, P, N, G, 256, 0, 0, _io_dtype(dt), F16)
+    dims = make_dims(Bsz, L, H, P, N, G, 256, 0, 0, _io_dtype(dt), F16, dt_softplus=int(bool(dt_softplus)))
     io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), None, None, None, None, None, _ptr(dt), _ptr(A), _ptr(D),
-                   _ptr(state_in), _ptr(state_out), _ptr(seqlens), None, None, _ptr(y))
+                   _ptr(state_in), _ptr(state_out), _ptr(seqlens), None, None, _ptr(y), _ptr(dt_bias))
     _check("mamba2_requant_window", load_library().mamba2_requant_window(ctypes.byref(dims), ctypes.byref(io),
                                                                          _stream(dt, stream)))
 
 
-def decode_step(x, dt, B, C, A, D, state, y, stream=None):
+def decode_step(x, dt, B, C, A, D, state, y, dt_softplus=False, dt_bias=None, stream=None):
     """One token for each of B sequences: x (B,H,P), dt (B,H), B/C (B,G,N),
     A/D (H) f32, state (B,H,P,N) f16 or f32 updated in place, y (B,H,P)."""
     Bsz, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     sd = F16 if state.dtype == torch.float16 else F32
-    dims = make_dims(Bsz, 1, H, P, N, G, 256, 0, 0, _io_dtype(x), sd)
-    io = _DecodeIO(_ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(state), _ptr(y))
+    dims = make_dims(Bsz, 1, H, P, N, G, 256, 0, 0, _io_dtype(x), sd, dt_softplus=int(bool(dt_softplus)))
+    io = _DecodeIO(_ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(state), _ptr(y), _ptr(dt_bias))
     _check("mamba2_decode_step", load_library().mamba2_decode_step(ctypes.byref(dims), ctypes.byref(io),
                                                                    _stream(x, stream)))
 

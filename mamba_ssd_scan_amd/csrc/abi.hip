@@ -10,7 +10,7 @@
 namespace m2 {
 hipError_t launch_decode(int io_f16, int state_f16, int N, const void* x, const void* dt, const void* Bm,
                          const void* Cm, const float* A, const float* D, void* state, void* y, int Bsz,
-                         int H, int P, int G, hipStream_t st);
+                         int H, int P, int G, int dt_sp, const float* dt_bias, hipStream_t st);
 hipError_t launch_state_convert(int to_resident, int state_f16, const void* src, void* dst, size_t n,
                                 hipStream_t st);
 size_t window_workspace_bytes(const mamba2_dims& d);
@@ -50,6 +50,7 @@ int32_t check_common(const mamba2_dims* d) {
   if (d->nheads % d->ngroups != 0) return MAMBA2_EINVAL;
   if (d->io_dtype != MAMBA2_F16 && d->io_dtype != MAMBA2_F32) return MAMBA2_EINVAL;
   if (d->state_dtype != MAMBA2_F16 && d->state_dtype != MAMBA2_F32) return MAMBA2_EINVAL;
+  if (d->dt_softplus != 0 && d->dt_softplus != 1) return MAMBA2_EINVAL;
   if (d->dstate != 16 && d->dstate != 64 && d->dstate != 128) return MAMBA2_EUNSUPPORTED;
   // Every tensor stays well inside 2^31 elements per sequence-head slice and
   // 2^62 bytes overall.
@@ -86,7 +87,8 @@ int32_t mamba2_decode_step(const mamba2_dims* d, const mamba2_decode_io* io, voi
   if (!aligned16(io->x) || !aligned16(io->B) || !aligned16(io->C) || !aligned16(io->state) ||
       !aligned16(io->y))
     return MAMBA2_EALIGN;
-  if (((uintptr_t)io->dt % esize(d->io_dtype)) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3))
+  if (((uintptr_t)io->dt % esize(d->io_dtype)) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3) ||
+      ((uintptr_t)io->dt_bias & 3))
     return MAMBA2_EALIGN;
   const size_t es = esize(d->io_dtype);
   const size_t BH = (size_t)d->batch * d->nheads;
@@ -94,13 +96,15 @@ int32_t mamba2_decode_step(const mamba2_dims* d, const mamba2_decode_io* io, voi
   Range ry = rng(io->y, BH * d->headdim * es);
   Range rs = rng(io->state, BH * d->headdim * d->dstate * esize(d->state_dtype));
   Range ins[] = {rng(io->x, BH * d->headdim * es), rng(io->dt, BH * es), rng(io->B, BG * d->dstate * es),
-                 rng(io->C, BG * d->dstate * es), rng(io->A, d->nheads * 4), rng(io->D, d->nheads * 4)};
+                 rng(io->C, BG * d->dstate * es), rng(io->A, d->nheads * 4), rng(io->D, d->nheads * 4),
+                 rng(io->dt_bias, d->dt_softplus ? d->nheads * 4 : 0)};
   if (overlap(ry, rs)) return MAMBA2_EINVAL;
   for (const Range& r : ins)
     if (overlap(r, ry) || overlap(r, rs)) return MAMBA2_EINVAL;
   return hip_status(m2::launch_decode(d->io_dtype == MAMBA2_F16, d->state_dtype == MAMBA2_F16, d->dstate,
                                       io->x, io->dt, io->B, io->C, io->A, io->D, io->state, io->y, d->batch,
-                                      d->nheads, d->headdim, d->ngroups, (hipStream_t)stream));
+                                      d->nheads, d->headdim, d->ngroups, d->dt_softplus,
+                                      d->dt_softplus ? io->dt_bias : nullptr, (hipStream_t)stream));
 }
 
 static int32_t state_convert(const mamba2_dims* d, const void* src, void* dst, int to_resident, void* stream) {
@@ -180,7 +184,7 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
     if (p && !aligned16(p)) return MAMBA2_EALIGN;
   if (((uintptr_t)io->dt % es) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3) ||
       ((uintptr_t)io->seqlens & 3) || ((uintptr_t)io->conv_b & 3) || ((uintptr_t)io->conv_state_in % es) ||
-      ((uintptr_t)io->conv_state_out % es))
+      ((uintptr_t)io->conv_state_out % es) || ((uintptr_t)io->dt_bias & 3))
     return MAMBA2_EALIGN;
   // workspace
   const size_t need = m2::window_workspace_bytes(*d);
@@ -200,7 +204,8 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
                  rng(io->dt, tok * H * es), rng(io->A, H * 4), rng(io->D, H * 4),
                  rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4),
                  rng(io->z, d->norm_group ? tok * H * P * es : 0),
-                 rng(io->norm_w, d->norm_group ? H * P * 4 : 0)};
+                 rng(io->norm_w, d->norm_group ? H * P * 4 : 0),
+                 rng(io->dt_bias, d->dt_softplus ? H * 4 : 0)};
   const size_t nout = sizeof(outs) / sizeof(outs[0]);
   for (size_t i = 0; i < nout; ++i) {
     for (const Range& r : ins)
@@ -226,13 +231,14 @@ int32_t mamba2_requant_window(const mamba2_dims* d, const mamba2_window_io* io, 
   for (const void* p : vec)
     if (p && !aligned16(p)) return MAMBA2_EALIGN;
   if (((uintptr_t)io->x % es) || ((uintptr_t)io->y % es) || ((uintptr_t)io->dt % es) || ((uintptr_t)io->A & 3) ||
-      ((uintptr_t)io->D & 3) || ((uintptr_t)io->seqlens & 3))
+      ((uintptr_t)io->D & 3) || ((uintptr_t)io->seqlens & 3) || ((uintptr_t)io->dt_bias & 3))
     return MAMBA2_EALIGN;
   const size_t tok = Bsz * L;
   Range outs[] = {rng(io->y, tok * H * P * es), rng(io->state_out, Bsz * H * P * N * 4)};
   Range ins[] = {rng(io->x, tok * H * P * es), rng(io->B, tok * G * N * es), rng(io->C, tok * G * N * es),
                  rng(io->dt, tok * H * es),    rng(io->A, H * 4),            rng(io->D, H * 4),
-                 rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4)};
+                 rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4),
+                 rng(io->dt_bias, d->dt_softplus ? H * 4 : 0)};
   for (const Range& o : outs)
     for (const Range& r : ins)
       if (overlap(o, r)) return MAMBA2_EINVAL;

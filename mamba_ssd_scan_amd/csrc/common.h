@@ -54,4 +54,12 @@ template <> struct io<float> {
   static __device__ __forceinline__ void store4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
 };
 
+// dt from its raw pre-activation (dims.dt_softplus): sp(raw + bias) in
+// double precision, rounded once to binary32; sp(v) = v above 20, else
+// log1p(exp(v)).
+__device__ __forceinline__ float dt_softplus(float raw, float bias) {
+  const double v = (double)raw + (double)bias;
+  return (float)(v > 20.0 ? v : log1p(exp(v)));
+}
+
 }  // namespace m2

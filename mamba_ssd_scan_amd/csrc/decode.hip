@@ -58,7 +58,8 @@ template <typename IO, typename ST, int N>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const IO* __restrict__ x, const IO* __restrict__ dt, const IO* __restrict__ Bm,
     const IO* __restrict__ Cm, const float* __restrict__ A, const float* __restrict__ D,
-    typename ST::T* __restrict__ state, IO* __restrict__ y, int H, int P, int G) {
+    typename ST::T* __restrict__ state, IO* __restrict__ y, int H, int P, int G, int dt_sp,
+    const float* __restrict__ dt_bias) {
   constexpr int LPR = N / 8;          // lanes per state row
   constexpr int RPP = 256 / LPR;      // rows per pass
   const int bh = blockIdx.x;
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const int nc = (tid % LPR) * 8;     // first n of this thread
   const int r0 = tid / LPR;
 
-  const float d = io<IO>::load1(dt + bh);
+  float d = io<IO>::load1(dt + bh);
+  if (dt_sp) d = dt_softplus(d, dt_bias ? dt_bias[h] : 0.f);
   const float Ah = A[h];
   // Decay rounded once from a double-precision exponential (binary32 contract).
   const float a = (float)exp((double)d * (double)Ah);
@@ -142,21 +144,21 @@ __global__ __launch_bounds__(256) void state_store_kernel(const typename ST::T* 
 template <typename IO, typename ST>
 static hipError_t launch_decode_T(int N, const void* x, const void* dt, const void* Bm, const void* Cm,
                                   const float* A, const float* D, void* state, void* y, int Bsz, int H,
-                                  int P, int G, hipStream_t st) {
+                                  int P, int G, int dt_sp, const float* dt_bias, hipStream_t st) {
   dim3 grid(Bsz * H), block(256);
   using S = typename ST::T;
   switch (N) {
     case 16:
       decode_step_kernel<IO, ST, 16><<<grid, block, 0, st>>>((const IO*)x, (const IO*)dt, (const IO*)Bm,
-                                                             (const IO*)Cm, A, D, (S*)state, (IO*)y, H, P, G);
+                                                             (const IO*)Cm, A, D, (S*)state, (IO*)y, H, P, G, dt_sp, dt_bias);
       break;
     case 64:
       decode_step_kernel<IO, ST, 64><<<grid, block, 0, st>>>((const IO*)x, (const IO*)dt, (const IO*)Bm,
-                                                             (const IO*)Cm, A, D, (S*)state, (IO*)y, H, P, G);
+                                                             (const IO*)Cm, A, D, (S*)state, (IO*)y, H, P, G, dt_sp, dt_bias);
       break;
     default:
       decode_step_kernel<IO, ST, 128><<<grid, block, 0, st>>>((const IO*)x, (const IO*)dt, (const IO*)Bm,
-                                                              (const IO*)Cm, A, D, (S*)state, (IO*)y, H, P, G);
+                                                              (const IO*)Cm, A, D, (S*)state, (IO*)y, H, P, G, dt_sp, dt_bias);
       break;
   }
   return hipGetLastError();
@@ -164,14 +166,16 @@ static hipError_t launch_decode_T(int N, const void* x, const void* dt, const vo
 
 hipError_t launch_decode(int io_f16, int state_f16, int N, const void* x, const void* dt, const void* Bm,
                          const void* Cm, const float* A, const float* D, void* state, void* y, int Bsz,
-                         int H, int P, int G, hipStream_t st) {
+                         int H, int P, int G, int dt_sp, const float* dt_bias, hipStream_t st) {
   if (io_f16 && state_f16)
-    return launch_decode_T<_Float16, StateF16<8>>(N, x, dt, Bm, Cm, A, D, state, y, Bsz, H, P, G, st);
+    return launch_decode_T<_Float16, StateF16<8>>(N, x, dt, Bm, Cm, A, D, state, y, Bsz, H, P, G, dt_sp, dt_bias,
+                                                  st);
   if (io_f16)
-    return launch_decode_T<_Float16, StateF32<8>>(N, x, dt, Bm, Cm, A, D, state, y, Bsz, H, P, G, st);
+    return launch_decode_T<_Float16, StateF32<8>>(N, x, dt, Bm, Cm, A, D, state, y, Bsz, H, P, G, dt_sp, dt_bias,
+                                                  st);
   if (state_f16)
-    return launch_decode_T<float, StateF16<8>>(N, x, dt, Bm, Cm, A, D, state, y, Bsz, H, P, G, st);
-  return launch_decode_T<float, StateF32<8>>(N, x, dt, Bm, Cm, A, D, state, y, Bsz, H, P, G, st);
+    return launch_decode_T<float, StateF16<8>>(N, x, dt, Bm, Cm, A, D, state, y, Bsz, H, P, G, dt_sp, dt_bias, st);
+  return launch_decode_T<float, StateF32<8>>(N, x, dt, Bm, Cm, A, D, state, y, Bsz, H, P, G, dt_sp, dt_bias, st);
 }
 
 hipError_t launch_state_convert(int to_resident, int state_f16, const void* src, void* dst, size_t n,

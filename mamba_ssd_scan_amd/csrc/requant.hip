@@ -84,7 +84,8 @@ template <typename IO, int N>
 __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     const IO* __restrict__ x, const IO* __restrict__ dt, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ state_in,
-    float* __restrict__ state_out, const int* __restrict__ seqlens, IO* __restrict__ y, int L, int H, int G) {
+    float* __restrict__ state_out, const int* __restrict__ seqlens, IO* __restrict__ y, int L, int H, int G,
+    int dt_sp, const float* __restrict__ dt_bias) {
   constexpr int P = 64;
   constexpr int ROWS = RqShape<N>::ROWS, RPT = RqShape<N>::RPT, NTH = RqShape<N>::NTH;
   constexpr int LPR = N / 8;                 // lanes per state row
@@ -109,6 +110,7 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
   int len = seqlens ? seqlens[b] : L;
   len = len < 0 ? 0 : (len > L ? L : len);
   const float Ah = A[h], Dh = D[h];
+  const float dtb = dt_sp && dt_bias ? dt_bias[h] : 0.f;
 
   // state: binary16 in registers (the mixed-precision fmas read it directly)
   _Float16 S[RPT][8];
@@ -161,6 +163,7 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     if (tid < kRqTB) {
       const int tt = min(t0 + tid, len - 1);
       r.d = io<IO>::load1(dt + (seqtok + tt) * H + h);
+      if (dt_sp) r.d = dt_softplus(r.d, dtb);
     }
   };
   auto stage = [&](const Pre& r, int buf) {
@@ -282,7 +285,8 @@ static hipError_t launch_rq(const mamba2_dims& d, const mamba2_window_io& io_, h
   const unsigned grid = (unsigned)(d.batch * d.nheads * (64 / ROWS));
   requant_window_kernel<IO, N><<<grid, NTH, 0, st>>>(
       (const IO*)io_.x, (const IO*)io_.dt, (const IO*)io_.B, (const IO*)io_.C, io_.A, io_.D, io_.state_in,
-      io_.state_out, io_.seqlens, (IO*)io_.y, d.seqlen, d.nheads, d.ngroups);
+      io_.state_out, io_.seqlens, (IO*)io_.y, d.seqlen, d.nheads, d.ngroups, d.dt_softplus,
+      d.dt_softplus ? io_.dt_bias : nullptr);
   return hipGetLastError();
 }
 

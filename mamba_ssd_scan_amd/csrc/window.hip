@@ -52,6 +52,8 @@ template <typename IO> struct WinArgs {
   int tree_lg;        // log2 of the radix of the segment tree
   int cps;            // chunks per segment: one workgroup runs a segment's chunks in order
   int nseg;           // segments per sequence
+  int dt_sp;          // dt is raw: dt_eff = softplus(dt + dt_bias[h])
+  const float* dt_bias;
 };
 
 // control block: eight claim counters and the done counter / generation /
@@ -493,11 +495,15 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 
   // ---- phase 0 (per chunk): dt and the running log2-decay over the chunk --
   // (4 tokens per lane); the dt of the next chunk is loaded while a chunk runs
+  const float dtb = a.dt_sp && a.dt_bias ? a.dt_bias[h] : 0.f;
   auto load_dt = [&](int cc, float (&d)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * lane + e;
       d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((cc * a.Q + i) * a.H) * ES) : 0.f;
+      // a raw dt goes through the softplus; tokens past the sequence keep
+      // dt = 0 (the state passes through them unchanged)
+      if (a.dt_sp) d[e] = i < a.Q && cc * a.Q + i < len ? dt_softplus(d[e], dtb) : 0.f;
     }
   };
   auto scan_dt = [&](const float (&d)[4]) {
@@ -1063,6 +1069,8 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   a.B = d.batch; a.L = d.seqlen; a.H = d.nheads; a.G = d.ngroups; a.Q = d.chunk;
   a.nchunks = (d.seqlen + d.chunk - 1) / d.chunk;
   a.nseg = d.segments;                           // 0: chosen at launch
+  a.dt_sp = d.dt_softplus;
+  a.dt_bias = d.dt_softplus ? io_.dt_bias : nullptr;
   a.dt = (const IO*)io_.dt; a.A = io_.A; a.D = io_.D;
   a.state_in = io_.state_in; a.state_out = io_.state_out; a.seqlens = io_.seqlens;
   a.z = (const IO*)io_.z; a.y = (IO*)io_.y;

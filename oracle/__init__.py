@@ -53,6 +53,8 @@ def _load():
         lib.oracle_ssd_scan.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, ip, dp, dp, dp, i]
         lib.oracle_gated_rmsnorm.argtypes = [i64, i, i, dp, dp, dp, ctypes.c_double, dp]
         lib.oracle_decode_f16state.argtypes = [i, i, i, i, i, i, fp, fp, fp, fp, fp, fp, u16p, dp, i, i, i]
+        lib.oracle_dt_softplus.argtypes = [i64, i, dp, dp, dp]
+        lib.oracle_dt_softplus_f32.argtypes = [i64, i, fp, fp, fp]
         lib.oracle_threads_used.restype = ctypes.c_int
         lib.oracle_threads_used.argtypes = [i]
         _lib = lib
@@ -104,10 +106,40 @@ def conv_silu(xin, w, bias=None, state_in=None, seqlens=None):
     return out, st
 
 
-def ssd_scan(x, dt, A, Bm, Cm, D, h0=None, seqlens=None, nthreads: int = 0):
+def dt_softplus(raw, bias=None):
+    """fp64 step sizes from raw dt: sp(raw + bias[h]) over the last axis (H)."""
+    raw = _f64(raw)
+    H = raw.shape[-1]
+    bias = _f64(bias) if bias is not None else None
+    assert bias is None or bias.shape == (H,)
+    out = np.empty_like(raw)
+    _load().oracle_dt_softplus(raw.size, H, _ptr(raw, ctypes.c_double), _ptr(bias, ctypes.c_double),
+                               _ptr(out, ctypes.c_double))
+    return out
+
+
+def dt_softplus_f32(raw, bias=None):
+    """Binary32 step sizes from binary32 raw dt: (float) sp((double) raw +
+    (double) bias[h]), the decode step's contract."""
+    raw = _f32(raw)
+    H = raw.shape[-1]
+    bias = _f32(bias) if bias is not None else None
+    assert bias is None or bias.shape == (H,)
+    out = np.empty_like(raw)
+    _load().oracle_dt_softplus_f32(raw.size, H, _ptr(raw, ctypes.c_float), _ptr(bias, ctypes.c_float),
+                                   _ptr(out, ctypes.c_float))
+    return out
+
+
+def ssd_scan(x, dt, A, Bm, Cm, D, h0=None, seqlens=None, nthreads: int = 0, dt_bias=None,
+             dt_softplus_raw: bool = False):
     """Sequential fp64 selective-scan.  x (B, L, H, P); dt (B, L, H); A, D (H);
-    Bm, Cm (B, L, G, N); h0 (B, H, P, N) or None.  Returns (y (B, L, H, P),
-    final state (B, H, P, N)); y rows t >= seqlens[b] are NaN."""
+    Bm, Cm (B, L, G, N); h0 (B, H, P, N) or None.  With dt_softplus_raw, dt is
+    the raw pre-activation and the step size is sp(dt + dt_bias[h]) in fp64.
+    Returns (y (B, L, H, P), final state (B, H, P, N)); y rows t >= seqlens[b]
+    are NaN."""
+    if dt_softplus_raw:
+        dt = dt_softplus(dt, dt_bias)
     x, dt, A, Bm, Cm, D = (_f64(a) for a in (x, dt, A, Bm, Cm, D))
     B, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
@@ -138,7 +170,8 @@ def gated_rmsnorm(y, z, w, group, eps=1e-5):
 
 
 def mixer_core(xin, conv_w, conv_b, dt, A, D, z, norm_w, H, P, G, N, norm_group, eps=1e-5,
-               conv_state=None, h0=None, seqlens=None, nthreads: int = 0):
+               conv_state=None, h0=None, seqlens=None, nthreads: int = 0, dt_bias=None,
+               dt_softplus_raw: bool = False):
     """Full mixer core minus projections: conv1d+SiLU over xBC, split into
     x | B | C, sequential scan, gated RMSNorm.  xin (B, L, H*P + 2*G*N).
     Returns (out (B, L, H*P), final state, conv state out)."""
@@ -149,7 +182,7 @@ def mixer_core(xin, conv_w, conv_b, dt, A, D, z, norm_w, H, P, G, N, norm_group,
     x = u[..., : H * P].reshape(Bsz, L, H, P)
     Bm = u[..., H * P: H * P + G * N].reshape(Bsz, L, G, N)
     Cm = u[..., H * P + G * N:].reshape(Bsz, L, G, N)
-    y, hT = ssd_scan(x, dt, A, Bm, Cm, D, h0, seqlens, nthreads)
+    y, hT = ssd_scan(x, dt, A, Bm, Cm, D, h0, seqlens, nthreads, dt_bias, dt_softplus_raw)
     yf = np.nan_to_num(y.reshape(Bsz, L, H * P), nan=0.0)
     out = gated_rmsnorm(yf, z, norm_w, norm_group, eps)
     if seqlens is not None:
@@ -158,12 +191,16 @@ def mixer_core(xin, conv_w, conv_b, dt, A, D, z, norm_w, H, P, G, N, norm_group,
     return out, hT, cst
 
 
-def decode_f16state(x, dt, A, Bm, Cm, D, state_bits, b_range=None, nthreads: int = 0):
+def decode_f16state(x, dt, A, Bm, Cm, D, state_bits, b_range=None, nthreads: int = 0, dt_bias=None,
+                    dt_softplus_raw: bool = False):
     """Consecutive single-token steps with the state stored to binary16 after
     each step.  x (T, B, H, P); dt (T, B, H); Bm, Cm (T, B, G, N); A, D (H);
     state_bits (B, H, P, N) uint16 binary16 patterns, updated in place for the
-    sequences in b_range = (lo, hi).  Returns y (T, B, H, P) in fp64 (NaN
-    outside b_range)."""
+    sequences in b_range = (lo, hi).  With dt_softplus_raw, dt is raw and the
+    binary32 step size is dt_softplus_f32(dt, dt_bias).  Returns y (T, B, H, P)
+    in fp64 (NaN outside b_range)."""
+    if dt_softplus_raw:
+        dt = dt_softplus_f32(dt, dt_bias)
     x, dt, A, Bm, Cm, D = (_f32(a) for a in (x, dt, A, Bm, Cm, D))
     T, B, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]

@@ -150,6 +150,31 @@ void oracle_conv_silu(int B, int L, int Cn, int W,
 }
 
 /* ------------------------------------------------------------------------ */
+/* dt preprocessing.  Mamba-2 (Dao and Gu 2024, listed under "References" on
+ * page "Mamb2_8B_FP4_Recall_SQ3.25") gets the step size from a raw projection
+ * output plus a per-head bias through softplus, sp(v) = log(1 + e^v).  The
+ * page does not spell this step out; the reading used here is the usual one,
+ * with the large-argument cut-off of the common softplus (sp(v) = v for
+ * v > 20, where log1p(e^v) - v < 2.1e-9):
+ *   dt_eff[i] = sp(raw[i] + bias[i % H])          (bias NULL: zero)
+ * raw is laid out with the head index fastest ((..., H)).  The fp64 form feeds
+ * the fp64 scan; the binary32 form is the decode step's contract, where the
+ * sum and the softplus are taken in fp64 and rounded once to binary32. */
+static double softplus_cut(double v) { return v > 20.0 ? v : log1p(exp(v)); }
+
+void oracle_dt_softplus(int64_t n, int H, const double* raw, const double* bias, double* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = softplus_cut(raw[i] + (bias ? bias[i % H] : 0.0));
+}
+
+void oracle_dt_softplus_f32(int64_t n, int H, const float* raw, const float* bias, float* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (float)softplus_cut((double)raw[i] + (bias ? (double)bias[i % H] : 0.0));
+}
+
+/* ------------------------------------------------------------------------ */
 /* Sequential selective state-space recurrence (fp64).
  * x (B, L, H, P); dt (B, L, H) (positive, used as given); A, D (H);
  * Bm, Cm (B, L, G, N); head h reads group g = h / (H / G).

@@ -95,8 +95,23 @@ def _dt_from_noise(noise, dt_mode, dt0):
     return _softplus(noise + np.log(np.expm1(dt0)))
 
 
-def window_inputs(s: WindowShape, seed: int):
-    """x (B,L,H,P), dt (B,L,H), Bm, Cm (B,L,G,N) in the I/O dtype; A, D (H) f32."""
+def _raw_dt_from_noise(noise, dt_mode):
+    """The pre-activation that _dt_from_noise passes through softplus, less the
+    per-head bias (see dt_bias)."""
+    return noise - 4.0 if dt_mode == "narrow" else noise
+
+
+def dt_bias(dt_mode, dt0):
+    """Per-head f32 bias that, added to the raw draw, gives the softplus
+    argument of _dt_from_noise: log(expm1(dt0)) (narrow mode: zero)."""
+    if dt_mode == "narrow":
+        return np.zeros(len(dt0), F32)
+    return np.log(np.expm1(dt0)).astype(F32)
+
+
+def window_inputs(s: WindowShape, seed: int, raw_dt: bool = False):
+    """x (B,L,H,P), dt (B,L,H), Bm, Cm (B,L,G,N) in the I/O dtype; A, D (H) f32.
+    raw_dt: dt holds the raw draw and dt_bias (H) f32 is added (same noise)."""
     B, L, H, P, N, G = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups
     A, D, dt0 = head_params(H, seed, s.dt_mode)
     x = np.empty((B, L, H, P), s.io_dtype)
@@ -106,13 +121,17 @@ def window_inputs(s: WindowShape, seed: int):
     for b in range(B):
         r = _rng(seed, 1, b)
         x[b] = r.standard_normal((L, H, P))
-        dt[b] = _dt_from_noise(r.standard_normal((L, H)), s.dt_mode, dt0)
+        noise = r.standard_normal((L, H))
+        dt[b] = _raw_dt_from_noise(noise, s.dt_mode) if raw_dt else _dt_from_noise(noise, s.dt_mode, dt0)
         Bm[b] = r.standard_normal((L, G, N)) / math.sqrt(N)
         Cm[b] = r.standard_normal((L, G, N)) / math.sqrt(N)
-    return dict(x=x, dt=dt, B=Bm, C=Cm, A=A, D=D)
+    out = dict(x=x, dt=dt, B=Bm, C=Cm, A=A, D=D)
+    if raw_dt:
+        out["dt_bias"] = dt_bias(s.dt_mode, dt0)
+    return out
 
 
-def mixer_inputs(s: WindowShape, seed: int):
+def mixer_inputs(s: WindowShape, seed: int, raw_dt: bool = False):
     """Raw xBC (B,L,H*P+2*G*N) ~ N(0,1), conv weights (conv_dim, 4) ~ N(0, 0.5)
     as f32 with zero bias, dt (B,L,H) as for the layer window, z ~ N(0,1),
     norm weight 1."""
@@ -128,10 +147,14 @@ def mixer_inputs(s: WindowShape, seed: int):
     for b in range(B):
         r = _rng(seed, 4, b)
         xBC[b] = r.standard_normal((L, Cn))
-        dt[b] = _dt_from_noise(r.standard_normal((L, H)), s.dt_mode, dt0)
+        noise = r.standard_normal((L, H))
+        dt[b] = _raw_dt_from_noise(noise, s.dt_mode) if raw_dt else _dt_from_noise(noise, s.dt_mode, dt0)
         z[b] = r.standard_normal((L, H * P))
-    return dict(xBC=xBC, conv_w=conv_w, conv_b=conv_b, dt=dt, z=z,
-                norm_w=np.ones(H * P, F32), A=A, D=D)
+    out = dict(xBC=xBC, conv_w=conv_w, conv_b=conv_b, dt=dt, z=z,
+               norm_w=np.ones(H * P, F32), A=A, D=D)
+    if raw_dt:
+        out["dt_bias"] = dt_bias(s.dt_mode, dt0)
+    return out
 
 
 def decode_params(seed: int, batch=64, nheads=128, headdim=64, dstate=128):
@@ -142,11 +165,13 @@ def decode_params(seed: int, batch=64, nheads=128, headdim=64, dstate=128):
 
 
 def decode_step_inputs(seed: int, step: int, dt0, batch=64, nheads=128, headdim=64, dstate=128,
-                       ngroups=8, io_dtype=F16):
-    """Per-step x (B,H,P), dt (B,H), Bm, Cm (B,G,N), drawn like the layer window."""
+                       ngroups=8, io_dtype=F16, raw_dt=False):
+    """Per-step x (B,H,P), dt (B,H), Bm, Cm (B,G,N), drawn like the layer window
+    (raw_dt: dt is the raw draw; the bias is dt_bias("wide", dt0))."""
     r = _rng(seed, 5, step)
     x = r.standard_normal((batch, nheads, headdim)).astype(io_dtype)
-    dt = _dt_from_noise(r.standard_normal((batch, nheads)), "wide", dt0).astype(io_dtype)
+    noise = r.standard_normal((batch, nheads))
+    dt = (noise if raw_dt else _dt_from_noise(noise, "wide", dt0)).astype(io_dtype)
     Bm = (r.standard_normal((batch, ngroups, dstate)) / math.sqrt(dstate)).astype(io_dtype)
     Cm = (r.standard_normal((batch, ngroups, dstate)) / math.sqrt(dstate)).astype(io_dtype)
     return dict(x=x, dt=dt, B=Bm, C=Cm)

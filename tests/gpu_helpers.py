@@ -30,6 +30,14 @@ def slice_err(got, ref, nlead):
     return float((np.abs(g - r).max(axis=1) / den).max())
 
 
+def raw_dt_args(inp):
+    """Keyword arguments that hand a raw dt and its bias to the kernels (empty
+    for a positive dt)."""
+    if "dt_bias" not in inp:
+        return {}
+    return dict(dt_softplus=True, dt_bias=to_dev(inp["dt_bias"]))
+
+
 def run_window(inp, chunk, seqlens=None, state_in=None, want_state=True, ws=None, y_fill=None, segments=0):
     """Run the window scan on the GPU from numpy inputs x, dt, B, C, A, D."""
     x, dt, Bm, Cm = (to_dev(inp[k]) for k in ("x", "dt", "B", "C"))
@@ -46,7 +54,7 @@ def run_window(inp, chunk, seqlens=None, state_in=None, want_state=True, ws=None
         dims = m2.make_dims(Bsz, L, H, P, N, G, chunk, io_dtype=m2.F16 if x.dtype == torch.float16 else m2.F32)
         ws = m2.alloc_workspace(dims, DEV)
     m2.conv_scan_window(dt, A, D, y, ws, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl, chunk=chunk,
-                        segments=segments)
+                        segments=segments, **raw_dt_args(inp))
     torch.cuda.synchronize()
     return y.cpu().numpy().reshape(Bsz, L, H, P), (hT.cpu().numpy() if want_state else None)
 
@@ -63,7 +71,7 @@ def run_requant(inp, seqlens=None, state_in=None, y_fill=None):
     hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=DEV)
     sl = torch.tensor(seqlens, dtype=torch.int32, device=DEV) if seqlens is not None else None
     h0 = to_dev(np.asarray(state_in, np.float32)) if state_in is not None else None
-    m2.requant_window(dt, A, D, y, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl)
+    m2.requant_window(dt, A, D, y, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl, **raw_dt_args(inp))
     torch.cuda.synchronize()
     return y.cpu().numpy().reshape(Bsz, L, H, P), hT.cpu().numpy()
 
@@ -86,6 +94,7 @@ def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=No
                         conv_state_out=cso, state_in=h0, state_out=hT, seqlens=sl,
                         z=to_dev(inp["z"]) if norm_group else None,
                         norm_w=to_dev(inp["norm_w"]) if norm_group else None,
-                        chunk=chunk, norm_group=norm_group, ngroups=G, dstate=N, headdim=P, segments=segments)
+                        chunk=chunk, norm_group=norm_group, ngroups=G, dstate=N, headdim=P, segments=segments,
+                        **raw_dt_args(inp))
     torch.cuda.synchronize()
     return y.cpu().numpy(), hT.cpu().numpy(), (cso.cpu().numpy() if want_conv_state else None)

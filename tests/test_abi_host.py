@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = m2.load_library()
-    assert m2.abi_version() == 1
+    assert m2.abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.mamba2_status_str(code)
     assert lib.mamba2_status_str(77) == b"unknown status"
@@ -78,7 +78,7 @@ def test_long_sequences_beyond_32_bit_rows_are_refused():
     (dict(headdim=32), -2), (dict(dstate=96), -2), (dict(chunk=100), -2), (dict(conv_width=3), -2),
     (dict(nheads=100, ngroups=8), -1), (dict(batch=0), -1), (dict(seqlen=0), -1),
     (dict(norm_group=1000), -1), (dict(norm_group=32), -2), (dict(norm_group=-1), -1),
-    (dict(io_dtype=7), -1), (dict(segments=-1), -1),
+    (dict(io_dtype=7), -1), (dict(segments=-1), -1), (dict(dt_softplus=2), -1),
 ])
 def test_workspace_query_rejects(kw, code):
     lib = m2.load_library()

@@ -37,7 +37,8 @@ def rand_window(seed, B, L, H, N, G, dtype=np.float16, dt_mode="wide", P=64):
 
 def oracle_window(inp, seqlens=None, state_in=None, nthreads=0):
     return oracle.ssd_scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], h0=state_in,
-                           seqlens=seqlens, nthreads=nthreads)
+                           seqlens=seqlens, nthreads=nthreads, dt_bias=inp.get("dt_bias"),
+                           dt_softplus_raw="dt_bias" in inp)
 
 
 def check_window(name, inp, chunk, seqlens=None, state_in=None, segments=0):
@@ -184,11 +185,13 @@ def oracle_requant(inp, seqlens=None, state_in=None, heads=None):
     state after every token).  heads: optional slice of heads sharing one
     group, checked on their own."""
     x, dt, Bm, Cm, A, D = (inp[k] for k in ("x", "dt", "B", "C", "A", "D"))
+    bias = inp.get("dt_bias")
     Bsz, L, H, P = x.shape
     N = Bm.shape[3]
     if heads is not None:
         g = heads.start // (H // Bm.shape[2])
         x, dt, A, D = x[:, :, heads], dt[:, :, heads], A[heads], D[heads]
+        bias = bias[heads] if bias is not None else None
         Bm, Cm = Bm[:, :, g:g + 1], Cm[:, :, g:g + 1]
         H = x.shape[2]
         if state_in is not None:
@@ -204,7 +207,8 @@ def oracle_requant(inp, seqlens=None, state_in=None, heads=None):
         yt = oracle.decode_f16state(np.ascontiguousarray(x[b:b + 1, :n].transpose(1, 0, 2, 3)),
                                     np.ascontiguousarray(dt[b:b + 1, :n].transpose(1, 0, 2)), A,
                                     np.ascontiguousarray(Bm[b:b + 1, :n].transpose(1, 0, 2, 3)),
-                                    np.ascontiguousarray(Cm[b:b + 1, :n].transpose(1, 0, 2, 3)), D, sb)
+                                    np.ascontiguousarray(Cm[b:b + 1, :n].transpose(1, 0, 2, 3)), D, sb,
+                                    dt_bias=bias, dt_softplus_raw=bias is not None)
         bits[b] = sb[0]
         y[b, :n] = yt[:, 0]
     return y, bits
@@ -253,6 +257,52 @@ def test_requant_window_layer_shape_sampled():
     ey = slice_err(np.transpose(y[:, :, heads], (0, 2, 1, 3)), np.transpose(yr, (0, 2, 1, 3)), 2)
     say(f"[requant] layer shape, heads 48..63: state identical {same:.6f}  y err {ey:.3e}")
     assert same == 1.0 and ey <= Y_TOL
+
+
+# ---- raw dt: bias + softplus inside the kernels ------------------------------------
+@pytest.mark.parametrize("segments", [0, 2])
+def test_raw_dt_window_ragged(segments):
+    # tokens past a sequence's length must keep dt = 0 although sp(0 + bias) > 0
+    s = synth.WindowShape(2, 600, 8, 64, 128, 2, 256, np.float16, "wide")
+    inp = synth.window_inputs(s, 81, raw_dt=True)
+    h0 = np.random.default_rng(82).standard_normal((2, 8, 64, 128)).astype(np.float32) * 0.3
+    check_window("raw dt", inp, 256, seqlens=[600, 411], state_in=h0, segments=segments)
+
+
+def test_raw_dt_window_fp32_narrow():
+    inp = synth.window_inputs(synth.WindowShape(1, 256, 4, 64, 16, 1, 64, np.float32, "narrow"), 83,
+                              raw_dt=True)
+    check_window("raw dt fp32", inp, 64)
+
+
+def test_raw_dt_layer_window_full_size():
+    s = synth.layer_window()
+    check_window("raw dt layer L=2048", synth.window_inputs(s, 1001, raw_dt=True), s.chunk)
+
+
+def test_raw_dt_requant_window():
+    inp = synth.window_inputs(synth.WindowShape(2, 300, 8, 64, 128, 2, 256, np.float16, "wide"), 84,
+                              raw_dt=True)
+    check_requant("raw dt", inp, seqlens=[300, 131])
+
+
+def test_raw_dt_mixer_core():
+    H, P, G, N, L, Bsz = 16, 64, 2, 128, 300, 2
+    s = synth.WindowShape(Bsz, L, H, P, N, G, 256, np.float16, "wide")
+    inp = synth.mixer_inputs(s, 85, raw_dt=True)
+    lens = [300, 157]
+    say("[mixer] raw dt, norm_group 1024")
+    y, hT, _ = run_mixer(inp, H, P, G, N, 256, 1024, seqlens=lens, want_conv_state=False)
+    out_r, h_r, _ = oracle.mixer_core(inp["xBC"], inp["conv_w"], inp["conv_b"], inp["dt"], inp["A"], inp["D"],
+                                      inp["z"], inp["norm_w"], H, P, G, N, 1024, seqlens=lens,
+                                      dt_bias=inp["dt_bias"], dt_softplus_raw=True)
+    for b, n in enumerate(lens):
+        got = y[b, :n].reshape(n, -1, 1024).transpose(1, 0, 2)
+        ref = out_r[b, :n].reshape(n, -1, 1024).transpose(1, 0, 2)
+        e = slice_err(got, ref, 1)
+        say(f"[mixer] raw dt out seq {b}: {e:.3e}")
+        assert e <= Y_TOL
+    assert slice_err(hT, h_r, 2) <= S_TOL
 
 
 # ---- fused conv + gated norm ----------------------------------------------------
@@ -343,6 +393,29 @@ def test_decode_f16_state_small(N):
     es = slice_err(sg.astype(np.float64), bits.view(np.float16).astype(np.float64), 2)
     say(f"[decode] N={N}: state identical {same:.6f} state err {es:.2e} y err {ey:.2e}")
     assert same >= 0.9999 and es <= S_TOL and ey <= Y_TOL
+
+
+def test_decode_raw_dt_f16_state_bit_exact():
+    T, Bsz, H, N, G = 6, 3, 16, 128, 2
+    prm = synth.decode_params(91, Bsz, H, 64, N)
+    steps = [synth.decode_step_inputs(91, t, prm["dt0"], Bsz, H, 64, N, G, raw_dt=True) for t in range(T)]
+    st = {k: np.stack([s[k] for s in steps]) for k in ("x", "dt", "B", "C")}
+    bias = synth.dt_bias("wide", prm["dt0"])
+    s16 = torch.empty((Bsz, H, 64, N), dtype=torch.float16, device=DEV)
+    m2.state_load(to_dev(prm["state"]), s16)
+    bits = prm["state"].astype(np.float16).view(np.uint16).copy()
+    yg = []
+    for t in range(T):
+        y = torch.empty((Bsz, H, 64), dtype=torch.float16, device=DEV)
+        m2.decode_step(to_dev(st["x"][t]), to_dev(st["dt"][t]), to_dev(st["B"][t]), to_dev(st["C"][t]),
+                       to_dev(prm["A"]), to_dev(prm["D"]), s16, y, dt_softplus=True, dt_bias=to_dev(bias))
+        yg.append(y.cpu().numpy())
+    yr = oracle.decode_f16state(st["x"], st["dt"], prm["A"], st["B"], st["C"], prm["D"], bits, dt_bias=bias,
+                                dt_softplus_raw=True)
+    same = np.mean(s16.cpu().numpy().view(np.uint16) == bits)
+    ey = slice_err(np.stack(yg).transpose(1, 2, 0, 3), yr.transpose(1, 2, 0, 3), 2)
+    say(f"[decode] raw dt: state identical {same:.6f} y err {ey:.2e}")
+    assert same == 1.0 and ey <= Y_TOL
 
 
 def test_decode_f32_state_matches_fp64_recurrence():

@@ -324,3 +324,58 @@ def test_mixer_core_composes_conv_split_scan_norm():
     assert rel(out[0], ref) < 1e-12 and rel(hT[0], hc) < 1e-12
     ysw, _ = chunked_fp64(x[0], dt[0], A, Cm[0], Bm[0], D, 8)
     assert rel(ysw, yc) > 1e-3
+
+
+# --- P16: dt preprocessing (raw dt + bias through softplus) -------------------
+def test_dt_softplus_closed_forms_and_multiprecision():
+    import mpmath
+    mpmath.mp.dps = 40
+    v = np.concatenate([np.linspace(-40, 40, 161), [0.0, 19.999, 20.0, 20.001, 700.0]])
+    got = oracle.dt_softplus(v.reshape(-1, 1)).ravel()
+    ref = np.array([float(mpmath.log1p(mpmath.exp(mpmath.mpf(float(t))))) for t in v])
+    # below the cut-off the value is log1p(exp(v)) to a few ulps; above it the
+    # value is v, which is short of the exact one by e^-v < 2.1e-9
+    assert np.all(np.abs(got - ref) <= 2.1e-9 + 4 * np.spacing(np.abs(ref)))
+    low = v <= 20
+    assert np.all(np.abs(got[low] - ref[low]) <= 4 * np.spacing(np.abs(ref[low])))
+    assert got[v == 700.0][0] == 700.0
+    assert oracle.dt_softplus(np.zeros((1, 1)))[0, 0] == pytest.approx(math.log(2), rel=1e-15)
+    # sp(v) - sp(-v) = v
+    w = np.linspace(0.01, 19.9, 50).reshape(-1, 1)
+    assert np.max(np.abs(oracle.dt_softplus(w) - oracle.dt_softplus(-w) - w)) < 1e-13
+    # binary32 form: one rounding of the fp64 value
+    raw32 = np.linspace(-12, 24, 301).astype(np.float32).reshape(-1, 1)
+    f32 = oracle.dt_softplus_f32(raw32).ravel()
+    ref32 = np.array([float(mpmath.log1p(mpmath.exp(mpmath.mpf(float(t))))) for t in raw32.ravel()])
+    ulp = np.spacing(np.abs(ref32).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(f32.astype(np.float64) - ref32) <= 0.5 * ulp + 2.1e-9)
+
+
+def test_dt_bias_is_per_head_and_inverts_expm1():
+    # bias[h] = log(expm1(d_h)) with raw 0 gives d_h in head h; a bias indexed
+    # by the wrong axis would mix the heads.
+    r = np.random.default_rng(28)
+    d = np.exp(r.uniform(math.log(1e-3), math.log(1e-1), 6))
+    bias = np.log(np.expm1(d))
+    out = oracle.dt_softplus(np.zeros((3, 5, 6)), bias)
+    assert np.allclose(out, np.broadcast_to(d, (3, 5, 6)), rtol=1e-13, atol=0)
+    out32 = oracle.dt_softplus_f32(np.zeros((4, 6), np.float32), bias.astype(np.float32))
+    assert np.allclose(out32, d[None, :], rtol=1e-6, atol=0)
+
+
+def test_raw_dt_scan_reproduces_the_plain_scan():
+    x, dt, A, Bm, Cm, D = rand_inputs(29, 2, 40, 4, 8, 16, 2)
+    dt = np.maximum(dt, 1e-4)
+    bias = np.random.default_rng(30).standard_normal(4)
+    raw = np.log(np.expm1(dt)) - bias
+    y0, h0 = oracle.ssd_scan(x, dt, A, Bm, Cm, D)
+    y1, h1 = oracle.ssd_scan(x, raw, A, Bm, Cm, D, dt_bias=bias, dt_softplus_raw=True)
+    assert rel(y1, y0) < 1e-12 and rel(h1, h0) < 1e-12
+    # the decode oracle takes the binary32 step size from the same definition
+    xd, dtd, Ad, Bd, Cd, Dd, s0 = _decode_inputs(31, 6, 2, 4, 8, 16, 2)
+    rawd = (r := np.random.default_rng(32)).standard_normal(dtd.shape).astype(np.float32)
+    bd = r.standard_normal(4).astype(np.float32)
+    b1, b2 = s0.view(np.uint16).copy(), s0.view(np.uint16).copy()
+    ya = oracle.decode_f16state(xd, rawd, Ad, Bd, Cd, Dd, b1, dt_bias=bd, dt_softplus_raw=True)
+    yb = oracle.decode_f16state(xd, oracle.dt_softplus_f32(rawd, bd), Ad, Bd, Cd, Dd, b2)
+    assert np.array_equal(b1, b2) and np.array_equal(ya, yb)
