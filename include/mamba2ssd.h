@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 2
+#define MAMBA2_ABI_VERSION 3
 
 enum {
     MAMBA2_OK = 0,
@@ -81,6 +81,16 @@ typedef struct mamba2_dims {
                             uses dt_eff = (float) sp((double) dt +
                             (double) dt_bias[h]), sp(v) = v for v > 20 and
                             log1p(exp(v)) otherwise (no clamp)              */
+    int32_t packed_tokens; /* window calls: 0 for the (B, L, ...) layout; T > 0
+                            for packed variable-length windows: every
+                            per-token tensor (x, B, C, xBC, dt, z, y) holds T
+                            rows and sequence b is rows cu_seqlens[b] ..
+                            cu_seqlens[b+1]-1 of it (io.cu_seqlens required,
+                            io.seqlens NULL); dims.seqlen is then the
+                            longest length.  A sequence longer than
+                            dims.seqlen is cut at dims.seqlen tokens and rows
+                            at or past T are never read or written.  Decode
+                            and state calls ignore it.                       */
 } mamba2_dims;
 
 /* ------------------------------------------------------------------------ */
@@ -104,6 +114,12 @@ typedef struct mamba2_dims {
  *   state_out (B,H,P,N) f32 or NULL: state after token seqlens[b]-1
  *   seqlens   device int32 (B) or NULL (all L); each value is clamped to
  *             [0, L].  Rows t >= seqlens[b] of y are not written.
+ *   cu_seqlens device int32 (B+1), packed layout only (dims.packed_tokens
+ *             > 0): non-decreasing row offsets of the sequences in the
+ *             packed tensors, which then have T = dims.packed_tokens rows in
+ *             place of (B, L): x (T,H,P), B/C (T,G,N), xBC (T,conv_dim),
+ *             dt (T,H), z and y (T,H*P).  Per-sequence tensors (state_*,
+ *             conv_state_*) keep their (B, ...) shapes.  NULL otherwise.
  *   norm_group == 0: y (B,L,H*P) io receives y.
  *   norm_group  > 0: z (B,L,H*P) io and norm_w (H*P) f32 are required and
  *             y receives the gated RMSNorm output.
@@ -131,6 +147,7 @@ typedef struct mamba2_window_io {
     const float* norm_w;
     void* y;
     const float* dt_bias;
+    const int32_t* cu_seqlens;
 } mamba2_window_io;
 
 /* Workspace size for a window call with these dims (host only, no GPU call).
@@ -160,7 +177,8 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* dims, const mamba2_window_io*
  *         state_out (B,H,P,N) f32 or NULL: the binary16 state after the
  *                   sequence's last token, widened exactly;
  *         seqlens   device int32 (B) or NULL: tokens at or past a sequence's
- *                   length are not processed and their y rows not written.
+ *                   length are not processed and their y rows not written;
+ *         cu_seqlens with dims.packed_tokens as for mamba2_conv_scan_window.
  * No workspace.  Outputs must not overlap inputs or each other.
  * Errors: EINVAL, EUNSUPPORTED, EALIGN, EHIP. */
 int32_t mamba2_requant_window(const mamba2_dims* dims, const mamba2_window_io* io, void* stream);

@@ -40,13 +40,14 @@ class Dims(ctypes.Structure):
         "batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk",
         "conv_width", "norm_group", "io_dtype", "state_dtype")] + [("norm_eps", ctypes.c_float),
                                                                    ("segments", ctypes.c_int32),
-                                                                   ("dt_softplus", ctypes.c_int32)]
+                                                                   ("dt_softplus", ctypes.c_int32),
+                                                                   ("packed_tokens", ctypes.c_int32)]
 
 
 class _WindowIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "B", "C", "xBC", "conv_w", "conv_b", "conv_state_in", "conv_state_out", "dt", "A", "D",
-        "state_in", "state_out", "seqlens", "z", "norm_w", "y", "dt_bias")]
+        "state_in", "state_out", "seqlens", "z", "norm_w", "y", "dt_bias", "cu_seqlens")]
 
 
 class _DecodeIO(ctypes.Structure):
@@ -126,9 +127,21 @@ def _io_dtype(t):
 
 
 def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=256, conv_width=0, norm_group=0,
-              io_dtype=F16, state_dtype=F32, norm_eps=1e-5, segments=0, dt_softplus=0) -> Dims:
+              io_dtype=F16, state_dtype=F32, norm_eps=1e-5, segments=0, dt_softplus=0, packed_tokens=0) -> Dims:
     return Dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, conv_width, norm_group, io_dtype,
-                state_dtype, norm_eps, segments, dt_softplus)
+                state_dtype, norm_eps, segments, dt_softplus, packed_tokens)
+
+
+def _window_shape(dt, cu_seqlens, max_seqlen):
+    """(batch, seqlen, nheads, packed_tokens) of a window call: dt (B,L,H), or
+    dt (T,H) with cu_seqlens (B+1) and the longest length max_seqlen."""
+    if cu_seqlens is None:
+        Bsz, L, H = dt.shape
+        return Bsz, L, H, 0
+    if max_seqlen is None:
+        raise ValueError("packed windows need max_seqlen (an upper bound on every length)")
+    T, H = dt.shape
+    return cu_seqlens.numel() - 1, int(max_seqlen), H, T
 
 
 def window_workspace_bytes(dims: Dims) -> int:
@@ -146,11 +159,15 @@ def alloc_workspace(dims: Dims, device) -> torch.Tensor:
 def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None, conv_w=None, conv_b=None,
                      conv_state_in=None, conv_state_out=None, state_in=None, state_out=None, seqlens=None,
                      z=None, norm_w=None, chunk=256, norm_group=0, norm_eps=1e-5, ngroups=None, dstate=None,
-                     headdim=None, segments=0, dt_softplus=False, dt_bias=None, stream=None):
+                     headdim=None, segments=0, dt_softplus=False, dt_bias=None, cu_seqlens=None, max_seqlen=None,
+                     stream=None):
     """Whole-window scan.  Shapes: x (B,L,H,P), B/C (B,L,G,N) -- or xBC
     (B,L,H*P+2*G*N) with conv_w (H*P+2*G*N, 4) for the fused conv --, dt
-    (B,L,H), A/D (H) f32, y (B,L,H*P) (or (B,L,H,P)).  See include/mamba2ssd.h."""
-    Bsz, L, H = dt.shape
+    (B,L,H), A/D (H) f32, y (B,L,H*P) (or (B,L,H,P)).  Packed windows: every
+    per-token tensor has T rows in place of (B,L), with cu_seqlens (B+1)
+    int32 row offsets and max_seqlen the longest length.  See
+    include/mamba2ssd.h."""
+    Bsz, L, H, T = _window_shape(dt, cu_seqlens, max_seqlen)
     conv = xBC is not None
     if conv:
         if ngroups is None or dstate is None:
@@ -158,29 +175,32 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
         P = 64 if headdim is None else headdim
         G, N = ngroups, dstate
     else:
-        P = x.shape[3]
-        G, N = B.shape[2], B.shape[3]
+        P = x.shape[-1]
+        G, N = B.shape[-2], B.shape[-1]
     dims = make_dims(Bsz, L, H, P, N, G, chunk, 4 if conv else 0, norm_group, _io_dtype(dt), F32, norm_eps,
-                     segments, int(bool(dt_softplus)))
+                     segments, int(bool(dt_softplus)), T)
     io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), _ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in),
                    _ptr(conv_state_out), _ptr(dt), _ptr(A), _ptr(D), _ptr(state_in), _ptr(state_out),
-                   _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y), _ptr(dt_bias))
+                   _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y), _ptr(dt_bias), _ptr(cu_seqlens))
     _check("mamba2_conv_scan_window",
            load_library().mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
                                                   workspace.numel(), _stream(dt, stream)))
 
 
 def requant_window(dt, A, D, y, *, x, B, C, state_in=None, state_out=None, seqlens=None, dt_softplus=False,
-                   dt_bias=None, stream=None):
+                   dt_bias=None, cu_seqlens=None, max_seqlen=None, stream=None):
     """Whole window with the state requantized to binary16 after every token.
     Shapes: x (B,L,H,P), B/C (B,L,G,N), dt (B,L,H), A/D (H) f32, y (B,L,H*P)
-    (or (B,L,H,P)); state_in/state_out (B,H,P,N) f32.  See include/mamba2ssd.h."""
-    Bsz, L, H = dt.shape
-    P = x.shape[3]
-    G, N = B.shape[2], B.shape[3]
-    dims = make_dims(Bsz, L, H, P, N, G, 256, 0, 0, _io_dtype(dt), F16, dt_softplus=int(bool(dt_softplus)))
+    (or (B,L,H,P)); state_in/state_out (B,H,P,N) f32; packed windows as for
+    conv_scan_window.  See include/mamba2ssd.h."""
+    Bsz, L, H, T = _window_shape(dt, cu_seqlens, max_seqlen)
+    P = x.shape[-1]
+    G, N = B.shape[-2], B.shape[-1]
+    dims = make_dims(Bsz, L, H, P, N, G, 256, 0, 0, _io_dtype(dt), F16, dt_softplus=int(bool(dt_softplus)),
+                     packed_tokens=T)
     io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), None, None, None, None, None, _ptr(dt), _ptr(A), _ptr(D),
-                   _ptr(state_in), _ptr(state_out), _ptr(seqlens), None, None, _ptr(y), _ptr(dt_bias))
+                   _ptr(state_in), _ptr(state_out), _ptr(seqlens), None, None, _ptr(y), _ptr(dt_bias),
+                   _ptr(cu_seqlens))
     _check("mamba2_requant_window", load_library().mamba2_requant_window(ctypes.byref(dims), ctypes.byref(io),
                                                                          _stream(dt, stream)))
 

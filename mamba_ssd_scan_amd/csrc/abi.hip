@@ -51,6 +51,7 @@ int32_t check_common(const mamba2_dims* d) {
   if (d->io_dtype != MAMBA2_F16 && d->io_dtype != MAMBA2_F32) return MAMBA2_EINVAL;
   if (d->state_dtype != MAMBA2_F16 && d->state_dtype != MAMBA2_F32) return MAMBA2_EINVAL;
   if (d->dt_softplus != 0 && d->dt_softplus != 1) return MAMBA2_EINVAL;
+  if (d->packed_tokens < 0) return MAMBA2_EINVAL;
   if (d->dstate != 16 && d->dstate != 64 && d->dstate != 128) return MAMBA2_EUNSUPPORTED;
   // Every tensor stays well inside 2^31 elements per sequence-head slice and
   // 2^62 bytes overall.
@@ -177,6 +178,9 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
   if (d->conv_width == 0 && (!io->x || !io->B || !io->C)) return MAMBA2_EINVAL;
   if (d->conv_width == 4 && (!io->xBC || !io->conv_w)) return MAMBA2_EINVAL;
   if (d->norm_group > 0 && (!io->z || !io->norm_w)) return MAMBA2_EINVAL;
+  // packed layout: row offsets instead of lengths
+  if ((d->packed_tokens > 0) != (io->cu_seqlens != nullptr) || (io->cu_seqlens && io->seqlens))
+    return MAMBA2_EINVAL;
   // alignment
   const void* vec[] = {io->x, io->B, io->C, io->xBC, io->z, io->y, io->state_in, io->state_out, io->conv_w,
                        io->norm_w};
@@ -184,14 +188,14 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
     if (p && !aligned16(p)) return MAMBA2_EALIGN;
   if (((uintptr_t)io->dt % es) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3) ||
       ((uintptr_t)io->seqlens & 3) || ((uintptr_t)io->conv_b & 3) || ((uintptr_t)io->conv_state_in % es) ||
-      ((uintptr_t)io->conv_state_out % es) || ((uintptr_t)io->dt_bias & 3))
+      ((uintptr_t)io->conv_state_out % es) || ((uintptr_t)io->dt_bias & 3) || ((uintptr_t)io->cu_seqlens & 3))
     return MAMBA2_EALIGN;
   // workspace
   const size_t need = m2::window_workspace_bytes(*d);
   if (!ws || ws_bytes < need) return MAMBA2_EWORKSPACE;
   if ((uintptr_t)ws & 255) return MAMBA2_EALIGN;
   // aliasing: outputs against inputs and against each other
-  const size_t tok = Bsz * L;
+  const size_t tok = d->packed_tokens > 0 ? (size_t)d->packed_tokens : Bsz * L;
   Range outs[] = {rng(io->y, tok * H * P * es), rng(io->state_out, Bsz * H * P * N * 4),
                   rng(io->conv_state_out, d->conv_width ? Bsz * conv_dim * 3 * es : 0), rng(ws, need)};
   Range ins[] = {rng(io->x, d->conv_width ? 0 : tok * H * P * es),
@@ -205,7 +209,7 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
                  rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4),
                  rng(io->z, d->norm_group ? tok * H * P * es : 0),
                  rng(io->norm_w, d->norm_group ? H * P * 4 : 0),
-                 rng(io->dt_bias, d->dt_softplus ? H * 4 : 0)};
+                 rng(io->dt_bias, d->dt_softplus ? H * 4 : 0), rng(io->cu_seqlens, (Bsz + 1) * 4)};
   const size_t nout = sizeof(outs) / sizeof(outs[0]);
   for (size_t i = 0; i < nout; ++i) {
     for (const Range& r : ins)
@@ -227,18 +231,21 @@ int32_t mamba2_requant_window(const mamba2_dims* d, const mamba2_window_io* io, 
   const size_t es = esize(d->io_dtype);
   const size_t Bsz = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
   if (!io->x || !io->B || !io->C || !io->dt || !io->A || !io->D || !io->y) return MAMBA2_EINVAL;
+  if ((d->packed_tokens > 0) != (io->cu_seqlens != nullptr) || (io->cu_seqlens && io->seqlens))
+    return MAMBA2_EINVAL;
   const void* vec[] = {io->B, io->C, io->state_in, io->state_out};
   for (const void* p : vec)
     if (p && !aligned16(p)) return MAMBA2_EALIGN;
   if (((uintptr_t)io->x % es) || ((uintptr_t)io->y % es) || ((uintptr_t)io->dt % es) || ((uintptr_t)io->A & 3) ||
-      ((uintptr_t)io->D & 3) || ((uintptr_t)io->seqlens & 3) || ((uintptr_t)io->dt_bias & 3))
+      ((uintptr_t)io->D & 3) || ((uintptr_t)io->seqlens & 3) || ((uintptr_t)io->dt_bias & 3) ||
+      ((uintptr_t)io->cu_seqlens & 3))
     return MAMBA2_EALIGN;
-  const size_t tok = Bsz * L;
+  const size_t tok = d->packed_tokens > 0 ? (size_t)d->packed_tokens : Bsz * L;
   Range outs[] = {rng(io->y, tok * H * P * es), rng(io->state_out, Bsz * H * P * N * 4)};
   Range ins[] = {rng(io->x, tok * H * P * es), rng(io->B, tok * G * N * es), rng(io->C, tok * G * N * es),
                  rng(io->dt, tok * H * es),    rng(io->A, H * 4),            rng(io->D, H * 4),
                  rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4),
-                 rng(io->dt_bias, d->dt_softplus ? H * 4 : 0)};
+                 rng(io->dt_bias, d->dt_softplus ? H * 4 : 0), rng(io->cu_seqlens, (Bsz + 1) * 4)};
   for (const Range& o : outs)
     for (const Range& r : ins)
       if (overlap(o, r)) return MAMBA2_EINVAL;

@@ -62,4 +62,23 @@ __device__ __forceinline__ float dt_softplus(float raw, float bias) {
   return (float)(v > 20.0 ? v : log1p(exp(v)));
 }
 
+// First row and length of sequence b in the caller's per-token tensors.
+// Packed (cu != nullptr): rows cu[b] .. cu[b+1]-1 of T rows.  Otherwise rows
+// b*L .., length seqlens[b] (or L).  Lengths are clamped to [0, L] and packed
+// rows to [0, T), so no access leaves the tensors whatever the offsets hold.
+struct SeqRows {
+  long long base;
+  int len;
+};
+__device__ __forceinline__ SeqRows seq_rows(const int* seqlens, const int* cu, int b, int L, int T) {
+  if (cu) {
+    const int s = min(max(cu[b], 0), T);
+    const int e = min(max(cu[b + 1], s), T);
+    return SeqRows{(long long)s, min(e - s, L)};
+  }
+  const int len = seqlens ? seqlens[b] : L;
+  return SeqRows{(long long)b * L, len < 0 ? 0 : (len > L ? L : len)};
+}
+
 }  // namespace m2
+

@@ -84,8 +84,8 @@ template <typename IO, int N>
 __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     const IO* __restrict__ x, const IO* __restrict__ dt, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ state_in,
-    float* __restrict__ state_out, const int* __restrict__ seqlens, IO* __restrict__ y, int L, int H, int G,
-    int dt_sp, const float* __restrict__ dt_bias) {
+    float* __restrict__ state_out, const int* __restrict__ seqlens, const int* __restrict__ cu_seqlens,
+    IO* __restrict__ y, int L, int T, int H, int G, int dt_sp, const float* __restrict__ dt_bias) {
   constexpr int P = 64;
   constexpr int ROWS = RqShape<N>::ROWS, RPT = RqShape<N>::RPT, NTH = RqShape<N>::NTH;
   constexpr int LPR = N / 8;                 // lanes per state row
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
   const int r0 = tid / LPR;                  // first of its rows (stride NTH / LPR)
   constexpr int RSTRIDE = NTH / LPR;
   const int p0 = blk * ROWS;
-  int len = seqlens ? seqlens[b] : L;
-  len = len < 0 ? 0 : (len > L ? L : len);
+  const SeqRows span = seq_rows(seqlens, cu_seqlens, b, L, T);
+  const int len = span.len;
   const float Ah = A[h], Dh = D[h];
   const float dtb = dt_sp && dt_bias ? dt_bias[h] : 0.f;
 
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     float xv[(XC + NTH - 1) / NTH];
     float d;
   };
-  const size_t seqtok = (size_t)b * L;
+  const size_t seqtok = (size_t)span.base;   // the sequence's first row
   auto fetch = [&](Pre& r, int t0) {
 #pragma unroll
     for (int k = 0; k < (BC8 + NTH - 1) / NTH; ++k) {
@@ -285,7 +285,8 @@ static hipError_t launch_rq(const mamba2_dims& d, const mamba2_window_io& io_, h
   const unsigned grid = (unsigned)(d.batch * d.nheads * (64 / ROWS));
   requant_window_kernel<IO, N><<<grid, NTH, 0, st>>>(
       (const IO*)io_.x, (const IO*)io_.dt, (const IO*)io_.B, (const IO*)io_.C, io_.A, io_.D, io_.state_in,
-      io_.state_out, io_.seqlens, (IO*)io_.y, d.seqlen, d.nheads, d.ngroups, d.dt_softplus,
+      io_.state_out, io_.seqlens, io_.cu_seqlens, (IO*)io_.y, d.seqlen, d.packed_tokens, d.nheads, d.ngroups,
+      d.dt_softplus,
       d.dt_softplus ? io_.dt_bias : nullptr);
   return hipGetLastError();
 }

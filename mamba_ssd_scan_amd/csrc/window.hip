@@ -54,6 +54,9 @@ template <typename IO> struct WinArgs {
   int nseg;           // segments per sequence
   int dt_sp;          // dt is raw: dt_eff = softplus(dt + dt_bias[h])
   const float* dt_bias;
+  const int* cu;      // packed layout: row offsets (B+1) of the sequences, else null
+  int T;              // packed layout: rows of the caller's per-token tensors
+  int xpk;            // x, B, C are the caller's packed rows (not the conv output)
 };
 
 // control block: eight claim counters and the done counter / generation /
@@ -120,7 +123,8 @@ template <typename IO>
 __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ xBC, const float* __restrict__ w,
                                                         const float* __restrict__ bias, const IO* __restrict__ cs_in,
                                                         IO* __restrict__ cs_out, const int* __restrict__ seqlens,
-                                                        IO* __restrict__ out, int B, int L, int Cd) {
+                                                        const int* __restrict__ cu, IO* __restrict__ out, int B,
+                                                        int L, int T, int Cd) {
   const int nch = Cd / 8, ntt = (L + kConvTT - 1) / kConvTT;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)B * ntt * nch) return;
@@ -128,9 +132,11 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
   const long long rest = idx / nch;
   const int tt = (int)(rest % ntt), b = (int)(rest / ntt);
   const int c0 = cc * 8, t0 = tt * kConvTT;
-  int len = seqlens ? seqlens[b] : L;
-  len = len < 0 ? 0 : (len > L ? L : len);
-  const IO* src = xBC + (size_t)b * L * Cd + c0;
+  const SeqRows span = seq_rows(seqlens, cu, b, L, T);
+  const int len = span.len;
+  // an empty sequence reads (and discards) row 0: its own first row may be
+  // the end of a packed tensor
+  const IO* src = xBC + (size_t)(len > 0 ? span.base : 0) * Cd + c0;
   // Row t >= 0 of these channels, zero at or past the length.  The address is
   // clamped into the sequence and the zero applied by a select, so the loads
   // carry no branch and a whole batch is in flight at once.
@@ -418,8 +424,12 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   const int hb = b * a.H + h;                   // (sequence, head) index
   const int bhv = b * HV + 2 * h + half;
   const unsigned item = (unsigned)(sg * BHV + bhv);
-  int len = a.seqlens ? __builtin_amdgcn_readfirstlane(a.seqlens[b]) : a.L;
-  len = len < 0 ? 0 : (len > a.L ? a.L : len);
+  // rows of the caller's tensors: sequence b starts at row ubase; x, B and C
+  // staged by the conv kernel keep the padded row b * L
+  const SeqRows span = seq_rows(a.seqlens, a.cu, b, a.L, a.T);
+  const int len = __builtin_amdgcn_readfirstlane(span.len);
+  const int ubase = __builtin_amdgcn_readfirstlane((int)span.base);
+  const size_t xbase = a.xpk ? (size_t)ubase : (size_t)b * a.L;
   const int cb = sg * a.cps;                    // the segment's first chunk
   // chunks of the segment that hold tokens of this sequence, and the steps of each
   const int ncv = min(max((len - cb * a.Q + a.Q - 1) / a.Q, 0), min(a.cps, a.nchunks - cb));
@@ -434,14 +444,14 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   const unsigned xspan = len > 0 && live ? (unsigned)(len - 1) * xrow + PH * ES : 0u;
   const unsigned yspan = len > 0 && live ? (unsigned)(len - 1) * yrow + PH * ES : 0u;
   const unsigned gspan = len > 0 ? (unsigned)(len - 1) * grow + N * ES : 0u;
-  const size_t seq_x = (size_t)b * a.L * a.xstride + (size_t)h * kP + PH * half;
-  const size_t seq_y = ((size_t)b * a.L * a.H + h) * kP + PH * half;
-  const size_t seq_g = (size_t)b * a.L * a.gstride + (size_t)g * N;
+  const size_t seq_x = xbase * a.xstride + (size_t)h * kP + PH * half;
+  const size_t seq_y = ((size_t)ubase * a.H + h) * kP + PH * half;
+  const size_t seq_g = xbase * a.gstride + (size_t)g * N;
   const rsrc_t rx = mkr(a.x + seq_x, xspan);
   const rsrc_t rb = mkr(a.Bm + seq_g, gspan);
   const rsrc_t rc = mkr(a.Cm + seq_g, gspan);
   const rsrc_t ry = mkr(a.y + seq_y, yspan);
-  const rsrc_t rdt = mkr(a.dt + (size_t)b * a.L * a.H + h, len > 0 && live ? (unsigned)((len - 1) * a.H + 1) * ES : 0u);
+  const rsrc_t rdt = mkr(a.dt + (size_t)ubase * a.H + h, len > 0 && live ? (unsigned)((len - 1) * a.H + 1) * ES : 0u);
   float* const Sw = sm.S[wid];
   _Float16* const dtw = sm.dts[wid];
   _Float16* const xs = sm.u.t.x[wid];
@@ -956,12 +966,12 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 template <typename IO>
 __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, const float* __restrict__ normsum,
                                                          const float* __restrict__ nw, const int* __restrict__ seqlens,
-                                                         int L, int H, int group, float eps) {
+                                                         const int* __restrict__ cu, int L, int T, int H, int group,
+                                                         float eps) {
   __shared__ float gs[256];
-  const int tok = blockIdx.x, b = tok / L, t = tok - b * L;
-  int len = seqlens ? seqlens[b] : L;
-  len = len < 0 ? 0 : (len > L ? L : len);
-  if (t >= len) return;
+  const int tok = blockIdx.x, b = tok / L, t = tok - b * L;   // (sequence, token) of the padded index
+  const SeqRows span = seq_rows(seqlens, cu, b, L, T);
+  if (t >= span.len) return;
   const int C = H * kP, ngr = C / group;
   const int np = H * kNormParts, seg = (group / kP) * kNormParts;   // partials per token, per group
   for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = 0.f;
@@ -982,7 +992,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
   __syncthreads();
   for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = rsqrtf(gs[gi] / (float)group + eps);
   __syncthreads();
-  IO* row = y + (size_t)tok * C;
+  IO* row = y + (size_t)(span.base + t) * C;
   for (int c0 = threadIdx.x * 8; c0 < C; c0 += 256 * 8) {
     float v[8];
     io<IO>::load8(row + c0, v);
@@ -1073,6 +1083,9 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   a.dt_bias = d.dt_softplus ? io_.dt_bias : nullptr;
   a.dt = (const IO*)io_.dt; a.A = io_.A; a.D = io_.D;
   a.state_in = io_.state_in; a.state_out = io_.state_out; a.seqlens = io_.seqlens;
+  a.cu = io_.cu_seqlens;
+  a.T = d.packed_tokens;
+  a.xpk = io_.cu_seqlens != nullptr && d.conv_width == 0;
   a.z = (const IO*)io_.z; a.y = (IO*)io_.y;
   a.ctrl = (unsigned*)(base + wl.ctrl);
   a.flags = (unsigned long long*)(base + wl.flags);
@@ -1084,7 +1097,7 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     const long long threads = (long long)d.batch * ((d.seqlen + kConvTT - 1) / kConvTT) * (cd / 8);
     conv_silu_kernel<IO><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(
         (const IO*)io_.xBC, io_.conv_w, io_.conv_b, (const IO*)io_.conv_state_in, (IO*)io_.conv_state_out,
-        io_.seqlens, xc, d.batch, d.seqlen, cd);
+        io_.seqlens, io_.cu_seqlens, xc, d.batch, d.seqlen, d.packed_tokens, cd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.x = xc;
@@ -1105,7 +1118,8 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   }
   if (e != hipSuccess || !norm) return e;
   gated_norm_kernel<IO><<<(unsigned)(d.batch * d.seqlen), 256, 0, st>>>(
-      (IO*)io_.y, a.normsum, io_.norm_w, io_.seqlens, d.seqlen, d.nheads, d.norm_group, d.norm_eps);
+      (IO*)io_.y, a.normsum, io_.norm_w, io_.seqlens, io_.cu_seqlens, d.seqlen, d.packed_tokens, d.nheads,
+      d.norm_group, d.norm_eps);
   return hipGetLastError();
 }
 

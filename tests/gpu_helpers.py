@@ -98,3 +98,43 @@ def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=No
                         **raw_dt_args(inp))
     torch.cuda.synchronize()
     return y.cpu().numpy(), hT.cpu().numpy(), (cso.cpu().numpy() if want_conv_state else None)
+
+
+def pack_rows(a, lens):
+    """Rows 0 .. lens[b]-1 of each sequence of a padded (B, L, ...) array,
+    concatenated into a packed (T, ...) array."""
+    return np.ascontiguousarray(np.concatenate([a[b, :n] for b, n in enumerate(lens)], 0))
+
+
+def cu_of(lens):
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+def unpack_rows(a, lens, L, fill=np.nan):
+    """Inverse of pack_rows: (T, ...) -> (B, L, ...), rows past a length = fill."""
+    out = np.full((len(lens), L) + a.shape[1:], fill, dtype=np.float64)
+    for b, (s, n) in enumerate(zip(cu_of(lens)[:-1], lens)):
+        out[b, :n] = a[s:s + n]
+    return out
+
+
+def run_window_packed(inp, lens, chunk, state_in=None, spare_rows=16, fill=12345.0, segments=0):
+    """The window scan on packed rows built from padded numpy inputs.  y gets
+    spare_rows extra rows filled with `fill`; returns (y packed incl. spare
+    rows, final state)."""
+    Bsz, L, H, P = inp["x"].shape
+    G, N = inp["B"].shape[2], inp["B"].shape[3]
+    x, dt, Bm, Cm = (to_dev(pack_rows(inp[k], lens)) for k in ("x", "dt", "B", "C"))
+    T = dt.shape[0]
+    y = torch.full((T + spare_rows, H * P), fill, dtype=x.dtype, device=DEV)
+    hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=DEV)
+    cu = to_dev(cu_of(lens))
+    h0 = to_dev(np.asarray(state_in, np.float32)) if state_in is not None else None
+    dims = m2.make_dims(Bsz, L, H, P, N, G, chunk, io_dtype=m2.F16 if x.dtype == torch.float16 else m2.F32,
+                        packed_tokens=T)
+    ws = m2.alloc_workspace(dims, DEV)
+    m2.conv_scan_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=x, B=Bm, C=Cm, state_in=h0,
+                        state_out=hT, chunk=chunk, segments=segments, cu_seqlens=cu, max_seqlen=L,
+                        **raw_dt_args(inp))
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), hT.cpu().numpy()

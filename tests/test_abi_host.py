@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = m2.load_library()
-    assert m2.abi_version() == 2
+    assert m2.abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.mamba2_status_str(code)
     assert lib.mamba2_status_str(77) == b"unknown status"
@@ -79,6 +79,7 @@ def test_long_sequences_beyond_32_bit_rows_are_refused():
     (dict(nheads=100, ngroups=8), -1), (dict(batch=0), -1), (dict(seqlen=0), -1),
     (dict(norm_group=1000), -1), (dict(norm_group=32), -2), (dict(norm_group=-1), -1),
     (dict(io_dtype=7), -1), (dict(segments=-1), -1), (dict(dt_softplus=2), -1),
+    (dict(packed_tokens=-1), -1),
 ])
 def test_workspace_query_rejects(kw, code):
     lib = m2.load_library()
@@ -120,6 +121,26 @@ def test_window_validation_codes():
     # fused conv needs xBC and conv weights; the norm needs z and its weight
     assert call_window(window_io(), dims=layer_dims(conv_width=4)) == -1
     assert call_window(window_io(), dims=layer_dims(norm_group=8192)) == -1
+
+
+def test_packed_layout_validation_codes():
+    MB = 1 << 26
+    packed = layer_dims(batch=4, packed_tokens=5000)
+    cu = FAKE + 5 * MB
+    # packed rows need their offsets, and offsets need the packed layout
+    assert call_window(window_io(), dims=packed) == -1
+    assert call_window(window_io(cu_seqlens=cu)) == -1
+    # lengths and offsets are exclusive
+    assert call_window(window_io(cu_seqlens=cu, seqlens=cu + 4096), dims=packed) == -1
+    assert call_window(window_io(cu_seqlens=cu + 2), dims=packed) == -3
+    # offsets overlapping an output
+    assert call_window(window_io(cu_seqlens=FAKE + 8 * MB + 64), dims=packed) == -1
+    # the same rules for the requantized window
+    assert call_requant(window_io(), dims=packed) == -1
+    assert call_requant(window_io(cu_seqlens=cu)) == -1
+    assert call_requant(window_io(cu_seqlens=cu + 2), dims=packed) == -3
+    # the workspace is sized by batch x seqlen whatever the packed row count
+    assert m2.window_workspace_bytes(packed) == m2.window_workspace_bytes(layer_dims(batch=4))
 
 
 def call_requant(io, dims=None):

@@ -20,7 +20,8 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
 import mamba_ssd_scan_amd as m2  # noqa: E402
-from tests.gpu_helpers import DEV, run_mixer, run_requant, run_window, slice_err, to_dev  # noqa: E402
+from tests.gpu_helpers import (DEV, cu_of, pack_rows, run_mixer, run_requant, run_window,  # noqa: E402
+                               run_window_packed, slice_err, to_dev, unpack_rows)
 
 Y_TOL, S_TOL = 2e-3, 1e-3
 
@@ -153,6 +154,109 @@ def test_batched_windows_full_size_sampled():
         say(f"[window] batched seq {b} (len {n}): y {ey:.3e} state {es:.3e}")
         assert ey <= Y_TOL and es <= S_TOL
         assert np.all(y[b, n:] == np.float16(12345.0))
+
+
+# ---- packed variable-length windows (row offsets instead of padding) ------------
+@pytest.mark.parametrize("segments", [0, 2])
+def test_packed_windows_match_oracle(segments):
+    lens = [600, 411, 0, 257, 1]
+    inp = rand_window(86, len(lens), 600, 8, 128, 2)
+    h0 = np.random.default_rng(87).standard_normal((len(lens), 8, 64, 128)).astype(np.float32) * 0.3
+    say(f"[packed] lengths {lens} segments {segments}")
+    yp, hT = run_window_packed(inp, lens, 256, state_in=h0, segments=segments)
+    T = sum(lens)
+    assert np.all(yp[T:] == np.float16(12345.0))       # nothing past the packed rows
+    y = unpack_rows(yp[:T], lens, 600).reshape(len(lens), 600, 8, 64)
+    yr, hr = oracle_window(inp, lens, h0)
+    ey = max(slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)), np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2)
+             for b, n in enumerate(lens) if n > 0)
+    es = slice_err(hT, hr, 2)
+    say(f"[packed] y err {ey:.3e} state err {es:.3e}")
+    assert ey <= Y_TOL and es <= S_TOL
+    # a zero-length sequence hands its initial state through
+    assert np.array_equal(hT[2], h0[2])
+
+
+def test_packed_batched_windows_equal_padded_bit_for_bit():
+    # eight windows of the layer shape packed back to back (7 x 2048 + 1955
+    # rows): only the row addressing differs from the padded call
+    s = synth.batched_windows()
+    inp = synth.window_inputs(s, 1002)
+    lens = s.seqlens
+    say(f"[packed] batched: {sum(lens)} rows")
+    yp, hp = run_window_packed(inp, lens, s.chunk)
+    y, hT = run_window(inp, s.chunk, seqlens=lens)
+    T = sum(lens)
+    assert np.all(yp[T:] == np.float16(12345.0))
+    assert np.array_equal(yp[:T], pack_rows(y.reshape(8, 2048, -1), lens))
+    assert np.array_equal(hp, hT)
+    b, n = 7, lens[7]
+    sub = {k: (v[b:b + 1] if v.ndim > 1 else v) for k, v in inp.items()}
+    yr, hr = oracle_window(sub, [n])
+    ey = slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)), np.transpose(yr[:, :n], (0, 2, 1, 3)), 2)
+    say(f"[packed] batched: identical to padded; seq 7 y {ey:.3e} state {slice_err(hp[7:], hr, 2):.3e}")
+    assert ey <= Y_TOL and slice_err(hp[7:], hr, 2) <= S_TOL
+
+
+def test_packed_requant_window_bit_exact_state():
+    lens = [300, 0, 177, 33]
+    inp = rand_window(88, len(lens), 300, 8, 64, 2)
+    x, dt, Bm, Cm = (to_dev(pack_rows(inp[k], lens)) for k in ("x", "dt", "B", "C"))
+    T = sum(lens)
+    y = torch.full((T + 8, 8 * 64), 12345.0, dtype=torch.float16, device=DEV)
+    hT = torch.empty((len(lens), 8, 64, 64), dtype=torch.float32, device=DEV)
+    say(f"[packed] requant lengths {lens}")
+    m2.requant_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, x=x, B=Bm, C=Cm, state_out=hT,
+                      cu_seqlens=to_dev(cu_of(lens)), max_seqlen=300)
+    torch.cuda.synchronize()
+    yp, hT = y.cpu().numpy(), hT.cpu().numpy()
+    assert np.all(yp[T:] == np.float16(12345.0))
+    yr, bits = oracle_requant(inp, lens)
+    got = np.ascontiguousarray(hT.astype(np.float16)).view(np.uint16)
+    yu = unpack_rows(yp[:T], lens, 300).reshape(len(lens), 300, 8, 64)
+    ey = max(slice_err(np.transpose(yu[b:b + 1, :n], (0, 2, 1, 3)), np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2)
+             for b, n in enumerate(lens) if n > 0)
+    say(f"[packed] requant: state identical {np.mean(got == bits):.6f} y err {ey:.3e}")
+    assert np.array_equal(got, bits) and ey <= Y_TOL
+
+
+def test_packed_mixer_core_with_conv_state_and_norm():
+    H, P, G, N, L = 16, 64, 2, 128, 300
+    lens = [300, 157, 0, 64]
+    s = synth.WindowShape(len(lens), L, H, P, N, G, 256, np.float16, "wide")
+    inp = synth.mixer_inputs(s, 89, raw_dt=True)
+    Cn = H * P + 2 * G * N
+    csi = np.random.default_rng(90).standard_normal((len(lens), Cn, 3)).astype(np.float16)
+    T = sum(lens)
+    xBC, dt, z = (to_dev(pack_rows(inp[k], lens)) for k in ("xBC", "dt", "z"))
+    y = torch.full((T + 8, H * P), 12345.0, dtype=torch.float16, device=DEV)
+    hT = torch.empty((len(lens), H, P, N), dtype=torch.float32, device=DEV)
+    cso = torch.empty((len(lens), Cn, 3), dtype=torch.float16, device=DEV)
+    dims = m2.make_dims(len(lens), L, H, P, N, G, 256, conv_width=4, norm_group=512, packed_tokens=T)
+    ws = m2.alloc_workspace(dims, DEV)
+    say(f"[packed] mixer lengths {lens}")
+    m2.conv_scan_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xBC, conv_w=to_dev(inp["conv_w"]),
+                        conv_b=to_dev(inp["conv_b"]), conv_state_in=to_dev(csi), conv_state_out=cso, state_out=hT,
+                        z=z, norm_w=to_dev(inp["norm_w"]), chunk=256, norm_group=512, ngroups=G, dstate=N,
+                        headdim=P, dt_softplus=True, dt_bias=to_dev(inp["dt_bias"]), cu_seqlens=to_dev(cu_of(lens)),
+                        max_seqlen=L)
+    torch.cuda.synchronize()
+    yp = y.cpu().numpy()
+    assert np.all(yp[T:] == np.float16(12345.0))
+    out_r, h_r, cs_r = oracle.mixer_core(inp["xBC"], inp["conv_w"], inp["conv_b"], inp["dt"], inp["A"], inp["D"],
+                                         inp["z"], inp["norm_w"], H, P, G, N, 512, conv_state=csi, seqlens=lens,
+                                         dt_bias=inp["dt_bias"], dt_softplus_raw=True)
+    yu = unpack_rows(yp[:T], lens, L)
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        got = yu[b, :n].reshape(n, -1, 512).transpose(1, 0, 2)
+        ref = out_r[b, :n].reshape(n, -1, 512).transpose(1, 0, 2)
+        e = slice_err(got, ref, 1)
+        say(f"[packed] mixer out seq {b}: {e:.3e}")
+        assert e <= Y_TOL
+    assert slice_err(hT.cpu().numpy(), h_r, 2) <= S_TOL
+    assert np.array_equal(cso.cpu().numpy().astype(np.float64), cs_r)
 
 
 def test_sequence_alone_equals_sequence_in_batch():
