@@ -95,6 +95,16 @@ def decode_bytes(B, H, P, N, G):
     return B * H * P * N * 2 * 2 + B * H * P * 2 * 2 + B * G * N * 2 * 2 + B * H * 2 + 2 * H * 4
 
 
+def mixer_decode_bytes(B, H, P, N, G):
+    """Algorithmic bytes of one fused mixer step (f16 I/O, binary16 resident
+    state): the state read and written, this token's raw xBC, dt and z read,
+    the conv history read and written, the output written, the conv weights,
+    conv bias, norm weight, A and D read."""
+    Cd = H * P + 2 * G * N
+    return (B * H * P * N * 2 * 2 + B * Cd * 2 + B * Cd * 3 * 2 * 2 + B * H * 2 + B * H * P * 2 * 2
+            + Cd * 4 * 4 + Cd * 4 + H * P * 4 + 2 * H * 4)
+
+
 def window_mfma_flops(L, H, P, N, Q=256, segments=8, step=32, half=32):
     """f16 MFMA flops the window kernel issues for one sequence with a final
     state (16x16x32 instructions, 16384 flops each), for the chunks split into
@@ -310,6 +320,35 @@ def main():
     dec_rot_us = ev0.elapsed_time(ev1) * 1e3 / T
     dbytes = decode_bytes(DB, DH, DP, DN, DG)
 
+    # ---- fused mixer step: conv history + SiLU + step + gated RMSNorm ---------
+    DCd = DH * DP + 2 * DG * DN
+    mgen = torch.Generator(device=dev).manual_seed(1006)
+    md_in = [{"xBC": torch.randn(DB, DCd, device=dev, generator=mgen).half(),
+              "z": torch.randn(DB, DH * DP, device=dev, generator=mgen).half()} for _ in range(nin)]
+    md_w = (torch.randn(DCd, 4, device=dev, generator=mgen) * 0.5).contiguous()
+    md_b = torch.zeros(DCd, device=dev)
+    md_cs = torch.randn(DB, DCd, 3, device=dev, generator=mgen).half()
+    md_nw = torch.ones(DH * DP, device=dev)
+    md_dims = m2.mixer_decode_dims(DB, DH, DP, DN, DG, DH * DP, m2.F16, m2.F16)
+    md_ws = m2.alloc_mixer_decode_workspace(md_dims, dev)
+    md_y = torch.empty(DB, DH * DP, dtype=torch.float16, device=dev)
+
+    def mdstep(k, st_):
+        si, mi = steps_in[k % nin], md_in[k % nin]
+        m2.mixer_decode_step(mi["xBC"], md_w, md_cs, si["dt"], A, Dd, st_, md_y, md_ws, conv_b=md_b, z=mi["z"],
+                             norm_w=md_nw, ngroups=DG, dstate=DN, norm_group=DH * DP, stream=stream)
+
+    for k in range(10):
+        mdstep(k, states[0])
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(T):
+        mdstep(k, states[k % nstate])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    md_us = ev0.elapsed_time(ev1) * 1e3 / T
+    mdbytes = mixer_decode_bytes(DB, DH, DP, DN, DG)
+
     # ---- batched windows: 8 sequences, seven of 2048 tokens and one of 1955 ----
     # timing only (parity of this workload is covered by the GPU tests); inputs
     # are drawn on the device with the layer window's distributions
@@ -417,6 +456,11 @@ def main():
                    "algorithmic_bytes": dbytes, "achieved_GBs": round(dbytes / (dec_rot_us * 1e-6) / 1e9, 1),
                    "frac": round(dbytes / (dec_rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "batch": DB, "steps": T, "state": "f16"},
+        "mixer_decode": {"workload": "one token of the full mixer: conv history + SiLU, step, gated RMSNorm "
+                                     "over 8192 channels", "us_per_step_rotated_states": round(md_us, 2),
+                         "algorithmic_bytes": mdbytes, "achieved_GBs": round(mdbytes / (md_us * 1e-6) / 1e9, 1),
+                         "frac": round(mdbytes / (md_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "batch": DB, "steps": T, "state": "f16"},
     }
     print(json.dumps(out), flush=True)
 

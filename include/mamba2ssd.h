@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 3
+#define MAMBA2_ABI_VERSION 4
 
 enum {
     MAMBA2_OK = 0,
@@ -207,6 +207,57 @@ typedef struct mamba2_decode_io {
 } mamba2_decode_io;
 
 int32_t mamba2_decode_step(const mamba2_dims* dims, const mamba2_decode_io* io, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Full one-token mixer step for B sequences: the generation path of one
+ * layer's mixer core (page "Mamb2_8B_FP4_Recall_SQ3.25": the convolution
+ * caches of section "Storage and runtime memory", the per-token requantized
+ * recurrent row of section "Representation", the gated RMSNorm of section
+ * "Compatible reference environment").  For every sequence:
+ *   u   = silu(conv_b + sum_k conv_w[:, k] * [history, xBC][k])  (width 4,
+ *         tap 3 on this token), rounded to the I/O type, split x | B | C;
+ *   history <- (history[1], history[2], xBC)                     (in place);
+ *   the decode step of mamba2_decode_step on (x, dt, B, C);
+ *   y = the step's output, or with norm_group > 0 the gated RMSNorm
+ *       g / sqrt(mean_group(g^2) + eps) * norm_w,  g = y * silu(z).
+ * T consecutive calls from the window's conv_state_out and state_out give
+ * that window's outputs for its next T tokens (the conv state layout is the
+ * one mamba2_conv_scan_window reads and writes).
+ *   dims: conv_width 4; headdim 64; dstate 16, 64 or 128; state_dtype the
+ *         resident type; norm_group 0 or a multiple of 64 dividing H*P (at
+ *         most H*P); norm_eps; dt_softplus.  seqlen, chunk, segments and
+ *         packed_tokens are ignored.
+ *   io:   xBC (B, conv_dim) io raw in_proj output for this token;
+ *         conv_w (conv_dim, 4) f32; conv_b (conv_dim) f32 or NULL;
+ *         conv_state (B, conv_dim, 3) io, the 3 raw tokens before this one
+ *         (oldest first), read and rolled IN PLACE;
+ *         dt (B, H) io, dt_bias (H) f32 or NULL (with dt_softplus); A, D (H);
+ *         state (B,H,P,N) resident type, read and updated IN PLACE;
+ *         z (B, H*P) io and norm_w (H*P) f32 when norm_group > 0;
+ *         y (B, H*P) io.
+ *   ws, ws_bytes: workspace of at least mamba2_mixer_decode_workspace_bytes()
+ *         bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE; every
+ *         call leaves it ready for the next one on the same stream (calls that
+ *         may overlap must not share it).
+ * Errors: EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP. */
+typedef struct mamba2_mixer_decode_io {
+    const void* xBC;
+    const float* conv_w;
+    const float* conv_b;
+    void* conv_state;
+    const void* dt;
+    const float* dt_bias;
+    const float* A;
+    const float* D;
+    void* state;
+    const void* z;
+    const float* norm_w;
+    void* y;
+} mamba2_mixer_decode_io;
+
+int32_t mamba2_mixer_decode_workspace_bytes(const mamba2_dims* dims, size_t* bytes);
+int32_t mamba2_mixer_decode_step(const mamba2_dims* dims, const mamba2_mixer_decode_io* io, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* State load/store between f32 (B,H,P,N) and the resident state_dtype
  * (f16: round to nearest even, subnormals kept; f32: copy).  src and dst must

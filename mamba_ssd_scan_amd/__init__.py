@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "F16", "F32", "Dims", "Mamba2Error", "library_path", "load_library",
-    "window_workspace_bytes", "alloc_workspace", "conv_scan_window", "decode_step",
+    "window_workspace_bytes", "alloc_workspace", "conv_scan_window", "decode_step", "requant_window",
+    "mixer_decode_workspace_bytes", "alloc_mixer_decode_workspace", "mixer_decode_step",
     "state_load", "state_store", "abi_version",
 ]
 
@@ -50,6 +51,11 @@ class _WindowIO(ctypes.Structure):
         "state_in", "state_out", "seqlens", "z", "norm_w", "y", "dt_bias", "cu_seqlens")]
 
 
+class _MixerDecodeIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "xBC", "conv_w", "conv_b", "conv_state", "dt", "dt_bias", "A", "D", "state", "z", "norm_w", "y")]
+
+
 class _DecodeIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("x", "dt", "B", "C", "A", "D", "state", "y", "dt_bias")]
 
@@ -81,6 +87,10 @@ def load_library():
         lib.mamba2_conv_scan_window.argtypes = [dp, ctypes.POINTER(_WindowIO), vp, ctypes.c_size_t, vp]
         lib.mamba2_requant_window.restype = ctypes.c_int32
         lib.mamba2_requant_window.argtypes = [dp, ctypes.POINTER(_WindowIO), vp]
+        lib.mamba2_mixer_decode_workspace_bytes.restype = ctypes.c_int32
+        lib.mamba2_mixer_decode_workspace_bytes.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
+        lib.mamba2_mixer_decode_step.restype = ctypes.c_int32
+        lib.mamba2_mixer_decode_step.argtypes = [dp, ctypes.POINTER(_MixerDecodeIO), vp, ctypes.c_size_t, vp]
         lib.mamba2_decode_step.restype = ctypes.c_int32
         lib.mamba2_decode_step.argtypes = [dp, ctypes.POINTER(_DecodeIO), vp]
         lib.mamba2_state_load.restype = ctypes.c_int32
@@ -215,6 +225,43 @@ def decode_step(x, dt, B, C, A, D, state, y, dt_softplus=False, dt_bias=None, st
     io = _DecodeIO(_ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(state), _ptr(y), _ptr(dt_bias))
     _check("mamba2_decode_step", load_library().mamba2_decode_step(ctypes.byref(dims), ctypes.byref(io),
                                                                    _stream(x, stream)))
+
+
+def mixer_decode_dims(batch, nheads, headdim, dstate, ngroups, norm_group=0, io_dtype=F16, state_dtype=F16,
+                      norm_eps=1e-5, dt_softplus=False) -> Dims:
+    return make_dims(batch, 1, nheads, headdim, dstate, ngroups, 256, 4, norm_group, io_dtype, state_dtype, norm_eps,
+                     dt_softplus=int(bool(dt_softplus)))
+
+
+def mixer_decode_workspace_bytes(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mamba2_mixer_decode_workspace_bytes",
+           load_library().mamba2_mixer_decode_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_mixer_decode_workspace(dims: Dims, device) -> torch.Tensor:
+    """A zero-filled workspace for fused decode steps with these dims (reusable
+    across calls on one stream)."""
+    return torch.zeros(max(mixer_decode_workspace_bytes(dims), 1), dtype=torch.uint8, device=device)
+
+
+def mixer_decode_step(xBC, conv_w, conv_state, dt, A, D, state, y, workspace, *, conv_b=None, z=None, norm_w=None,
+                      ngroups, dstate, headdim=64, norm_group=0, norm_eps=1e-5, dt_softplus=False, dt_bias=None,
+                      stream=None):
+    """One token of the full mixer for B sequences: xBC (B, H*P+2*G*N) raw,
+    conv_w (conv_dim, 4) f32, conv_state (B, conv_dim, 3) rolled in place,
+    dt (B, H), A/D (H) f32, state (B,H,P,N) f16 or f32 updated in place,
+    y (B, H*P); z (B, H*P) and norm_w (H*P) with norm_group > 0.  See
+    include/mamba2ssd.h."""
+    Bsz, H = dt.shape
+    sd = F16 if state.dtype == torch.float16 else F32
+    dims = mixer_decode_dims(Bsz, H, headdim, dstate, ngroups, norm_group, _io_dtype(xBC), sd, norm_eps, dt_softplus)
+    io = _MixerDecodeIO(_ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                        _ptr(D), _ptr(state), _ptr(z), _ptr(norm_w), _ptr(y))
+    _check("mamba2_mixer_decode_step",
+           load_library().mamba2_mixer_decode_step(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
+                                                   workspace.numel(), _stream(xBC, stream)))
 
 
 def _state_dims(t, resident_dtype):

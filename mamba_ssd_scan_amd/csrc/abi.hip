@@ -16,6 +16,8 @@ hipError_t launch_state_convert(int to_resident, int state_f16, const void* src,
 size_t window_workspace_bytes(const mamba2_dims& d);
 hipError_t launch_window(const mamba2_dims& d, const mamba2_window_io& io, void* ws, hipStream_t st);
 hipError_t launch_requant_window(const mamba2_dims& d, const mamba2_window_io& io, hipStream_t st);
+size_t mixer_decode_workspace_bytes(const mamba2_dims& d);
+hipError_t launch_mixer_decode(const mamba2_dims& d, const mamba2_mixer_decode_io& io, void* ws, hipStream_t st);
 }  // namespace m2
 
 namespace {
@@ -251,6 +253,68 @@ int32_t mamba2_requant_window(const mamba2_dims* d, const mamba2_window_io* io, 
       if (overlap(o, r)) return MAMBA2_EINVAL;
   if (overlap(outs[0], outs[1])) return MAMBA2_EINVAL;
   return hip_status(m2::launch_requant_window(*d, *io, (hipStream_t)stream));
+}
+
+// Validation for the fused one-token mixer step.
+static int32_t check_mixer_decode(const mamba2_dims* d) {
+  int32_t s = check_common(d);
+  if (s != MAMBA2_OK) return s;
+  if (d->conv_width != 4) return MAMBA2_EUNSUPPORTED;
+  if (d->headdim != 64) return MAMBA2_EUNSUPPORTED;
+  const int64_t hp = (int64_t)d->nheads * d->headdim;
+  if (d->norm_group < 0 || d->norm_group > hp) return MAMBA2_EINVAL;
+  if (d->norm_group > 0 && (hp % d->norm_group != 0 || !(d->norm_eps >= 0.f))) return MAMBA2_EINVAL;
+  if (d->norm_group > 0 && d->norm_group % d->headdim != 0) return MAMBA2_EUNSUPPORTED;
+  // the norm finish keeps one scale per norm group of a token in LDS (256 slots)
+  if (d->norm_group > 0 && hp / d->norm_group > 256) return MAMBA2_EUNSUPPORTED;
+  if ((int64_t)d->batch * d->nheads > ((int64_t)1 << 31) - 1) return MAMBA2_EUNSUPPORTED;
+  return MAMBA2_OK;
+}
+
+int32_t mamba2_mixer_decode_workspace_bytes(const mamba2_dims* d, size_t* bytes) {
+  if (!bytes) return MAMBA2_EINVAL;
+  int32_t s = check_mixer_decode(d);
+  if (s != MAMBA2_OK) return s;
+  *bytes = m2::mixer_decode_workspace_bytes(*d);
+  return MAMBA2_OK;
+}
+
+int32_t mamba2_mixer_decode_step(const mamba2_dims* d, const mamba2_mixer_decode_io* io, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  int32_t s = check_mixer_decode(d);
+  if (s != MAMBA2_OK) return s;
+  if (!io) return MAMBA2_EINVAL;
+  const size_t es = esize(d->io_dtype);
+  const size_t Bsz = d->batch, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+  const size_t cd = H * P + 2 * G * N;
+  if (!io->xBC || !io->conv_w || !io->conv_state || !io->dt || !io->A || !io->D || !io->state || !io->y)
+    return MAMBA2_EINVAL;
+  if (d->norm_group > 0 && (!io->z || !io->norm_w)) return MAMBA2_EINVAL;
+  if (!aligned16(io->conv_w) || !aligned16(io->state)) return MAMBA2_EALIGN;
+  if (((uintptr_t)io->xBC % es) || ((uintptr_t)io->conv_state % es) || ((uintptr_t)io->dt % es) ||
+      ((uintptr_t)io->z % es) || ((uintptr_t)io->y % es) || ((uintptr_t)io->conv_b & 3) ||
+      ((uintptr_t)io->dt_bias & 3) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3) ||
+      ((uintptr_t)io->norm_w & 3))
+    return MAMBA2_EALIGN;
+  const size_t need = m2::mixer_decode_workspace_bytes(*d);
+  if (!ws || ws_bytes < need) return MAMBA2_EWORKSPACE;
+  if ((uintptr_t)ws & 255) return MAMBA2_EALIGN;
+  // outputs (y; state and conv_state in place; workspace) against inputs and
+  // against each other
+  Range outs[] = {rng(io->y, Bsz * H * P * es), rng(io->state, Bsz * H * P * N * esize(d->state_dtype)),
+                  rng(io->conv_state, Bsz * cd * 3 * es), rng(ws, need)};
+  Range ins[] = {rng(io->xBC, Bsz * cd * es), rng(io->conv_w, cd * 16), rng(io->conv_b, io->conv_b ? cd * 4 : 0),
+                 rng(io->dt, Bsz * H * es), rng(io->dt_bias, d->dt_softplus ? H * 4 : 0), rng(io->A, H * 4),
+                 rng(io->D, H * 4), rng(io->z, d->norm_group ? Bsz * H * P * es : 0),
+                 rng(io->norm_w, d->norm_group ? H * P * 4 : 0)};
+  const size_t nout = sizeof(outs) / sizeof(outs[0]);
+  for (size_t i = 0; i < nout; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return MAMBA2_EINVAL;
+    for (size_t j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return MAMBA2_EINVAL;
+  }
+  return hip_status(m2::launch_mixer_decode(*d, *io, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

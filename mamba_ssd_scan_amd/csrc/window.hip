@@ -1005,6 +1005,22 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
   }
 }
 
+// The norm finish over ntok independent tokens of H*P channels, with the
+// partial sums laid out as the scan epilogue writes them ((token, head,
+// kNormParts)); the one-token mixer step uses it with one token per sequence.
+hipError_t launch_gated_norm_tokens(int io_f16, void* y, const float* normsum, const float* nw, int ntok, int H,
+                                    int group, float eps, hipStream_t st) {
+  if (ntok <= 0) return hipSuccess;
+  if (io_f16)
+    gated_norm_kernel<_Float16><<<(unsigned)ntok, 256, 0, st>>>((_Float16*)y, normsum, nw, nullptr, nullptr, 1, ntok,
+                                                                  H, group, eps);
+  else
+    gated_norm_kernel<float><<<(unsigned)ntok, 256, 0, st>>>((float*)y, normsum, nw, nullptr, nullptr, 1, ntok, H,
+                                                               group, eps);
+  return hipGetLastError();
+}
+int norm_parts_per_head() { return kNormParts; }
+
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t ctrl, flags, agg, normsum, convx, total;

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = m2.load_library()
-    assert m2.abi_version() == 3
+    assert m2.abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.mamba2_status_str(code)
     assert lib.mamba2_status_str(77) == b"unknown status"
@@ -183,6 +183,58 @@ def test_decode_and_state_validation_codes():
     assert lib.mamba2_state_load(ctypes.byref(d), None, ctypes.c_void_p(FAKE), None) == -1
     assert lib.mamba2_state_store(ctypes.byref(d), ctypes.c_void_p(FAKE + 2), ctypes.c_void_p(FAKE + MB * 40),
                                   None) == -3
+
+
+def test_mixer_decode_validation_codes():
+    lib = m2.load_library()
+    MB = 1 << 26
+    H, P, N, G = 128, 64, 128, 8
+
+    def dims(**kw):
+        base = dict(batch=64, nheads=H, headdim=P, dstate=N, ngroups=G, norm_group=8192)
+        base.update(kw)
+        return m2.mixer_decode_dims(**base)
+
+    def io(**over):
+        base = dict(xBC=FAKE, conv_w=FAKE + MB, conv_state=FAKE + 2 * MB, dt=FAKE + 3 * MB, A=FAKE + 4 * MB,
+                    D=FAKE + 4 * MB + 4096, state=FAKE + 8 * MB, z=FAKE + 5 * MB, norm_w=FAKE + 6 * MB,
+                    y=FAKE + 7 * MB)
+        base.update(over)
+        return m2._MixerDecodeIO(**base)
+
+    def call(i, d=None, ws=FAKE + (1 << 30), ws_bytes=None):
+        d = d or dims()
+        if ws_bytes is None:
+            ws_bytes = m2.mixer_decode_workspace_bytes(d)
+        return lib.mamba2_mixer_decode_step(ctypes.byref(d), ctypes.byref(i), ctypes.c_void_p(ws), ws_bytes, None)
+
+    n = ctypes.c_size_t(0)
+    for kw, code in ((dict(norm_group=100), -1), (dict(norm_group=16384), -1), (dict(norm_group=32), -2),
+                     (dict(norm_group=-1), -1), (dict(headdim=32), -2), (dict(dstate=96), -2)):
+        assert lib.mamba2_mixer_decode_workspace_bytes(ctypes.byref(dims(**kw)), ctypes.byref(n)) == code, kw
+    d3 = m2.make_dims(64, 1, H, P, N, G, 256, conv_width=0)
+    assert lib.mamba2_mixer_decode_workspace_bytes(ctypes.byref(d3), ctypes.byref(n)) == -2   # needs the conv
+    # one arrival counter per (sequence, group); with the norm, the sums of g^2
+    # over each half of every head
+    up = lambda v: (v + 255) // 256 * 256
+    assert m2.mixer_decode_workspace_bytes(dims()) == up(up(64 * G * 4) + 64 * H * 2 * 4)
+    assert m2.mixer_decode_workspace_bytes(dims(norm_group=0)) == up(64 * G * 4)
+    # more than 256 norm groups per token
+    assert lib.mamba2_mixer_decode_workspace_bytes(ctypes.byref(m2.mixer_decode_dims(4, 512, 64, 128, 8, 64)),
+                                                   ctypes.byref(n)) == -2
+    assert call(io(xBC=None)) == -1
+    assert call(io(z=None)) == -1
+    assert call(io(conv_w=FAKE + MB + 4)) == -3
+    assert call(io(state=FAKE + 8 * MB + 8)) == -3
+    assert call(io(y=FAKE + 7 * MB + 1)) == -3
+    assert call(io(), ws=None) == -4
+    assert call(io(), ws_bytes=1024) == -4
+    assert call(io(), ws=FAKE + (1 << 30) + 64) == -3
+    # y inside the state; the conv history overlapping the raw input; the
+    # workspace overlapping the conv history
+    assert call(io(y=FAKE + 8 * MB + 4096)) == -1
+    assert call(io(conv_state=FAKE + 1024)) == -1
+    assert call(io(), ws=FAKE + 2 * MB) == -1
 
 
 def test_binding_raises_without_gpu_tensors():

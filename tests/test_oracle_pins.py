@@ -379,3 +379,33 @@ def test_raw_dt_scan_reproduces_the_plain_scan():
     ya = oracle.decode_f16state(xd, rawd, Ad, Bd, Cd, Dd, b1, dt_bias=bd, dt_softplus_raw=True)
     yb = oracle.decode_f16state(xd, oracle.dt_softplus_f32(rawd, bd), Ad, Bd, Cd, Dd, b2)
     assert np.array_equal(b1, b2) and np.array_equal(ya, yb)
+
+
+# --- P17: one token at a time equals the whole window (the decode identity) ----
+def test_mixer_token_by_token_equals_window():
+    # Carrying the conv history and the state through single-token calls must
+    # give the whole-window outputs: the conv sees the same taps, the scan the
+    # same recurrence and the norm is per token.
+    H, P, G, N, L = 4, 4, 2, 8, 12
+    Cn = H * P + 2 * G * N
+    r = np.random.default_rng(33)
+    xin = r.standard_normal((2, L, Cn))
+    w = r.standard_normal((Cn, 4)) * 0.5
+    bias = r.standard_normal(Cn) * 0.1
+    dt = r.uniform(0.01, 0.2, (2, L, H))
+    A = -np.exp(r.uniform(0, 2, H))
+    D = r.standard_normal(H)
+    z = r.standard_normal((2, L, H * P))
+    nw = r.uniform(0.5, 1.5, H * P)
+    cs0 = r.standard_normal((2, Cn, 3))
+    h0 = r.standard_normal((2, H, P, N)) * 0.3
+    out, hT, cs = oracle.mixer_core(xin, w, bias, dt, A, D, z, nw, H, P, G, N, 8, conv_state=cs0, h0=h0)
+    c, h = cs0, h0
+    for t in range(L):
+        o, h, c = oracle.mixer_core(xin[:, t:t + 1], w, bias, dt[:, t:t + 1], A, D, z[:, t:t + 1], nw, H, P, G, N,
+                                    8, conv_state=c, h0=h)
+        assert rel(o[:, 0], out[:, t]) < 1e-12
+    assert rel(h, hT) < 1e-12
+    assert np.array_equal(c, cs)
+    # the rolled history is the last three raw inputs
+    assert np.array_equal(cs, np.transpose(xin[:, L - 3:], (0, 2, 1)))
