@@ -54,6 +54,8 @@ def _load():
         lib.oracle_gated_rmsnorm.argtypes = [i64, i, i, dp, dp, dp, ctypes.c_double, dp]
         lib.oracle_decode_f16state.argtypes = [i, i, i, i, i, i, fp, fp, fp, fp, fp, fp, u16p, dp, i, i, i]
         lib.oracle_dt_softplus.argtypes = [i64, i, dp, dp, dp]
+        lib.oracle_ssd_scan_grad.argtypes = [i, i, i, i, i, i] + [dp] * 7 + [ip] + [dp] * 10 + [i]
+        lib.oracle_dt_softplus_grad.argtypes = [i64, i, dp, dp, dp, dp]
         lib.oracle_dt_softplus_f32.argtypes = [i64, i, fp, fp, fp]
         lib.oracle_threads_used.restype = ctypes.c_int
         lib.oracle_threads_used.argtypes = [i]
@@ -154,6 +156,41 @@ def ssd_scan(x, dt, A, Bm, Cm, D, h0=None, seqlens=None, nthreads: int = 0, dt_b
                             _ptr(sl, ctypes.c_int32), _ptr(y, ctypes.c_double), _ptr(hT, ctypes.c_double),
                             _ptr(work, ctypes.c_double), int(nthreads))
     return y, hT
+
+
+def ssd_scan_grad(x, dt, A, Bm, Cm, D, dy, h0=None, dhT=None, seqlens=None, nthreads: int = 0, dt_bias=None,
+                  dt_softplus_raw: bool = False):
+    """Gradients of ssd_scan (fp64 reverse mode) for the loss whose gradients
+    with respect to y and the final state are dy (B, L, H, P) and dhT (B, H,
+    P, N) or None.  Returns a dict with dx, ddt, dB, dC, dA, dD, dh0 (and
+    ddt_bias with a raw dt, when ddt is with respect to the raw dt)."""
+    raw = dt
+    if dt_softplus_raw:
+        dt = dt_softplus(dt, dt_bias)
+    x, dt, A, Bm, Cm, D, dy = (_f64(a) for a in (x, dt, A, Bm, Cm, D, dy))
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    assert dt.shape == (B, L, H) and Bm.shape == (B, L, G, N) and Cm.shape == Bm.shape and dy.shape == x.shape
+    h0 = _f64(h0) if h0 is not None else None
+    dhT = _f64(dhT) if dhT is not None else None
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32)) if seqlens is not None else None
+    nt = threads_used(nthreads)
+    out = dict(dx=np.empty((B, L, H, P)), ddt=np.empty((B, L, H)), dB=np.empty((B, L, G, N)),
+               dC=np.empty((B, L, G, N)), dA=np.empty(H), dD=np.empty(H), dh0=np.empty((B, H, P, N)))
+    work = np.empty(2 * B * L * H * N + 2 * B * H + nt * (L + 1) * P * N)
+    _load().oracle_ssd_scan_grad(B, L, H, P, N, G, *(_ptr(a, ctypes.c_double) for a in (x, dt, A, Bm, Cm, D, h0)),
+                                 _ptr(sl, ctypes.c_int32), _ptr(dy, ctypes.c_double), _ptr(dhT, ctypes.c_double),
+                                 *(_ptr(out[k], ctypes.c_double) for k in ("dx", "ddt", "dB", "dC", "dA", "dD", "dh0")),
+                                 _ptr(work, ctypes.c_double), int(nt))
+    if dt_softplus_raw:
+        raw = _f64(raw)
+        bias = _f64(dt_bias) if dt_bias is not None else None
+        g = np.empty_like(raw)
+        _load().oracle_dt_softplus_grad(raw.size, H, _ptr(raw, ctypes.c_double), _ptr(bias, ctypes.c_double),
+                                        _ptr(out["ddt"], ctypes.c_double), _ptr(g, ctypes.c_double))
+        out["ddt"] = g
+        out["ddt_bias"] = g.reshape(-1, H).sum(0)
+    return out
 
 
 def gated_rmsnorm(y, z, w, group, eps=1e-5):

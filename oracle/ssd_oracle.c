@@ -44,6 +44,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -218,6 +219,148 @@ void oracle_ssd_scan(int B, int L, int H, int P, int N, int G,
         }
         if (hT)
             for (int i = 0; i < P * N; ++i) hT[(size_t)bh * P * N + i] = S[i];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gradients of the selective scan above (reverse mode, fp64).  The loss is
+ * any scalar whose gradients with respect to the outputs are dy (B, L, H, P)
+ * for y and dhT (B, H, P, N) or NULL (zero) for the final state.  Written from
+ * the recurrence itself: with h_t = a_t h_{t-1} + dt_t x_t (outer) B_t,
+ * a_t = exp(dt_t A) and y_t = h_t . C_t + D x_t, the gradient g with respect
+ * to h_t collects C_t (outer) dy_t and a_{t+1} times the gradient of
+ * h_{t+1}; every input's gradient is read off the same step:
+ *   dx_t[p]  = D dy_t[p] + dt_t sum_n g[p,n] B_t[n]
+ *   dB_t[n] += dt_t sum_p g[p,n] x_t[p]         (summed over the group's heads)
+ *   dC_t[n] += sum_p dy_t[p] h_t[p,n]           (summed over the group's heads)
+ *   ddt_t    = sum_{p,n} g[p,n] (A a_t h_{t-1}[p,n] + x_t[p] B_t[n])
+ *   dA      += dt_t a_t sum_{p,n} g[p,n] h_{t-1}[p,n]
+ *   dD      += sum_p dy_t[p] x_t[p]
+ *   dh0      = the gradient with respect to h_0 after the first token.
+ * Every state of the sequence is kept (work: (L+1) P N doubles per (b, h)
+ * being processed; at most nthreads at a time), so h_{t-1} is at hand.
+ * Rows t >= len_b of dx, ddt, dB, dC are zero.  dA, dD sum over the batch. */
+void oracle_ssd_scan_grad(int B, int L, int H, int P, int N, int G,
+                          const double* x, const double* dt, const double* A,
+                          const double* Bm, const double* Cm, const double* D,
+                          const double* h0, const int32_t* seqlens,
+                          const double* dy, const double* dhT,
+                          double* dx, double* ddt, double* dB, double* dC,
+                          double* dA, double* dD, double* dh0, double* work, int nthreads)
+{
+    const int hpg = H / G;
+    const size_t PN = (size_t)P * N;
+    memset(dx, 0, sizeof(double) * (size_t)B * L * H * P);
+    memset(ddt, 0, sizeof(double) * (size_t)B * L * H);
+    memset(dB, 0, sizeof(double) * (size_t)B * L * G * N);
+    memset(dC, 0, sizeof(double) * (size_t)B * L * G * N);
+    memset(dA, 0, sizeof(double) * (size_t)H);
+    memset(dD, 0, sizeof(double) * (size_t)H);
+    /* one (b, h) at a time per thread; the group sums and the batch sums are
+     * taken afterwards in a fixed order from per-(b, h) buffers */
+    double* dBh = work;                                  /* (B, L, H, N) */
+    double* dCh = dBh + (size_t)B * L * H * N;           /* (B, L, H, N) */
+    double* dAh = dCh + (size_t)B * L * H * N;           /* (B, H) */
+    double* dDh = dAh + (size_t)B * H;                   /* (B, H) */
+    double* hist = dDh + (size_t)B * H;                  /* nthreads x (L+1) P N */
+    memset(work, 0, sizeof(double) * ((size_t)2 * B * L * H * N + 2 * (size_t)B * H));
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; ++bh) {
+#ifdef _OPENMP
+        const int tid = omp_get_thread_num();
+#else
+        const int tid = 0;
+#endif
+        const int b = bh / H, h = bh % H, g = h / hpg;
+        int len = seqlens ? seqlens[b] : L;
+        len = len < 0 ? 0 : (len > L ? L : len);
+        double* hs = hist + (size_t)tid * (L + 1) * PN;  /* hs[t] = state after t tokens */
+        for (size_t i = 0; i < PN; ++i) hs[i] = h0 ? h0[(size_t)bh * PN + i] : 0.0;
+        #define IX(t) (((size_t)b * L + (t)) * H + h)
+        #define GX(t) (((size_t)b * L + (t)) * G + g)
+        for (int t = 0; t < len; ++t) {
+            const double d = dt[IX(t)], a = exp(d * A[h]);
+            const double* xt = x + IX(t) * P;
+            const double* Bt = Bm + GX(t) * N;
+            double* prev = hs + (size_t)t * PN;
+            double* cur = prev + PN;
+            for (int p = 0; p < P; ++p)
+                for (int n = 0; n < N; ++n)
+                    cur[p * N + n] = a * prev[p * N + n] + d * xt[p] * Bt[n];
+        }
+        /* reverse sweep: gs = gradient with respect to the state after t+1 tokens */
+        double* gs = (double*)malloc(sizeof(double) * PN);
+        for (size_t i = 0; i < PN; ++i) gs[i] = dhT ? dhT[(size_t)bh * PN + i] : 0.0;
+        double dAacc = 0.0, dDacc = 0.0;
+        for (int t = len - 1; t >= 0; --t) {
+            const double d = dt[IX(t)], a = exp(d * A[h]);
+            const double* xt = x + IX(t) * P;
+            const double* Bt = Bm + GX(t) * N;
+            const double* Ct = Cm + GX(t) * N;
+            const double* dyt = dy + IX(t) * P;
+            const double* ht = hs + (size_t)(t + 1) * PN;
+            const double* hp = hs + (size_t)t * PN;
+            double* dBt = dBh + IX(t) * N;
+            double* dCt = dCh + IX(t) * N;
+            for (int p = 0; p < P; ++p)
+                for (int n = 0; n < N; ++n) gs[p * N + n] += Ct[n] * dyt[p];
+            double ddt_t = 0.0, dA_t = 0.0;
+            for (int p = 0; p < P; ++p) {
+                double v = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    const double gv = gs[p * N + n];
+                    v += gv * Bt[n];
+                    dBt[n] += d * gv * xt[p];
+                    dCt[n] += dyt[p] * ht[p * N + n];
+                    ddt_t += gv * (A[h] * a * hp[p * N + n] + xt[p] * Bt[n]);
+                    dA_t += gv * hp[p * N + n];
+                }
+                dx[IX(t) * P + p] = D[h] * dyt[p] + d * v;
+                dDacc += dyt[p] * xt[p];
+            }
+            ddt[IX(t)] = ddt_t;
+            dAacc += d * a * dA_t;
+            for (size_t i = 0; i < PN; ++i) gs[i] *= a;
+        }
+        for (size_t i = 0; i < PN; ++i) dh0[(size_t)bh * PN + i] = gs[i];
+        dAh[bh] = dAacc;
+        dDh[bh] = dDacc;
+        free(gs);
+        #undef IX
+        #undef GX
+    }
+    /* group sums (heads in index order) and batch sums (sequences in order) */
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < L; ++t)
+            for (int h = 0; h < H; ++h) {
+                const int g = h / hpg;
+                for (int n = 0; n < N; ++n) {
+                    dB[(((size_t)b * L + t) * G + g) * N + n] += dBh[(((size_t)b * L + t) * H + h) * N + n];
+                    dC[(((size_t)b * L + t) * G + g) * N + n] += dCh[(((size_t)b * L + t) * H + h) * N + n];
+                }
+            }
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            dA[h] += dAh[(size_t)b * H + h];
+            dD[h] += dDh[(size_t)b * H + h];
+        }
+}
+
+/* Chain rule through the dt preprocessing: the gradient with respect to the
+ * raw dt is the gradient with respect to dt_eff times sp'(raw + bias), with
+ * sp'(v) = 1 above the cut-off and the logistic function 1 / (1 + e^-v)
+ * below it (the derivative of log1p(exp(v))). */
+void oracle_dt_softplus_grad(int64_t n, int H, const double* raw, const double* bias, const double* g_eff,
+                             double* g_raw)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const double v = raw[i] + (bias ? bias[i % H] : 0.0);
+        g_raw[i] = g_eff[i] * (v > 20.0 ? 1.0 : 1.0 / (1.0 + exp(-v)));
     }
 }
 

@@ -409,3 +409,83 @@ def test_mixer_token_by_token_equals_window():
     assert np.array_equal(c, cs)
     # the rolled history is the last three raw inputs
     assert np.array_equal(cs, np.transpose(xin[:, L - 3:], (0, 2, 1)))
+
+
+# --- P18: the backward pass against central differences of the forward -------
+def _grad_case(seed, raw=False):
+    B, L, H, P, N, G = 2, 7, 4, 3, 5, 2
+    r = np.random.default_rng(seed)
+    inp = dict(x=r.standard_normal((B, L, H, P)), dt=r.uniform(0.05, 0.4, (B, L, H)),
+               A=-r.uniform(0.3, 2.0, H), B=r.standard_normal((B, L, G, N)), C=r.standard_normal((B, L, G, N)),
+               D=r.standard_normal(H), h0=r.standard_normal((B, H, P, N)) * 0.5)
+    if raw:
+        inp["dt"] = r.standard_normal((B, L, H))
+        inp["bias"] = r.standard_normal(H)
+    dy = r.standard_normal((B, L, H, P))
+    dhT = r.standard_normal((B, H, P, N))
+    return inp, dy, dhT, [7, 5]
+
+
+def _loss(inp, dy, dhT, lens, raw=False):
+    y, hT = oracle.ssd_scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], h0=inp["h0"], seqlens=lens,
+                            dt_bias=inp.get("bias"), dt_softplus_raw=raw)
+    return float(np.sum(np.nan_to_num(y, nan=0.0) * dy) + np.sum(hT * dhT))
+
+
+def _check_fd(inp, dy, dhT, lens, grads, raw=False):
+    names = dict(x="dx", dt="ddt", A="dA", B="dB", C="dC", D="dD", h0="dh0")
+    if raw:
+        names["bias"] = "ddt_bias"
+    eps = 1e-6
+    for k, gk in names.items():
+        base = inp[k]
+        fd = np.empty_like(base)
+        for idx in np.ndindex(base.shape):
+            old = base[idx]
+            base[idx] = old + eps
+            lp = _loss(inp, dy, dhT, lens, raw)
+            base[idx] = old - eps
+            lm = _loss(inp, dy, dhT, lens, raw)
+            base[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(fd - grads[gk])) / max(np.max(np.abs(fd)), 1e-30)
+        assert err < 1e-7, (k, err)
+
+
+def test_scan_gradients_match_central_differences():
+    # every coordinate of every input, a ragged batch, an initial state and a
+    # final-state gradient: a dropped term, a wrong sign or index, a missing
+    # group sum or decay factor each move some coordinate far beyond 1e-7
+    inp, dy, dhT, lens = _grad_case(34)
+    g = oracle.ssd_scan_grad(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], dy, h0=inp["h0"],
+                             dhT=dhT, seqlens=lens)
+    _check_fd(inp, dy, dhT, lens, g)
+    # rows past a sequence's length get exactly zero
+    for k in ("dx", "ddt", "dB", "dC"):
+        assert np.all(g[k][1, 5:] == 0)
+
+
+def test_scan_gradients_through_raw_dt_softplus():
+    inp, dy, dhT, lens = _grad_case(35, raw=True)
+    g = oracle.ssd_scan_grad(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], dy, h0=inp["h0"],
+                             dhT=dhT, seqlens=lens, dt_bias=inp["bias"], dt_softplus_raw=True)
+    _check_fd(inp, dy, dhT, lens, g, raw=True)
+
+
+def test_scan_gradient_closed_forms():
+    # dt = 0 everywhere: y = C.h0 + D x and hT = h0, so dx = D dy, dD = sum dy x,
+    # dC = sum_p dy h0, dh0 = dhT + sum_t C_t (outer) dy_t, dB = 0
+    inp, dy, dhT, _ = _grad_case(36)
+    z = np.zeros_like(inp["dt"])
+    g = oracle.ssd_scan_grad(inp["x"], z, inp["A"], inp["B"], inp["C"], inp["D"], dy, h0=inp["h0"], dhT=dhT)
+    H, G = 4, 2
+    gm = np.arange(H) // (H // G)
+    assert np.allclose(g["dx"], inp["D"][None, None, :, None] * dy, rtol=1e-13, atol=1e-13)
+    assert np.allclose(g["dD"], np.einsum("blhp,blhp->h", dy, inp["x"]), rtol=1e-12)
+    assert np.all(g["dB"] == 0)
+    dC = np.zeros_like(g["dC"])
+    for h in range(H):
+        dC[:, :, gm[h]] += np.einsum("blp,bpn->bln", dy[:, :, h], inp["h0"][:, h])
+    assert np.allclose(g["dC"], dC, rtol=1e-12, atol=1e-12)
+    dh0 = dhT + np.einsum("blhn,blhp->bhpn", inp["C"][:, :, gm], dy)
+    assert np.allclose(g["dh0"], dh0, rtol=1e-12, atol=1e-12)
