@@ -236,6 +236,35 @@ def main():
     torch.cuda.synchronize()
     rq_us = ev0.elapsed_time(ev1) * 1e3 / 10
     rq_updates = B * L * H * P * N
+
+    # ---- backward pass of the layer window scan ------------------------------------
+    gdims = m2.make_dims(B, L, H, P, N, G, Q)
+    gws = m2.alloc_scan_grad_workspace(gdims, dev)
+    ggen = torch.Generator(device=dev).manual_seed(1007)
+    gdy = torch.randn(B, L, H, P, device=dev, generator=ggen).half()
+    gdhT = torch.randn(B, H, P, N, device=dev, generator=ggen) * 0.3
+    f32 = dict(dtype=torch.float32, device=dev)
+    gout = dict(dx=torch.empty(B, L, H, P, **f32), ddt=torch.empty(B, L, H, **f32),
+                dB=torch.empty(B, L, G, N, **f32), dC=torch.empty(B, L, G, N, **f32), dA=torch.empty(H, **f32),
+                dD=torch.empty(H, **f32), dstate_in=torch.empty(B, H, P, N, **f32))
+
+    def gstep(k):
+        t = sets[k % len(sets)]
+        m2.scan_grad(t["dt"], t["A"], t["D"], gdy, gws, x=t["x"], B=t["B"], C=t["C"], dstate_out=gdhT,
+                     stream=stream, **gout)
+
+    for k in range(2):
+        gstep(k)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(5):
+        gstep(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    grad_us = ev0.elapsed_time(ev1) * 1e3 / 5
+    # two sweeps, four lane-operations per state element and token in each
+    grad_ops = 8 * B * L * H * P * N
+    del gws, gdy, gdhT, gout
     del sets
     torch.cuda.empty_cache()
 
@@ -452,6 +481,12 @@ def main():
                                         "achieved": round(4 * rq_updates / (rq_us * 1e-6) / 1e12, 2),
                                         "peak": VALU_PEAK_TOPS, "unit": "T lane-ops/s",
                                         "frac": round(4 * rq_updates / (rq_us * 1e-6) / 1e12 / VALU_PEAK_TOPS, 4)}},
+        "scan_grad": {"workload": "backward of the layer window scan: dx, ddt, dB, dC, dA, dD, dstate_in",
+                      "us": round(grad_us, 2), "tokens_per_s": round(B * L / (grad_us * 1e-6), 1),
+                      "roofline": {"bound": "alu", "ops_per_update": 8,
+                                   "achieved": round(grad_ops / (grad_us * 1e-6) / 1e12, 2),
+                                   "peak": VALU_PEAK_TOPS, "unit": "T lane-ops/s",
+                                   "frac": round(grad_ops / (grad_us * 1e-6) / 1e12 / VALU_PEAK_TOPS, 4)}},
         "decode": {"us_per_step": round(dec_us, 2), "us_per_step_rotated_states": round(dec_rot_us, 2),
                    "algorithmic_bytes": dbytes, "achieved_GBs": round(dbytes / (dec_rot_us * 1e-6) / 1e9, 1),
                    "frac": round(dbytes / (dec_rot_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 4
+#define MAMBA2_ABI_VERSION 5
 
 enum {
     MAMBA2_OK = 0,
@@ -182,6 +182,58 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* dims, const mamba2_window_io*
  * No workspace.  Outputs must not overlap inputs or each other.
  * Errors: EINVAL, EUNSUPPORTED, EALIGN, EHIP. */
 int32_t mamba2_requant_window(const mamba2_dims* dims, const mamba2_window_io* io, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Gradients of the window scan (the backward pass), for training through the
+ * frozen mixer core (page "Mamb2_8B_FP4_Recall_SQ3.25" trains an adapter
+ * through the frozen stack).  For the scan of mamba2_conv_scan_window with
+ * conv_width 0 and norm_group 0 (y and the final state as outputs), and a
+ * loss whose gradients with respect to them are dy and dstate_out, returns
+ * the gradients with respect to every input.
+ *   dims: conv_width 0, norm_group 0, packed_tokens 0 (EUNSUPPORTED
+ *         otherwise); headdim 64; dstate 16, 64 or 128; dt_softplus as in
+ *         the forward call; chunk and segments are ignored.
+ *   inputs (as for mamba2_conv_scan_window, element alignment suffices for
+ *         the io tensors): x, dt, dt_bias (with dt_softplus), A, B, C, D,
+ *         state_in (B,H,P,N) f32 or NULL, seqlens or NULL;
+ *         dy (B,L,H,P) io: the gradient with respect to y;
+ *         dstate_out (B,H,P,N) f32 or NULL (zero).
+ *   outputs, all f32 and written in full (rows at or past a sequence's
+ *         length are zero):
+ *         dx (B,L,H,P); ddt (B,L,H), with respect to the dt given (the raw
+ *         one with dt_softplus); dB, dC (B,L,G,N), summed over each group's
+ *         heads; dA, dD (H), summed over the batch; dstate_in (B,H,P,N) or
+ *         NULL (not computed; 16-byte aligned); ddt_bias (H) with
+ *         dt_softplus (summed over batch and tokens), else ignored.
+ *   ws, ws_bytes: workspace of at least mamba2_scan_grad_workspace_bytes()
+ *         bytes, 256-byte aligned; its contents on entry do not matter.
+ * Outputs must not overlap inputs or each other.
+ * Errors: EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP. */
+typedef struct mamba2_scan_grad_io {
+    const void* x;
+    const void* dt;
+    const float* dt_bias;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* state_in;
+    const int32_t* seqlens;
+    const void* dy;
+    const float* dstate_out;
+    float* dx;
+    float* ddt;
+    float* dB;
+    float* dC;
+    float* dA;
+    float* dD;
+    float* dstate_in;
+    float* ddt_bias;
+} mamba2_scan_grad_io;
+
+int32_t mamba2_scan_grad_workspace_bytes(const mamba2_dims* dims, size_t* bytes);
+int32_t mamba2_scan_grad(const mamba2_dims* dims, const mamba2_scan_grad_io* io, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* One-token recurrent step for B sequences (dims.seqlen is ignored).

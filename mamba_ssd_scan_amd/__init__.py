@@ -17,6 +17,7 @@ __all__ = [
     "F16", "F32", "Dims", "Mamba2Error", "library_path", "load_library",
     "window_workspace_bytes", "alloc_workspace", "conv_scan_window", "decode_step", "requant_window",
     "mixer_decode_workspace_bytes", "alloc_mixer_decode_workspace", "mixer_decode_step",
+    "scan_grad_workspace_bytes", "alloc_scan_grad_workspace", "scan_grad",
     "state_load", "state_store", "abi_version",
 ]
 
@@ -56,6 +57,12 @@ class _MixerDecodeIO(ctypes.Structure):
         "xBC", "conv_w", "conv_b", "conv_state", "dt", "dt_bias", "A", "D", "state", "z", "norm_w", "y")]
 
 
+class _ScanGradIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "dt", "dt_bias", "A", "B", "C", "D", "state_in", "seqlens", "dy", "dstate_out",
+        "dx", "ddt", "dB", "dC", "dA", "dD", "dstate_in", "ddt_bias")]
+
+
 class _DecodeIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("x", "dt", "B", "C", "A", "D", "state", "y", "dt_bias")]
 
@@ -91,6 +98,10 @@ def load_library():
         lib.mamba2_mixer_decode_workspace_bytes.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
         lib.mamba2_mixer_decode_step.restype = ctypes.c_int32
         lib.mamba2_mixer_decode_step.argtypes = [dp, ctypes.POINTER(_MixerDecodeIO), vp, ctypes.c_size_t, vp]
+        lib.mamba2_scan_grad_workspace_bytes.restype = ctypes.c_int32
+        lib.mamba2_scan_grad_workspace_bytes.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
+        lib.mamba2_scan_grad.restype = ctypes.c_int32
+        lib.mamba2_scan_grad.argtypes = [dp, ctypes.POINTER(_ScanGradIO), vp, ctypes.c_size_t, vp]
         lib.mamba2_decode_step.restype = ctypes.c_int32
         lib.mamba2_decode_step.argtypes = [dp, ctypes.POINTER(_DecodeIO), vp]
         lib.mamba2_state_load.restype = ctypes.c_int32
@@ -262,6 +273,35 @@ def mixer_decode_step(xBC, conv_w, conv_state, dt, A, D, state, y, workspace, *,
     _check("mamba2_mixer_decode_step",
            load_library().mamba2_mixer_decode_step(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
                                                    workspace.numel(), _stream(xBC, stream)))
+
+
+def scan_grad_workspace_bytes(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mamba2_scan_grad_workspace_bytes",
+           load_library().mamba2_scan_grad_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_scan_grad_workspace(dims: Dims, device) -> torch.Tensor:
+    """Workspace for scan_grad calls with these dims (no clearing needed)."""
+    return torch.empty(scan_grad_workspace_bytes(dims), dtype=torch.uint8, device=device)
+
+
+def scan_grad(dt, A, D, dy, workspace, *, x, B, C, dx, ddt, dB, dC, dA, dD, state_in=None, seqlens=None,
+              dstate_out=None, dstate_in=None, dt_softplus=False, dt_bias=None, ddt_bias=None, stream=None):
+    """Gradients of the window scan.  Inputs as conv_scan_window (x (B,L,H,P),
+    B/C (B,L,G,N), dt (B,L,H)), dy (B,L,H,P) and dstate_out (B,H,P,N) f32 or
+    None; f32 outputs dx, ddt, dB, dC, dA, dD, dstate_in (or None) and, with
+    dt_softplus, ddt_bias.  See include/mamba2ssd.h."""
+    Bsz, L, H = dt.shape
+    P = x.shape[-1]
+    G, N = B.shape[-2], B.shape[-1]
+    dims = make_dims(Bsz, L, H, P, N, G, 256, 0, 0, _io_dtype(dt), F32, dt_softplus=int(bool(dt_softplus)))
+    io = _ScanGradIO(_ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state_in),
+                     _ptr(seqlens), _ptr(dy), _ptr(dstate_out), _ptr(dx), _ptr(ddt), _ptr(dB), _ptr(dC), _ptr(dA),
+                     _ptr(dD), _ptr(dstate_in), _ptr(ddt_bias))
+    _check("mamba2_scan_grad", load_library().mamba2_scan_grad(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
+                                                               workspace.numel(), _stream(dt, stream)))
 
 
 def _state_dims(t, resident_dtype):

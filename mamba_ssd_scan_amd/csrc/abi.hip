@@ -17,6 +17,8 @@ size_t window_workspace_bytes(const mamba2_dims& d);
 hipError_t launch_window(const mamba2_dims& d, const mamba2_window_io& io, void* ws, hipStream_t st);
 hipError_t launch_requant_window(const mamba2_dims& d, const mamba2_window_io& io, hipStream_t st);
 size_t mixer_decode_workspace_bytes(const mamba2_dims& d);
+size_t scan_grad_workspace_bytes(const mamba2_dims& d);
+hipError_t launch_scan_grad(const mamba2_dims& d, const mamba2_scan_grad_io& io, void* ws, hipStream_t st);
 hipError_t launch_mixer_decode(const mamba2_dims& d, const mamba2_mixer_decode_io& io, void* ws, hipStream_t st);
 }  // namespace m2
 
@@ -315,6 +317,65 @@ int32_t mamba2_mixer_decode_step(const mamba2_dims* d, const mamba2_mixer_decode
       if (overlap(outs[i], outs[j])) return MAMBA2_EINVAL;
   }
   return hip_status(m2::launch_mixer_decode(*d, *io, ws, (hipStream_t)stream));
+}
+
+// Validation for the scan's backward pass.
+static int32_t check_scan_grad(const mamba2_dims* d) {
+  int32_t s = check_common(d);
+  if (s != MAMBA2_OK) return s;
+  if (d->seqlen < 1) return MAMBA2_EINVAL;
+  if (d->conv_width != 0 || d->norm_group != 0 || d->packed_tokens != 0) return MAMBA2_EUNSUPPORTED;
+  if (d->headdim != 64) return MAMBA2_EUNSUPPORTED;
+  if ((int64_t)d->batch * d->seqlen * d->nheads * d->dstate > ((int64_t)1 << 40)) return MAMBA2_EUNSUPPORTED;
+  return MAMBA2_OK;
+}
+
+int32_t mamba2_scan_grad_workspace_bytes(const mamba2_dims* d, size_t* bytes) {
+  if (!bytes) return MAMBA2_EINVAL;
+  int32_t s = check_scan_grad(d);
+  if (s != MAMBA2_OK) return s;
+  *bytes = m2::scan_grad_workspace_bytes(*d);
+  return MAMBA2_OK;
+}
+
+int32_t mamba2_scan_grad(const mamba2_dims* d, const mamba2_scan_grad_io* io, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int32_t s = check_scan_grad(d);
+  if (s != MAMBA2_OK) return s;
+  if (!io) return MAMBA2_EINVAL;
+  const size_t es = esize(d->io_dtype);
+  const size_t Bsz = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+  if (!io->x || !io->dt || !io->A || !io->B || !io->C || !io->D || !io->dy || !io->dx || !io->ddt || !io->dB ||
+      !io->dC || !io->dA || !io->dD)
+    return MAMBA2_EINVAL;
+  if (d->dt_softplus && !io->ddt_bias) return MAMBA2_EINVAL;
+  if (((uintptr_t)io->x % es) || ((uintptr_t)io->dt % es) || ((uintptr_t)io->B % es) || ((uintptr_t)io->C % es) ||
+      ((uintptr_t)io->dy % es) || ((uintptr_t)io->dt_bias & 3) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3) ||
+      ((uintptr_t)io->state_in & 3) || ((uintptr_t)io->seqlens & 3) || ((uintptr_t)io->dstate_out & 3) ||
+      ((uintptr_t)io->dx & 3) || ((uintptr_t)io->ddt & 3) || ((uintptr_t)io->dB & 3) || ((uintptr_t)io->dC & 3) ||
+      ((uintptr_t)io->dA & 3) || ((uintptr_t)io->dD & 3) || ((uintptr_t)io->ddt_bias & 3) ||
+      (io->dstate_in && !aligned16(io->dstate_in)))
+    return MAMBA2_EALIGN;
+  const size_t need = m2::scan_grad_workspace_bytes(*d);
+  if (!ws || ws_bytes < need) return MAMBA2_EWORKSPACE;
+  if ((uintptr_t)ws & 255) return MAMBA2_EALIGN;
+  const size_t tok = Bsz * L;
+  Range outs[] = {rng(io->dx, tok * H * P * 4), rng(io->ddt, tok * H * 4), rng(io->dB, tok * G * N * 4),
+                  rng(io->dC, tok * G * N * 4), rng(io->dA, H * 4), rng(io->dD, H * 4),
+                  rng(io->dstate_in, Bsz * H * P * N * 4), rng(io->ddt_bias, d->dt_softplus ? H * 4 : 0),
+                  rng(ws, need)};
+  Range ins[] = {rng(io->x, tok * H * P * es), rng(io->dt, tok * H * es), rng(io->dt_bias, d->dt_softplus ? H * 4 : 0),
+                 rng(io->A, H * 4), rng(io->B, tok * G * N * es), rng(io->C, tok * G * N * es), rng(io->D, H * 4),
+                 rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4), rng(io->dy, tok * H * P * es),
+                 rng(io->dstate_out, Bsz * H * P * N * 4)};
+  const size_t nout = sizeof(outs) / sizeof(outs[0]);
+  for (size_t i = 0; i < nout; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return MAMBA2_EINVAL;
+    for (size_t j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return MAMBA2_EINVAL;
+  }
+  return hip_status(m2::launch_scan_grad(*d, *io, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

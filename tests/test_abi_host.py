@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = m2.load_library()
-    assert m2.abi_version() == 4
+    assert m2.abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.mamba2_status_str(code)
     assert lib.mamba2_status_str(77) == b"unknown status"
@@ -235,6 +235,49 @@ def test_mixer_decode_validation_codes():
     assert call(io(y=FAKE + 8 * MB + 4096)) == -1
     assert call(io(conv_state=FAKE + 1024)) == -1
     assert call(io(), ws=FAKE + 2 * MB) == -1
+
+
+def test_scan_grad_validation_codes():
+    lib = m2.load_library()
+    MB = 1 << 26
+    n = ctypes.c_size_t(0)
+    for kw, code in ((dict(conv_width=4), -2), (dict(norm_group=8192), -2), (dict(packed_tokens=100), -2),
+                     (dict(headdim=32), -2), (dict(dstate=96), -2), (dict(seqlen=0), -1)):
+        assert lib.mamba2_scan_grad_workspace_bytes(ctypes.byref(layer_dims(**kw)), ctypes.byref(n)) == code, kw
+    # per-head dB and dC, then e per (token, head) and four per-(sequence, head) scalars
+    up = lambda v: (v + 255) // 256 * 256
+    L, H, N = 2048, 128, 128
+    w = up(L * H * N * 4)
+    w = up(w + L * H * N * 4)
+    w = up(w + L * H * 4)
+    for _ in range(4):
+        w = up(w + H * 4)
+    assert m2.scan_grad_workspace_bytes(layer_dims()) == w
+
+    def io(**over):
+        base = dict(x=FAKE, dt=FAKE + MB, A=FAKE + 2 * MB, B=FAKE + 3 * MB, C=FAKE + 4 * MB, D=FAKE + 2 * MB + 4096,
+                    dy=FAKE + 5 * MB, dx=FAKE + 8 * MB, ddt=FAKE + 10 * MB, dB=FAKE + 11 * MB, dC=FAKE + 12 * MB,
+                    dA=FAKE + 13 * MB, dD=FAKE + 13 * MB + 4096)
+        base.update(over)
+        return m2._ScanGradIO(**base)
+
+    def call(i, d=None, ws=FAKE + (1 << 32), ws_bytes=None):
+        d = d or layer_dims()
+        if ws_bytes is None:
+            ws_bytes = m2.scan_grad_workspace_bytes(d)
+        return lib.mamba2_scan_grad(ctypes.byref(d), ctypes.byref(i), ctypes.c_void_p(ws), ws_bytes, None)
+
+    assert call(io(dy=None)) == -1
+    assert call(io(dC=None)) == -1
+    assert call(io(), d=layer_dims(dt_softplus=1)) == -1          # needs ddt_bias
+    assert call(io(dx=FAKE + 8 * MB + 2)) == -3
+    assert call(io(dstate_in=FAKE + 14 * MB + 4)) == -3
+    assert call(io(), ws=None) == -4
+    assert call(io(), ws_bytes=1024) == -4
+    assert call(io(), ws=FAKE + (1 << 32) + 128) == -3
+    assert call(io(dx=FAKE + 1024)) == -1                            # dx over x
+    assert call(io(dB=FAKE + 10 * MB + 4096)) == -1                  # dB over ddt
+    assert call(io(), ws=FAKE + 8 * MB) == -1                        # workspace over dx
 
 
 def test_binding_raises_without_gpu_tensors():
