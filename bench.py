@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=5, help="rotated input/output buffer sets")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the layer window and print its fields (for kernel traces of that workload)")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe)
@@ -217,6 +219,12 @@ def main():
         torch.cuda.synchronize()
         lat.append(ev0.elapsed_time(ev1) * 1e3)
     lat_us = float(np.median(lat))
+    if args.headline_only:
+        print(json.dumps({"metric": "SSD window-scan tokens/s at 8B layer shape L=2048", "value": round(tok_s, 1),
+                          "unit": "tokens/s", "ms_per_step": round(ms, 6), "steps": args.steps,
+                          "warmup": args.warmup, "window_us": round(ms * 1e3, 2),
+                          "achieved_GBs": round(achieved, 1)}), flush=True)
+        return
 
     # ---- the same window with the state requantized to binary16 every token ----
     # (the pages' scoring semantics; VALU-bound: per state element and token a
