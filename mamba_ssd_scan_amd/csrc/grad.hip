@@ -30,7 +30,6 @@
 
 namespace m2 {
 
-constexpr int kGTB = 16;       // tokens staged per block
 constexpr int kGP = 64;        // head dim
 
 template <typename IO> struct GradArgs {
@@ -58,8 +57,9 @@ template <typename IO> struct GradArgs {
   // workspace
   float* dBh;              // (B,L,H,N) per-head dB
   float* dCh;              // (B,L,H,N) per-head dC
-  float* e;                // (B,L,H)
-  float* eT;               // (B,H)
+  float* e;                // (B,L,H) dy_t . (h_t . C_t)
+  float* q;                // (B,L,H) x_t . (gh_t . B_t)
+  float* eT;               // (B,H) <dhT, h_len>
   float* dAp;              // (B,H) per-sequence dA
   float* dDp;              // (B,H) per-sequence dD
   float* dbp;              // (B,H) per-sequence dt-bias gradient
@@ -67,33 +67,51 @@ template <typename IO> struct GradArgs {
 
 template <typename IO> __device__ __forceinline__ float ldf(const IO* p) { return (float)*p; }
 
-// Staging of one block of up to kGTB tokens into LDS (zeros past nt).
-template <typename IO, int N> struct GradStage {
-  float x[kGTB][kGP];
-  float dy[kGTB][kGP];
-  float b[kGTB][N];
-  float c[kGTB][N];
-  float dt[kGTB];
+// Thread layout of a sweep: a thread owns 8 consecutive n (LPR lanes per row)
+// of KR rows p = r0 + k * RPP.  N = 128 takes 512 threads with two rows each;
+// the smaller N one row per thread.
+template <int N> struct GradShape {
+  static constexpr int LPR = N / 8;
+  static constexpr int NTH = N == 128 ? 512 : 64 * LPR;
+  static constexpr int RPP = NTH / LPR;
+  static constexpr int KR = kGP / RPP;
+  static constexpr int NW = NTH / 64;
+  static constexpr int TB = N == 128 ? 8 : 16;   // tokens staged per block
+  static_assert(KR * RPP == kGP, "rows");
+};
+
+template <int N> struct GradSmem {
+  static constexpr int TB = GradShape<N>::TB, NW = GradShape<N>::NW;
+  float x[TB][kGP];
+  float dy[TB][kGP];
+  float b[TB][N];
+  float c[TB][N];
+  float dt[TB];
+  float col[TB][NW][N];     // per-wave partial sums over p (dC or dB)
+  float sc[TB][NW];         // per-wave partial scalars (e or q)
+  float dx[TB][kGP];
+  float red[2][16];
 };
 
 template <typename IO, int N>
-__device__ __forceinline__ void grad_stage(GradStage<IO, N>& st, const GradArgs<IO>& a, int b, int h, int g, int t0,
+__device__ __forceinline__ void grad_stage(GradSmem<N>& st, const GradArgs<IO>& a, int b, int h, int g, int t0,
                                            int nt, int tid) {
-  for (int id = tid; id < kGTB * kGP; id += 256) {
+  constexpr int TB = GradShape<N>::TB, NTH = GradShape<N>::NTH;
+  for (int id = tid; id < TB * kGP; id += NTH) {
     const int j = id / kGP, p = id % kGP;
     const bool ok = j < nt;
     const size_t row = ((size_t)b * a.L + t0 + j) * a.H + h;
     st.x[j][p] = ok ? ldf(a.x + row * kGP + p) : 0.f;
     st.dy[j][p] = ok ? ldf(a.dy + row * kGP + p) : 0.f;
   }
-  for (int id = tid; id < kGTB * N; id += 256) {
+  for (int id = tid; id < TB * N; id += NTH) {
     const int j = id / N, n = id % N;
     const bool ok = j < nt;
     const size_t row = ((size_t)b * a.L + t0 + j) * a.G + g;
     st.b[j][n] = ok ? ldf(a.Bm + row * N + n) : 0.f;
     st.c[j][n] = ok ? ldf(a.Cm + row * N + n) : 0.f;
   }
-  if (tid < kGTB) {
+  if (tid < TB) {
     float d = 0.f;
     if (tid < nt) {
       d = ldf(a.dt + ((size_t)b * a.L + t0 + tid) * a.H + h);
@@ -103,17 +121,23 @@ __device__ __forceinline__ void grad_stage(GradStage<IO, N>& st, const GradArgs<
   }
 }
 
-// Sum of v over the lanes of each row (LPR consecutive lanes): every lane of
-// the row ends with the row's sum.
-template <int LPR> __device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+// Sum over the W lanes of a row (W <= 16, rows aligned to W): every lane of the
+// row ends with the row's sum (DPP quad permutes, then half-row and row
+// mirrors).
+template <int W> __device__ __forceinline__ float row_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  if constexpr (W >= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if constexpr (W >= 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  if constexpr (W >= 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
   return v;
 }
-// Sum over the row groups of a wave (lanes with the same lane % LPR).
-template <int LPR> __device__ __forceinline__ float col_sum(float v) {
+// Sum over the row groups of a wave (lanes with the same lane % W).
+template <int W> __device__ __forceinline__ float col_sum(float v) {
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+  for (int off = W; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) {
@@ -122,224 +146,231 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// ---- forward sweep: h_t, dC (per head), e_t, eT --------------------------------
+// ---- the two sweeps, one launch: workgroups [0, B*H) run the forward sweep
+// (h_t, dC per head, e_t, eT), workgroups [B*H, 2*B*H) the reverse sweep (gh_t,
+// dx, dB per head, q_t, dD, dh0).  They share nothing, so they run side by side.
 template <typename IO, int N>
-__global__ __launch_bounds__(256) void grad_forward_kernel(const GradArgs<IO> a) {
-  constexpr int LPR = N / 8, RPP = 256 / LPR;
-  constexpr int KR = RPP >= kGP ? 1 : kGP / RPP;
-  constexpr bool ROW_GUARD = RPP > kGP;
-  __shared__ GradStage<IO, N> st;
-  __shared__ float sdc[kGTB][4][N];       // per-wave dC partials
-  __shared__ float se[kGTB][4];
-  __shared__ float sred[4];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
+__global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const GradArgs<IO> a) {
+  using S = GradShape<N>;
+  constexpr int LPR = S::LPR, RPP = S::RPP, KR = S::KR, NW = S::NW, TB = S::TB;
+  __shared__ GradSmem<N> st;
+  const int BH = a.B * a.H;
+  const bool rev = (int)blockIdx.x >= BH;
+  const int bh = rev ? (int)blockIdx.x - BH : (int)blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nc = (tid % LPR) * 8, r0 = tid / LPR;
-  const bool has_row = !ROW_GUARD || r0 < kGP;
-  int len = a.seqlens ? a.seqlens[b] : a.L;
-  len = len < 0 ? 0 : (len > a.L ? a.L : len);
-  const float Ah = a.A[h];
-
-  float hs[KR][8];
-#pragma unroll
-  for (int k = 0; k < KR; ++k)
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      hs[k][i] = (a.h0 && has_row) ? a.h0[((size_t)bh * kGP + r0 + k * RPP) * N + nc + i] : 0.f;
-
-  for (int t0 = 0; t0 < len; t0 += kGTB) {
-    const int nt = min(kGTB, len - t0);
-    grad_stage<IO, N>(st, a, b, h, g, t0, nt, tid);
-    __syncthreads();
-    for (int j = 0; j < nt; ++j) {
-      const float d = st.dt[j];
-      const float dec = __expf(d * Ah);
-      float bv[8], cv[8], dc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bv[i] = st.b[j][nc + i];
-        cv[i] = st.c[j][nc + i];
-        dc[i] = 0.f;
-      }
-      float ep = 0.f;
-#pragma unroll
-      for (int k = 0; k < KR; ++k) {
-        const int p = r0 + k * RPP;
-        const float xp = has_row ? st.x[j][p] : 0.f;
-        const float dyp = has_row ? st.dy[j][p] : 0.f;
-        const float u = d * xp;
-        float yc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          hs[k][i] = __builtin_fmaf(dec, hs[k][i], u * bv[i]);
-          yc = __builtin_fmaf(hs[k][i], cv[i], yc);
-          dc[i] = __builtin_fmaf(dyp, hs[k][i], dc[i]);
-        }
-        yc = row_sum<LPR>(yc);
-        if ((tid % LPR) == 0) ep = __builtin_fmaf(dyp, yc, ep);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dc[i] = col_sum<LPR>(dc[i]);
-      if (lane < LPR) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sdc[j][wv][nc + i] = dc[i];
-      }
-      ep = wave_sum(ep);
-      if (lane == 0) se[j][wv] = ep;
-    }
-    __syncthreads();
-    for (int id = tid; id < nt * N; id += 256) {
-      const int j = id / N, n = id % N;
-      const float v = (sdc[j][0][n] + sdc[j][1][n]) + (sdc[j][2][n] + sdc[j][3][n]);
-      a.dCh[(((size_t)b * a.L + t0 + j) * a.H + h) * N + n] = v;
-    }
-    if (tid < nt) a.e[((size_t)b * a.L + t0 + tid) * a.H + h] = (se[tid][0] + se[tid][1]) + (se[tid][2] + se[tid][3]);
-    __syncthreads();
-  }
-  // eT = <dhT, h_len>
-  float et = 0.f;
-  if (a.dhT && has_row) {
-#pragma unroll
-    for (int k = 0; k < KR; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        et = __builtin_fmaf(a.dhT[((size_t)bh * kGP + r0 + k * RPP) * N + nc + i], hs[k][i], et);
-  }
-  et = wave_sum(et);
-  if (lane == 0) sred[wv] = et;
-  __syncthreads();
-  if (tid == 0) a.eT[bh] = (sred[0] + sred[1]) + (sred[2] + sred[3]);
-}
-
-// ---- reverse sweep: gh_t, dx, dB (per head), ddt, dA, dD, dh0 ------------------
-template <typename IO, int N>
-__global__ __launch_bounds__(256) void grad_reverse_kernel(const GradArgs<IO> a) {
-  constexpr int LPR = N / 8, RPP = 256 / LPR;
-  constexpr int KR = RPP >= kGP ? 1 : kGP / RPP;
-  constexpr bool ROW_GUARD = RPP > kGP;
-  __shared__ GradStage<IO, N> st;
-  __shared__ float sdb[kGTB][4][N];       // per-wave dB partials (before the dt factor)
-  __shared__ float sq[kGTB][4];
-  __shared__ float sdx[kGTB][kGP];
-  __shared__ float sred[2][4];
-  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nc = (tid % LPR) * 8, r0 = tid / LPR;
-  const bool has_row = !ROW_GUARD || r0 < kGP;
   int len = a.seqlens ? a.seqlens[b] : a.L;
   len = len < 0 ? 0 : (len > a.L ? a.L : len);
   const float Ah = a.A[h], Dh = a.D[h];
-  const float dtb = a.dt_sp && a.dt_bias ? a.dt_bias[h] : 0.f;
 
-  float gh[KR][8];
+  // h (forward) or gh (reverse), in registers
+  float sv[KR][8];
+  const float* init = rev ? a.dhT : a.h0;
 #pragma unroll
   for (int k = 0; k < KR; ++k)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      gh[k][i] = (a.dhT && has_row) ? a.dhT[((size_t)bh * kGP + r0 + k * RPP) * N + nc + i] : 0.f;
+    for (int i = 0; i < 8; ++i) sv[k][i] = init ? init[((size_t)bh * kGP + r0 + k * RPP) * N + nc + i] : 0.f;
   float dDacc = 0.f;
-  // thread 0 runs the scalar chain over the tokens (in double)
-  double R = 0.0, dA_acc = 0.0, dbias_acc = 0.0;
-  const float eT = a.eT[bh];
 
-  const int nblk = (len + kGTB - 1) / kGTB;
-  for (int kb = nblk - 1; kb >= 0; --kb) {
-    const int t0 = kb * kGTB;
-    const int nt = min(kGTB, len - t0);
+  const int nblk = (len + TB - 1) / TB;
+  for (int kk = 0; kk < nblk; ++kk) {
+    const int kb = rev ? nblk - 1 - kk : kk;
+    const int t0 = kb * TB;
+    const int nt = min(TB, len - t0);
     grad_stage<IO, N>(st, a, b, h, g, t0, nt, tid);
     __syncthreads();
-    for (int j = nt - 1; j >= 0; --j) {
+    for (int jj = 0; jj < nt; ++jj) {
+      const int j = rev ? nt - 1 - jj : jj;
       const float d = st.dt[j];
       const float dec = __expf(d * Ah);
-      float bv[8], cv[8], db[8];
+      float bv[8], cv[8], cs[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         bv[i] = st.b[j][nc + i];
         cv[i] = st.c[j][nc + i];
-        db[i] = 0.f;
+        cs[i] = 0.f;
       }
-      float qp = 0.f;
+      float sp = 0.f;     // this thread's share of e_t (forward) or q_t (reverse)
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
         const int p = r0 + k * RPP;
-        const float xp = has_row ? st.x[j][p] : 0.f;
-        const float dyp = has_row ? st.dy[j][p] : 0.f;
-        float v = 0.f;
+        const float xp = st.x[j][p];
+        const float dyp = st.dy[j][p];
+        float r = 0.f;
+        if (!rev) {
+          const float u = d * xp;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          gh[k][i] = __builtin_fmaf(cv[i], dyp, gh[k][i]);   // gradient with respect to h_t
-          v = __builtin_fmaf(gh[k][i], bv[i], v);
-          db[i] = __builtin_fmaf(xp, gh[k][i], db[i]);
-        }
-        v = row_sum<LPR>(v);
-        if (has_row && (tid % LPR) == 0) {
-          sdx[j][p] = __builtin_fmaf(d, v, Dh * dyp);
-          qp = __builtin_fmaf(xp, v, qp);
-          dDacc = __builtin_fmaf(dyp, xp, dDacc);
-        }
+          for (int i = 0; i < 8; ++i) {
+            sv[k][i] = __builtin_fmaf(dec, sv[k][i], u * bv[i]);   // h_t
+            r = __builtin_fmaf(sv[k][i], cv[i], r);                // (h_t . C_t)[p]
+            cs[i] = __builtin_fmaf(dyp, sv[k][i], cs[i]);          // dC partial
+          }
+          r = row_sum<LPR>(r);
+          if ((tid % LPR) == 0) sp = __builtin_fmaf(dyp, r, sp);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) gh[k][i] *= dec;                // ... and with respect to h_{t-1}
+          for (int i = 0; i < 8; ++i) {
+            sv[k][i] = __builtin_fmaf(cv[i], dyp, sv[k][i]);       // gradient with respect to h_t
+            r = __builtin_fmaf(sv[k][i], bv[i], r);                // v_t[p]
+            cs[i] = __builtin_fmaf(xp, sv[k][i], cs[i]);           // dB partial (before dt)
+          }
+          r = row_sum<LPR>(r);
+          if ((tid % LPR) == 0) {
+            st.dx[j][p] = __builtin_fmaf(d, r, Dh * dyp);
+            sp = __builtin_fmaf(xp, r, sp);
+            dDacc = __builtin_fmaf(dyp, xp, dDacc);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sv[k][i] *= dec;             // ... and with respect to h_{t-1}
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) db[i] = col_sum<LPR>(db[i]);
+      for (int i = 0; i < 8; ++i) cs[i] = col_sum<LPR>(cs[i]);
       if (lane < LPR) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sdb[j][wv][nc + i] = db[i];
+        for (int i = 0; i < 8; i += 4)
+          *reinterpret_cast<f4*>(&st.col[j][wv][nc + i]) = f4{cs[i], cs[i + 1], cs[i + 2], cs[i + 3]};
       }
-      qp = wave_sum(qp);
-      if (lane == 0) sq[j][wv] = qp;
+      sp = wave_sum(sp);
+      if (lane == 0) st.sc[j][wv] = sp;
     }
     __syncthreads();
-    for (int id = tid; id < nt * N; id += 256) {
+    // the block's outputs: sums over the waves in a fixed order
+    float* colout = rev ? a.dBh : a.dCh;
+    for (int id = tid; id < nt * N; id += S::NTH) {
       const int j = id / N, n = id % N;
-      const float v = (sdb[j][0][n] + sdb[j][1][n]) + (sdb[j][2][n] + sdb[j][3][n]);
-      a.dBh[(((size_t)b * a.L + t0 + j) * a.H + h) * N + n] = st.dt[j] * v;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += st.col[j][w][n];
+      colout[(((size_t)b * a.L + t0 + j) * a.H + h) * N + n] = rev ? st.dt[j] * v : v;
     }
-    for (int id = tid; id < nt * kGP; id += 256) {
-      const int j = id / kGP, p = id % kGP;
-      a.dx[(((size_t)b * a.L + t0 + j) * a.H + h) * kGP + p] = sdx[j][p];
+    if (tid < nt) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += st.sc[tid][w];
+      (rev ? a.q : a.e)[((size_t)b * a.L + t0 + tid) * a.H + h] = v;
     }
-    if (tid == 0) {
-      for (int j = nt - 1; j >= 0; --j) {
-        const int t = t0 + j;
-        const size_t ti = ((size_t)b * a.L + t) * a.H + h;
-        const double q = (double)((sq[j][0] + sq[j][1]) + (sq[j][2] + sq[j][3]));
-        const double d = (double)st.dt[j];
-        R += (double)a.e[ti] + (t == len - 1 ? (double)eT : 0.0) - d * q;
-        const double gdt = q + (double)Ah * R;
-        dA_acc += d * R;
-        double graw = gdt;
-        if (a.dt_sp) {
-          const double v = (double)ldf(a.dt + ti) + (double)dtb;
-          graw = gdt * (v > 20.0 ? 1.0 : 1.0 / (1.0 + exp(-v)));
-          dbias_acc += graw;
-        }
-        a.ddt[ti] = (float)graw;
+    if (rev) {
+      for (int id = tid; id < nt * kGP; id += S::NTH) {
+        const int j = id / kGP, p = id % kGP;
+        a.dx[(((size_t)b * a.L + t0 + j) * a.H + h) * kGP + p] = st.dx[j][p];
       }
     }
     __syncthreads();
   }
-  // rows past the length: zero gradients
-  for (int id = tid; id < (a.L - len) * kGP; id += 256) {
+
+  if (!rev) {
+    // eT = <dhT, h_len>
+    float et = 0.f;
+    if (a.dhT) {
+#pragma unroll
+      for (int k = 0; k < KR; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          et = __builtin_fmaf(a.dhT[((size_t)bh * kGP + r0 + k * RPP) * N + nc + i], sv[k][i], et);
+    }
+    et = wave_sum(et);
+    if (lane == 0) st.red[0][wv] = et;
+    __syncthreads();
+    if (tid == 0) {
+      float v = 0.f;
+      for (int w = 0; w < NW; ++w) v += st.red[0][w];
+      a.eT[bh] = v;
+    }
+    return;
+  }
+  // reverse: rows past the length get zero gradients; dh0; dD
+  for (int id = tid; id < (a.L - len) * kGP; id += S::NTH) {
     const int t = len + id / kGP, p = id % kGP;
     a.dx[(((size_t)b * a.L + t) * a.H + h) * kGP + p] = 0.f;
   }
-  for (int t = len + tid; t < a.L; t += 256) a.ddt[((size_t)b * a.L + t) * a.H + h] = 0.f;
-  if (a.dh0 && has_row) {
+  if (a.dh0) {
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
       float* dst = a.dh0 + ((size_t)bh * kGP + r0 + k * RPP) * N + nc;
-      *reinterpret_cast<f4*>(dst) = f4{gh[k][0], gh[k][1], gh[k][2], gh[k][3]};
-      *reinterpret_cast<f4*>(dst + 4) = f4{gh[k][4], gh[k][5], gh[k][6], gh[k][7]};
+      *reinterpret_cast<f4*>(dst) = f4{sv[k][0], sv[k][1], sv[k][2], sv[k][3]};
+      *reinterpret_cast<f4*>(dst + 4) = f4{sv[k][4], sv[k][5], sv[k][6], sv[k][7]};
     }
   }
   dDacc = wave_sum(dDacc);
-  if (lane == 0) sred[0][wv] = dDacc;
+  if (lane == 0) st.red[1][wv] = dDacc;
   __syncthreads();
   if (tid == 0) {
-    a.dDp[bh] = (sred[0][0] + sred[0][1]) + (sred[0][2] + sred[0][3]);
-    a.dAp[bh] = (float)dA_acc;
-    a.dbp[bh] = (float)dbias_acc;
+    float v = 0.f;
+    for (int w = 0; w < NW; ++w) v += st.red[1][w];
+    a.dDp[bh] = v;
+  }
+}
+
+// ---- the dt chain: R_t = sum_{t' >= t} dL/dS_t' with dL/dS_t = e_t + [t = last]
+// eT - dt_t q_t, then ddt_t = q_t + A R_t (times sp'(raw + bias) for a raw dt),
+// dA += dt_t R_t.  One 256-thread block per (sequence, head): each thread takes
+// a run of consecutive tokens, the runs' totals are suffix-summed across the
+// block, all in double.
+constexpr int kChainT = 256;
+template <typename IO>
+__global__ __launch_bounds__(kChainT) void grad_chain_kernel(const GradArgs<IO> a) {
+  __shared__ double tot[kChainT];
+  __shared__ double red[2][kChainT];
+  const int bh = blockIdx.x, b = bh / a.H, h = bh - b * a.H;
+  const int tid = threadIdx.x;
+  int len = a.seqlens ? a.seqlens[b] : a.L;
+  len = len < 0 ? 0 : (len > a.L ? a.L : len);
+  const int per = (len + kChainT - 1) / kChainT;
+  const int ta = min(tid * per, len), tb = min(ta + per, len);
+  const double Ah = (double)a.A[h];
+  const double eT = (double)a.eT[bh];
+  const float bias = a.dt_sp && a.dt_bias ? a.dt_bias[h] : 0.f;
+  auto dt_eff = [&](size_t ti) {
+    const float d = ldf(a.dt + ti);
+    return (double)(a.dt_sp ? dt_softplus(d, bias) : d);
+  };
+  auto dS = [&](int t) {
+    const size_t ti = ((size_t)b * a.L + t) * a.H + h;
+    return (double)a.e[ti] + (t == len - 1 ? eT : 0.0) - dt_eff(ti) * (double)a.q[ti];
+  };
+  double run = 0.0;
+  for (int t = tb - 1; t >= ta; --t) run += dS(t);
+  tot[tid] = run;
+  __syncthreads();
+  // suffix sums of the run totals (Hillis-Steele over the block)
+  for (int off = 1; off < kChainT; off <<= 1) {
+    const double v = tid + off < kChainT ? tot[tid + off] : 0.0;
+    __syncthreads();
+    tot[tid] += v;
+    __syncthreads();
+  }
+  double R = tid + 1 < kChainT ? tot[tid + 1] : 0.0;   // everything after this run
+  double dA_acc = 0.0, db_acc = 0.0;
+  for (int t = tb - 1; t >= ta; --t) {
+    const size_t ti = ((size_t)b * a.L + t) * a.H + h;
+    R += dS(t);
+    const double dte = dt_eff(ti);
+    const double gdt = (double)a.q[ti] + Ah * R;
+    dA_acc += dte * R;
+    double graw = gdt;
+    if (a.dt_sp) {
+      const double v = (double)ldf(a.dt + ti) + (double)bias;
+      graw = gdt * (v > 20.0 ? 1.0 : 1.0 / (1.0 + exp(-v)));
+      db_acc += graw;
+    }
+    a.ddt[ti] = (float)graw;
+  }
+  for (int t = len + tid; t < a.L; t += kChainT) a.ddt[((size_t)b * a.L + t) * a.H + h] = 0.f;
+  red[0][tid] = dA_acc;
+  red[1][tid] = db_acc;
+  __syncthreads();
+  for (int off = kChainT / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      red[0][tid] += red[0][tid + off];
+      red[1][tid] += red[1][tid + off];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.dAp[bh] = (float)red[0][0];
+    a.dbp[bh] = (float)red[1][0];
   }
 }
 
@@ -348,7 +379,7 @@ __global__ __launch_bounds__(256) void grad_reverse_kernel(const GradArgs<IO> a)
 // past a sequence's length are zero); dA, dD, dt-bias: one thread per head,
 // sequences in index order.
 template <int N>
-__global__ __launch_bounds__(256) void grad_reduce_kernel(const GradArgs<float> a, int io_unused) {
+__global__ __launch_bounds__(256) void grad_reduce_kernel(const GradArgs<float> a) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long total = (long long)a.B * a.L * a.G * N;
   const int hpg = a.H / a.G;
@@ -388,7 +419,7 @@ __global__ __launch_bounds__(256) void grad_reduce_kernel(const GradArgs<float> 
 
 // ---------------------------------------------------------------------------
 struct GradWs {
-  size_t dBh, dCh, e, eT, dAp, dDp, dbp, total;
+  size_t dBh, dCh, e, q, eT, dAp, dDp, dbp, total;
 };
 static GradWs grad_ws(const mamba2_dims& d) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
@@ -397,7 +428,8 @@ static GradWs grad_ws(const mamba2_dims& d) {
   w.dBh = 0;
   w.dCh = up(w.dBh + B * L * H * N * 4);
   w.e = up(w.dCh + B * L * H * N * 4);
-  w.eT = up(w.e + B * L * H * 4);
+  w.q = up(w.e + B * L * H * 4);
+  w.eT = up(w.q + B * L * H * 4);
   w.dAp = up(w.eT + B * H * 4);
   w.dDp = up(w.dAp + B * H * 4);
   w.dbp = up(w.dDp + B * H * 4);
@@ -409,23 +441,22 @@ size_t scan_grad_workspace_bytes(const mamba2_dims& d) { return grad_ws(d).total
 
 template <typename IO, int N>
 static hipError_t launch_grad_N(const mamba2_dims& d, const GradArgs<IO>& a, hipStream_t st) {
-  const unsigned grid = (unsigned)(d.batch * d.nheads);
-  grad_forward_kernel<IO, N><<<grid, 256, 0, st>>>(a);
+  const unsigned bh = (unsigned)(d.batch * d.nheads);
+  grad_sweep_kernel<IO, N><<<2 * bh, GradShape<N>::NTH, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  grad_reverse_kernel<IO, N><<<grid, 256, 0, st>>>(a);
+  grad_chain_kernel<IO><<<bh, kChainT, 0, st>>>(a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // the reduction reads only workspace and lengths: reuse the argument block
-  // with the I/O pointers left out
+  // the reduction reads only workspace and lengths: an argument block with
+  // the I/O pointers left out
   GradArgs<float> r{};
   r.seqlens = a.seqlens;
   r.B = a.B; r.L = a.L; r.H = a.H; r.G = a.G;
   r.dB = a.dB; r.dC = a.dC; r.dA = a.dA; r.dD = a.dD; r.dbias = a.dbias;
   r.dBh = a.dBh; r.dCh = a.dCh; r.dAp = a.dAp; r.dDp = a.dDp; r.dbp = a.dbp;
   const long long total = (long long)d.batch * d.seqlen * d.ngroups * N;
-  const unsigned rg = (unsigned)((total + 255) / 256);
-  grad_reduce_kernel<N><<<rg > 0 ? rg : 1, 256, 0, st>>>(r, 0);
+  grad_reduce_kernel<N><<<(unsigned)((total + 255) / 256), 256, 0, st>>>(r);
   return hipGetLastError();
 }
 
@@ -453,6 +484,7 @@ static hipError_t launch_grad_IO(const mamba2_dims& d, const mamba2_scan_grad_io
   a.dBh = (float*)(base + wl.dBh);
   a.dCh = (float*)(base + wl.dCh);
   a.e = (float*)(base + wl.e);
+  a.q = (float*)(base + wl.q);
   a.eT = (float*)(base + wl.eT);
   a.dAp = (float*)(base + wl.dAp);
   a.dDp = (float*)(base + wl.dDp);
