@@ -80,7 +80,7 @@ template <int N> struct GradShape {
   static_assert(KR * RPP == kGP, "rows");
 };
 
-template <int N> struct GradSmem {
+template <int N> struct alignas(16) GradSmem {
   static constexpr int TB = GradShape<N>::TB, NW = GradShape<N>::NW;
   float x[TB][kGP];
   float dy[TB][kGP];
@@ -88,8 +88,7 @@ template <int N> struct GradSmem {
   float c[TB][N];
   float dt[TB];
   float col[TB][NW][N];     // per-wave partial sums over p (dC or dB)
-  float sc[TB][NW];         // per-wave partial scalars (e or q)
-  float dx[TB][kGP];
+  float rv[TB][kGP];        // per-row sums over n: (h_t . C_t)[p] or v_t[p]
   float red[2][16];
 };
 
@@ -134,10 +133,28 @@ template <int W> __device__ __forceinline__ float row_sum(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
   return v;
 }
-// Sum over the row groups of a wave (lanes with the same lane % W).
+// DPP rotation inside each 16-lane row: lane i receives lane (i + R) mod 16.
+template <int R> __device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + R, 0xF, 0xF, false));
+}
+// Sum over the row groups of a wave (lanes with the same lane % W), valid in
+// lanes 0 .. 15: rotations by W, 2W, .. 8 inside each row, then the rows are
+// paired with the lane-swap instructions (rows 1 and 3 onto rows 0 and 2, then
+// lanes 32-63 onto lanes 0-31), all in the vector ALU.
 template <int W> __device__ __forceinline__ float col_sum(float v) {
-#pragma unroll
-  for (int off = W; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+  if constexpr (W <= 8) v += row_ror<8>(v);
+  if constexpr (W <= 4) v += row_ror<4>(v);
+  if constexpr (W <= 2) v += row_ror<2>(v);
+  // v_permlane16_swap a, b: odd rows of a <-> even rows of b; afterwards b's
+  // even rows hold v's odd rows.  v_permlane32_swap a, b: lanes 32-63 of a <->
+  // lanes 0-31 of b.  (Written out so that both operands are distinct
+  // registers; the wait states cover the VALU writes before and after.)
+  float a0 = v, b0 = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a0), "+v"(b0));
+  v += b0;
+  float a1 = v, b1 = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a1), "+v"(b1));
+  v += b1;
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) {
@@ -149,14 +166,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---- the two sweeps, one launch: workgroups [0, B*H) run the forward sweep
 // (h_t, dC per head, e_t, eT), workgroups [B*H, 2*B*H) the reverse sweep (gh_t,
 // dx, dB per head, q_t, dD, dh0).  They share nothing, so they run side by side.
-template <typename IO, int N>
-__global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const GradArgs<IO> a) {
+template <typename IO, int N, bool rev>
+__device__ __forceinline__ void grad_sweep(const GradArgs<IO>& a, GradSmem<N>& st, int bh) {
   using S = GradShape<N>;
   constexpr int LPR = S::LPR, RPP = S::RPP, KR = S::KR, NW = S::NW, TB = S::TB;
-  __shared__ GradSmem<N> st;
-  const int BH = a.B * a.H;
-  const bool rev = (int)blockIdx.x >= BH;
-  const int bh = rev ? (int)blockIdx.x - BH : (int)blockIdx.x;
   const int b = bh / a.H, h = bh - b * a.H, g = h / (a.H / a.G);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nc = (tid % LPR) * 8, r0 = tid / LPR;
@@ -185,20 +198,26 @@ __global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const Gra
       const float d = st.dt[j];
       const float dec = __expf(d * Ah);
       float bv[8], cv[8], cs[8];
+      {
+        const f4 b0 = *reinterpret_cast<const f4*>(&st.b[j][nc]), b1 = *reinterpret_cast<const f4*>(&st.b[j][nc + 4]);
+        const f4 c0 = *reinterpret_cast<const f4*>(&st.c[j][nc]), c1 = *reinterpret_cast<const f4*>(&st.c[j][nc + 4]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bv[i] = st.b[j][nc + i];
-        cv[i] = st.c[j][nc + i];
-        cs[i] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+          bv[i] = b0[i];
+          bv[4 + i] = b1[i];
+          cv[i] = c0[i];
+          cv[4 + i] = c1[i];
+        }
       }
-      float sp = 0.f;     // this thread's share of e_t (forward) or q_t (reverse)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cs[i] = 0.f;
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
         const int p = r0 + k * RPP;
         const float xp = st.x[j][p];
         const float dyp = st.dy[j][p];
         float r = 0.f;
-        if (!rev) {
+        if constexpr (!rev) {
           const float u = d * xp;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -207,7 +226,7 @@ __global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const Gra
             cs[i] = __builtin_fmaf(dyp, sv[k][i], cs[i]);          // dC partial
           }
           r = row_sum<LPR>(r);
-          if ((tid % LPR) == 0) sp = __builtin_fmaf(dyp, r, sp);
+          if ((tid % LPR) == 0) st.rv[j][p] = r;
         } else {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -216,11 +235,7 @@ __global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const Gra
             cs[i] = __builtin_fmaf(xp, sv[k][i], cs[i]);           // dB partial (before dt)
           }
           r = row_sum<LPR>(r);
-          if ((tid % LPR) == 0) {
-            st.dx[j][p] = __builtin_fmaf(d, r, Dh * dyp);
-            sp = __builtin_fmaf(xp, r, sp);
-            dDacc = __builtin_fmaf(dyp, xp, dDacc);
-          }
+          if ((tid % LPR) == 0) st.rv[j][p] = r;
 #pragma unroll
           for (int i = 0; i < 8; ++i) sv[k][i] *= dec;             // ... and with respect to h_{t-1}
         }
@@ -232,8 +247,6 @@ __global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const Gra
         for (int i = 0; i < 8; i += 4)
           *reinterpret_cast<f4*>(&st.col[j][wv][nc + i]) = f4{cs[i], cs[i + 1], cs[i + 2], cs[i + 3]};
       }
-      sp = wave_sum(sp);
-      if (lane == 0) st.sc[j][wv] = sp;
     }
     __syncthreads();
     // the block's outputs: sums over the waves in a fixed order
@@ -245,22 +258,25 @@ __global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const Gra
       for (int w = 0; w < NW; ++w) v += st.col[j][w][n];
       colout[(((size_t)b * a.L + t0 + j) * a.H + h) * N + n] = rev ? st.dt[j] * v : v;
     }
-    if (tid < nt) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) v += st.sc[tid][w];
-      (rev ? a.q : a.e)[((size_t)b * a.L + t0 + tid) * a.H + h] = v;
-    }
-    if (rev) {
-      for (int id = tid; id < nt * kGP; id += S::NTH) {
-        const int j = id / kGP, p = id % kGP;
-        a.dx[(((size_t)b * a.L + t0 + j) * a.H + h) * kGP + p] = st.dx[j][p];
+    // per token (one wave each, lane = row p): e_t = dy . (h . C), or
+    // dx = D dy + dt v, q_t = x . v and the token's share of dD
+    for (int j = wv; j < nt; j += NW) {
+      const float r = st.rv[j][lane], dyp = st.dy[j][lane], xp = st.x[j][lane];
+      const size_t ti = ((size_t)b * a.L + t0 + j) * a.H + h;
+      if constexpr (!rev) {
+        const float ev = wave_sum(dyp * r);
+        if (lane == 0) a.e[ti] = ev;
+      } else {
+        a.dx[ti * kGP + lane] = __builtin_fmaf(st.dt[j], r, Dh * dyp);
+        const float qv = wave_sum(xp * r);
+        if (lane == 0) a.q[ti] = qv;
+        dDacc = __builtin_fmaf(dyp, xp, dDacc);
       }
     }
     __syncthreads();
   }
 
-  if (!rev) {
+  if constexpr (!rev) {
     // eT = <dhT, h_len>
     float et = 0.f;
     if (a.dhT) {
@@ -279,7 +295,7 @@ __global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const Gra
       a.eT[bh] = v;
     }
     return;
-  }
+  } else {
   // reverse: rows past the length get zero gradients; dh0; dD
   for (int id = tid; id < (a.L - len) * kGP; id += S::NTH) {
     const int t = len + id / kGP, p = id % kGP;
@@ -301,6 +317,15 @@ __global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const Gra
     for (int w = 0; w < NW; ++w) v += st.red[1][w];
     a.dDp[bh] = v;
   }
+  }
+}
+
+template <typename IO, int N>
+__global__ __launch_bounds__(GradShape<N>::NTH) void grad_sweep_kernel(const GradArgs<IO> a) {
+  __shared__ GradSmem<N> st;
+  const int BH = a.B * a.H;
+  if ((int)blockIdx.x >= BH) grad_sweep<IO, N, true>(a, st, (int)blockIdx.x - BH);
+  else grad_sweep<IO, N, false>(a, st, (int)blockIdx.x);
 }
 
 // ---- the dt chain: R_t = sum_{t' >= t} dL/dS_t' with dL/dS_t = e_t + [t = last]
