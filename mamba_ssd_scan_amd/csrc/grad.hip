@@ -76,49 +76,73 @@ template <int N> struct GradShape {
   static constexpr int RPP = NTH / LPR;
   static constexpr int KR = kGP / RPP;
   static constexpr int NW = NTH / 64;
-  static constexpr int TB = N == 128 ? 8 : 16;   // tokens staged per block
+  static constexpr int TB = N == 16 ? 16 : 4;    // tokens staged per block
   static_assert(KR * RPP == kGP, "rows");
 };
 
 template <int N> struct alignas(16) GradSmem {
   static constexpr int TB = GradShape<N>::TB, NW = GradShape<N>::NW;
-  float x[TB][kGP];
-  float dy[TB][kGP];
-  float b[TB][N];
-  float c[TB][N];
-  float dt[TB];
-  float col[TB][NW][N];     // per-wave partial sums over p (dC or dB)
+  float x[2][TB][kGP];       // two staging buffers: the next block lands while this one is used
+  float dy[2][TB][kGP];
+  float b[2][TB][N];
+  float c[2][TB][N];
+  float dt[2][TB];
+  float col[TB][GradShape<N>::RPP][N];   // per-thread partial sums over its rows (dC or dB)
   float rv[TB][kGP];        // per-row sums over n: (h_t . C_t)[p] or v_t[p]
   float red[2][16];
 };
 
-template <typename IO, int N>
-__device__ __forceinline__ void grad_stage(GradSmem<N>& st, const GradArgs<IO>& a, int b, int h, int g, int t0,
-                                           int nt, int tid) {
-  constexpr int TB = GradShape<N>::TB, NTH = GradShape<N>::NTH;
-  for (int id = tid; id < TB * kGP; id += NTH) {
-    const int j = id / kGP, p = id % kGP;
-    const bool ok = j < nt;
-    const size_t row = ((size_t)b * a.L + t0 + j) * a.H + h;
-    st.x[j][p] = ok ? ldf(a.x + row * kGP + p) : 0.f;
-    st.dy[j][p] = ok ? ldf(a.dy + row * kGP + p) : 0.f;
-  }
-  for (int id = tid; id < TB * N; id += NTH) {
-    const int j = id / N, n = id % N;
-    const bool ok = j < nt;
-    const size_t row = ((size_t)b * a.L + t0 + j) * a.G + g;
-    st.b[j][n] = ok ? ldf(a.Bm + row * N + n) : 0.f;
-    st.c[j][n] = ok ? ldf(a.Cm + row * N + n) : 0.f;
-  }
-  if (tid < TB) {
-    float d = 0.f;
-    if (tid < nt) {
-      d = ldf(a.dt + ((size_t)b * a.L + t0 + tid) * a.H + h);
-      if (a.dt_sp) d = dt_softplus(d, a.dt_bias ? a.dt_bias[h] : 0.f);
+// One block of up to TB tokens: loaded into registers (zeros past nt) while
+// the previous block is computed, then written to a staging buffer.
+template <typename IO, int N> struct GradPre {
+  static constexpr int TB = GradShape<N>::TB, NTH = GradShape<N>::NTH;
+  static constexpr int PX = (TB * kGP + NTH - 1) / NTH, PB = (TB * N + NTH - 1) / NTH;
+  IO x[PX], dy[PX], b[PB], c[PB];
+  IO d;
+
+  __device__ __forceinline__ void fetch(const GradArgs<IO>& a, int b_, int h, int g, int t0, int nt, int tid) {
+#pragma unroll
+    for (int k = 0; k < PX; ++k) {
+      const int id = tid + k * NTH, j = id / kGP, p = id % kGP;
+      const bool ok = id < TB * kGP && j < nt;
+      const size_t row = ((size_t)b_ * a.L + t0 + j) * a.H + h;
+      x[k] = ok ? a.x[row * kGP + p] : (IO)0;
+      dy[k] = ok ? a.dy[row * kGP + p] : (IO)0;
     }
-    st.dt[tid] = d;
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int id = tid + k * NTH, j = id / N, n = id % N;
+      const bool ok = id < TB * N && j < nt;
+      const size_t row = ((size_t)b_ * a.L + t0 + j) * a.G + g;
+      b[k] = ok ? a.Bm[row * N + n] : (IO)0;
+      c[k] = ok ? a.Cm[row * N + n] : (IO)0;
+    }
+    d = tid < nt ? a.dt[((size_t)b_ * a.L + t0 + tid) * a.H + h] : (IO)0;
   }
-}
+  __device__ __forceinline__ void put(GradSmem<N>& st, int buf, const GradArgs<IO>& a, int h, int nt, int tid) const {
+#pragma unroll
+    for (int k = 0; k < PX; ++k) {
+      const int id = tid + k * NTH;
+      if (id < TB * kGP) {
+        st.x[buf][id / kGP][id % kGP] = (float)x[k];
+        st.dy[buf][id / kGP][id % kGP] = (float)dy[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int id = tid + k * NTH;
+      if (id < TB * N) {
+        st.b[buf][id / N][id % N] = (float)b[k];
+        st.c[buf][id / N][id % N] = (float)c[k];
+      }
+    }
+    if (tid < TB) {
+      float v = (float)d;
+      if (a.dt_sp && tid < nt) v = dt_softplus(v, a.dt_bias ? a.dt_bias[h] : 0.f);
+      st.dt[buf][tid] = v;
+    }
+  }
+};
 
 // Sum over the W lanes of a row (W <= 16, rows aligned to W): every lane of the
 // row ends with the row's sum (DPP quad permutes, then half-row and row
@@ -187,20 +211,32 @@ __device__ __forceinline__ void grad_sweep(const GradArgs<IO>& a, GradSmem<N>& s
   float dDacc = 0.f;
 
   const int nblk = (len + TB - 1) / TB;
+  auto block_of = [&](int kk) { return rev ? nblk - 1 - kk : kk; };
+  GradPre<IO, N> pre;
+  if (nblk > 0) {
+    const int t00 = block_of(0) * TB;
+    pre.fetch(a, b, h, g, t00, min(TB, len - t00), tid);
+    pre.put(st, 0, a, h, min(TB, len - t00), tid);
+  }
+  __syncthreads();
   for (int kk = 0; kk < nblk; ++kk) {
-    const int kb = rev ? nblk - 1 - kk : kk;
-    const int t0 = kb * TB;
+    const int cur = kk & 1;
+    const int t0 = block_of(kk) * TB;
     const int nt = min(TB, len - t0);
-    grad_stage<IO, N>(st, a, b, h, g, t0, nt, tid);
-    __syncthreads();
+    int tn = 0, ntn = 0;
+    if (kk + 1 < nblk) {           // the next block's loads, in flight during this block
+      tn = block_of(kk + 1) * TB;
+      ntn = min(TB, len - tn);
+      pre.fetch(a, b, h, g, tn, ntn, tid);
+    }
     for (int jj = 0; jj < nt; ++jj) {
       const int j = rev ? nt - 1 - jj : jj;
-      const float d = st.dt[j];
+      const float d = st.dt[cur][j];
       const float dec = __expf(d * Ah);
       float bv[8], cv[8], cs[8];
       {
-        const f4 b0 = *reinterpret_cast<const f4*>(&st.b[j][nc]), b1 = *reinterpret_cast<const f4*>(&st.b[j][nc + 4]);
-        const f4 c0 = *reinterpret_cast<const f4*>(&st.c[j][nc]), c1 = *reinterpret_cast<const f4*>(&st.c[j][nc + 4]);
+        const f4 b0 = *reinterpret_cast<const f4*>(&st.b[cur][j][nc]), b1 = *reinterpret_cast<const f4*>(&st.b[cur][j][nc + 4]);
+        const f4 c0 = *reinterpret_cast<const f4*>(&st.c[cur][j][nc]), c1 = *reinterpret_cast<const f4*>(&st.c[cur][j][nc + 4]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bv[i] = b0[i];
@@ -214,8 +250,8 @@ __device__ __forceinline__ void grad_sweep(const GradArgs<IO>& a, GradSmem<N>& s
 #pragma unroll
       for (int k = 0; k < KR; ++k) {
         const int p = r0 + k * RPP;
-        const float xp = st.x[j][p];
-        const float dyp = st.dy[j][p];
+        const float xp = st.x[cur][j][p];
+        const float dyp = st.dy[cur][j][p];
         float r = 0.f;
         if constexpr (!rev) {
           const float u = d * xp;
@@ -240,34 +276,32 @@ __device__ __forceinline__ void grad_sweep(const GradArgs<IO>& a, GradSmem<N>& s
           for (int i = 0; i < 8; ++i) sv[k][i] *= dec;             // ... and with respect to h_{t-1}
         }
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) cs[i] = col_sum<LPR>(cs[i]);
-      if (lane < LPR) {
-#pragma unroll
-        for (int i = 0; i < 8; i += 4)
-          *reinterpret_cast<f4*>(&st.col[j][wv][nc + i]) = f4{cs[i], cs[i + 1], cs[i + 2], cs[i + 3]};
-      }
+      // this thread's partial over its rows; the sum over the row groups is
+      // taken once per block
+      *reinterpret_cast<f4*>(&st.col[j][r0][nc]) = f4{cs[0], cs[1], cs[2], cs[3]};
+      *reinterpret_cast<f4*>(&st.col[j][r0][nc + 4]) = f4{cs[4], cs[5], cs[6], cs[7]};
     }
     __syncthreads();
-    // the block's outputs: sums over the waves in a fixed order
+    if (kk + 1 < nblk) pre.put(st, cur ^ 1, a, h, ntn, tid);
+    // the block's outputs: sums over the row groups in a fixed order
     float* colout = rev ? a.dBh : a.dCh;
     for (int id = tid; id < nt * N; id += S::NTH) {
       const int j = id / N, n = id % N;
       float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) v += st.col[j][w][n];
-      colout[(((size_t)b * a.L + t0 + j) * a.H + h) * N + n] = rev ? st.dt[j] * v : v;
+#pragma unroll 8
+      for (int r = 0; r < RPP; ++r) v += st.col[j][r][n];
+      colout[(((size_t)b * a.L + t0 + j) * a.H + h) * N + n] = rev ? st.dt[cur][j] * v : v;
     }
     // per token (one wave each, lane = row p): e_t = dy . (h . C), or
     // dx = D dy + dt v, q_t = x . v and the token's share of dD
     for (int j = wv; j < nt; j += NW) {
-      const float r = st.rv[j][lane], dyp = st.dy[j][lane], xp = st.x[j][lane];
+      const float r = st.rv[j][lane], dyp = st.dy[cur][j][lane], xp = st.x[cur][j][lane];
       const size_t ti = ((size_t)b * a.L + t0 + j) * a.H + h;
       if constexpr (!rev) {
         const float ev = wave_sum(dyp * r);
         if (lane == 0) a.e[ti] = ev;
       } else {
-        a.dx[ti * kGP + lane] = __builtin_fmaf(st.dt[j], r, Dh * dyp);
+        a.dx[ti * kGP + lane] = __builtin_fmaf(st.dt[cur][j], r, Dh * dyp);
         const float qv = wave_sum(xp * r);
         if (lane == 0) a.q[ti] = qv;
         dDacc = __builtin_fmaf(dyp, xp, dDacc);
