@@ -181,11 +181,9 @@ template <int W> __device__ __forceinline__ float col_sum(float v) {
   v += b1;
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
+// Sum over the 64 lanes of a wave, valid in lanes 0 .. 15 (DPP inside rows,
+// then the lane-swap steps across rows).
+__device__ __forceinline__ float wave_sum(float v) { return col_sum<16>(row_sum<16>(v)); }
 
 // ---- the two sweeps, one launch: workgroups [0, B*H) run the forward sweep
 // (h_t, dC per head, e_t, eT), workgroups [B*H, 2*B*H) the reverse sweep (gh_t,
