@@ -147,20 +147,20 @@ template <typename IO, int N> struct GradPre {
 // Sum over the W lanes of a row (W <= 16, rows aligned to W): every lane of the
 // row ends with the row's sum (DPP quad permutes, then half-row and row
 // mirrors).
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  // old value 0 with bound control on: lets the compiler fold the move into
+  // the add that consumes it (a single add with a DPP source)
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 template <int W> __device__ __forceinline__ float row_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  if constexpr (W >= 4)
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  if constexpr (W >= 8)
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-  if constexpr (W >= 16)
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  v += dpp_f<0xB1>(v);
+  if constexpr (W >= 4) v += dpp_f<0x4E>(v);
+  if constexpr (W >= 8) v += dpp_f<0x141>(v);
+  if constexpr (W >= 16) v += dpp_f<0x140>(v);
   return v;
 }
 // DPP rotation inside each 16-lane row: lane i receives lane (i + R) mod 16.
-template <int R> __device__ __forceinline__ float row_ror(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + R, 0xF, 0xF, false));
-}
+template <int R> __device__ __forceinline__ float row_ror(float v) { return dpp_f<0x120 + R>(v); }
 // Sum over the row groups of a wave (lanes with the same lane % W), valid in
 // lanes 0 .. 15: rotations by W, 2W, .. 8 inside each row, then the rows are
 // paired with the lane-swap instructions (rows 1 and 3 onto rows 0 and 2, then
