@@ -36,14 +36,16 @@ constexpr int kRqTB = 32;   // tokens per staged block
 // Sum over groups of W consecutive lanes (W = 2, 8 or 16), left in every lane
 // of the group: cross-lane DPP moves inside a row (swap neighbours, swap
 // pairs, mirror within 8, mirror within 16) instead of LDS permutes.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  // old value 0 with bound control on: the compiler folds the move into the
+  // add that consumes it (a single add with a DPP source)
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 template <int W> __device__ __forceinline__ float row_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  if constexpr (W >= 4)
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  if constexpr (W >= 8)
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-  if constexpr (W >= 16)
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  v += dpp_f<0xB1>(v);
+  if constexpr (W >= 4) v += dpp_f<0x4E>(v);
+  if constexpr (W >= 8) v += dpp_f<0x141>(v);
+  if constexpr (W >= 16) v += dpp_f<0x140>(v);
   return v;
 }
 
