@@ -160,6 +160,37 @@ def test_mixer_decode_f16_state(N, norm_group):
     assert np.array_equal(cs.astype(np.float64), csr)
 
 
+def test_mixer_decode_fp32_io():
+    Bsz, T, H, G, N = 2, 4, 8, 2, 64
+    s = synth.WindowShape(Bsz, T, H, 64, N, G, 256, np.float32, "narrow")
+    inp = synth.mixer_inputs(s, 250)
+    r = np.random.default_rng(251)
+    Cn = H * 64 + 2 * G * N
+    cs0 = r.standard_normal((Bsz, Cn, 3)).astype(np.float32)
+    h0 = (r.standard_normal((Bsz, H, 64, N)) * 0.1).astype(np.float32)
+    cs = to_dev(cs0).clone()
+    st = to_dev(h0).clone()
+    dims = m2.mixer_decode_dims(Bsz, H, 64, N, G, 512, m2.F32, m2.F32)
+    ws = m2.alloc_mixer_decode_workspace(dims, DEV)
+    say("[mixer decode] f32 I/O")
+    ys = []
+    for t in range(T):
+        y = torch.empty((Bsz, H * 64), dtype=torch.float32, device=DEV)
+        m2.mixer_decode_step(to_dev(np.ascontiguousarray(inp["xBC"][:, t])), to_dev(inp["conv_w"]), cs,
+                             to_dev(np.ascontiguousarray(inp["dt"][:, t])), to_dev(inp["A"]), to_dev(inp["D"]), st, y,
+                             ws, conv_b=to_dev(inp["conv_b"]), z=to_dev(np.ascontiguousarray(inp["z"][:, t])),
+                             norm_w=to_dev(inp["norm_w"]), ngroups=G, dstate=N, norm_group=512)
+        ys.append(y)
+    torch.cuda.synchronize()
+    y = torch.stack(ys, 1).cpu().numpy()
+    out_r, h_r, cs_r = oracle.mixer_core(inp["xBC"], inp["conv_w"], inp["conv_b"], inp["dt"], inp["A"], inp["D"],
+                                         inp["z"], inp["norm_w"], H, 64, G, N, 512, conv_state=cs0, h0=h0)
+    ey, es = out_err(y, out_r, 512, H), slice_err(st.cpu().numpy(), h_r, 2)
+    say(f"[mixer decode] f32 I/O: out err {ey:.3e} state err {es:.3e}")
+    assert ey <= Y_TOL and es <= S_TOL
+    assert np.array_equal(cs.cpu().numpy().astype(np.float64), cs_r)
+
+
 def test_window_then_mixer_decode_continues_the_window():
     # a window of 300 tokens through the window entry, then 4 fused steps from
     # its conv history and state: the outputs are those of a 304-token window

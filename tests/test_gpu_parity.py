@@ -177,6 +177,31 @@ def test_packed_windows_match_oracle(segments):
     assert np.array_equal(hT[2], h0[2])
 
 
+def test_packed_sequence_longer_than_seqlen_is_cut():
+    # dims.seqlen bounds every length: a longer packed sequence is processed
+    # for its first seqlen tokens and its later rows are left untouched
+    lens = [300, 500]
+    inp = rand_window(91, 2, 500, 4, 64, 1)
+    x, dt, Bm, Cm = (to_dev(pack_rows(inp[k], lens)) for k in ("x", "dt", "B", "C"))
+    T = sum(lens)
+    y = torch.full((T, 4 * 64), 12345.0, dtype=torch.float16, device=DEV)
+    hT = torch.empty((2, 4, 64, 64), dtype=torch.float32, device=DEV)
+    dims = m2.make_dims(2, 400, 4, 64, 64, 1, 256, packed_tokens=T)
+    ws = m2.alloc_workspace(dims, DEV)
+    say("[packed] second sequence cut at seqlen 400")
+    m2.conv_scan_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=x, B=Bm, C=Cm, state_out=hT,
+                        cu_seqlens=to_dev(cu_of(lens)), max_seqlen=400)
+    torch.cuda.synchronize()
+    yp, hT = y.cpu().numpy(), hT.cpu().numpy()
+    assert np.all(yp[300 + 400:] == np.float16(12345.0))
+    sub = {k: (v[1:2, :400] if v.ndim > 1 else v) for k, v in inp.items()}
+    yr, hr = oracle_window(sub)
+    ey = slice_err(np.transpose(yp[300:700].reshape(1, 400, 4, 64), (0, 2, 1, 3)), np.transpose(yr, (0, 2, 1, 3)), 2)
+    es = slice_err(hT[1:2], hr, 2)
+    say(f"[packed] cut sequence: y {ey:.3e} state {es:.3e}")
+    assert ey <= Y_TOL and es <= S_TOL
+
+
 def test_packed_batched_windows_equal_padded_bit_for_bit():
     # eight windows of the layer shape packed back to back (7 x 2048 + 1955
     # rows): only the row addressing differs from the padded call
