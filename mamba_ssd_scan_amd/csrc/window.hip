@@ -67,6 +67,19 @@ constexpr int kCtrlGen = 9 * kCtrlStride;
 constexpr int kCtrlErr = 10 * kCtrlStride;
 constexpr int kCtrlBytes = 11 * kCtrlStride * 4;
 
+// The dt softplus of a raw dt in binary32 with the hardware exponential and
+// logarithm: v above 20, e (1 - e/2) for e = exp(v) below 1e-3 (the series of
+// log1p, error below e^3/3), else log(1 + e) (relative error below about
+// 6e-5, from rounding 1 + e).  The window scan only needs dt within its
+// tolerance; the double-precision form of the decode contract would keep its
+// constants in registers across the whole scan.
+__device__ __forceinline__ float dt_softplus_fast(float raw, float bias) {
+  const float v = raw + bias;
+  const float e = __expf(v);
+  const float sp = e < 1e-3f ? e * (1.f - 0.5f * e) : __logf(1.f + e);
+  return v > 20.f ? v : sp;
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() would also wait for
 // every outstanding global load, which would drain the loads prefetched for
 // the next step at each barrier.
@@ -513,7 +526,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((cc * a.Q + i) * a.H) * ES) : 0.f;
       // a raw dt goes through the softplus; tokens past the sequence keep
       // dt = 0 (the state passes through them unchanged)
-      if (a.dt_sp) d[e] = i < a.Q && cc * a.Q + i < len ? dt_softplus(d[e], dtb) : 0.f;
+      if (a.dt_sp) d[e] = i < a.Q && cc * a.Q + i < len ? dt_softplus_fast(d[e], dtb) : 0.f;
     }
   };
   auto scan_dt = [&](const float (&d)[4]) {
