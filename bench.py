@@ -142,8 +142,8 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the scan shards by sequence and head with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the scan shards by sequence and by head group with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
