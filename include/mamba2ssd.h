@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 5
+#define MAMBA2_ABI_VERSION 6
 
 enum {
     MAMBA2_OK = 0,
@@ -100,7 +100,12 @@ typedef struct mamba2_dims {
  *   conv_width == 0:  x (B,L,H,P) io;  B, C (B,L,G,N) io
  *   conv_width == 4:  xBC (B,L,H*P+2*G*N) io, raw pre-conv activations with
  *                     channel order x | B | C (x channel h*P+p, B/C channel
- *                     g*N+n); conv_w (H*P+2*G*N, 4) f32 with tap 3 applied to
+ *                     g*N+n).  xBC_ld: elements between consecutive tokens'
+ *                     rows of xBC, 0 for dense rows (H*P+2*G*N); a larger
+ *                     stride reads xBC as a slice of wider rows (such as the
+ *                     input projection's output) without a copy, and must
+ *                     keep every row 16-byte aligned;
+ *                     conv_w (H*P+2*G*N, 4) f32 with tap 3 applied to
  *                     the current token and tap 3-k to the token k back;
  *                     conv_b (H*P+2*G*N) f32 or NULL (zero);
  *                     conv_state_in (B, H*P+2*G*N, 3) io or NULL (zero history,
@@ -148,6 +153,7 @@ typedef struct mamba2_window_io {
     void* y;
     const float* dt_bias;
     const int32_t* cu_seqlens;
+    int64_t xBC_ld;
 } mamba2_window_io;
 
 /* Workspace size for a window call with these dims (host only, no GPU call).

@@ -49,7 +49,8 @@ class Dims(ctypes.Structure):
 class _WindowIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "B", "C", "xBC", "conv_w", "conv_b", "conv_state_in", "conv_state_out", "dt", "A", "D",
-        "state_in", "state_out", "seqlens", "z", "norm_w", "y", "dt_bias", "cu_seqlens")]
+        "state_in", "state_out", "seqlens", "z", "norm_w", "y", "dt_bias", "cu_seqlens")] + [
+        ("xBC_ld", ctypes.c_int64)]
 
 
 class _MixerDecodeIO(ctypes.Structure):
@@ -133,6 +134,24 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _rows(t):
+    """(pointer, row stride) of a tensor whose rows may be a slice of wider
+    rows: the last dimension contiguous and the leading dimensions dense in
+    units of the row stride."""
+    if t is None:
+        return None, 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if t.is_contiguous():
+        return t.data_ptr(), 0
+    ld = t.stride(-2)
+    if t.stride(-1) != 1 or ld < t.shape[-1] or (t.dim() == 3 and t.stride(0) != t.shape[1] * ld):
+        raise ValueError("xBC must have contiguous channels and evenly strided token rows")
+    return t.data_ptr(), ld
+
+
 def _stream(t, stream):
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
@@ -186,8 +205,10 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
     (B,L,H*P+2*G*N) with conv_w (H*P+2*G*N, 4) for the fused conv --, dt
     (B,L,H), A/D (H) f32, y (B,L,H*P) (or (B,L,H,P)).  Packed windows: every
     per-token tensor has T rows in place of (B,L), with cu_seqlens (B+1)
-    int32 row offsets and max_seqlen the longest length.  See
-    include/mamba2ssd.h."""
+    int32 row offsets and max_seqlen the longest length.  xBC may be a
+    column slice of wider rows (e.g. ``zxbcdt[..., a:b]`` of the input
+    projection's output): contiguous channels, rows a fixed stride apart,
+    16-byte aligned.  See include/mamba2ssd.h."""
     Bsz, L, H, T = _window_shape(dt, cu_seqlens, max_seqlen)
     conv = xBC is not None
     if conv:
@@ -200,9 +221,10 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
         G, N = B.shape[-2], B.shape[-1]
     dims = make_dims(Bsz, L, H, P, N, G, chunk, 4 if conv else 0, norm_group, _io_dtype(dt), F32, norm_eps,
                      segments, int(bool(dt_softplus)), T)
-    io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), _ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in),
+    xp, xld = _rows(xBC)
+    io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), xp, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in),
                    _ptr(conv_state_out), _ptr(dt), _ptr(A), _ptr(D), _ptr(state_in), _ptr(state_out),
-                   _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y), _ptr(dt_bias), _ptr(cu_seqlens))
+                   _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y), _ptr(dt_bias), _ptr(cu_seqlens), xld)
     _check("mamba2_conv_scan_window",
            load_library().mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
                                                   workspace.numel(), _stream(dt, stream)))

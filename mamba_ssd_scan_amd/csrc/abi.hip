@@ -185,6 +185,13 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
   // packed layout: row offsets instead of lengths
   if ((d->packed_tokens > 0) != (io->cu_seqlens != nullptr) || (io->cu_seqlens && io->seqlens))
     return MAMBA2_EINVAL;
+  // xBC rows: dense, or a stride of at least conv_dim that keeps rows 16-byte aligned
+  const size_t xld = d->conv_width == 4 && io->xBC_ld > 0 ? (size_t)io->xBC_ld : conv_dim;
+  if (d->conv_width == 4 && io->xBC_ld < 0) return MAMBA2_EINVAL;
+  if (d->conv_width == 4 && io->xBC_ld > 0) {
+    if ((size_t)io->xBC_ld < conv_dim || io->xBC_ld > ((int64_t)1 << 40)) return MAMBA2_EINVAL;
+    if ((xld * es) % 16) return MAMBA2_EALIGN;
+  }
   // alignment
   const void* vec[] = {io->x, io->B, io->C, io->xBC, io->z, io->y, io->state_in, io->state_out, io->conv_w,
                        io->norm_w};
@@ -205,7 +212,7 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
   Range ins[] = {rng(io->x, d->conv_width ? 0 : tok * H * P * es),
                  rng(io->B, d->conv_width ? 0 : tok * G * N * es),
                  rng(io->C, d->conv_width ? 0 : tok * G * N * es),
-                 rng(io->xBC, d->conv_width ? tok * conv_dim * es : 0),
+                 rng(io->xBC, d->conv_width ? ((tok - 1) * xld + conv_dim) * es : 0),
                  rng(io->conv_w, d->conv_width ? conv_dim * 4 * 4 : 0),
                  rng(io->conv_b, d->conv_width ? conv_dim * 4 : 0),
                  rng(io->conv_state_in, d->conv_width ? Bsz * conv_dim * 3 * es : 0),

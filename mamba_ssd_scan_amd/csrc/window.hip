@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
                                                         const float* __restrict__ bias, const IO* __restrict__ cs_in,
                                                         IO* __restrict__ cs_out, const int* __restrict__ seqlens,
                                                         const int* __restrict__ cu, IO* __restrict__ out, int B,
-                                                        int L, int T, int Cd) {
+                                                        int L, int T, int Cd, long long ld) {
   const int nch = Cd / 8, ntt = (L + kConvTT - 1) / kConvTT;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)B * ntt * nch) return;
@@ -149,13 +149,13 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
   const int len = span.len;
   // an empty sequence reads (and discards) row 0: its own first row may be
   // the end of a packed tensor
-  const IO* src = xBC + (size_t)(len > 0 ? span.base : 0) * Cd + c0;
+  const IO* src = xBC + (size_t)(len > 0 ? span.base : 0) * (size_t)ld + c0;
   // Row t >= 0 of these channels, zero at or past the length.  The address is
   // clamped into the sequence and the zero applied by a select, so the loads
   // carry no branch and a whole batch is in flight at once.
   const int tmax = len > 0 ? len - 1 : 0;
   auto row = [&](int t, Raw8<IO>& v) {
-    v.load(src + (size_t)min(t, tmax) * Cd);
+    v.load(src + (size_t)min(t, tmax) * (size_t)ld);
     if (t >= len) v.zero();
   };
   Raw8<IO> h[3], cur[kConvRB], nxt[kConvRB];              // h: the 3 raw rows before the batch
@@ -1126,7 +1126,8 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     const long long threads = (long long)d.batch * ((d.seqlen + kConvTT - 1) / kConvTT) * (cd / 8);
     conv_silu_kernel<IO><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(
         (const IO*)io_.xBC, io_.conv_w, io_.conv_b, (const IO*)io_.conv_state_in, (IO*)io_.conv_state_out,
-        io_.seqlens, io_.cu_seqlens, xc, d.batch, d.seqlen, d.packed_tokens, cd);
+        io_.seqlens, io_.cu_seqlens, xc, d.batch, d.seqlen, d.packed_tokens, cd,
+        io_.xBC_ld > 0 ? io_.xBC_ld : (long long)cd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.x = xc;

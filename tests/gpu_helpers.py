@@ -76,9 +76,20 @@ def run_requant(inp, seqlens=None, state_in=None, y_fill=None):
     return y.cpu().numpy().reshape(Bsz, L, H, P), hT.cpu().numpy()
 
 
+def projection_rows(xbc, lead, tail):
+    """xBC as the column slice [lead, lead + Cn) of wider rows, the columns
+    around it NaN, so that a read outside the slice shows in the output."""
+    Cn = xbc.shape[-1]
+    wide = torch.full(xbc.shape[:-1] + (lead + Cn + tail,), float("nan"), dtype=xbc.dtype, device=xbc.device)
+    wide[..., lead:lead + Cn] = xbc
+    return wide[..., lead:lead + Cn]
+
+
 def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=None, state_in=None,
-              want_conv_state=True, segments=0):
+              want_conv_state=True, segments=0, xbc_in_rows=None):
     xBC = to_dev(inp["xBC"])
+    if xbc_in_rows is not None:
+        xBC = projection_rows(xBC, *xbc_in_rows)
     Bsz, L, Cn = inp["xBC"].shape
     y = torch.empty((Bsz, L, H * P), dtype=xBC.dtype, device=DEV)
     hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=DEV)

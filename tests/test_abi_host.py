@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = m2.load_library()
-    assert m2.abi_version() == 5
+    assert m2.abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.mamba2_status_str(code)
     assert lib.mamba2_status_str(77) == b"unknown status"
@@ -143,6 +143,20 @@ def test_packed_layout_validation_codes():
     assert m2.window_workspace_bytes(packed) == m2.window_workspace_bytes(layer_dims(batch=4))
 
 
+def test_xbc_row_stride_validation_codes():
+    # xBC as a slice of wider rows: at least conv_dim (10240) elements apart,
+    # 16-byte aligned rows; the stride sets the range checked for overlaps
+    MB = 1 << 26
+    conv = layer_dims(conv_width=4)
+    io = lambda **kw: window_io(x=None, B=None, C=None, xBC=FAKE + 6 * MB, conv_w=FAKE + 5 * MB, **kw)
+    assert call_window(io(xBC_ld=10239), dims=conv) == -1
+    assert call_window(io(xBC_ld=-1), dims=conv) == -1
+    assert call_window(io(xBC_ld=1 << 41), dims=conv) == -1
+    assert call_window(io(xBC_ld=10244), dims=conv) == -3       # 20488-byte rows
+    # 2048 rows of 4 x 10240 elements from 6 x 64 MiB reach y at 8 x 64 MiB
+    assert call_window(io(xBC_ld=40960), dims=conv) == -1
+
+
 def call_requant(io, dims=None):
     lib = m2.load_library()
     dims = dims or layer_dims()
@@ -244,12 +258,13 @@ def test_scan_grad_validation_codes():
     for kw, code in ((dict(conv_width=4), -2), (dict(norm_group=8192), -2), (dict(packed_tokens=100), -2),
                      (dict(headdim=32), -2), (dict(dstate=96), -2), (dict(seqlen=0), -1)):
         assert lib.mamba2_scan_grad_workspace_bytes(ctypes.byref(layer_dims(**kw)), ctypes.byref(n)) == code, kw
-    # per-head dB and dC, then e per (token, head) and four per-(sequence, head) scalars
+    # per-head dB and dC, then e and q per (token, head) and four per-(sequence, head) scalars
     up = lambda v: (v + 255) // 256 * 256
     L, H, N = 2048, 128, 128
     w = up(L * H * N * 4)
     w = up(w + L * H * N * 4)
-    w = up(w + L * H * 4)
+    for _ in range(2):
+        w = up(w + L * H * 4)
     for _ in range(4):
         w = up(w + H * 4)
     assert m2.scan_grad_workspace_bytes(layer_dims()) == w

@@ -20,7 +20,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
 import mamba_ssd_scan_amd as m2  # noqa: E402
-from tests.gpu_helpers import (DEV, cu_of, pack_rows, run_mixer, run_requant, run_window,  # noqa: E402
+from tests.gpu_helpers import (DEV, cu_of, pack_rows, projection_rows, run_mixer, run_requant, run_window,  # noqa: E402
                                run_window_packed, slice_err, to_dev, unpack_rows)
 
 Y_TOL, S_TOL = 2e-3, 1e-3
@@ -474,6 +474,51 @@ def test_mixer_core_small(norm_group, segments):
     es = slice_err(hT, h_r, 2)
     assert es <= S_TOL, es
     assert np.array_equal(cso.astype(np.float64), cs_r)
+
+
+def test_mixer_core_xbc_slice_of_projection_rows():
+    # xBC read in place from the input projection's rows [z | xBC | dt]: the
+    # same bits as from a dense copy, and nothing read outside the slice
+    H, P, G, N, L, Bsz = 16, 64, 2, 128, 300, 2
+    inp = small_mixer(45, Bsz, L, H, G, N)
+    Cn = H * P + 2 * G * N
+    csi = (np.random.default_rng(46).standard_normal((Bsz, Cn, 3))).astype(np.float16)
+    lens = [300, 157]
+    say(f"[mixer] xBC as columns [{H * P}, {H * P + Cn}) of {2 * H * P + 2 * G * N + H + 8}-wide rows")
+    dense = run_mixer(inp, H, P, G, N, 256, 512, seqlens=lens, conv_state_in=csi)
+    strided = run_mixer(inp, H, P, G, N, 256, 512, seqlens=lens, conv_state_in=csi, xbc_in_rows=(H * P, H + 8))
+    # y rows past a sequence's length are not written
+    for b, n in enumerate(lens):
+        assert np.array_equal(dense[0][b, :n], strided[0][b, :n])
+        assert not np.isnan(strided[0][b, :n]).any()
+    assert np.array_equal(dense[1], strided[1]) and np.array_equal(dense[2], strided[2])
+
+
+def test_packed_mixer_core_xbc_slice_of_projection_rows():
+    H, P, G, N, L = 16, 64, 2, 128, 300
+    lens = [300, 0, 157, 64]
+    s = synth.WindowShape(len(lens), L, H, P, N, G, 256, np.float16, "wide")
+    inp = synth.mixer_inputs(s, 47)
+    Cn = H * P + 2 * G * N
+    T = sum(lens)
+    xBC, dt, z = (to_dev(pack_rows(inp[k], lens)) for k in ("xBC", "dt", "z"))
+    outs = []
+    for x in (xBC, projection_rows(xBC, H * P, H + 24)):
+        y = torch.full((T, H * P), 12345.0, dtype=torch.float16, device=DEV)
+        hT = torch.empty((len(lens), H, P, N), dtype=torch.float32, device=DEV)
+        cso = torch.empty((len(lens), Cn, 3), dtype=torch.float16, device=DEV)
+        dims = m2.make_dims(len(lens), L, H, P, N, G, 256, conv_width=4, norm_group=1024, packed_tokens=T)
+        ws = m2.alloc_workspace(dims, DEV)
+        m2.conv_scan_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=x, conv_w=to_dev(inp["conv_w"]),
+                            conv_b=to_dev(inp["conv_b"]), conv_state_out=cso, state_out=hT, z=z,
+                            norm_w=to_dev(inp["norm_w"]), chunk=256, norm_group=1024, ngroups=G, dstate=N,
+                            headdim=P, cu_seqlens=to_dev(cu_of(lens)), max_seqlen=L)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (y, hT, cso)])
+    say(f"[packed] mixer with xBC in projection rows, lengths {lens}")
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    assert not np.isnan(outs[1][0]).any()
 
 
 def test_mixer_core_full_size_sampled():
