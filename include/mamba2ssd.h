@@ -103,8 +103,10 @@ typedef struct mamba2_dims {
  *                     g*N+n).  xBC_ld: elements between consecutive tokens'
  *                     rows of xBC, 0 for dense rows (H*P+2*G*N); a larger
  *                     stride reads xBC as a slice of wider rows (such as the
- *                     input projection's output) without a copy, and must
- *                     keep every row 16-byte aligned;
+ *                     input projection's output) without a copy.  A
+ *                     negative stride or one below H*P+2*G*N is
+ *                     MAMBA2_EINVAL, rows not 16-byte aligned MAMBA2_EALIGN;
+ *                     the field is ignored without the fused conv;
  *                     conv_w (H*P+2*G*N, 4) f32 with tap 3 applied to
  *                     the current token and tap 3-k to the token k back;
  *                     conv_b (H*P+2*G*N) f32 or NULL (zero);
