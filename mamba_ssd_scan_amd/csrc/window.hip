@@ -29,7 +29,7 @@ namespace m2 {
 
 constexpr int kP = 64;                     // head dim
 constexpr unsigned kSpinLimit = 1u << 22;  // bounded waits: an error flag instead of a hang
-constexpr int kNormParts = 2;              // partial sums of g^2 per (token, head): one per head half
+constexpr int kNormParts = 2;              // partial sums of g^2 per (token, head) handed to the norm finish
 
 template <typename IO> struct WinArgs {
   int B, L, H, G, Q, nchunks;
@@ -43,8 +43,6 @@ template <typename IO> struct WinArgs {
   const float* state_in;
   float* state_out;
   const int* seqlens;
-  const IO* z;
-  float* normsum;     // (B, L, H, kNormParts) partial sums of g^2 (norm epilogue)
   IO* y;
   unsigned* ctrl;     // per-partition claim counters, done counter, generation, error
   unsigned long long* flags;   // per item: decay bits << 32 | generation tag | 1 once its aggregate is published
@@ -375,9 +373,8 @@ template <int N> __device__ __forceinline__ int ncol(int nt, int j) {
 }
 }  // namespace wv
 
-static_assert(kNormParts >= 2, "one g^2 partial per head half");
 
-template <typename IO, int N, bool NORM>
+template <typename IO, int N>
 __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<IO> a) {
   using namespace wv;
   constexpr unsigned ES = sizeof(IO);
@@ -473,27 +470,9 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   _Float16* const smc = sm.u.t.c;
 
   // ---- per-step operands ---------------------------------------------------
-  // the norm gate's z rows of this wave (output pass only): 4 values per
-  // (p-tile, t-tile), raw I/O bits
-  typedef typename std::conditional<sizeof(IO) == 2, u2, u4>::type zraw_t;
-  constexpr int ZN = NORM ? 1 : 0;
-  struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; zraw_t z[ZN ? PT : 1][2]; };
-  rsrc_t rz = ry;
-  if constexpr (NORM) rz = mkr(a.z + seq_y, yspan);
+  struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; };
   auto fetch = [&](XB& r, int tok0, bool with_c) {   // the step starting at token tok0
     const unsigned tok = (unsigned)tok0;
-    if constexpr (NORM) {
-      if (with_c) {
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-          for (int T = 0; T < 2; ++T) {
-            const unsigned off = (tok + 16 * T + lr) * yrow + (unsigned)(16 * pt + 4 * q) * ES;
-            if constexpr (sizeof(IO) == 2) r.z[pt][T] = __builtin_amdgcn_raw_buffer_load_b64(rz, off, 0, 0);
-            else r.z[pt][T] = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
-          }
-      }
-    }
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
       const int s = (lane >> 2) + 16 * k, pc = lane & 3;   // token, 16-byte column chunk
@@ -825,13 +804,6 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     const float Sj_start = j ? Sw[i0 - 1] : 0.f;
     const float Sj_end = Sw[i0 + TS - 1];
     stage(xb, j, Sj_end, true);
-    zraw_t zc[ZN ? PT : 1][2];                            // this step's z, before the prefetch reuses xb
-    if constexpr (NORM) {
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-        for (int T = 0; T < 2; ++T) zc[pt][T] = xb.z[pt][T];
-    }
     lds_barrier();
     if (j + 1 < Jv) fetch(xb, t0 + (j + 1) * TS, true);
     else if (more) fetch(xb, t0 + a.Q, true);
@@ -872,7 +844,6 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       float sc[2];
 #pragma unroll
       for (int T = 0; T < 2; ++T) sc[T] = ex2(Sw[i0 + 16 * T + lr] - Sj_start);
-      float gsq[2] = {0.f, 0.f};
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
         // diagonal: sum_s x[s, p] M[s, t]; x rows s = 4q..4q+3 and 16+4q..16+4q+3
@@ -900,39 +871,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           f4 out;
 #pragma unroll
           for (int i = 0; i < 4; ++i) out[i] = __builtin_fmaf(sc[T], yr[i], yd[i]) + Dh * (float)xr[i];
-          if constexpr (NORM) {
-            f4 zz;
-            if constexpr (sizeof(IO) == 2) {
-              const h4 zh = __builtin_bit_cast(h4, zc[pt][T]);
-              zz = f4{(float)zh[0], (float)zh[1], (float)zh[2], (float)zh[3]};
-            } else {
-              zz = __builtin_bit_cast(f4, zc[pt][T]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // SiLU(z) with the hardware reciprocal (about 1 ulp of binary32)
-              out[i] = out[i] * (zz[i] * __builtin_amdgcn_rcpf(1.f + __expf(-zz[i])));
-              gsq[T] += out[i] * out[i];
-            }
-          }
           st4<IO>(ry, off, out);
-        }
-      }
-      if constexpr (NORM) {
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-          float v = gsq[T];
-          v += __shfl_xor(v, 16, 64);
-          v += __shfl_xor(v, 32, 64);
-          const int tl = 16 * T + lr;
-          if (q == 0 && t0 + i0 + tl < len) {
-            const size_t tok = (size_t)b * a.L + t0 + i0 + tl;
-            a.normsum[(tok * a.H + h) * kNormParts + half] = v;
-            if (half == 0) {
-#pragma unroll
-              for (int k = 2; k < kNormParts; ++k) a.normsum[(tok * a.H + h) * kNormParts + k] = 0.f;
-            }
-          }
         }
       }
       // running state for the next step: R <- e^{S_end_j - S_start_j} R + sum_s w_s B_s x_s
@@ -971,10 +910,11 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   }
 }
 
-// Gated RMSNorm finish: out = g * rsqrt(mean_group(g^2) + eps) * w, with the
-// partial sums of g^2 (one per head half) produced by the scan's epilogue.
-// One block per token: the partials of a norm group are summed in LDS (a
-// whole wave at a time when a group spans at least 64 partials), then every
+// Gated RMSNorm finish from partial sums: out = g * rsqrt(mean_group(g^2) +
+// eps) * w, where y already holds g and the kNormParts partial sums of g^2 per
+// (token, head) come from the kernel that produced g (the one-token mixer
+// step).  One block per token: the partials of a norm group are summed in LDS
+// (a whole wave at a time when a group spans at least 64 partials), then every
 // channel is rescaled in place.
 template <typename IO>
 __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, const float* __restrict__ normsum,
@@ -1021,6 +961,95 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
 // The norm finish over ntok independent tokens of H*P channels, with the
 // partial sums laid out as the scan epilogue writes them ((token, head,
 // kNormParts)); the one-token mixer step uses it with one token per sequence.
+// Gated RMSNorm of the window's outputs, one block per (padded) token: g =
+// y * SiLU(z) over the token's C = H*P channels, out = g * rsqrt(mean of g^2
+// over its norm group + eps) * w, written over y.  A thread takes 8 channels
+// at a time, 2048 channels apart; the first kGateRegs of its runs keep g in
+// registers between the sums and the rescale, later runs (C above 8192)
+// recompute g from y and z, which the block has not yet overwritten.  The
+// sums of g^2 are reduced per wave (a group spans whole 512-channel wave
+// runs) or per 8 lanes (every group is whole heads of 64 channels), then
+// added in LDS.  Rows past a sequence's length are left untouched.
+constexpr int kGateRegs = 4;
+template <typename IO>
+__device__ __forceinline__ void gate8(const IO* y, const IO* z, float (&g)[8]) {
+  float v[8], u[8];
+  io<IO>::load8(y, v);
+  io<IO>::load8(z, u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) g[e] = v[e] * (u[e] * __builtin_amdgcn_rcpf(1.f + __expf(-u[e])));
+}
+template <typename IO>
+__global__ __launch_bounds__(256) void gate_norm_kernel(IO* __restrict__ y, const IO* __restrict__ z,
+                                                        const float* __restrict__ nw, const int* __restrict__ seqlens,
+                                                        const int* __restrict__ cu, int L, int T, int C, int group,
+                                                        float eps) {
+  __shared__ float gs[256];
+  const int tok = blockIdx.x, b = tok / L, t = tok - b * L;   // (sequence, token) of the padded index
+  const SeqRows span = seq_rows(seqlens, cu, b, L, T);
+  if (t >= span.len) return;
+  const int ngr = C / group, lane = threadIdx.x & 63;
+  for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = 0.f;
+  __syncthreads();
+  const size_t row = (size_t)(span.base + t) * C;
+  IO* const yr = y + row;
+  const IO* const zr = z + row;
+  const bool wave_runs = group % 512 == 0;
+  auto add = [&](int c0, const float (&g)[8]) {   // every lane of the wave calls this together
+    float sq = 0.f;
+    if (c0 < C) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq = __builtin_fmaf(g[e], g[e], sq);
+    }
+    sq += __shfl_xor(sq, 1, 64);
+    sq += __shfl_xor(sq, 2, 64);
+    sq += __shfl_xor(sq, 4, 64);
+    if (wave_runs) {
+      sq += __shfl_xor(sq, 8, 64);
+      sq += __shfl_xor(sq, 16, 64);
+      sq += __shfl_xor(sq, 32, 64);
+      if (lane == 0 && c0 < C) atomicAdd(&gs[c0 / group], sq);
+    } else if ((lane & 7) == 0 && c0 < C) {
+      atomicAdd(&gs[c0 / group], sq);
+    }
+  };
+  float g[kGateRegs][8];
+#pragma unroll
+  for (int k = 0; k < kGateRegs; ++k) {
+    const int c0 = (int)threadIdx.x * 8 + 2048 * k;
+    if (c0 < C) gate8<IO>(yr + c0, zr + c0, g[k]);
+    add(c0, g[k]);
+  }
+  for (int k = kGateRegs; 2048 * k < C; ++k) {
+    const int c0 = (int)threadIdx.x * 8 + 2048 * k;
+    float gk[8];
+    if (c0 < C) gate8<IO>(yr + c0, zr + c0, gk);
+    add(c0, gk);
+  }
+  __syncthreads();
+  for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = rsqrtf(gs[gi] / (float)group + eps);
+  __syncthreads();
+  auto put = [&](int c0, const float (&gk)[8]) {
+    const float r = gs[c0 / group];
+    const f4 w0 = *reinterpret_cast<const f4*>(nw + c0), w1 = *reinterpret_cast<const f4*>(nw + c0 + 4);
+    f4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { lo[e] = gk[e] * r * w0[e]; hi[e] = gk[4 + e] * r * w1[e]; }
+    io<IO>::store4(yr + c0, lo);
+    io<IO>::store4(yr + c0 + 4, hi);
+  };
+#pragma unroll
+  for (int k = 0; k < kGateRegs; ++k) {
+    const int c0 = (int)threadIdx.x * 8 + 2048 * k;
+    if (c0 < C) put(c0, g[k]);
+  }
+  for (int c0 = (int)threadIdx.x * 8 + 2048 * kGateRegs; c0 < C; c0 += 2048) {
+    float gk[8];
+    gate8<IO>(yr + c0, zr + c0, gk);
+    put(c0, gk);
+  }
+}
+
 hipError_t launch_gated_norm_tokens(int io_f16, void* y, const float* normsum, const float* nw, int ntok, int H,
                                     int group, float eps, hipStream_t st) {
   if (ntok <= 0) return hipSuccess;
@@ -1036,7 +1065,7 @@ int norm_parts_per_head() { return kNormParts; }
 
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t ctrl, flags, agg, normsum, convx, total;
+  size_t ctrl, flags, agg, convx, total;
 };
 static WsLayout ws_layout(const mamba2_dims& d) {
   const size_t nchunks = ((size_t)d.seqlen + d.chunk - 1) / d.chunk;
@@ -1047,8 +1076,7 @@ static WsLayout ws_layout(const mamba2_dims& d) {
   w.ctrl = 0;
   w.flags = up(kCtrlBytes);
   w.agg = up(w.flags + items * 8);
-  w.normsum = up(w.agg + items * (size_t)d.dstate * (kP / 2) * 4);
-  w.convx = up(w.normsum + (d.norm_group > 0 ? (size_t)d.batch * d.seqlen * d.nheads * kNormParts * 4 : 0));
+  w.convx = up(w.agg + items * (size_t)d.dstate * (kP / 2) * 4);
   const size_t cd = (size_t)d.nheads * kP + 2 * (size_t)d.ngroups * d.dstate;
   w.total = up(w.convx + (d.conv_width == 4 ? (size_t)d.batch * d.seqlen * cd * es : 0));
   return w;
@@ -1068,7 +1096,7 @@ static int device_cus() {
   return n;
 }
 
-template <typename IO, int N, bool NORM>
+template <typename IO, int N>
 static hipError_t launch_scan(const WinArgs<IO>& a, hipStream_t st) {
   const int hpg = a.H / a.G;
   const long long slots = (long long)a.B * a.G * ((hpg + wv::KH - 1) / wv::KH);   // workgroups per segment index
@@ -1076,7 +1104,7 @@ static hipError_t launch_scan(const WinArgs<IO>& a, hipStream_t st) {
   static int per_cu = 0;
   if (per_cu <= 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ssd_window_group_kernel<IO, N, NORM>, 64 * wv::NWV, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ssd_window_group_kernel<IO, N>, 64 * wv::NWV, 0) !=
             hipSuccess || n <= 0)
       n = 1;
     per_cu = n;
@@ -1096,7 +1124,7 @@ static hipError_t launch_scan(const WinArgs<IO>& a, hipStream_t st) {
   // radix-8 tree.  Otherwise segment levels are staggered in time and
   // aggregate traffic matters more: radix 4.
   b.tree_lg = wgs <= resident ? 3 : 2;
-  ssd_window_group_kernel<IO, N, NORM><<<wgs, 64 * wv::NWV, 0, st>>>(b);
+  ssd_window_group_kernel<IO, N><<<wgs, 64 * wv::NWV, 0, st>>>(b);
   return hipGetLastError();
 }
 
@@ -1115,11 +1143,10 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   a.cu = io_.cu_seqlens;
   a.T = d.packed_tokens;
   a.xpk = io_.cu_seqlens != nullptr && d.conv_width == 0;
-  a.z = (const IO*)io_.z; a.y = (IO*)io_.y;
+  a.y = (IO*)io_.y;
   a.ctrl = (unsigned*)(base + wl.ctrl);
   a.flags = (unsigned long long*)(base + wl.flags);
   a.agg = (float*)(base + wl.agg);
-  a.normsum = (float*)(base + wl.normsum);
   if (d.conv_width == 4) {
     const int cd = d.nheads * kP + 2 * d.ngroups * d.dstate;
     IO* xc = (IO*)(base + wl.convx);
@@ -1139,17 +1166,16 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     a.xstride = d.nheads * kP;
     a.gstride = d.ngroups * d.dstate;
   }
-  const bool norm = d.norm_group > 0;
   hipError_t e;
   switch (d.dstate) {
-    case 16: e = norm ? launch_scan<IO, 16, true>(a, st) : launch_scan<IO, 16, false>(a, st); break;
-    case 64: e = norm ? launch_scan<IO, 64, true>(a, st) : launch_scan<IO, 64, false>(a, st); break;
-    default: e = norm ? launch_scan<IO, 128, true>(a, st) : launch_scan<IO, 128, false>(a, st); break;
+    case 16: e = launch_scan<IO, 16>(a, st); break;
+    case 64: e = launch_scan<IO, 64>(a, st); break;
+    default: e = launch_scan<IO, 128>(a, st); break;
   }
-  if (e != hipSuccess || !norm) return e;
-  gated_norm_kernel<IO><<<(unsigned)(d.batch * d.seqlen), 256, 0, st>>>(
-      (IO*)io_.y, a.normsum, io_.norm_w, io_.seqlens, io_.cu_seqlens, d.seqlen, d.packed_tokens, d.nheads,
-      d.norm_group, d.norm_eps);
+  if (e != hipSuccess || d.norm_group == 0) return e;
+  gate_norm_kernel<IO><<<(unsigned)(d.batch * d.seqlen), 256, 0, st>>>(
+      (IO*)io_.y, (const IO*)io_.z, io_.norm_w, io_.seqlens, io_.cu_seqlens, d.seqlen, d.packed_tokens,
+      d.nheads * kP, d.norm_group, d.norm_eps);
   return hipGetLastError();
 }
 
