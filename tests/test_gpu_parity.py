@@ -476,6 +476,41 @@ def test_mixer_core_small(norm_group, segments):
     assert np.array_equal(cso.astype(np.float64), cs_r)
 
 
+@pytest.mark.parametrize("H,G,group,dtype", [
+    (12, 2, 192, np.float16),     # groups of 3 heads: sums per 8 lanes
+    (12, 2, 64, np.float32),      # one head per group, binary32 I/O
+    (160, 2, 2048, np.float16),   # 10240-channel rows: g recomputed past 8192, sums per wave
+    (160, 2, 640, np.float16),    # 10240-channel rows, sums per 8 lanes
+])
+def test_window_gated_norm_group_shapes(H, G, group, dtype):
+    # the scan with the gated norm on post-conv inputs, against the oracle's
+    # scan followed by its gated RMSNorm; rows past a length keep their canary
+    L, N, P = 100, 16, 64
+    lens = [100, 37]
+    inp = rand_window(60 + H + group, 2, L, H, N, G, dtype=dtype)
+    r = np.random.default_rng(61)
+    z = r.standard_normal((2, L, H * P)).astype(dtype)
+    w = (1.0 + 0.1 * r.standard_normal(H * P)).astype(np.float32)
+    tdt = torch.float16 if dtype == np.float16 else torch.float32
+    y = torch.full((2, L, H * P), 1234.0, dtype=tdt, device=DEV)   # exact in binary16
+    dims = m2.make_dims(2, L, H, P, N, G, 64, norm_group=group, io_dtype=m2.F16 if dtype == np.float16 else m2.F32)
+    ws = m2.alloc_workspace(dims, DEV)
+    say(f"[norm] H={H} G={G} group={group} {np.dtype(dtype).name}")
+    m2.conv_scan_window(to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=to_dev(inp["x"]),
+                        B=to_dev(inp["B"]), C=to_dev(inp["C"]), seqlens=torch.tensor(lens, dtype=torch.int32,
+                                                                                     device=DEV),
+                        z=to_dev(z), norm_w=to_dev(w), chunk=64, norm_group=group)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    yr, _ = oracle.ssd_scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], seqlens=lens)
+    for b, n in enumerate(lens):
+        ref = oracle.gated_rmsnorm(yr[b, :n].reshape(n, H * P), z[b, :n], w, group)
+        e = slice_err(got[b, :n].reshape(n, -1, group).transpose(1, 0, 2), ref.reshape(n, -1, group).transpose(1, 0, 2), 1)
+        say(f"[norm] seq {b}: {e:.3e}")
+        assert e <= Y_TOL
+        assert np.all(got[b, n:] == 1234.0)
+
+
 def test_mixer_core_xbc_slice_of_projection_rows():
     # xBC read in place from the input projection's rows [z | xBC | dt]: the
     # same bits as from a dense copy, and nothing read outside the slice
