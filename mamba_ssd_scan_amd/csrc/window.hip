@@ -362,6 +362,7 @@ template <int N> struct SmG {
   } u;
   alignas(16) float S[NWV][256];       // per wave: running log2-decay from the chunk start (inclusive)
   alignas(16) _Float16 dts[NWV][256];
+  alignas(16) float dtl[KH][256];      // a chunk's dt of the block's heads, as loaded by the whole workgroup
   unsigned ticket, gen;
 };
 
@@ -461,7 +462,9 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   const rsrc_t rb = mkr(a.Bm + seq_g, gspan);
   const rsrc_t rc = mkr(a.Cm + seq_g, gspan);
   const rsrc_t ry = mkr(a.y + seq_y, yspan);
-  const rsrc_t rdt = mkr(a.dt + (size_t)ubase * a.H + h, len > 0 && live ? (unsigned)((len - 1) * a.H + 1) * ES : 0u);
+  // dt of the block's KH heads (the row's last heads bound the range)
+  const int h0 = g * hpg + hblk * KH;
+  const rsrc_t rdt = mkr(a.dt + (size_t)ubase * a.H + h0, len > 0 ? (unsigned)((len - 1) * a.H + (a.H - h0)) * ES : 0u);
   float* const Sw = sm.S[wid];
   _Float16* const dtw = sm.dts[wid];
   _Float16* const xs = sm.u.t.x[wid];
@@ -497,18 +500,35 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 
   // ---- phase 0 (per chunk): dt and the running log2-decay over the chunk --
   // (4 tokens per lane); the dt of the next chunk is loaded while a chunk runs
-  const float dtb = a.dt_sp && a.dt_bias ? a.dt_bias[h] : 0.f;
-  auto load_dt = [&](int cc, float (&d)[4]) {
+  // The workgroup loads a chunk's dt together: thread tid takes head tid % 4
+  // of the block for tokens tid / 4 + 128 e, so the four lanes of a token
+  // read one cache line (a wave-by-wave load of one head each would touch
+  // 64 lines per instruction, eight times over).  scan_dt shares them out.
+  const int dh = tid & 3, dtok = tid >> 2;
+  const float dtbl = a.dt_sp && a.dt_bias ? a.dt_bias[min(h0 + dh, a.H - 1)] : 0.f;
+  auto load_dt = [&](int cc, float (&d)[2]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = dtok + 128 * e;
+      d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((cc * a.Q + i) * a.H + dh) * ES) : 0.f;
+      // a raw dt goes through the softplus; tokens past the sequence keep
+      // dt = 0 (the state passes through them unchanged)
+      if (a.dt_sp) d[e] = i < a.Q && cc * a.Q + i < len ? dt_softplus_fast(d[e], dtbl) : 0.f;
+    }
+  };
+  auto scan_dt = [&](const float (&dl)[2]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = dtok + 128 * e;
+      if (i < a.Q) sm.dtl[dh][i] = dl[e];
+    }
+    __syncthreads();
+    float d[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * lane + e;
-      d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((cc * a.Q + i) * a.H) * ES) : 0.f;
-      // a raw dt goes through the softplus; tokens past the sequence keep
-      // dt = 0 (the state passes through them unchanged)
-      if (a.dt_sp) d[e] = i < a.Q && cc * a.Q + i < len ? dt_softplus_fast(d[e], dtb) : 0.f;
+      d[e] = i < a.Q ? sm.dtl[wid >> 1][i] : 0.f;
     }
-  };
-  auto scan_dt = [&](const float (&d)[4]) {
     float v[4];
     float run = 0.f;
 #pragma unroll
@@ -535,7 +555,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
-  float dtv[4];
+  float dtv[2];
   if (ncv > 0) load_dt(cb, dtv);
 
   // stage step j: B (and C) as read, x as read (phase 3 only) and x weighted
