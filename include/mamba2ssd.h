@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 6
+#define MAMBA2_ABI_VERSION 7
 
 enum {
     MAMBA2_OK = 0,
@@ -129,7 +129,15 @@ typedef struct mamba2_dims {
  *             conv_state_*) keep their (B, ...) shapes.  NULL otherwise.
  *   norm_group == 0: y (B,L,H*P) io receives y.
  *   norm_group  > 0: z (B,L,H*P) io and norm_w (H*P) f32 are required and
- *             y receives the gated RMSNorm output.
+ *             y receives the gated RMSNorm output.  z_ld: elements between
+ *             consecutive tokens' rows of z, 0 for dense rows (H*P); a larger
+ *             stride reads z in place from wider rows (16-byte aligned rows;
+ *             below H*P or negative is MAMBA2_EINVAL, misaligned
+ *             MAMBA2_EALIGN).  Ignored without the norm.
+ *   dt_ld:    elements between consecutive tokens' rows of dt, 0 for dense
+ *             rows (H); a larger stride reads dt in place from wider rows,
+ *             e.g. the last H columns of the input projection's output
+ *             [z | xBC | dt].  Below H or negative is MAMBA2_EINVAL.
  *   ws, ws_bytes: workspace of at least mamba2_window_workspace_bytes()
  *             bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE.  The
  *             library leaves it ready for the next call on the same stream; it
@@ -156,6 +164,8 @@ typedef struct mamba2_window_io {
     const float* dt_bias;
     const int32_t* cu_seqlens;
     int64_t xBC_ld;
+    int64_t z_ld;
+    int64_t dt_ld;
 } mamba2_window_io;
 
 /* Workspace size for a window call with these dims (host only, no GPU call).

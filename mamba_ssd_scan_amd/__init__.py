@@ -50,7 +50,7 @@ class _WindowIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "B", "C", "xBC", "conv_w", "conv_b", "conv_state_in", "conv_state_out", "dt", "A", "D",
         "state_in", "state_out", "seqlens", "z", "norm_w", "y", "dt_bias", "cu_seqlens")] + [
-        ("xBC_ld", ctypes.c_int64)]
+        ("xBC_ld", ctypes.c_int64), ("z_ld", ctypes.c_int64), ("dt_ld", ctypes.c_int64)]
 
 
 class _MixerDecodeIO(ctypes.Structure):
@@ -134,7 +134,7 @@ def _ptr(t):
     return t.data_ptr()
 
 
-def _rows(t):
+def _rows(t, name="xBC"):
     """(pointer, row stride) of a tensor whose rows may be a slice of wider
     rows: the last dimension contiguous and the leading dimensions dense in
     units of the row stride."""
@@ -148,7 +148,7 @@ def _rows(t):
         return t.data_ptr(), 0
     ld = t.stride(-2)
     if t.stride(-1) != 1 or ld < t.shape[-1] or (t.dim() == 3 and t.stride(0) != t.shape[1] * ld):
-        raise ValueError("xBC must have contiguous channels and evenly strided token rows")
+        raise ValueError(f"{name} must have contiguous channels and evenly strided token rows")
     return t.data_ptr(), ld
 
 
@@ -205,10 +205,10 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
     (B,L,H*P+2*G*N) with conv_w (H*P+2*G*N, 4) for the fused conv --, dt
     (B,L,H), A/D (H) f32, y (B,L,H*P) (or (B,L,H,P)).  Packed windows: every
     per-token tensor has T rows in place of (B,L), with cu_seqlens (B+1)
-    int32 row offsets and max_seqlen the longest length.  xBC may be a
-    column slice of wider rows (e.g. ``zxbcdt[..., a:b]`` of the input
-    projection's output): contiguous channels, rows a fixed stride apart,
-    16-byte aligned.  See include/mamba2ssd.h."""
+    int32 row offsets and max_seqlen the longest length.  xBC, z and dt may
+    be column slices of wider rows, e.g. of the input projection's output
+    ``zxbcdt = [z | xBC | dt]``: contiguous channels, rows a fixed stride
+    apart (16-byte aligned for xBC and z).  See include/mamba2ssd.h."""
     Bsz, L, H, T = _window_shape(dt, cu_seqlens, max_seqlen)
     conv = xBC is not None
     if conv:
@@ -222,9 +222,11 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
     dims = make_dims(Bsz, L, H, P, N, G, chunk, 4 if conv else 0, norm_group, _io_dtype(dt), F32, norm_eps,
                      segments, int(bool(dt_softplus)), T)
     xp, xld = _rows(xBC)
+    zp, zld = _rows(z, "z")
+    dp, dld = _rows(dt, "dt")
     io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), xp, _ptr(conv_w), _ptr(conv_b), _ptr(conv_state_in),
-                   _ptr(conv_state_out), _ptr(dt), _ptr(A), _ptr(D), _ptr(state_in), _ptr(state_out),
-                   _ptr(seqlens), _ptr(z), _ptr(norm_w), _ptr(y), _ptr(dt_bias), _ptr(cu_seqlens), xld)
+                   _ptr(conv_state_out), dp, _ptr(A), _ptr(D), _ptr(state_in), _ptr(state_out),
+                   _ptr(seqlens), zp, _ptr(norm_w), _ptr(y), _ptr(dt_bias), _ptr(cu_seqlens), xld, zld, dld)
     _check("mamba2_conv_scan_window",
            load_library().mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
                                                   workspace.numel(), _stream(dt, stream)))
@@ -241,9 +243,10 @@ def requant_window(dt, A, D, y, *, x, B, C, state_in=None, state_out=None, seqle
     G, N = B.shape[-2], B.shape[-1]
     dims = make_dims(Bsz, L, H, P, N, G, 256, 0, 0, _io_dtype(dt), F16, dt_softplus=int(bool(dt_softplus)),
                      packed_tokens=T)
-    io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), None, None, None, None, None, _ptr(dt), _ptr(A), _ptr(D),
+    dp, dld = _rows(dt, "dt")
+    io = _WindowIO(_ptr(x), _ptr(B), _ptr(C), None, None, None, None, None, dp, _ptr(A), _ptr(D),
                    _ptr(state_in), _ptr(state_out), _ptr(seqlens), None, None, _ptr(y), _ptr(dt_bias),
-                   _ptr(cu_seqlens))
+                   _ptr(cu_seqlens), 0, 0, dld)
     _check("mamba2_requant_window", load_library().mamba2_requant_window(ctypes.byref(dims), ctypes.byref(io),
                                                                          _stream(dt, stream)))
 

@@ -192,6 +192,16 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
     if ((size_t)io->xBC_ld < conv_dim || io->xBC_ld > ((int64_t)1 << 40)) return MAMBA2_EINVAL;
     if ((xld * es) % 16) return MAMBA2_EALIGN;
   }
+  // z and dt rows: dense, or strides of at least a row (z rows 16-byte aligned)
+  const size_t zld = d->norm_group > 0 && io->z_ld > 0 ? (size_t)io->z_ld : H * P;
+  if (d->norm_group > 0 && io->z_ld != 0) {
+    if (io->z_ld < 0 || (size_t)io->z_ld < H * P || io->z_ld > ((int64_t)1 << 40)) return MAMBA2_EINVAL;
+    if ((zld * es) % 16) return MAMBA2_EALIGN;
+  }
+  if (io->dt_ld < 0 || (io->dt_ld > 0 && ((size_t)io->dt_ld < H || io->dt_ld > ((int64_t)1 << 40))))
+    return MAMBA2_EINVAL;
+  const size_t dtld = io->dt_ld > 0 ? (size_t)io->dt_ld : H;
+  if ((L - 1) * dtld * es + H * es >= ((size_t)1 << 31)) return MAMBA2_EUNSUPPORTED;   // one sequence's dt rows
   // alignment
   const void* vec[] = {io->x, io->B, io->C, io->xBC, io->z, io->y, io->state_in, io->state_out, io->conv_w,
                        io->norm_w};
@@ -216,9 +226,9 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
                  rng(io->conv_w, d->conv_width ? conv_dim * 4 * 4 : 0),
                  rng(io->conv_b, d->conv_width ? conv_dim * 4 : 0),
                  rng(io->conv_state_in, d->conv_width ? Bsz * conv_dim * 3 * es : 0),
-                 rng(io->dt, tok * H * es), rng(io->A, H * 4), rng(io->D, H * 4),
+                 rng(io->dt, ((tok - 1) * dtld + H) * es), rng(io->A, H * 4), rng(io->D, H * 4),
                  rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4),
-                 rng(io->z, d->norm_group ? tok * H * P * es : 0),
+                 rng(io->z, d->norm_group ? ((tok - 1) * zld + H * P) * es : 0),
                  rng(io->norm_w, d->norm_group ? H * P * 4 : 0),
                  rng(io->dt_bias, d->dt_softplus ? H * 4 : 0), rng(io->cu_seqlens, (Bsz + 1) * 4)};
   const size_t nout = sizeof(outs) / sizeof(outs[0]);
@@ -251,10 +261,13 @@ int32_t mamba2_requant_window(const mamba2_dims* d, const mamba2_window_io* io, 
       ((uintptr_t)io->D & 3) || ((uintptr_t)io->seqlens & 3) || ((uintptr_t)io->dt_bias & 3) ||
       ((uintptr_t)io->cu_seqlens & 3))
     return MAMBA2_EALIGN;
+  if (io->dt_ld < 0 || (io->dt_ld > 0 && ((size_t)io->dt_ld < H || io->dt_ld > ((int64_t)1 << 40))))
+    return MAMBA2_EINVAL;
+  const size_t dtld = io->dt_ld > 0 ? (size_t)io->dt_ld : H;
   const size_t tok = d->packed_tokens > 0 ? (size_t)d->packed_tokens : Bsz * L;
   Range outs[] = {rng(io->y, tok * H * P * es), rng(io->state_out, Bsz * H * P * N * 4)};
   Range ins[] = {rng(io->x, tok * H * P * es), rng(io->B, tok * G * N * es), rng(io->C, tok * G * N * es),
-                 rng(io->dt, tok * H * es),    rng(io->A, H * 4),            rng(io->D, H * 4),
+                 rng(io->dt, ((tok - 1) * dtld + H) * es), rng(io->A, H * 4), rng(io->D, H * 4),
                  rng(io->state_in, Bsz * H * P * N * 4), rng(io->seqlens, Bsz * 4),
                  rng(io->dt_bias, d->dt_softplus ? H * 4 : 0), rng(io->cu_seqlens, (Bsz + 1) * 4)};
   for (const Range& o : outs)

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     const IO* __restrict__ x, const IO* __restrict__ dt, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ state_in,
     float* __restrict__ state_out, const int* __restrict__ seqlens, const int* __restrict__ cu_seqlens,
-    IO* __restrict__ y, int L, int T, int H, int G, int dt_sp, const float* __restrict__ dt_bias) {
+    IO* __restrict__ y, int L, int T, int H, int G, int dt_sp, const float* __restrict__ dt_bias, long long dtld) {
   constexpr int P = 64;
   constexpr int ROWS = RqShape<N>::ROWS, RPT = RqShape<N>::RPT, NTH = RqShape<N>::NTH;
   constexpr int LPR = N / 8;                 // lanes per state row
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     r.d = 0.f;
     if (tid < kRqTB) {
       const int tt = min(t0 + tid, len - 1);
-      r.d = io<IO>::load1(dt + (seqtok + tt) * H + h);
+      r.d = io<IO>::load1(dt + (seqtok + tt) * dtld + h);
       if (dt_sp) r.d = dt_softplus(r.d, dtb);
     }
   };
@@ -289,7 +289,7 @@ static hipError_t launch_rq(const mamba2_dims& d, const mamba2_window_io& io_, h
       (const IO*)io_.x, (const IO*)io_.dt, (const IO*)io_.B, (const IO*)io_.C, io_.A, io_.D, io_.state_in,
       io_.state_out, io_.seqlens, io_.cu_seqlens, (IO*)io_.y, d.seqlen, d.packed_tokens, d.nheads, d.ngroups,
       d.dt_softplus,
-      d.dt_softplus ? io_.dt_bias : nullptr);
+      d.dt_softplus ? io_.dt_bias : nullptr, io_.dt_ld > 0 ? (long long)io_.dt_ld : (long long)d.nheads);
   return hipGetLastError();
 }
 

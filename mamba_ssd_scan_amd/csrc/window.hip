@@ -38,6 +38,7 @@ template <typename IO> struct WinArgs {
   const IO* Cm;       // C rows: token stride gstride elements
   int xstride, gstride;
   const IO* dt;
+  long long dtld;     // dt rows: token stride in elements
   const float* A;
   const float* D;
   const float* state_in;
@@ -464,7 +465,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   const rsrc_t ry = mkr(a.y + seq_y, yspan);
   // dt of the block's KH heads (the row's last heads bound the range)
   const int h0 = g * hpg + hblk * KH;
-  const rsrc_t rdt = mkr(a.dt + (size_t)ubase * a.H + h0, len > 0 ? (unsigned)((len - 1) * a.H + (a.H - h0)) * ES : 0u);
+  const rsrc_t rdt = mkr(a.dt + (size_t)ubase * a.dtld + h0,
+                         len > 0 ? (unsigned)((len - 1) * a.dtld + (a.H - h0)) * ES : 0u);
   float* const Sw = sm.S[wid];
   _Float16* const dtw = sm.dts[wid];
   _Float16* const xs = sm.u.t.x[wid];
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int i = dtok + 128 * e;
-      d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((cc * a.Q + i) * a.H + dh) * ES) : 0.f;
+      d[e] = i < a.Q ? ld1<IO>(rdt, (unsigned)((cc * a.Q + i) * a.dtld + dh) * ES) : 0.f;
       // a raw dt goes through the softplus; tokens past the sequence keep
       // dt = 0 (the state passes through them unchanged)
       if (a.dt_sp) d[e] = i < a.Q && cc * a.Q + i < len ? dt_softplus_fast(d[e], dtbl) : 0.f;
@@ -1003,7 +1005,7 @@ template <typename IO>
 __global__ __launch_bounds__(256) void gate_norm_kernel(IO* __restrict__ y, const IO* __restrict__ z,
                                                         const float* __restrict__ nw, const int* __restrict__ seqlens,
                                                         const int* __restrict__ cu, int L, int T, int C, int group,
-                                                        float eps) {
+                                                        float eps, long long zld) {
   __shared__ float gs[256];
   const int tok = blockIdx.x, b = tok / L, t = tok - b * L;   // (sequence, token) of the padded index
   const SeqRows span = seq_rows(seqlens, cu, b, L, T);
@@ -1011,9 +1013,8 @@ __global__ __launch_bounds__(256) void gate_norm_kernel(IO* __restrict__ y, cons
   const int ngr = C / group, lane = threadIdx.x & 63;
   for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = 0.f;
   __syncthreads();
-  const size_t row = (size_t)(span.base + t) * C;
-  IO* const yr = y + row;
-  const IO* const zr = z + row;
+  IO* const yr = y + (size_t)(span.base + t) * C;
+  const IO* const zr = z + (size_t)(span.base + t) * (size_t)zld;
   const bool wave_runs = group % 512 == 0;
   auto add = [&](int c0, const float (&g)[8]) {   // every lane of the wave calls this together
     float sq = 0.f;
@@ -1159,6 +1160,7 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   a.dt_sp = d.dt_softplus;
   a.dt_bias = d.dt_softplus ? io_.dt_bias : nullptr;
   a.dt = (const IO*)io_.dt; a.A = io_.A; a.D = io_.D;
+  a.dtld = io_.dt_ld > 0 ? (long long)io_.dt_ld : (long long)d.nheads;
   a.state_in = io_.state_in; a.state_out = io_.state_out; a.seqlens = io_.seqlens;
   a.cu = io_.cu_seqlens;
   a.T = d.packed_tokens;
@@ -1195,7 +1197,7 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   if (e != hipSuccess || d.norm_group == 0) return e;
   gate_norm_kernel<IO><<<(unsigned)(d.batch * d.seqlen), 256, 0, st>>>(
       (IO*)io_.y, (const IO*)io_.z, io_.norm_w, io_.seqlens, io_.cu_seqlens, d.seqlen, d.packed_tokens,
-      d.nheads * kP, d.norm_group, d.norm_eps);
+      d.nheads * kP, d.norm_group, d.norm_eps, io_.z_ld > 0 ? (long long)io_.z_ld : (long long)d.nheads * kP);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = m2.load_library()
-    assert m2.abi_version() == 6
+    assert m2.abi_version() == 7
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.mamba2_status_str(code)
     assert lib.mamba2_status_str(77) == b"unknown status"
@@ -90,6 +90,19 @@ def test_workspace_query_rejects(kw, code):
 FAKE = 0x7F0000000000  # never dereferenced: every call below is refused on the host
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0   # counts devices without initialising them
+    except Exception:
+        return False
+
+
+# The refusals below pass placeholder pointers: they run where no GPU is
+# visible, so that a refusal that failed could never launch on them.
+fake_pointers = pytest.mark.skipif(_gpu_visible(), reason="placeholder-pointer calls run only where no GPU is visible")
+
+
 def window_io(**over):
     L, H, P, N, G = 2048, 128, 64, 128, 8
     MB = 1 << 26
@@ -107,6 +120,7 @@ def call_window(io, dims=None, ws=FAKE + (1 << 30), ws_bytes=None):
     return lib.mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), ctypes.c_void_p(ws), ws_bytes, None)
 
 
+@fake_pointers
 def test_window_validation_codes():
     assert call_window(window_io(x=None)) == -1
     assert call_window(window_io(y=None)) == -1
@@ -123,6 +137,7 @@ def test_window_validation_codes():
     assert call_window(window_io(), dims=layer_dims(norm_group=8192)) == -1
 
 
+@fake_pointers
 def test_packed_layout_validation_codes():
     MB = 1 << 26
     packed = layer_dims(batch=4, packed_tokens=5000)
@@ -143,6 +158,7 @@ def test_packed_layout_validation_codes():
     assert m2.window_workspace_bytes(packed) == m2.window_workspace_bytes(layer_dims(batch=4))
 
 
+@fake_pointers
 def test_xbc_row_stride_validation_codes():
     # xBC as a slice of wider rows: at least conv_dim (10240) elements apart,
     # 16-byte aligned rows; the stride sets the range checked for overlaps
@@ -157,12 +173,34 @@ def test_xbc_row_stride_validation_codes():
     assert call_window(io(xBC_ld=40960), dims=conv) == -1
 
 
+@fake_pointers
+def test_z_and_dt_row_stride_validation_codes():
+    # z rows: at least H*P (8192) elements apart, 16-byte aligned; dt rows at
+    # least H (128) apart; a negative stride is invalid
+    MB = 1 << 26
+    norm = layer_dims(norm_group=8192)
+    io = lambda **kw: window_io(z=FAKE + 5 * MB, norm_w=FAKE + 4 * MB + 8192, **kw)
+    assert call_window(io(z_ld=8191), dims=norm) == -1
+    assert call_window(io(z_ld=-8), dims=norm) == -1
+    assert call_window(io(z_ld=8196), dims=norm) == -3        # 16392-byte rows
+    assert call_window(window_io(dt_ld=127)) == -1
+    assert call_window(window_io(dt_ld=-1)) == -1
+    # one sequence's dt rows must stay within 2^31 bytes: 2048 rows of 2^20 elements
+    assert call_window(window_io(dt_ld=1 << 20)) == -2
+    # the stride sets the range checked for overlaps: 2048 rows 120000
+    # elements apart from 3 x 64 MiB run past y at 8 x 64 MiB
+    assert call_window(window_io(dt_ld=120000)) == -1
+    assert call_requant(window_io(dt_ld=127)) == -1
+    assert call_requant(window_io(dt_ld=120000)) == -1
+
+
 def call_requant(io, dims=None):
     lib = m2.load_library()
     dims = dims or layer_dims()
     return lib.mamba2_requant_window(ctypes.byref(dims), ctypes.byref(io), None)
 
 
+@fake_pointers
 def test_requant_window_validation_codes():
     # plain x, B, C only; every refusal happens on the host
     assert call_requant(window_io(), dims=layer_dims(conv_width=4)) == -2
@@ -176,6 +214,7 @@ def test_requant_window_validation_codes():
     assert call_requant(window_io(y=FAKE + 1024)) == -1
 
 
+@fake_pointers
 def test_decode_and_state_validation_codes():
     lib = m2.load_library()
     d = m2.make_dims(64, 1, 128, 64, 128, 8, 256, state_dtype=m2.F16)
@@ -199,6 +238,7 @@ def test_decode_and_state_validation_codes():
                                   None) == -3
 
 
+@fake_pointers
 def test_mixer_decode_validation_codes():
     lib = m2.load_library()
     MB = 1 << 26
@@ -251,6 +291,7 @@ def test_mixer_decode_validation_codes():
     assert call(io(), ws=FAKE + 2 * MB) == -1
 
 
+@fake_pointers
 def test_scan_grad_validation_codes():
     lib = m2.load_library()
     MB = 1 << 26

@@ -529,6 +529,87 @@ def test_mixer_core_xbc_slice_of_projection_rows():
     assert np.array_equal(dense[1], strided[1]) and np.array_equal(dense[2], strided[2])
 
 
+def _projection(parts, pad):
+    """The parts side by side in one tensor of wider rows ([z | xBC | dt] of
+    an input projection, then `pad` NaN columns), and a view of each part."""
+    lead = parts[0].shape[:-1]
+    widths = [p.shape[-1] for p in parts]
+    full = torch.full(lead + (sum(widths) + pad,), float("nan"), dtype=parts[0].dtype, device=DEV)
+    views, c = [], 0
+    for p, w in zip(parts, widths):
+        full[..., c:c + w] = p
+        views.append(full[..., c:c + w])
+        c += w
+    return views
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_mixer_core_reads_z_xbc_dt_in_projection_rows(packed):
+    # the whole mixer core on one projection output [z | xBC | dt]: raw dt
+    # with its bias, conv state in and out, the gated norm; bit for bit the
+    # result of dense copies, with NaN columns around the parts
+    H, P, G, N, L = 16, 64, 2, 128, 300
+    lens = [300, 157, 0, 64] if packed else [300, 157]
+    s = synth.WindowShape(len(lens), L, H, P, N, G, 256, np.float16, "wide")
+    inp = synth.mixer_inputs(s, 91, raw_dt=True)
+    Cn = H * P + 2 * G * N
+    csi = to_dev(np.random.default_rng(92).standard_normal((len(lens), Cn, 3)).astype(np.float16))
+    if packed:
+        z, xBC, dt = (to_dev(pack_rows(inp[k], lens)) for k in ("z", "xBC", "dt"))
+        T = sum(lens)
+        extra = dict(cu_seqlens=to_dev(cu_of(lens)), max_seqlen=L)
+        dims = m2.make_dims(len(lens), L, H, P, N, G, 256, conv_width=4, norm_group=1024, packed_tokens=T)
+        yshape = (T, H * P)
+    else:
+        z, xBC, dt = (to_dev(inp[k]) for k in ("z", "xBC", "dt"))
+        extra = dict(seqlens=torch.tensor(lens, dtype=torch.int32, device=DEV))
+        dims = m2.make_dims(len(lens), L, H, P, N, G, 256, conv_width=4, norm_group=1024)
+        yshape = (len(lens), L, H * P)
+    outs = []
+    for zz, xx, dd in ((z, xBC, dt), tuple(_projection([z, xBC, dt], 24))):
+        y = torch.full(yshape, 1234.0, dtype=torch.float16, device=DEV)
+        hT = torch.empty((len(lens), H, P, N), dtype=torch.float32, device=DEV)
+        cso = torch.empty((len(lens), Cn, 3), dtype=torch.float16, device=DEV)
+        ws = m2.alloc_workspace(dims, DEV)
+        m2.conv_scan_window(dd, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xx, conv_w=to_dev(inp["conv_w"]),
+                            conv_b=to_dev(inp["conv_b"]), conv_state_in=csi, conv_state_out=cso, state_out=hT, z=zz,
+                            norm_w=to_dev(inp["norm_w"]), chunk=256, norm_group=1024, ngroups=G, dstate=N,
+                            headdim=P, dt_softplus=True, dt_bias=to_dev(inp["dt_bias"]), **extra)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (y, hT, cso)])
+    say(f"[mixer] z, xBC and dt in projection rows, packed={packed}, lengths {lens}")
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    assert not np.isnan(outs[1][0]).any()
+    # and the dense run against the oracle
+    out_r, h_r, _ = oracle.mixer_core(inp["xBC"], inp["conv_w"], inp["conv_b"], inp["dt"], inp["A"], inp["D"],
+                                      inp["z"], inp["norm_w"], H, P, G, N, 1024, conv_state=csi.cpu().numpy(),
+                                      seqlens=lens, dt_bias=inp["dt_bias"], dt_softplus_raw=True)
+    yd = unpack_rows(outs[0][0], lens, L) if packed else outs[0][0]
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        e = slice_err(yd[b, :n].reshape(n, -1, 1024).transpose(1, 0, 2), out_r[b, :n].reshape(n, -1, 1024).transpose(1, 0, 2), 1)
+        assert e <= Y_TOL, (b, e)
+    assert slice_err(outs[0][1], h_r, 2) <= S_TOL
+
+
+def test_requant_window_reads_dt_in_wider_rows():
+    inp = rand_window(93, 2, 300, 8, 128, 2)
+    dense = run_requant(inp, seqlens=[300, 190])
+    x, Bm, Cm = (to_dev(inp[k]) for k in ("x", "B", "C"))
+    dt = _projection([to_dev(inp["dt"])], 40)[0]
+    y = torch.empty((2, 300, 8 * 64), dtype=torch.float16, device=DEV)
+    hT = torch.empty((2, 8, 64, 128), dtype=torch.float32, device=DEV)
+    m2.requant_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, x=x, B=Bm, C=Cm, state_out=hT,
+                      seqlens=torch.tensor([300, 190], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    say("[requant] dt read from 48-column rows")
+    got = y.cpu().numpy().reshape(2, 300, 8, 64)
+    assert np.array_equal(got[0], dense[0][0]) and np.array_equal(got[1, :190], dense[0][1, :190])
+    assert np.array_equal(hT.cpu().numpy(), dense[1])
+
+
 def test_packed_mixer_core_xbc_slice_of_projection_rows():
     H, P, G, N, L = 16, 64, 2, 128, 300
     lens = [300, 0, 157, 64]
