@@ -141,7 +141,7 @@ static int32_t check_window(const mamba2_dims* d) {
   if (d->conv_width != 0 && d->conv_width != 4) return MAMBA2_EUNSUPPORTED;
   if (d->norm_group < 0) return MAMBA2_EINVAL;
   if (d->norm_group > 0 && (d->nheads * d->headdim) % d->norm_group != 0) return MAMBA2_EINVAL;
-  // the norm epilogue reduces whole heads: a group must be a multiple of P
+  // the norm kernels sum whole heads: a group must be a multiple of P
   if (d->norm_group > 0 && d->norm_group % d->headdim != 0) return MAMBA2_EUNSUPPORTED;
   if (d->norm_group > 0 && !(d->norm_eps >= 0.f)) return MAMBA2_EINVAL;
   // the norm finish keeps one scale per group of a token in LDS (256 slots)

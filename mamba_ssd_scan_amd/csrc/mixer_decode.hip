@@ -25,10 +25,10 @@
 // workspace, after every head has read it; the counter wraps back to zero for
 // the next call.
 //
-// The norm spans norm_group / P heads, that is several workgroups.  As in the
-// window scan's epilogue, each head writes g = y silu(z) into y (I/O type)
-// and the sums of g^2 over its two halves; the window path's norm kernel then
-// finishes every sequence's token on the same stream.  (Finishing inside this
+// The norm spans norm_group / P heads, that is several workgroups.  Each head
+// writes g = y silu(z) into y (I/O type) and the sums of g^2 over its two
+// halves; the norm-finish kernel of the window source then finishes every
+// sequence's token on the same stream.  (Finishing inside this
 // kernel, by the last head of each norm group, needs every head to wait for
 // its stores and an atomic before it retires; measured at 64 sequences that
 // costs more than the second launch.)

@@ -1,5 +1,5 @@
 // Whole-window Mamba-2 scan in its chunked state-space-dual form, with an
-// optional causal conv1d(4)+SiLU prologue and a gated-RMSNorm epilogue.
+// optional causal conv1d(4)+SiLU before it and a gated RMSNorm after it.
 //
 // The method is Mamba-2 / structured state-space duality (Dao and Gu 2024,
 // listed under "References" on page "Mamb2_8B_FP4_Recall_SQ3.25").  For one
@@ -19,7 +19,10 @@
 //    written to a workspace copy in the xBC layout; it also writes the conv
 //    state out;
 //  * ssd_window_group_kernel: the chunked scan (see the comment above it);
-//  * gated_norm_kernel: the RMS finish of the gated norm.
+//  * gate_norm_kernel: the gated RMSNorm of the window's outputs, one
+//    streaming pass over y and z;
+//  * gated_norm_kernel: the norm finish from per-head partial sums, for the
+//    one-token mixer step.
 #include <type_traits>
 
 #include "common.h"
@@ -980,9 +983,6 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
   }
 }
 
-// The norm finish over ntok independent tokens of H*P channels, with the
-// partial sums laid out as the scan epilogue writes them ((token, head,
-// kNormParts)); the one-token mixer step uses it with one token per sequence.
 // Gated RMSNorm of the window's outputs, one block per (padded) token: g =
 // y * SiLU(z) over the token's C = H*P channels, out = g * rsqrt(mean of g^2
 // over its norm group + eps) * w, written over y.  A thread takes 8 channels
@@ -1071,6 +1071,9 @@ __global__ __launch_bounds__(256) void gate_norm_kernel(IO* __restrict__ y, cons
   }
 }
 
+// The norm finish over ntok independent tokens of H*P channels, with the
+// partial sums laid out as (token, head, kNormParts); the one-token mixer
+// step uses it with one token per sequence.
 hipError_t launch_gated_norm_tokens(int io_f16, void* y, const float* normsum, const float* nw, int ntok, int H,
                                     int group, float eps, hipStream_t st) {
   if (ntok <= 0) return hipSuccess;
