@@ -357,6 +357,7 @@ template <int N> struct SmG {
     alignas(16) _Float16 c[TS * NP];     // [t][n] C as read
     alignas(16) _Float16 x[NWV][TS * XP];   // per wave: [s][p] x as read
     alignas(16) _Float16 xw[NWV][TS * XP];  // per wave: x times the state weight of token s
+    alignas(16) _Float16 blo[TS * NP];   // binary32 B: what its binary16 copy leaves out
   };
   // the step tiles are idle during the hand-off, where each wave lands one
   // aggregate state in LDS while another one is in flight to its registers
@@ -475,23 +476,39 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   _Float16* const xs = sm.u.t.x[wid];
   _Float16* const xws = sm.u.t.xw[wid];
   _Float16* const smb = sm.u.t.b;
+  _Float16* const smblo = sm.u.t.blo;
   _Float16* const smc = sm.u.t.c;
 
   // ---- per-step operands ---------------------------------------------------
-  struct XB { h8 x[XPL]; h8 b[BK]; h8 c[BK]; };
+  // With binary32 I/O, x and B stay binary32 until staging: x is rounded to
+  // binary16 once, after its weighting, and B goes to the state contraction
+  // as a binary16 pair (high part and remainder), so that the final state
+  // carries one binary16 rounding per term, as with binary16 inputs.
+  constexpr bool F32IO = sizeof(IO) == 4;
+  struct F8 { f4 a, b; };
+  using xv_t = typename std::conditional<F32IO, F8, h8>::type;
+  struct XB { xv_t x[XPL]; xv_t b[BK]; h8 c[BK]; };
+  auto ldx = [&](xv_t& v, rsrc_t r, unsigned off) {
+    if constexpr (F32IO) {
+      v.a = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+      v.b = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    } else {
+      v = ldh<IO, 8>(r, off);
+    }
+  };
   auto fetch = [&](XB& r, int tok0, bool with_c) {   // the step starting at token tok0
     const unsigned tok = (unsigned)tok0;
 #pragma unroll
     for (int k = 0; k < XPL; ++k) {
       const int s = (lane >> 2) + 16 * k, pc = lane & 3;   // token, 16-byte column chunk
-      r.x[k] = ldh<IO, 8>(rx, (tok + s) * xrow + (unsigned)(pc * 8) * ES);
+      ldx(r.x[k], rx, (tok + s) * xrow + (unsigned)(pc * 8) * ES);
     }
 #pragma unroll
     for (int k = 0; k < BK; ++k) {
       const int id = tid + NTH * k, s = id / NCH, nc = id % NCH;
       if (id < TS * NCH) {
         const unsigned off = (tok + s) * grow + (unsigned)(nc * 8) * ES;
-        r.b[k] = ldh<IO, 8>(rb, off);
+        ldx(r.b[k], rb, off);
         if (with_c) r.c[k] = ldh<IO, 8>(rc, off);
       }
     }
@@ -571,17 +588,41 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
     for (int k = 0; k < XPL; ++k) {
       const int s = (lane >> 2) + 16 * k, pc = lane & 3;   // token, 16-byte column chunk
       const float w = (float)dtw[i0 + s] * ex2(Sref - Sw[i0 + s]);
-      h8 xw;
+      h8 xw, xh;
+      if constexpr (F32IO) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xw[e] = (_Float16)__builtin_fmaf((float)r.x[k][e], w, 0.f);   // one mixed-precision op
+        for (int e = 0; e < 4; ++e) {
+          xw[e] = (_Float16)(r.x[k].a[e] * w);
+          xw[4 + e] = (_Float16)(r.x[k].b[e] * w);
+          xh[e] = (_Float16)r.x[k].a[e];
+          xh[4 + e] = (_Float16)r.x[k].b[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xw[e] = (_Float16)__builtin_fmaf((float)r.x[k][e], w, 0.f);   // one mixed-precision op
+        xh = r.x[k];
+      }
       *reinterpret_cast<h8*>(&xws[s * XP + pc * 8]) = xw;
-      if (with_c) *reinterpret_cast<h8*>(&xs[s * XP + pc * 8]) = r.x[k];
+      if (with_c) *reinterpret_cast<h8*>(&xs[s * XP + pc * 8]) = xh;
     }
 #pragma unroll
     for (int k = 0; k < BK; ++k) {
       const int id = tid + NTH * k, s = id / NCH, nc = id % NCH;
       if (id < TS * NCH) {
-        *reinterpret_cast<h8*>(&smb[s * NP + nc * 8]) = r.b[k];
+        if constexpr (F32IO) {
+          h8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hi[e] = (_Float16)r.b[k].a[e];
+            hi[4 + e] = (_Float16)r.b[k].b[e];
+            lo[e] = (_Float16)(r.b[k].a[e] - (float)hi[e]);
+            lo[4 + e] = (_Float16)(r.b[k].b[e] - (float)hi[4 + e]);
+          }
+          *reinterpret_cast<h8*>(&smb[s * NP + nc * 8]) = hi;
+          *reinterpret_cast<h8*>(&smblo[s * NP + nc * 8]) = lo;
+        } else {
+          *reinterpret_cast<h8*>(&smb[s * NP + nc * 8]) = r.b[k];
+        }
         if (with_c) *reinterpret_cast<h8*>(&smc[s * NP + nc * 8]) = r.c[k];
       }
     }
@@ -601,6 +642,11 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       const h8 af = cat(tr4(&smb[(4 * q + (lr >> 2)) * NP + col]), tr4(&smb[(16 + 4 * q + (lr >> 2)) * NP + col]));
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(af, xf[pt], acc[nt][pt]);
+      if constexpr (F32IO) {
+        const h8 al = cat(tr4(&smblo[(4 * q + (lr >> 2)) * NP + col]), tr4(&smblo[(16 + 4 * q + (lr >> 2)) * NP + col]));
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(al, xf[pt], acc[nt][pt]);
+      }
     }
   };
   // 8 (or 4) n of row r of an LDS [s][n] tile at the n-slots of k-step m
