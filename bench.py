@@ -174,8 +174,10 @@ def main():
         m2.conv_scan_window(t["dt"], t["A"], t["D"], t["y"], ws, x=t["x"], B=t["B"], C=t["C"], state_out=t["hT"],
                             chunk=Q, stream=stream)
 
-    for k in range(args.warmup):
-        step(k)
+    # one call on the first buffer set for the parity check, which runs on the
+    # host; the warmup follows it, so that the timed calls do not start on a
+    # GPU that idled through the check
+    step(0)
     torch.cuda.synchronize()
 
     # ---- parity on the timed buffers (sampled heads, one per group) -----------
@@ -196,6 +198,10 @@ def main():
         print(f"parity check failed before timing: y {worst_y:.3e} state {worst_s:.3e}", file=sys.stderr)
         sys.exit(1)
 
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
     # ---- timed region: K window calls ------------------------------------------
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -208,6 +214,17 @@ def main():
     tok_s = B * L / (ms * 1e-3)
     wbytes = window_bytes(B, L, H, P, N, G)
     achieved = wbytes / (ms * 1e-3) / 1e9
+
+    # three more repeats of 50 back-to-back calls each, for the spread
+    rep_us = []
+    for r in range(3):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for k in range(50):
+            step(k)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        rep_us.append(ev0.elapsed_time(ev1) / 50 * 1e3)
 
     # single-call latency (one launch, synchronized)
     lat = []
@@ -470,6 +487,8 @@ def main():
         "cpu_baseline": cpu,
         "window_us": round(ms * 1e3, 2),
         "window_latency_us": round(lat_us, 2),
+        "window_repeats_us": {"median": round(float(np.median(rep_us)), 2), "min": round(float(np.min(rep_us)), 2),
+                              "sd": round(float(np.std(rep_us)), 2), "repeats": len(rep_us), "calls_each": 50},
         "window_algorithmic_bytes": wbytes,
         "window_mfma_tflops": round(mflops / (ms * 1e-3) / 1e12, 1),
         "window_mfma_frac": round(mflops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK, 4),
