@@ -39,6 +39,8 @@ template <typename IO> struct WinArgs {
   const IO* x;        // x rows: token stride xstride elements
   const IO* Bm;       // B rows: token stride gstride elements
   const IO* Cm;       // C rows: token stride gstride elements
+  const _Float16* Blo; // binary16 B from the conv: what its rounding dropped, rows of gn (else null)
+  int gn;
   int xstride, gstride;
   const IO* dt;
   long long dtld;     // dt rows: token stride in elements
@@ -139,7 +141,8 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
                                                         const float* __restrict__ bias, const IO* __restrict__ cs_in,
                                                         IO* __restrict__ cs_out, const int* __restrict__ seqlens,
                                                         const int* __restrict__ cu, IO* __restrict__ out, int B,
-                                                        int L, int T, int Cd, long long ld) {
+                                                        int L, int T, int Cd, long long ld,
+                                                        _Float16* __restrict__ blo, int bbeg, int gn) {
   const int nch = Cd / 8, ntt = (L + kConvTT - 1) / kConvTT;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)B * ntt * nch) return;
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
   };
   if (len == 0 && tt == 0) put_state(h[0], h[1], h[2]);
   IO* dst = out + (size_t)b * L * Cd + c0;
+  const bool lo_here = blo != nullptr && c0 >= bbeg && c0 < bbeg + gn;
 #pragma unroll
   for (int kb = 0; kb < kConvTT / kConvRB; ++kb) {
     const int tb = t0 + kb * kConvRB;
@@ -212,6 +216,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
       const Raw8<IO>& r1 = k >= 2 ? cur[k - 2] : h[k + 1];
       const Raw8<IO>& r2 = k >= 1 ? cur[k - 1] : h[2];
       Raw8<IO> o;
+      float uo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float u = bs[e];
@@ -219,9 +224,20 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
         u = __builtin_fmaf(wk[1][e], r1[e], u);
         u = __builtin_fmaf(wk[2][e], r2[e], u);
         u = __builtin_fmaf(wk[3][e], cur[k][e], u);
-        o.set(e, u * __builtin_amdgcn_rcpf(1.f + __expf(-u)));
+        uo[e] = u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
+        o.set(e, uo[e]);
       }
       store_raw8(dst + (size_t)t * Cd, o);
+      if constexpr (sizeof(IO) == 2) {
+        // B's channels also leave what their binary16 copy drops, for the
+        // scan's state contraction
+        if (lo_here) {
+          h8 lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lo[e] = (_Float16)(uo[e] - (float)o.v[e]);
+          *reinterpret_cast<h8*>(blo + ((size_t)b * L + t) * gn + (c0 - bbeg)) = lo;
+        }
+      }
       if (t == len - 1) put_state(r1, r2, cur[k]);
     }
 #pragma unroll
@@ -380,7 +396,7 @@ template <int N> __device__ __forceinline__ int ncol(int nt, int j) {
 }  // namespace wv
 
 
-template <typename IO, int N>
+template <typename IO, int N, bool BLO>
 __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<IO> a) {
   using namespace wv;
   constexpr unsigned ES = sizeof(IO);
@@ -484,10 +500,15 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
   // binary16 once, after its weighting, and B goes to the state contraction
   // as a binary16 pair (high part and remainder), so that the final state
   // carries one binary16 rounding per term, as with binary16 inputs.
+  // Binary16 B from the conv kernel comes with the remainder its rounding
+  // dropped (BLO), for the same two-part contraction.
   constexpr bool F32IO = sizeof(IO) == 4;
+  constexpr bool BSPLIT = F32IO || BLO;
   struct F8 { f4 a, b; };
   using xv_t = typename std::conditional<F32IO, F8, h8>::type;
-  struct XB { xv_t x[XPL]; xv_t b[BK]; h8 c[BK]; };
+  struct XB { xv_t x[XPL]; xv_t b[BK]; h8 c[BK]; h8 bl[BLO ? BK : 1]; };
+  rsrc_t rbl = rb;
+  if constexpr (BLO) rbl = mkr(a.Blo + xbase * (size_t)a.gn + (size_t)g * N, len > 0 ? (unsigned)((len - 1) * a.gn + N) * 2u : 0u);
   auto ldx = [&](xv_t& v, rsrc_t r, unsigned off) {
     if constexpr (F32IO) {
       v.a = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -509,6 +530,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       if (id < TS * NCH) {
         const unsigned off = (tok + s) * grow + (unsigned)(nc * 8) * ES;
         ldx(r.b[k], rb, off);
+        if constexpr (BLO) r.bl[k] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rbl, ((tok + s) * (unsigned)a.gn + (unsigned)(nc * 8)) * 2u, 0, 0));
         if (with_c) r.c[k] = ldh<IO, 8>(rc, off);
       }
     }
@@ -622,6 +644,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           *reinterpret_cast<h8*>(&smblo[s * NP + nc * 8]) = lo;
         } else {
           *reinterpret_cast<h8*>(&smb[s * NP + nc * 8]) = r.b[k];
+          if constexpr (BLO) *reinterpret_cast<h8*>(&smblo[s * NP + nc * 8]) = r.bl[k];
         }
         if (with_c) *reinterpret_cast<h8*>(&smc[s * NP + nc * 8]) = r.c[k];
       }
@@ -642,7 +665,7 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
       const h8 af = cat(tr4(&smb[(4 * q + (lr >> 2)) * NP + col]), tr4(&smb[(16 + 4 * q + (lr >> 2)) * NP + col]));
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(af, xf[pt], acc[nt][pt]);
-      if constexpr (F32IO) {
+      if constexpr (BSPLIT) {
         const h8 al = cat(tr4(&smblo[(4 * q + (lr >> 2)) * NP + col]), tr4(&smblo[(16 + 4 * q + (lr >> 2)) * NP + col]));
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(al, xf[pt], acc[nt][pt]);
@@ -1135,7 +1158,7 @@ int norm_parts_per_head() { return kNormParts; }
 
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t ctrl, flags, agg, convx, total;
+  size_t ctrl, flags, agg, convx, blo, total;
 };
 static WsLayout ws_layout(const mamba2_dims& d) {
   const size_t nchunks = ((size_t)d.seqlen + d.chunk - 1) / d.chunk;
@@ -1148,7 +1171,10 @@ static WsLayout ws_layout(const mamba2_dims& d) {
   w.agg = up(w.flags + items * 8);
   w.convx = up(w.agg + items * (size_t)d.dstate * (kP / 2) * 4);
   const size_t cd = (size_t)d.nheads * kP + 2 * (size_t)d.ngroups * d.dstate;
-  w.total = up(w.convx + (d.conv_width == 4 ? (size_t)d.batch * d.seqlen * cd * es : 0));
+  w.blo = up(w.convx + (d.conv_width == 4 ? (size_t)d.batch * d.seqlen * cd * es : 0));
+  // binary16 conv output: the remainder of its B channels
+  const bool blo = d.conv_width == 4 && d.io_dtype == MAMBA2_F16;
+  w.total = up(w.blo + (blo ? (size_t)d.batch * d.seqlen * d.ngroups * d.dstate * 2 : 0));
   return w;
 }
 
@@ -1166,7 +1192,7 @@ static int device_cus() {
   return n;
 }
 
-template <typename IO, int N>
+template <typename IO, int N, bool BLO>
 static hipError_t launch_scan(const WinArgs<IO>& a, hipStream_t st) {
   const int hpg = a.H / a.G;
   const long long slots = (long long)a.B * a.G * ((hpg + wv::KH - 1) / wv::KH);   // workgroups per segment index
@@ -1174,7 +1200,7 @@ static hipError_t launch_scan(const WinArgs<IO>& a, hipStream_t st) {
   static int per_cu = 0;
   if (per_cu <= 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ssd_window_group_kernel<IO, N>, 64 * wv::NWV, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ssd_window_group_kernel<IO, N, BLO>, 64 * wv::NWV, 0) !=
             hipSuccess || n <= 0)
       n = 1;
     per_cu = n;
@@ -1194,7 +1220,7 @@ static hipError_t launch_scan(const WinArgs<IO>& a, hipStream_t st) {
   // radix-8 tree.  Otherwise segment levels are staggered in time and
   // aggregate traffic matters more: radix 4.
   b.tree_lg = wgs <= resident ? 3 : 2;
-  ssd_window_group_kernel<IO, N><<<wgs, 64 * wv::NWV, 0, st>>>(b);
+  ssd_window_group_kernel<IO, N, BLO><<<wgs, 64 * wv::NWV, 0, st>>>(b);
   return hipGetLastError();
 }
 
@@ -1221,27 +1247,34 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   if (d.conv_width == 4) {
     const int cd = d.nheads * kP + 2 * d.ngroups * d.dstate;
     IO* xc = (IO*)(base + wl.convx);
+    _Float16* blo = sizeof(IO) == 2 ? (_Float16*)(base + wl.blo) : nullptr;
     const long long threads = (long long)d.batch * ((d.seqlen + kConvTT - 1) / kConvTT) * (cd / 8);
     conv_silu_kernel<IO><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(
         (const IO*)io_.xBC, io_.conv_w, io_.conv_b, (const IO*)io_.conv_state_in, (IO*)io_.conv_state_out,
         io_.seqlens, io_.cu_seqlens, xc, d.batch, d.seqlen, d.packed_tokens, cd,
-        io_.xBC_ld > 0 ? io_.xBC_ld : (long long)cd);
+        io_.xBC_ld > 0 ? io_.xBC_ld : (long long)cd, blo, d.nheads * kP, d.ngroups * d.dstate);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.x = xc;
     a.Bm = xc + d.nheads * kP;
     a.Cm = xc + d.nheads * kP + d.ngroups * d.dstate;
     a.xstride = a.gstride = cd;
+    a.Blo = blo;
+    a.gn = d.ngroups * d.dstate;
   } else {
+    a.Blo = nullptr;
+    a.gn = 0;
     a.x = (const IO*)io_.x; a.Bm = (const IO*)io_.B; a.Cm = (const IO*)io_.C;
     a.xstride = d.nheads * kP;
     a.gstride = d.ngroups * d.dstate;
   }
   hipError_t e;
+  constexpr bool F16IO = sizeof(IO) == 2;   // only binary16 conv output carries a remainder
+  const bool blo = a.Blo != nullptr;
   switch (d.dstate) {
-    case 16: e = launch_scan<IO, 16>(a, st); break;
-    case 64: e = launch_scan<IO, 64>(a, st); break;
-    default: e = launch_scan<IO, 128>(a, st); break;
+    case 16: e = blo ? launch_scan<IO, 16, F16IO>(a, st) : launch_scan<IO, 16, false>(a, st); break;
+    case 64: e = blo ? launch_scan<IO, 64, F16IO>(a, st) : launch_scan<IO, 64, false>(a, st); break;
+    default: e = blo ? launch_scan<IO, 128, F16IO>(a, st) : launch_scan<IO, 128, false>(a, st); break;
   }
   if (e != hipSuccess || d.norm_group == 0) return e;
   gate_norm_kernel<IO><<<(unsigned)(d.batch * d.seqlen), 256, 0, st>>>(

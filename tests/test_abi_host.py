@@ -40,22 +40,23 @@ def layer_dims(**kw):
     return m2.make_dims(**base)
 
 
-def ws_formula(chunk_items, N, conv_bytes=0):
+def ws_formula(chunk_items, N, conv_bytes=0, blo_bytes=0):
     # control block; per (chunk, sequence, head, half) item a 64-bit flag word
-    # and an fp32 aggregate of N x 32; the conv output (the gated norm needs no
-    # workspace)
+    # and an fp32 aggregate of N x 32; the conv output and, for binary16, the
+    # remainder of its B channels (the gated norm needs no workspace)
     up = lambda v: (v + 255) // 256 * 256
     items = 2 * chunk_items
     off = up(11 * 32 * 4)
     off = up(off + items * 8)
     off = up(off + items * N * 32 * 4)
-    return up(off + conv_bytes)
+    off = up(off + conv_bytes)
+    return up(off + blo_bytes)
 
 
 def test_workspace_size_formula():
     assert m2.window_workspace_bytes(layer_dims()) == ws_formula(8 * 128, 128)
     n2 = m2.window_workspace_bytes(layer_dims(batch=4, norm_group=8192, conv_width=4))
-    assert n2 == ws_formula(8 * 4 * 128, 128, 4 * 2048 * 10240 * 2)
+    assert n2 == ws_formula(8 * 4 * 128, 128, 4 * 2048 * 10240 * 2, 4 * 2048 * 8 * 128 * 2)
     assert m2.window_workspace_bytes(layer_dims(dstate=16, ngroups=1, nheads=4, seqlen=256, chunk=64)) == \
         ws_formula(4 * 4, 16)
 

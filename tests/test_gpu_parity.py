@@ -643,7 +643,7 @@ def test_mixer_core_full_size_sampled():
     H, P, G, N = s.nheads, s.headdim, s.ngroups, s.dstate
     say("[mixer] full size B=4 L=2048")
     y, hT, _ = run_mixer(inp, H, P, G, N, s.chunk, H * P, want_conv_state=False)
-    for b in (0, 3):
+    for b in range(s.batch):
         sub = {k: (v[b:b + 1] if (v.ndim > 1 and k in ("xBC", "dt", "z")) else v) for k, v in inp.items()}
         out_r, h_r, _ = oracle.mixer_core(sub["xBC"], inp["conv_w"], inp["conv_b"], sub["dt"], inp["A"], inp["D"],
                                           sub["z"], inp["norm_w"], H, P, G, N, H * P)
