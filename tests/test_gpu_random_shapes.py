@@ -85,3 +85,12 @@ def test_window_random_configuration(seed):
     es = slice_err(hT.cpu().numpy(), hr, 2)
     print(f"[random] seed {seed}: y {ey:.3e} state {es:.3e}", flush=True)
     assert ey <= Y_TOL and es <= S_TOL
+
+
+@pytest.mark.xfail(strict=False, reason="binary32 one-token windows whose per-head factor dt C.B + D nearly "
+                   "cancels: the diagonal term's binary16 operands leave y about 5e-3 off the tiny reference "
+                   "(a known limitation of the binary32 path)")
+def test_window_one_token_cancelling_factor_f32():
+    # draw 304 of the sweep: three one-token binary32 windows with a raw dt;
+    # sequence 1, head 5 has dt C.B = +0.0027 against D = -0.0037
+    test_window_random_configuration(304)
