@@ -74,6 +74,68 @@ def copy_probe(mib):
     print(json.dumps({"copy_bytes_per_launch_read": n, "copy_bytes_per_launch_write": n, "launches": 5}), flush=True)
 
 
+def run_metadata(torch, m2):
+    """Where the numbers come from: the tree the library was built from, its
+    ABI version, the GPU architecture, the ROCm and torch builds, the host
+    CPU."""
+    meta = {"abi_version": m2.abi_version()}
+    info = os.path.join(ROOT, "mamba_ssd_scan_amd", "build_info.json")
+    try:
+        with open(info) as f:
+            meta.update(json.load(f))
+    except (OSError, ValueError):
+        meta["git_sha"] = None
+    props = torch.cuda.get_device_properties(0)
+    meta["gpu"] = props.name
+    meta["gfx_arch"] = getattr(props, "gcnArchName", None)
+    meta["cus"] = props.multi_processor_count
+    meta["torch"] = torch.__version__
+    meta["hip"] = getattr(torch.version, "hip", None)
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            meta["rocm"] = f.read().strip()
+    except OSError:
+        meta["rocm"] = None
+    meta["cpu_model"] = cpu_model()
+    meta["cpu_threads_available"] = len(os.sched_getaffinity(0))
+    return meta
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def copy_bandwidth(torch, dev, stream, mib=1024, reps=10):
+    """Read + write bytes per second of a plain device-to-device copy of
+    `mib` MiB, timed with events on the benchmark's stream (the practical
+    ceiling of a streaming kernel on this part)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / sec / 1e9
+
+
 def window_bytes(B, L, H, P, N, G, lens=None):
     """Algorithmic HBM bytes of one window call: every input element read once,
     every output written once, fp16 I/O, fp32 final state."""
@@ -124,6 +186,84 @@ def window_mfma_flops(L, H, P, N, Q=256, segments=8, step=32, half=32):
     out = (3 * km + 2 * pt + 2 * pt * km) * J * C
     upd = nt * pt * (J * C - (nseg - 1))
     return H * (P // half) * (local + out + upd) * 16384
+
+
+def _timed(fn, min_s=2.0, max_reps=20):
+    """Seconds per call of fn, repeated until min_s has passed."""
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or reps >= max_reps:
+            return el / reps, reps
+
+
+def cpu_baselines(inp, s, args):
+    """The oracle as it stands (fp64 sequential C, OpenMP over (sequence,
+    head)), timed on this host on bounded samples of each workload and scaled
+    to the whole workload: all available cores and one thread.  Reported
+    beside the GPU figures, never a target."""
+    import oracle
+    import synth
+    nth = len(os.sched_getaffinity(0))
+    used = oracle.threads_used(nth)
+    B, L, H, P, N, G = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups
+    hpg = H // G
+
+    def window_rate(x, dt, A, Bm, Cm, D, heads, threads, seqlens=None, min_s=3.0):
+        g = max(heads // hpg, 1)
+        sec, reps = _timed(lambda: oracle.ssd_scan(x[:, :, :heads], dt[:, :, :heads], A[:heads], Bm[:, :, :g],
+                                                    Cm[:, :, :g], D[:heads], seqlens=seqlens, nthreads=threads),
+                           min_s)
+        return sec * (H / heads), reps
+
+    # layer window: all cores on 32 heads, one thread on 2 heads
+    per_win, reps = window_rate(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], 32, nth)
+    per_win1, reps1 = window_rate(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], 2, 1, min_s=2.0)
+    out = {"value": round(B * L / per_win, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": f"32 of {H} heads of one L={L} layer window (fp64 sequential recurrence, OpenMP over heads), "
+                     f"{reps} runs, scaled to all {H} heads",
+           "cpu_model": cpu_model(),
+           "single_thread": {"value": round(B * L / per_win1, 1), "unit": "tokens/s", "cores": 1,
+                             "sample": f"2 of {H} heads, {reps1} runs, scaled to all {H} heads"}}
+    # batched windows: the 1955-token partial window and one full window, 16 heads each
+    sb = synth.batched_windows()
+    sub = synth.window_inputs(synth.WindowShape(2, L, 16, P, N, 1, s.chunk), 1102)
+    lens2 = [L, sb.seqlens[-1]]
+    sec, reps = _timed(lambda: oracle.ssd_scan(sub["x"], sub["dt"], sub["A"], sub["B"], sub["C"], sub["D"],
+                                               seqlens=lens2, nthreads=nth), 3.0)
+    tok_s = sum(lens2) * 16 / H / sec
+    out["batched"] = {"value": round(tok_s, 1), "unit": "tokens/s", "cores": used,
+                      "sample": f"2 of 8 windows (2048 and 1955 tokens), 16 of {H} heads, {reps} runs, scaled"}
+    # decode: 4 steps of 4 of 64 sequences on all cores; a 16-step prefix of one sequence on one thread
+    d = synth.DECODE
+    prm = synth.decode_params(1003, d["batch"], d["nheads"], d["headdim"], d["dstate"])
+    steps = [synth.decode_step_inputs(1003, t, prm["dt0"], d["batch"], d["nheads"], d["headdim"], d["dstate"],
+                                      d["ngroups"]) for t in range(16)]
+    stk = {k: np.stack([st[k] for st in steps]) for k in ("x", "dt", "B", "C")}
+
+    def dec(T, b_hi, threads):
+        bits = prm["state"].astype(np.float16).view(np.uint16).copy()
+        oracle.decode_f16state(stk["x"][:T], stk["dt"][:T], prm["A"], stk["B"][:T], stk["C"][:T], prm["D"], bits,
+                               b_range=(0, b_hi), nthreads=threads)
+
+    sec, reps = _timed(lambda: dec(4, 4, nth), 2.0)
+    sec1, reps1 = _timed(lambda: dec(16, 1, 1), 2.0, max_reps=3)
+    out["decode"] = {"us_per_step": round(sec / 4 * (d["batch"] / 4) * 1e6, 1), "cores": used,
+                     "sample": f"4 steps of 4 of {d['batch']} sequences, {reps} runs, scaled to {d['batch']}",
+                     "single_thread_us_per_step": round(sec1 / 16 * d["batch"] * 1e6, 1),
+                     "single_thread_sample": f"16-step prefix of 1 of {d['batch']} sequences, {reps1} runs, scaled"}
+    # mixer core: 512 tokens of one sequence, every head (conv, scan, norm)
+    sm = synth.mixer_window()
+    msub = synth.mixer_inputs(synth.WindowShape(1, 512, sm.nheads, P, sm.dstate, sm.ngroups, s.chunk), 1104)
+    sec, reps = _timed(lambda: oracle.mixer_core(msub["xBC"], msub["conv_w"], msub["conv_b"], msub["dt"], msub["A"],
+                                                 msub["D"], msub["z"], msub["norm_w"], sm.nheads, P, sm.ngroups,
+                                                 sm.dstate, sm.nheads * P, nthreads=nth), 3.0)
+    out["mixer"] = {"value": round(512 / sec, 1), "unit": "tokens/s", "cores": used,
+                    "sample": f"512 tokens of one sequence, all {sm.nheads} heads, {reps} runs"}
+    return out
 
 
 def main():
@@ -236,6 +376,10 @@ def main():
         torch.cuda.synchronize()
         lat.append(ev0.elapsed_time(ev1) * 1e3)
     lat_us = float(np.median(lat))
+    if m2.window_take_error(ws, stream=stream) != 0:
+        print("a segment hand-off gave up during the timed calls: results invalid", file=sys.stderr)
+        sys.exit(1)
+    copy_gbs = copy_bandwidth(torch, dev, stream)
     if args.headline_only:
         print(json.dumps({"metric": "SSD window-scan tokens/s at 8B layer shape L=2048", "value": round(tok_s, 1),
                           "unit": "tokens/s", "ms_per_step": round(ms, 6), "steps": args.steps,
@@ -304,7 +448,12 @@ def main():
         "xBC": torch.randn(MB_, ML_, Cd_, device=dev, generator=gen).half(),
         "conv_w": torch.randn(Cd_, 4, device=dev, generator=gen) * 0.5,
         "conv_b": torch.zeros(Cd_, device=dev),
-        "dt": torch.nn.functional.softplus(torch.randn(MB_, ML_, MH_, device=dev, generator=gen) - 3.0).half(),
+        # dt as the layer window draws it: softplus(N(0,1) + log(expm1(dt0))),
+        # dt0 log-uniform on [1e-3, 1e-1], one per head
+        "dt": torch.nn.functional.softplus(
+            torch.randn(MB_, ML_, MH_, device=dev, generator=gen)
+            + torch.log(torch.expm1(torch.exp(torch.rand(MH_, device=dev, generator=gen) * float(np.log(100.0))
+                                              + float(np.log(1e-3)))))).half(),
         "z": torch.randn(MB_, ML_, MH_ * P, device=dev, generator=gen).half(),
         "norm_w": torch.ones(MH_ * P, device=dev),
     }
@@ -330,6 +479,9 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     mix_us = ev0.elapsed_time(ev1) * 1e3 / 20
+    if m2.window_take_error(mws, stream=stream) != 0:
+        print("a segment hand-off gave up in the mixer calls: results invalid", file=sys.stderr)
+        sys.exit(1)
     mbytes = mixer_bytes(MB_, ML_, MH_, P, MN_, MG_)
     del mx, my, mh, mcs, mws
     torch.cuda.empty_cache()
@@ -440,30 +592,15 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     bat_us = ev0.elapsed_time(ev1) * 1e3 / 20
+    if m2.window_take_error(bws, stream=stream) != 0:
+        print("a segment hand-off gave up in the batched calls: results invalid", file=sys.stderr)
+        sys.exit(1)
     bbytes = window_bytes(BB, L, H, P, N, G, lens=blens)
     del bsets, bws
     torch.cuda.empty_cache()
 
-    # ---- CPU baseline: the oracle on a bounded sample of the window ------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        nth = len(os.sched_getaffinity(0))
-        used = oracle.threads_used(nth)
-        hs = 32
-        sub = {k: v for k, v in inp.items()}
-        t_start = time.perf_counter()
-        reps = 0
-        while True:
-            oracle.ssd_scan(sub["x"][:, :, :hs], sub["dt"][:, :, :hs], sub["A"][:hs], sub["B"][:, :, :hs // 16],
-                            sub["C"][:, :, :hs // 16], sub["D"][:hs], nthreads=nth)
-            reps += 1
-            el = time.perf_counter() - t_start
-            if el > 10.0 or reps >= 20:
-                break
-        per_window = el / reps * (H / hs)
-        cpu = {"value": round(B * L / per_window, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
-               "sample": f"{hs} of {H} heads of one L={L} window (fp64 sequential recurrence), {reps} runs, "
-                         f"scaled to all {H} heads"}
+    # ---- CPU baseline: the oracle on bounded samples of each workload ----------
+    cpu = cpu_baselines(inp, s, args) if not args.no_cpu_baseline else None
 
     mflops = window_mfma_flops(L, H, P, N, Q)
     out = {
@@ -485,6 +622,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
         "cpu_baseline": cpu,
+        "copy_GBs": round(copy_gbs, 1),
+        "frac_of_copy": round(achieved / copy_gbs, 4),
+        "meta": run_metadata(torch, m2),
         "window_us": round(ms * 1e3, 2),
         "window_latency_us": round(lat_us, 2),
         "window_repeats_us": {"median": round(float(np.median(rep_us)), 2), "min": round(float(np.min(rep_us)), 2),

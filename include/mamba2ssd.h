@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 7
+#define MAMBA2_ABI_VERSION 8
 
 enum {
     MAMBA2_OK = 0,
@@ -177,6 +177,19 @@ int32_t mamba2_window_workspace_bytes(const mamba2_dims* dims, size_t* bytes);
 int32_t mamba2_conv_scan_window(const mamba2_dims* dims, const mamba2_window_io* io,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* Reads and clears the error word of a window workspace.  Waits for all
+ * work queued on `stream` so far (synchronous), then stores the word in
+ * *flags and, when it is set, clears it (also synchronously, with a kernel on
+ * the same stream).  *flags == 0: every window call on this workspace since
+ * the last query completed its hand-offs.  Bit 0 set: in some call a
+ * segment's bounded wait for an earlier segment's aggregate gave up (it
+ * never returns early otherwise), so that call's y and final states are not
+ * valid; the window entry point itself cannot report this, since it returns
+ * before the kernels run.  ws and ws_bytes as given to the window calls
+ * (at least the control block: MAMBA2_EWORKSPACE otherwise).
+ * Errors: EINVAL (NULL ws or flags), EWORKSPACE, EALIGN, EHIP. */
+int32_t mamba2_window_take_error(void* ws, size_t ws_bytes, uint32_t* flags, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Whole window with the recurrent state requantized to binary16 after every
  * token, the way page "Mamb2_8B_FP4_Recall_SQ3.25" scores its windows (carry
@@ -285,7 +298,7 @@ int32_t mamba2_decode_step(const mamba2_dims* dims, const mamba2_decode_io* io, 
  * recurrent row of section "Representation", the gated RMSNorm of section
  * "Compatible reference environment").  For every sequence:
  *   u   = silu(conv_b + sum_k conv_w[:, k] * [history, xBC][k])  (width 4,
- *         tap 3 on this token), rounded to the I/O type, split x | B | C;
+ *         tap 3 on this token), rounded once (correctly) to the I/O type, split x | B | C;
  *   history <- (history[1], history[2], xBC)                     (in place);
  *   the decode step of mamba2_decode_step on (x, dt, B, C);
  *   y = the step's output, or with norm_group > 0 the gated RMSNorm

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "F16", "F32", "Dims", "Mamba2Error", "library_path", "load_library",
-    "window_workspace_bytes", "alloc_workspace", "conv_scan_window", "decode_step", "requant_window",
+    "window_workspace_bytes", "alloc_workspace", "conv_scan_window", "window_take_error", "decode_step", "requant_window",
     "mixer_decode_workspace_bytes", "alloc_mixer_decode_workspace", "mixer_decode_step",
     "scan_grad_workspace_bytes", "alloc_scan_grad_workspace", "scan_grad",
     "state_load", "state_store", "abi_version",
@@ -93,6 +93,8 @@ def load_library():
         lib.mamba2_window_workspace_bytes.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
         lib.mamba2_conv_scan_window.restype = ctypes.c_int32
         lib.mamba2_conv_scan_window.argtypes = [dp, ctypes.POINTER(_WindowIO), vp, ctypes.c_size_t, vp]
+        lib.mamba2_window_take_error.restype = ctypes.c_int32
+        lib.mamba2_window_take_error.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
         lib.mamba2_requant_window.restype = ctypes.c_int32
         lib.mamba2_requant_window.argtypes = [dp, ctypes.POINTER(_WindowIO), vp]
         lib.mamba2_mixer_decode_workspace_bytes.restype = ctypes.c_int32
@@ -230,6 +232,18 @@ def conv_scan_window(dt, A, D, y, workspace, *, x=None, B=None, C=None, xBC=None
     _check("mamba2_conv_scan_window",
            load_library().mamba2_conv_scan_window(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
                                                   workspace.numel(), _stream(dt, stream)))
+
+
+def window_take_error(workspace, stream=None) -> int:
+    """Error word of a window workspace after the work queued on the stream
+    (0: every hand-off completed; bit 0: a bounded wait gave up and that
+    call's outputs are invalid); the word is cleared.  Synchronizes the
+    stream."""
+    v = ctypes.c_uint32(0)
+    _check("mamba2_window_take_error",
+           load_library().mamba2_window_take_error(_ptr(workspace), workspace.numel(), ctypes.byref(v),
+                                                   _stream(workspace, stream)))
+    return v.value
 
 
 def requant_window(dt, A, D, y, *, x, B, C, state_in=None, state_out=None, seqlens=None, dt_softplus=False,

@@ -29,7 +29,35 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed to build libmamba2ssd.so")
     os.replace(tmp, LIB)
+    write_build_info()
     return LIB
+
+
+def write_build_info() -> None:
+    """Record, beside the library, which tree it was built from (the git
+    commit when there is one, whether tracked files differed from it, and a
+    hash of the sources), for the benchmark's metadata."""
+    import hashlib
+    import json
+    root = os.path.dirname(HERE)
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(root, "include", "mamba2ssd.h"), "rb") as f:
+        h.update(f.read())
+    info = {"source_sha256_16": h.hexdigest()[:16], "git_sha": None, "git_dirty": None}
+    try:
+        sha = subprocess.run(["git", "rev-parse", "HEAD"], cwd=root, capture_output=True, text=True)
+        if sha.returncode == 0:
+            info["git_sha"] = sha.stdout.strip()
+            st = subprocess.run(["git", "status", "--porcelain", "--untracked-files=no"], cwd=root,
+                                capture_output=True, text=True)
+            info["git_dirty"] = bool(st.stdout.strip()) if st.returncode == 0 else None
+    except OSError:
+        pass
+    with open(os.path.join(HERE, "build_info.json"), "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":

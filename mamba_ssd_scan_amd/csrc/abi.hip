@@ -14,6 +14,8 @@ hipError_t launch_decode(int io_f16, int state_f16, int N, const void* x, const 
 hipError_t launch_state_convert(int to_resident, int state_f16, const void* src, void* dst, size_t n,
                                 hipStream_t st);
 size_t window_workspace_bytes(const mamba2_dims& d);
+size_t window_control_bytes();
+hipError_t window_take_error(void* ws, unsigned* flags, hipStream_t st);
 hipError_t launch_window(const mamba2_dims& d, const mamba2_window_io& io, void* ws, hipStream_t st);
 hipError_t launch_requant_window(const mamba2_dims& d, const mamba2_window_io& io, hipStream_t st);
 size_t mixer_decode_workspace_bytes(const mamba2_dims& d);
@@ -146,6 +148,8 @@ static int32_t check_window(const mamba2_dims* d) {
   if (d->norm_group > 0 && !(d->norm_eps >= 0.f)) return MAMBA2_EINVAL;
   // the norm finish keeps one scale per group of a token in LDS (256 slots)
   if (d->norm_group > 0 && (d->nheads * d->headdim) / d->norm_group > 256) return MAMBA2_EUNSUPPORTED;
+  // the norm sums g^2 over runs of 64 channels in LDS (1024 slots)
+  if (d->norm_group > 0 && (int64_t)d->nheads * d->headdim > 1024 * 64) return MAMBA2_EUNSUPPORTED;
   if (d->headdim != 64) return MAMBA2_EUNSUPPORTED;
   if (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) return MAMBA2_EUNSUPPORTED;
   if (d->segments < 0) return MAMBA2_EINVAL;
@@ -241,6 +245,17 @@ int32_t mamba2_conv_scan_window(const mamba2_dims* d, const mamba2_window_io* io
   return hip_status(m2::launch_window(*d, *io, ws, (hipStream_t)stream));
 }
 
+int32_t mamba2_window_take_error(void* ws, size_t ws_bytes, uint32_t* flags, void* stream) {
+  if (!ws || !flags) return MAMBA2_EINVAL;
+  if (ws_bytes < m2::window_control_bytes()) return MAMBA2_EWORKSPACE;
+  if ((uintptr_t)ws & 255) return MAMBA2_EALIGN;
+  unsigned v = 0;
+  const int32_t s = hip_status(m2::window_take_error(ws, &v, (hipStream_t)stream));
+  if (s != MAMBA2_OK) return s;
+  *flags = v;
+  return MAMBA2_OK;
+}
+
 int32_t mamba2_requant_window(const mamba2_dims* d, const mamba2_window_io* io, void* stream) {
   int32_t s = check_common(d);
   if (s != MAMBA2_OK) return s;
@@ -289,6 +304,8 @@ static int32_t check_mixer_decode(const mamba2_dims* d) {
   if (d->norm_group > 0 && d->norm_group % d->headdim != 0) return MAMBA2_EUNSUPPORTED;
   // the norm finish keeps one scale per norm group of a token in LDS (256 slots)
   if (d->norm_group > 0 && hp / d->norm_group > 256) return MAMBA2_EUNSUPPORTED;
+  // the norm finish stages two partial sums per head in LDS (1024 slots)
+  if (d->norm_group > 0 && d->nheads > 512) return MAMBA2_EUNSUPPORTED;
   if ((int64_t)d->batch * d->nheads > ((int64_t)1 << 31) - 1) return MAMBA2_EUNSUPPORTED;
   return MAMBA2_OK;
 }
@@ -301,10 +318,11 @@ int32_t mamba2_mixer_decode_workspace_bytes(const mamba2_dims* d, size_t* bytes)
   return MAMBA2_OK;
 }
 
-int32_t mamba2_mixer_decode_step(const mamba2_dims* d, const mamba2_mixer_decode_io* io, void* ws, size_t ws_bytes,
-                                 void* stream) {
-  int32_t s = check_mixer_decode(d);
-  if (s != MAMBA2_OK) return s;
+// Arguments of a fused one-token mixer step.  ws is the workspace the
+// kernels will use (caller-owned, or null for the library's static one, in
+// which case need is only checked against its size by the caller).
+static int32_t check_mixer_decode_args(const mamba2_dims* d, const mamba2_mixer_decode_io* io, const void* ws,
+                                       size_t need) {
   if (!io) return MAMBA2_EINVAL;
   const size_t es = esize(d->io_dtype);
   const size_t Bsz = d->batch, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
@@ -318,13 +336,10 @@ int32_t mamba2_mixer_decode_step(const mamba2_dims* d, const mamba2_mixer_decode
       ((uintptr_t)io->dt_bias & 3) || ((uintptr_t)io->A & 3) || ((uintptr_t)io->D & 3) ||
       ((uintptr_t)io->norm_w & 3))
     return MAMBA2_EALIGN;
-  const size_t need = m2::mixer_decode_workspace_bytes(*d);
-  if (!ws || ws_bytes < need) return MAMBA2_EWORKSPACE;
-  if ((uintptr_t)ws & 255) return MAMBA2_EALIGN;
   // outputs (y; state and conv_state in place; workspace) against inputs and
   // against each other
   Range outs[] = {rng(io->y, Bsz * H * P * es), rng(io->state, Bsz * H * P * N * esize(d->state_dtype)),
-                  rng(io->conv_state, Bsz * cd * 3 * es), rng(ws, need)};
+                  rng(io->conv_state, Bsz * cd * 3 * es), rng(ws, ws ? need : 0)};
   Range ins[] = {rng(io->xBC, Bsz * cd * es), rng(io->conv_w, cd * 16), rng(io->conv_b, io->conv_b ? cd * 4 : 0),
                  rng(io->dt, Bsz * H * es), rng(io->dt_bias, d->dt_softplus ? H * 4 : 0), rng(io->A, H * 4),
                  rng(io->D, H * 4), rng(io->z, d->norm_group ? Bsz * H * P * es : 0),
@@ -336,6 +351,21 @@ int32_t mamba2_mixer_decode_step(const mamba2_dims* d, const mamba2_mixer_decode
     for (size_t j = i + 1; j < nout; ++j)
       if (overlap(outs[i], outs[j])) return MAMBA2_EINVAL;
   }
+  return MAMBA2_OK;
+}
+
+int32_t mamba2_mixer_decode_step(const mamba2_dims* d, const mamba2_mixer_decode_io* io, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  int32_t s = check_mixer_decode(d);
+  if (s != MAMBA2_OK) return s;
+  if (!io) return MAMBA2_EINVAL;
+  const size_t need = m2::mixer_decode_workspace_bytes(*d);
+  s = check_mixer_decode_args(d, io, nullptr, 0);
+  if (s != MAMBA2_OK) return s;
+  if (!ws || ws_bytes < need) return MAMBA2_EWORKSPACE;
+  if ((uintptr_t)ws & 255) return MAMBA2_EALIGN;
+  s = check_mixer_decode_args(d, io, ws, need);
+  if (s != MAMBA2_OK) return s;
   return hip_status(m2::launch_mixer_decode(*d, *io, ws, (hipStream_t)stream));
 }
 

@@ -37,9 +37,28 @@
 
 namespace m2 {
 
-template <typename IO> __device__ __forceinline__ float io_round(float v);
-template <> __device__ __forceinline__ float io_round<_Float16>(float v) { return (float)(_Float16)v; }
-template <> __device__ __forceinline__ float io_round<float>(float v) { return v; }
+// SiLU of the conv output u (taken in double precision: each tap product of a
+// binary32 weight and an I/O value is exact in double, and the sum runs in
+// the conv's tap order), rounded once to the I/O type (a few hundred channels
+// per workgroup, so the cost is negligible).  The staged values are then the
+// correctly rounded SiLU of the conv, not one that a binary32 evaluation may
+// put on the other side of a rounding boundary.  Binary16 goes through
+// binary32 with round-to-odd, which keeps the final round-to-nearest-even
+// exact (binary32 carries 13 more fraction bits).
+template <typename IO> __device__ __forceinline__ float silu_io(double u);
+template <> __device__ __forceinline__ float silu_io<float>(double u) {
+  const double v = u / (1.0 + exp(-u));
+  return (float)v;
+}
+template <> __device__ __forceinline__ float silu_io<_Float16>(double u) {
+  const double v = u / (1.0 + exp(-u));
+  float f = (float)v;                                   // nearest binary32
+  if ((double)f != v && (__float_as_uint(f) & 1u) == 0u) {  // inexact with an even last bit: the odd neighbour
+    if (f == 0.f) f = __uint_as_float(v > 0.0 ? 1u : 0x80000001u);
+    else f = __uint_as_float(__float_as_uint(f) + (fabs(v) > fabs((double)f) ? 1u : 0xffffffffu));
+  }
+  return (float)(_Float16)f;
+}
 
 template <typename IO> struct MixDecArgs {
   const IO* xBC;          // (B, Cd) this token's raw x | B | C
@@ -139,12 +158,12 @@ __global__ __launch_bounds__(256) void mixer_decode_kernel(const MixDecArgs<IO> 
       keep[k][1] = (float)rh[k][1];
       keep[k][2] = (float)rh[k][2];
       const float xk = (float)rx[k];
-      float u = cb[k];
-      u = __builtin_fmaf(w[k][0], keep[k][0], u);
-      u = __builtin_fmaf(w[k][1], keep[k][1], u);
-      u = __builtin_fmaf(w[k][2], keep[k][2], u);
-      u = __builtin_fmaf(w[k][3], xk, u);
-      const float v = io_round<IO>(u * __builtin_amdgcn_rcpf(1.f + __expf(-u)));
+      double u = (double)cb[k];
+      u = __builtin_fma((double)w[k][0], (double)keep[k][0], u);
+      u = __builtin_fma((double)w[k][1], (double)keep[k][1], u);
+      u = __builtin_fma((double)w[k][2], (double)keep[k][2], u);
+      u = __builtin_fma((double)w[k][3], (double)xk, u);
+      const float v = silu_io<IO>(u);
       if (i < P) sx[i] = v;
       else if (i < P + N) sB[i - P] = v;
       else sC[i - P - N] = v;

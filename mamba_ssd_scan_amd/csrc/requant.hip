@@ -13,6 +13,11 @@
 //   S  <- binary16_rne(s)
 // so the stored state after any number of tokens is reproducible bit for bit.
 //
+// The same kernel without the binary16 rounding (state kept in binary32) is
+// the window scan for binary32 I/O: the recurrence itself, token by token,
+// with every operand binary32 (a = (float) exp((double) dt A), s = fma(a, S,
+// dt x B), y = sum_n s C_n + D x), so no input is rounded to binary16.
+//
 // Work split: a workgroup owns one (sequence, head, block of ROWS state rows
 // p) for the whole window; each thread keeps RPT rows x 8 consecutive n of
 // the state in registers (binary16 values held as binary32).  Tokens are
@@ -21,6 +26,8 @@
 // the current block runs; y of a block is gathered in LDS and stored as 64
 // contiguous bytes per token.  The work is fp32 VALU-bound: per state element
 // and token one multiply, two fmas and a binary16 rounding.
+#include <type_traits>
+
 #include "common.h"
 #include "../../include/mamba2ssd.h"
 
@@ -82,12 +89,19 @@ template <> struct Raw8<float> {
   }
 };
 
-template <typename IO, int N>
+// RQ: the state is requantized to binary16 after every token (the pages'
+// scoring mode); otherwise it stays binary32, the exact token-sequential form
+// that serves binary32-I/O windows (the recurrence evaluated directly, with
+// no binary16 operand anywhere).  x, B and C rows are xld and gld elements
+// apart; xpk: their rows follow the caller's (packed) rows like dt and y,
+// else the padded row b * L + t of a conv output staged in the workspace.
+template <typename IO, int N, bool RQ>
 __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     const IO* __restrict__ x, const IO* __restrict__ dt, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ state_in,
     float* __restrict__ state_out, const int* __restrict__ seqlens, const int* __restrict__ cu_seqlens,
-    IO* __restrict__ y, int L, int T, int H, int G, int dt_sp, const float* __restrict__ dt_bias, long long dtld) {
+    IO* __restrict__ y, int L, int T, int H, int G, int dt_sp, const float* __restrict__ dt_bias, long long dtld,
+    long long xld, long long gld, int xpk) {
   constexpr int P = 64;
   constexpr int ROWS = RqShape<N>::ROWS, RPT = RqShape<N>::RPT, NTH = RqShape<N>::NTH;
   constexpr int LPR = N / 8;                 // lanes per state row
@@ -114,18 +128,20 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
   const float Ah = A[h], Dh = D[h];
   const float dtb = dt_sp && dt_bias ? dt_bias[h] : 0.f;
 
-  // state: binary16 in registers (the mixed-precision fmas read it directly)
-  _Float16 S[RPT][8];
+  // state: binary16 in registers (the mixed-precision fmas read it directly),
+  // or binary32 for the exact form
+  using st_t = typename std::conditional<RQ, _Float16, float>::type;
+  st_t S[RPT][8];
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     const int p = p0 + r0 + k * RSTRIDE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) S[k][i] = (_Float16)0.f;
+    for (int i = 0; i < 8; ++i) S[k][i] = (st_t)0.f;
     if (state_in) {
       float v[8];
       io<float>::load8(state_in + (((size_t)bh * P + p) * N + nc), v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) S[k][i] = (_Float16)v[i];
+      for (int i = 0; i < 8; ++i) S[k][i] = (st_t)v[i];
     }
   }
 
@@ -140,6 +156,7 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
     float d;
   };
   const size_t seqtok = (size_t)span.base;   // the sequence's first row
+  const size_t xtok = xpk ? seqtok : (size_t)b * L;   // its first row of x, B and C
   auto fetch = [&](Pre& r, int t0) {
 #pragma unroll
     for (int k = 0; k < (BC8 + NTH - 1) / NTH; ++k) {
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
       if (id < BC8) {
         const int t = id / (N / 8), c8 = id % (N / 8);
         const int tt = min(t0 + t, len - 1);
-        const size_t off = ((seqtok + tt) * G + g) * N + c8 * 8;
+        const size_t off = (xtok + tt) * (size_t)gld + (size_t)g * N + c8 * 8;
         r.b[k].load(Bm + off);
         r.c[k].load(Cm + off);
       }
@@ -158,7 +175,7 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
       if (id < XC) {
         const int t = id / ROWS, rr = id % ROWS;
         const int tt = min(t0 + t, len - 1);
-        r.xv[k] = io<IO>::load1(x + ((seqtok + tt) * H + h) * P + p0 + rr);
+        r.xv[k] = io<IO>::load1(x + (xtok + tt) * (size_t)xld + (size_t)h * P + p0 + rr);
       }
     }
     r.d = 0.f;
@@ -231,10 +248,12 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
             const float v = __builtin_fmaf(u, bv[i], mzero);   // exactly u * B
             float sn = __builtin_fmaf(a, (float)S[k][i], v);
             acc = __builtin_fmaf(sn, cv[i], acc);
-            // binary32 first, then binary16 (the empty asm keeps the two
-            // roundings apart: a fused fma-to-binary16 would round once)
-            asm volatile("" : "+v"(sn));
-            S[k][i] = (_Float16)sn;
+            if constexpr (RQ) {
+              // binary32 first, then binary16 (the empty asm keeps the two
+              // roundings apart: a fused fma-to-binary16 would round once)
+              asm volatile("" : "+v"(sn));
+            }
+            S[k][i] = (st_t)sn;
           }
         }
         acc = row_sum<LPR>(acc);
@@ -281,25 +300,44 @@ __global__ __launch_bounds__(RqShape<N>::NTH) void requant_window_kernel(
   }
 }
 
-template <typename IO, int N>
-static hipError_t launch_rq(const mamba2_dims& d, const mamba2_window_io& io_, hipStream_t st) {
+template <typename IO, int N, bool RQ>
+static hipError_t launch_rq(const mamba2_dims& d, const mamba2_window_io& io_, const IO* x, const IO* Bm,
+                            const IO* Cm, long long xld, long long gld, int xpk, hipStream_t st) {
   constexpr int ROWS = RqShape<N>::ROWS, NTH = RqShape<N>::NTH;
   const unsigned grid = (unsigned)(d.batch * d.nheads * (64 / ROWS));
-  requant_window_kernel<IO, N><<<grid, NTH, 0, st>>>(
-      (const IO*)io_.x, (const IO*)io_.dt, (const IO*)io_.B, (const IO*)io_.C, io_.A, io_.D, io_.state_in,
-      io_.state_out, io_.seqlens, io_.cu_seqlens, (IO*)io_.y, d.seqlen, d.packed_tokens, d.nheads, d.ngroups,
-      d.dt_softplus,
-      d.dt_softplus ? io_.dt_bias : nullptr, io_.dt_ld > 0 ? (long long)io_.dt_ld : (long long)d.nheads);
+  requant_window_kernel<IO, N, RQ><<<grid, NTH, 0, st>>>(
+      x, (const IO*)io_.dt, Bm, Cm, io_.A, io_.D, io_.state_in, io_.state_out, io_.seqlens, io_.cu_seqlens,
+      (IO*)io_.y, d.seqlen, d.packed_tokens, d.nheads, d.ngroups, d.dt_softplus,
+      d.dt_softplus ? io_.dt_bias : nullptr, io_.dt_ld > 0 ? (long long)io_.dt_ld : (long long)d.nheads, xld, gld,
+      xpk);
   return hipGetLastError();
 }
 
-hipError_t launch_requant_window(const mamba2_dims& d, const mamba2_window_io& io_, hipStream_t st) {
-  const bool f16 = d.io_dtype == MAMBA2_F16;
+template <typename IO, bool RQ>
+static hipError_t launch_rq_N(const mamba2_dims& d, const mamba2_window_io& io_, const IO* x, const IO* Bm,
+                              const IO* Cm, long long xld, long long gld, int xpk, hipStream_t st) {
   switch (d.dstate) {
-    case 16: return f16 ? launch_rq<_Float16, 16>(d, io_, st) : launch_rq<float, 16>(d, io_, st);
-    case 64: return f16 ? launch_rq<_Float16, 64>(d, io_, st) : launch_rq<float, 64>(d, io_, st);
-    default: return f16 ? launch_rq<_Float16, 128>(d, io_, st) : launch_rq<float, 128>(d, io_, st);
+    case 16: return launch_rq<IO, 16, RQ>(d, io_, x, Bm, Cm, xld, gld, xpk, st);
+    case 64: return launch_rq<IO, 64, RQ>(d, io_, x, Bm, Cm, xld, gld, xpk, st);
+    default: return launch_rq<IO, 128, RQ>(d, io_, x, Bm, Cm, xld, gld, xpk, st);
   }
+}
+
+hipError_t launch_requant_window(const mamba2_dims& d, const mamba2_window_io& io_, hipStream_t st) {
+  const long long xld = (long long)d.nheads * 64, gld = (long long)d.ngroups * d.dstate;
+  if (d.io_dtype == MAMBA2_F16)
+    return launch_rq_N<_Float16, true>(d, io_, (const _Float16*)io_.x, (const _Float16*)io_.B,
+                                       (const _Float16*)io_.C, xld, gld, 1, st);
+  return launch_rq_N<float, true>(d, io_, (const float*)io_.x, (const float*)io_.B, (const float*)io_.C, xld, gld, 1,
+                                  st);
+}
+
+// The exact binary32 window scan (binary32 I/O): x, B, C are the caller's
+// rows (xpk = 1) or the conv output staged in the workspace (xpk = 0, rows of
+// xld = gld = conv_dim elements).
+hipError_t launch_exact_window_f32(const mamba2_dims& d, const mamba2_window_io& io_, const float* x, const float* Bm,
+                                   const float* Cm, long long xld, long long gld, int xpk, hipStream_t st) {
+  return launch_rq_N<float, false>(d, io_, x, Bm, Cm, xld, gld, xpk, st);
 }
 
 }  // namespace m2

@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gfx950_ops.h"
 #include "../../include/mamba2ssd.h"
 
 namespace m2 {
@@ -71,18 +72,6 @@ constexpr int kCtrlGen = 9 * kCtrlStride;
 constexpr int kCtrlErr = 10 * kCtrlStride;
 constexpr int kCtrlBytes = 11 * kCtrlStride * 4;
 
-// The dt softplus of a raw dt in binary32 with the hardware exponential and
-// logarithm: v above 20, e (1 - e/2) for e = exp(v) below 1e-3 (the series of
-// log1p, error below e^3/3), else log(1 + e) (relative error below about
-// 6e-5, from rounding 1 + e).  The window scan only needs dt within its
-// tolerance; the double-precision form of the decode contract would keep its
-// constants in registers across the whole scan.
-__device__ __forceinline__ float dt_softplus_fast(float raw, float bias) {
-  const float v = raw + bias;
-  const float e = __expf(v);
-  const float sp = e < 1e-3f ? e * (1.f - 0.5f * e) : __logf(1.f + e);
-  return v > 20.f ? v : sp;
-}
 
 // Workgroup barrier that orders LDS only.  __syncthreads() would also wait for
 // every outstanding global load, which would drain the loads prefetched for
@@ -93,7 +82,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ h8 cat(h4 lo, h4 hi) { return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
 
 // ---------------------------------------------------------------------------
 // Causal depthwise conv1d (width 4) + SiLU over raw xBC (the mixer's input
@@ -281,40 +269,10 @@ constexpr int TS = 32;                 // tokens per step
 constexpr int PH = 32;                 // head-dim columns per item
 constexpr int PT = PH / 16;            // p-tiles per item
 constexpr int XP = PH + 8;             // pitch (halfs) of the [s][p] x tiles
-constexpr int kSc1 = 16;               // cache policy: device-coherent access
 static_assert(TS == 32 && PH == 32, "the x tiles are moved as 16 tokens x 4 chunks of 16 bytes per wave access");
 // (four neighbouring lanes load one token's 64 contiguous bytes: global
 //  coalescing outweighs the LDS bank conflicts of the matching tile writes)
 
-typedef short s4 __attribute__((ext_vector_type(4)));
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
-typedef unsigned u2 __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Buffer descriptor over [p, p + bytes).  p and bytes must be wave-uniform;
-// they are read from the first lane so that the descriptor is built in SGPRs
-// (a descriptor the compiler cannot prove uniform turns every access through
-// it into a loop over lanes).
-__device__ __forceinline__ rsrc_t mkr(const void* p, unsigned bytes) {
-  const unsigned long long v = (unsigned long long)p;
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
-  void* const pu = (void*)(((unsigned long long)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-
-// 2^x with the hardware exponential (arguments here are <= 0; results below
-// the binary32 normal range are negligible against the terms they scale)
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Transposed 64-bit LDS read: within each 16-lane group, lane i receives the
-// 16-bit elements at column (i % 4) of the 8-byte chunks addressed by lanes
-// 4k + i / 4, k = 0..3.
-__device__ __forceinline__ h4 tr4(const _Float16* p) {
-  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s4*)(__attribute__((address_space(3))) void*)(p));
-  return __builtin_bit_cast(h4, v);
-}
 
 // NV (4 or 8) consecutive elements at byte offset off, as binary16, zero-padded to 8
 template <typename IO, int NV> __device__ __forceinline__ h8 ldh(rsrc_t r, unsigned off) {
@@ -762,6 +720,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
         }
       __builtin_amdgcn_s_waitcnt(0);
+      // compiler-only fence: no data store may be moved past the flag store
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       // one 64-bit word carries the aggregate's decay and the ready tag
       const unsigned long long f =
           ((unsigned long long)__float_as_uint(segdec * scale) << 32) | (unsigned long long)(tag | 1u);
@@ -792,6 +752,8 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
           break;
         }
       }
+      // compiler-only fence: the aggregate loads stay after the poll
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
     // Aggregates k0 .. k1-1 are folded with two in flight: even positions land
     // in registers, odd ones in this wave's LDS area (direct loads, 1 KB per
@@ -1007,22 +969,24 @@ __global__ __launch_bounds__(64 * wv::NWV) void ssd_window_group_kernel(WinArgs<
 // Gated RMSNorm finish from partial sums: out = g * rsqrt(mean_group(g^2) +
 // eps) * w, where y already holds g and the kNormParts partial sums of g^2 per
 // (token, head) come from the kernel that produced g (the one-token mixer
-// step).  One block per token: the partials of a norm group are summed in LDS
-// (a whole wave at a time when a group spans at least 64 partials), then every
-// channel is rescaled in place.
+// step).  One block per token.  The partials of a norm group are summed in a
+// fixed order, so the result does not depend on timing: when a group spans
+// whole waves of 64 partials, each wave sums its 64 with a butterfly and
+// leaves one value per wave; otherwise each group's partials are added in
+// index order by one thread.  Then every channel is rescaled in place.
 template <typename IO>
 __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, const float* __restrict__ normsum,
                                                          const float* __restrict__ nw, const int* __restrict__ seqlens,
                                                          const int* __restrict__ cu, int L, int T, int H, int group,
                                                          float eps) {
+  constexpr int kMaxParts = 1024;                 // H * kNormParts <= 1024 is checked by the caller
   __shared__ float gs[256];
+  __shared__ float part[kMaxParts];
   const int tok = blockIdx.x, b = tok / L, t = tok - b * L;   // (sequence, token) of the padded index
   const SeqRows span = seq_rows(seqlens, cu, b, L, T);
   if (t >= span.len) return;
   const int C = H * kP, ngr = C / group;
   const int np = H * kNormParts, seg = (group / kP) * kNormParts;   // partials per token, per group
-  for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = 0.f;
-  __syncthreads();
   const float* ps = normsum + (size_t)tok * np;
   const bool wave_sums = seg % 64 == 0;
   for (int k0 = 0; k0 < np; k0 += 256) {
@@ -1031,13 +995,18 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
     if (wave_sums) {
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-      if ((threadIdx.x & 63) == 0 && k < np) atomicAdd(&gs[k / seg], v);
+      if ((threadIdx.x & 63) == 0 && k < np) part[k / 64] = v;
     } else if (k < np) {
-      atomicAdd(&gs[k / seg], v);
+      part[k] = v;
     }
   }
   __syncthreads();
-  for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = rsqrtf(gs[gi] / (float)group + eps);
+  const int per = wave_sums ? seg / 64 : seg;     // values per group in `part`
+  for (int gi = threadIdx.x; gi < ngr; gi += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < per; ++j) acc += part[gi * per + j];
+    gs[gi] = rsqrtf(acc / (float)group + eps);
+  }
   __syncthreads();
   IO* row = y + (size_t)(span.base + t) * C;
   for (int c0 = threadIdx.x * 8; c0 < C; c0 += 256 * 8) {
@@ -1058,9 +1027,11 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(IO* __restrict__ y, con
 // at a time, 2048 channels apart; the first kGateRegs of its runs keep g in
 // registers between the sums and the rescale, later runs (C above 8192)
 // recompute g from y and z, which the block has not yet overwritten.  The
-// sums of g^2 are reduced per wave (a group spans whole 512-channel wave
-// runs) or per 8 lanes (every group is whole heads of 64 channels), then
-// added in LDS.  Rows past a sequence's length are left untouched.
+// sums of g^2 are taken in a fixed order, so the result does not depend on
+// timing: each wave sums a run of 512 channels (a group spans whole runs) or
+// 8 lanes sum 64 channels (every group is whole heads of 64 channels), into
+// one LDS slot per run; then each group's slots are added in channel order.
+// Rows past a sequence's length are left untouched.
 constexpr int kGateRegs = 4;
 template <typename IO>
 __device__ __forceinline__ void gate8(const IO* y, const IO* z, float (&g)[8]) {
@@ -1075,16 +1046,17 @@ __global__ __launch_bounds__(256) void gate_norm_kernel(IO* __restrict__ y, cons
                                                         const float* __restrict__ nw, const int* __restrict__ seqlens,
                                                         const int* __restrict__ cu, int L, int T, int C, int group,
                                                         float eps, long long zld) {
+  constexpr int kMaxRuns = 1024;                  // C / 64 <= 1024 is checked by the caller
   __shared__ float gs[256];
+  __shared__ float runs[kMaxRuns];
   const int tok = blockIdx.x, b = tok / L, t = tok - b * L;   // (sequence, token) of the padded index
   const SeqRows span = seq_rows(seqlens, cu, b, L, T);
   if (t >= span.len) return;
   const int ngr = C / group, lane = threadIdx.x & 63;
-  for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = 0.f;
-  __syncthreads();
   IO* const yr = y + (size_t)(span.base + t) * C;
   const IO* const zr = z + (size_t)(span.base + t) * (size_t)zld;
   const bool wave_runs = group % 512 == 0;
+  const int run = wave_runs ? 512 : 64;           // channels per slot
   auto add = [&](int c0, const float (&g)[8]) {   // every lane of the wave calls this together
     float sq = 0.f;
     if (c0 < C) {
@@ -1098,9 +1070,9 @@ __global__ __launch_bounds__(256) void gate_norm_kernel(IO* __restrict__ y, cons
       sq += __shfl_xor(sq, 8, 64);
       sq += __shfl_xor(sq, 16, 64);
       sq += __shfl_xor(sq, 32, 64);
-      if (lane == 0 && c0 < C) atomicAdd(&gs[c0 / group], sq);
+      if (lane == 0 && c0 < C) runs[c0 / 512] = sq;
     } else if ((lane & 7) == 0 && c0 < C) {
-      atomicAdd(&gs[c0 / group], sq);
+      runs[c0 / 64] = sq;
     }
   };
   float g[kGateRegs][8];
@@ -1117,7 +1089,12 @@ __global__ __launch_bounds__(256) void gate_norm_kernel(IO* __restrict__ y, cons
     add(c0, gk);
   }
   __syncthreads();
-  for (int gi = threadIdx.x; gi < ngr; gi += 256) gs[gi] = rsqrtf(gs[gi] / (float)group + eps);
+  const int per = group / run;                    // slots per group
+  for (int gi = threadIdx.x; gi < ngr; gi += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < per; ++j) acc += runs[gi * per + j];
+    gs[gi] = rsqrtf(acc / (float)group + eps);
+  }
   __syncthreads();
   auto put = [&](int c0, const float (&gk)[8]) {
     const float r = gs[c0 / group];
@@ -1155,6 +1132,9 @@ hipError_t launch_gated_norm_tokens(int io_f16, void* y, const float* normsum, c
   return hipGetLastError();
 }
 int norm_parts_per_head() { return kNormParts; }
+
+hipError_t launch_exact_window_f32(const mamba2_dims& d, const mamba2_window_io& io_, const float* x, const float* Bm,
+                                   const float* Cm, long long xld, long long gld, int xpk, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 struct WsLayout {
@@ -1269,18 +1249,48 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     a.gstride = d.ngroups * d.dstate;
   }
   hipError_t e;
-  constexpr bool F16IO = sizeof(IO) == 2;   // only binary16 conv output carries a remainder
-  const bool blo = a.Blo != nullptr;
-  switch (d.dstate) {
-    case 16: e = blo ? launch_scan<IO, 16, F16IO>(a, st) : launch_scan<IO, 16, false>(a, st); break;
-    case 64: e = blo ? launch_scan<IO, 64, F16IO>(a, st) : launch_scan<IO, 64, false>(a, st); break;
-    default: e = blo ? launch_scan<IO, 128, F16IO>(a, st) : launch_scan<IO, 128, false>(a, st); break;
+  if constexpr (sizeof(IO) == 4) {
+    // binary32 I/O: the exact token-sequential form in binary32 (the chunked
+    // form's MFMA operands are binary16 and would round binary32 inputs)
+    e = launch_exact_window_f32(d, io_, a.x, a.Bm, a.Cm, a.xstride, a.gstride, d.conv_width == 4 ? 0 : 1, st);
+  } else {
+    const bool blo = a.Blo != nullptr;   // only binary16 conv output carries a remainder
+    switch (d.dstate) {
+      case 16: e = blo ? launch_scan<IO, 16, true>(a, st) : launch_scan<IO, 16, false>(a, st); break;
+      case 64: e = blo ? launch_scan<IO, 64, true>(a, st) : launch_scan<IO, 64, false>(a, st); break;
+      default: e = blo ? launch_scan<IO, 128, true>(a, st) : launch_scan<IO, 128, false>(a, st); break;
+    }
   }
   if (e != hipSuccess || d.norm_group == 0) return e;
   gate_norm_kernel<IO><<<(unsigned)(d.batch * d.seqlen), 256, 0, st>>>(
       (IO*)io_.y, (const IO*)io_.z, io_.norm_w, io_.seqlens, io_.cu_seqlens, d.seqlen, d.packed_tokens,
       d.nheads * kP, d.norm_group, d.norm_eps, io_.z_ld > 0 ? (long long)io_.z_ld : (long long)d.nheads * kP);
   return hipGetLastError();
+}
+
+// The workspace's error word, read after the stream's queued work and
+// cleared when set.  Bit 0: some segment's bounded wait for an aggregate gave
+// up (the outputs of that call are not valid).
+__global__ void clear_word_kernel(unsigned* w) { *w = 0u; }
+
+size_t window_control_bytes() { return (size_t)kCtrlBytes; }
+
+hipError_t window_take_error(void* ws, unsigned* flags, hipStream_t st) {
+  unsigned* w = (unsigned*)ws + kCtrlErr;
+  unsigned v = 0;
+  hipError_t e = hipMemcpyAsync(&v, w, sizeof(unsigned), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return e;
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return e;
+  if (v != 0u) {
+    clear_word_kernel<<<1, 1, 0, st>>>(w);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return e;
+  }
+  *flags = v;
+  return hipSuccess;
 }
 
 hipError_t launch_window(const mamba2_dims& d, const mamba2_window_io& io_, void* ws, hipStream_t st) {

@@ -49,6 +49,9 @@ def _load():
         lib.oracle_f16_round.restype = ctypes.c_double
         lib.oracle_f16_round.argtypes = [ctypes.c_double]
         lib.oracle_f16_round_array.argtypes = [dp, dp, i64]
+        lib.oracle_f16_bits_to_double_array.argtypes = [u16p, dp, i64]
+        lib.oracle_double_to_f16_bits_array.argtypes = [dp, u16p, i64]
+        lib.oracle_decode_f16state_fp64.argtypes = [i, i, i, i, i, i, fp, fp, fp, fp, fp, fp, u16p, dp, i, i, i]
         lib.oracle_conv_silu.argtypes = [i, i, i, i, dp, dp, dp, dp, ip, dp, dp]
         lib.oracle_ssd_scan.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, ip, dp, dp, dp, i]
         lib.oracle_gated_rmsnorm.argtypes = [i64, i, i, dp, dp, dp, ctypes.c_double, dp]
@@ -87,6 +90,22 @@ def f16_round(v):
     v = _f64(v)
     out = np.empty_like(v)
     _load().oracle_f16_round_array(_ptr(v, ctypes.c_double), _ptr(out, ctypes.c_double), v.size)
+    return out
+
+
+def f16_bits_to_double(bits):
+    """binary16 bit patterns (uint16) -> their exact values as fp64."""
+    bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(bits.shape, np.float64)
+    _load().oracle_f16_bits_to_double_array(_ptr(bits, ctypes.c_uint16), _ptr(out, ctypes.c_double), bits.size)
+    return out
+
+
+def double_to_f16_bits(v):
+    """fp64 values that are binary16 values -> their bit patterns (uint16)."""
+    v = _f64(v)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_double_to_f16_bits_array(_ptr(v, ctypes.c_double), _ptr(out, ctypes.c_uint16), v.size)
     return out
 
 
@@ -247,4 +266,20 @@ def decode_f16state(x, dt, A, Bm, Cm, D, state_bits, b_range=None, nthreads: int
     _load().oracle_decode_f16state(T, B, H, P, N, G, *(_ptr(a, ctypes.c_float) for a in (x, dt, A, Bm, Cm, D)),
                                    _ptr(state_bits, ctypes.c_uint16), _ptr(y, ctypes.c_double), int(lo), int(hi),
                                    int(nthreads))
+    return y
+
+
+def decode_f16state_fp64(x, dt, A, Bm, Cm, D, state_bits, b_range=None, nthreads: int = 0):
+    """decode_f16state with every step taken in fp64 and rounded straight to
+    binary16 (no binary32 stage).  Same arguments and layouts (dt positive);
+    the state is updated in place for the sequences in b_range; returns y."""
+    x, dt, A, Bm, Cm, D = (_f32(a) for a in (x, dt, A, Bm, Cm, D))
+    T, B, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    assert state_bits.dtype == np.uint16 and state_bits.shape == (B, H, P, N) and state_bits.flags.c_contiguous
+    lo, hi = b_range if b_range is not None else (0, B)
+    y = np.full((T, B, H, P), np.nan)
+    _load().oracle_decode_f16state_fp64(T, B, H, P, N, G, *(_ptr(a, ctypes.c_float) for a in (x, dt, A, Bm, Cm, D)),
+                                        _ptr(state_bits, ctypes.c_uint16), _ptr(y, ctypes.c_double), int(lo),
+                                        int(hi), int(nthreads))
     return y

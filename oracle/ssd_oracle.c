@@ -108,10 +108,20 @@ uint16_t oracle_double_to_f16_bits(double v)
     return s | (uint16_t)(ex << 10) | fr;
 }
 
-/* Vector helpers used by the Python side (rounding pins). */
+/* Vector helpers used by the Python side (rounding and conversion pins). */
 void oracle_f16_round_array(const double* in, double* out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_round(in[i]);
+}
+
+void oracle_f16_bits_to_double_array(const uint16_t* in, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_bits_to_double(in[i]);
+}
+
+void oracle_double_to_f16_bits_array(const double* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_double_to_f16_bits(in[i]);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -430,6 +440,50 @@ void oracle_decode_f16state(int T, int B, int H, int P, int N, int G,
                     const float s_new = fmaf(a, s_old, v);
                     acc += (double)s_new * (double)Ct[n];
                     St[p * N + n] = oracle_double_to_f16_bits((double)f16_round_f(s_new));
+                }
+                yt[p] = acc + (double)D[h] * (double)xt[p];
+            }
+        }
+    }
+}
+
+/* The same steps read the other way: every step taken in fp64 from the
+ * binary16 state and rounded straight to binary16, with no binary32 stage:
+ *   a  = exp(dt * A);   s = a * S + dt * x * B   (fp64, one value per element)
+ *   y += s * C (fp64);  S <- f16_rne(s)
+ * Inputs as for oracle_decode_f16state (binary32 values, used exactly).  It
+ * serves to measure how far the binary32 contract above drifts from an fp64
+ * step over many tokens; no kernel follows it. */
+void oracle_decode_f16state_fp64(int T, int B, int H, int P, int N, int G,
+                                 const float* x, const float* dt, const float* A,
+                                 const float* Bm, const float* Cm, const float* D,
+                                 uint16_t* state, double* y, int b_lo, int b_hi,
+                                 int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int hpg = H / G;
+    const int nbh = (b_hi - b_lo) * H;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nbh; ++i) {
+        const int b = b_lo + i / H, h = i % H, g = h / hpg;
+        uint16_t* St = state + ((size_t)b * H + h) * P * N;
+        for (int t = 0; t < T; ++t) {
+            const double d = dt[((size_t)t * B + b) * H + h];
+            const double a = exp(d * (double)A[h]);
+            const float* xt = x + (((size_t)t * B + b) * H + h) * P;
+            const float* Bt = Bm + (((size_t)t * B + b) * G + g) * N;
+            const float* Ct = Cm + (((size_t)t * B + b) * G + g) * N;
+            double* yt = y + (((size_t)t * B + b) * H + h) * P;
+            for (int p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    const double s = a * oracle_f16_bits_to_double(St[p * N + n]) + d * (double)xt[p] * (double)Bt[n];
+                    acc += s * (double)Ct[n];
+                    St[p * N + n] = oracle_double_to_f16_bits(oracle_f16_round(s));
                 }
                 yt[p] = acc + (double)D[h] * (double)xt[p];
             }

@@ -15,6 +15,14 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
+def window_checked(dt, A, D, y, workspace, **kw):
+    """mamba2_conv_scan_window, then the workspace's error word, which must
+    be clear (every segment hand-off completed)."""
+    m2.conv_scan_window(dt, A, D, y, workspace, **kw)
+    flags = m2.window_take_error(workspace)
+    assert flags == 0, f"window hand-off error word {flags:#x}"
+
+
 def slice_err(got, ref, nlead):
     """max over slices of max|got-ref| / max|ref|; a slice is one index of the
     first `nlead` axes (e.g. (b, h)).  NaN/Inf anywhere in got -> inf."""
@@ -53,7 +61,7 @@ def run_window(inp, chunk, seqlens=None, state_in=None, want_state=True, ws=None
     if ws is None:
         dims = m2.make_dims(Bsz, L, H, P, N, G, chunk, io_dtype=m2.F16 if x.dtype == torch.float16 else m2.F32)
         ws = m2.alloc_workspace(dims, DEV)
-    m2.conv_scan_window(dt, A, D, y, ws, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl, chunk=chunk,
+    window_checked(dt, A, D, y, ws, x=x, B=Bm, C=Cm, state_in=h0, state_out=hT, seqlens=sl, chunk=chunk,
                         segments=segments, **raw_dt_args(inp))
     torch.cuda.synchronize()
     return y.cpu().numpy().reshape(Bsz, L, H, P), (hT.cpu().numpy() if want_state else None)
@@ -100,7 +108,7 @@ def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=No
     dims = m2.make_dims(Bsz, L, H, P, N, G, chunk, conv_width=4, norm_group=norm_group,
                         io_dtype=m2.F16 if xBC.dtype == torch.float16 else m2.F32)
     ws = m2.alloc_workspace(dims, DEV)
-    m2.conv_scan_window(to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xBC,
+    window_checked(to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xBC,
                         conv_w=to_dev(inp["conv_w"]), conv_b=to_dev(inp["conv_b"]), conv_state_in=csi,
                         conv_state_out=cso, state_in=h0, state_out=hT, seqlens=sl,
                         z=to_dev(inp["z"]) if norm_group else None,
@@ -144,7 +152,7 @@ def run_window_packed(inp, lens, chunk, state_in=None, spare_rows=16, fill=12345
     dims = m2.make_dims(Bsz, L, H, P, N, G, chunk, io_dtype=m2.F16 if x.dtype == torch.float16 else m2.F32,
                         packed_tokens=T)
     ws = m2.alloc_workspace(dims, DEV)
-    m2.conv_scan_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=x, B=Bm, C=Cm, state_in=h0,
+    window_checked(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=x, B=Bm, C=Cm, state_in=h0,
                         state_out=hT, chunk=chunk, segments=segments, cu_seqlens=cu, max_seqlen=L,
                         **raw_dt_args(inp))
     torch.cuda.synchronize()

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = m2.load_library()
-    assert m2.abi_version() == 7
+    assert m2.abi_version() == 8
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.mamba2_status_str(code)
     assert lib.mamba2_status_str(77) == b"unknown status"
@@ -290,6 +290,18 @@ def test_mixer_decode_validation_codes():
     assert call(io(y=FAKE + 8 * MB + 4096)) == -1
     assert call(io(conv_state=FAKE + 1024)) == -1
     assert call(io(), ws=FAKE + 2 * MB) == -1
+
+
+@fake_pointers
+def test_window_take_error_validation_codes():
+    lib = m2.load_library()
+    v = ctypes.c_uint32(7)
+    ws = ctypes.c_void_p(FAKE)
+    assert lib.mamba2_window_take_error(None, 1 << 20, ctypes.byref(v), None) == -1
+    assert lib.mamba2_window_take_error(ws, 1 << 20, None, None) == -1
+    assert lib.mamba2_window_take_error(ws, 64, ctypes.byref(v), None) == -4      # smaller than the control block
+    assert lib.mamba2_window_take_error(ctypes.c_void_p(FAKE + 128), 1 << 20, ctypes.byref(v), None) == -3
+    assert v.value == 7                                                            # untouched on error
 
 
 @fake_pointers

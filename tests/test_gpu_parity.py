@@ -21,7 +21,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 
 import mamba_ssd_scan_amd as m2  # noqa: E402
 from tests.gpu_helpers import (DEV, cu_of, pack_rows, projection_rows, run_mixer, run_requant, run_window,  # noqa: E402
-                               run_window_packed, slice_err, to_dev, unpack_rows)
+                               run_window_packed, slice_err, to_dev, unpack_rows, window_checked)
 
 Y_TOL, S_TOL = 2e-3, 1e-3
 
@@ -140,17 +140,18 @@ def test_layer_window_full_size():
     check_window("layer L=2048", synth.window_inputs(s, 1001), s.chunk)
 
 
-def test_batched_windows_full_size_sampled():
+def test_batched_windows_full_size():
+    # all eight sequences (seven of 2048 tokens and the 1955-token partial
+    # window) and all eight final states against the oracle
     s = synth.batched_windows()
     inp = synth.window_inputs(s, 1002)
     say(f"[window] batched: x{inp['x'].shape} lengths {s.seqlens}")
     y, hT = run_window(inp, s.chunk, seqlens=s.seqlens, y_fill=12345.0)
-    for b in (0, 7):      # a full window and the 1955-token partial window
-        sub = {k: (v[b:b + 1] if v.ndim > 1 else v) for k, v in inp.items()}
+    yr, hr = oracle_window(inp, list(s.seqlens))
+    for b in range(s.batch):
         n = s.seqlens[b]
-        yr, hr = oracle_window(sub, [n])
-        ey = slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)), np.transpose(yr[:, :n], (0, 2, 1, 3)), 2)
-        es = slice_err(hT[b:b + 1], hr, 2)
+        ey = slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)), np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2)
+        es = slice_err(hT[b:b + 1], hr[b:b + 1], 2)
         say(f"[window] batched seq {b} (len {n}): y {ey:.3e} state {es:.3e}")
         assert ey <= Y_TOL and es <= S_TOL
         assert np.all(y[b, n:] == np.float16(12345.0))
@@ -189,7 +190,7 @@ def test_packed_sequence_longer_than_seqlen_is_cut():
     dims = m2.make_dims(2, 400, 4, 64, 64, 1, 256, packed_tokens=T)
     ws = m2.alloc_workspace(dims, DEV)
     say("[packed] second sequence cut at seqlen 400")
-    m2.conv_scan_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=x, B=Bm, C=Cm, state_out=hT,
+    window_checked(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=x, B=Bm, C=Cm, state_out=hT,
                         cu_seqlens=to_dev(cu_of(lens)), max_seqlen=400)
     torch.cuda.synchronize()
     yp, hT = y.cpu().numpy(), hT.cpu().numpy()
@@ -260,7 +261,7 @@ def test_packed_mixer_core_with_conv_state_and_norm():
     dims = m2.make_dims(len(lens), L, H, P, N, G, 256, conv_width=4, norm_group=512, packed_tokens=T)
     ws = m2.alloc_workspace(dims, DEV)
     say(f"[packed] mixer lengths {lens}")
-    m2.conv_scan_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xBC, conv_w=to_dev(inp["conv_w"]),
+    window_checked(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xBC, conv_w=to_dev(inp["conv_w"]),
                         conv_b=to_dev(inp["conv_b"]), conv_state_in=to_dev(csi), conv_state_out=cso, state_out=hT,
                         z=z, norm_w=to_dev(inp["norm_w"]), chunk=256, norm_group=512, ngroups=G, dstate=N,
                         headdim=P, dt_softplus=True, dt_bias=to_dev(inp["dt_bias"]), cu_seqlens=to_dev(cu_of(lens)),
@@ -496,7 +497,7 @@ def test_window_gated_norm_group_shapes(H, G, group, dtype):
     dims = m2.make_dims(2, L, H, P, N, G, 64, norm_group=group, io_dtype=m2.F16 if dtype == np.float16 else m2.F32)
     ws = m2.alloc_workspace(dims, DEV)
     say(f"[norm] H={H} G={G} group={group} {np.dtype(dtype).name}")
-    m2.conv_scan_window(to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=to_dev(inp["x"]),
+    window_checked(to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=to_dev(inp["x"]),
                         B=to_dev(inp["B"]), C=to_dev(inp["C"]), seqlens=torch.tensor(lens, dtype=torch.int32,
                                                                                      device=DEV),
                         z=to_dev(z), norm_w=to_dev(w), chunk=64, norm_group=group)
@@ -571,7 +572,7 @@ def test_mixer_core_reads_z_xbc_dt_in_projection_rows(packed):
         hT = torch.empty((len(lens), H, P, N), dtype=torch.float32, device=DEV)
         cso = torch.empty((len(lens), Cn, 3), dtype=torch.float16, device=DEV)
         ws = m2.alloc_workspace(dims, DEV)
-        m2.conv_scan_window(dd, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xx, conv_w=to_dev(inp["conv_w"]),
+        window_checked(dd, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=xx, conv_w=to_dev(inp["conv_w"]),
                             conv_b=to_dev(inp["conv_b"]), conv_state_in=csi, conv_state_out=cso, state_out=hT, z=zz,
                             norm_w=to_dev(inp["norm_w"]), chunk=256, norm_group=1024, ngroups=G, dstate=N,
                             headdim=P, dt_softplus=True, dt_bias=to_dev(inp["dt_bias"]), **extra)
@@ -625,7 +626,7 @@ def test_packed_mixer_core_xbc_slice_of_projection_rows():
         cso = torch.empty((len(lens), Cn, 3), dtype=torch.float16, device=DEV)
         dims = m2.make_dims(len(lens), L, H, P, N, G, 256, conv_width=4, norm_group=1024, packed_tokens=T)
         ws = m2.alloc_workspace(dims, DEV)
-        m2.conv_scan_window(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=x, conv_w=to_dev(inp["conv_w"]),
+        window_checked(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, xBC=x, conv_w=to_dev(inp["conv_w"]),
                             conv_b=to_dev(inp["conv_b"]), conv_state_out=cso, state_out=hT, z=z,
                             norm_w=to_dev(inp["norm_w"]), chunk=256, norm_group=1024, ngroups=G, dstate=N,
                             headdim=P, cu_seqlens=to_dev(cu_of(lens)), max_seqlen=L)
@@ -682,7 +683,7 @@ def test_decode_f16_state_small(N):
     ey = slice_err(np.stack(yg).transpose(1, 2, 0, 3), yr.transpose(1, 2, 0, 3), 2)
     es = slice_err(sg.astype(np.float64), bits.view(np.float16).astype(np.float64), 2)
     say(f"[decode] N={N}: state identical {same:.6f} state err {es:.2e} y err {ey:.2e}")
-    assert same >= 0.9999 and es <= S_TOL and ey <= Y_TOL
+    assert same == 1.0 and es <= S_TOL and ey <= Y_TOL
 
 
 def test_decode_raw_dt_f16_state_bit_exact():
@@ -746,7 +747,7 @@ def test_decode_full_size_1024_steps_sampled():
     prm = synth.decode_params(seed, Bsz, H, P, N)
     s16 = torch.empty((Bsz, H, P, N), dtype=torch.float16, device=DEV)
     m2.state_load(to_dev(prm["state"]), s16)
-    sample = (0, 37)
+    sample = (0, 9, 18, 27, 37, 45, 54, 63)     # eight sequences spread over the 64, the last included
     keep = {k: [] for k in ("x", "dt", "B", "C", "y")}
     A, D = to_dev(prm["A"]), to_dev(prm["D"])
     y = torch.empty((Bsz, H, P), dtype=torch.float16, device=DEV)
@@ -766,4 +767,4 @@ def test_decode_full_size_1024_steps_sampled():
     es = slice_err(sg.astype(np.float64), bits.view(np.float16).astype(np.float64), 2)
     ey = slice_err(np.stack(keep["y"]).transpose(1, 2, 0, 3), yr.transpose(1, 2, 0, 3), 2)
     say(f"[decode] full sampled: identical {same:.6f} state err {es:.2e} y err {ey:.2e}")
-    assert es <= S_TOL and ey <= Y_TOL
+    assert same == 1.0 and es <= S_TOL and ey <= Y_TOL

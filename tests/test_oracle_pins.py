@@ -212,7 +212,48 @@ def test_gated_norm_closed_forms():
         assert rel(og[:, sl], oracle.gated_rmsnorm(y[:, sl], zz[:, sl], w[sl], 16)) < 1e-15
 
 
+def test_gated_norm_weight_is_a_per_channel_factor():
+    # The output is linear in the weight and the weight of channel c scales
+    # channel c only: out(w) == w * out(1) exactly (one more fp64 product), a
+    # one-hot weight leaves one channel.  A dropped weight, a weight inside the
+    # mean, or one indexed by group or position in the group fails.
+    C, group = 96, 32
+    r = np.random.default_rng(26)
+    y, z = r.standard_normal((5, C)), r.standard_normal((5, C))
+    w = r.standard_normal(C) * 3.0
+    o1 = oracle.gated_rmsnorm(y, z, np.ones(C), group)
+    ow = oracle.gated_rmsnorm(y, z, w, group)
+    assert np.array_equal(ow, o1 * w)
+    assert not np.array_equal(ow, o1)
+    for c in (0, 31, 32, 95):
+        e = np.zeros(C)
+        e[c] = 1.0
+        oc = oracle.gated_rmsnorm(y, z, e, group)
+        assert np.array_equal(oc[:, c], o1[:, c])
+        assert np.count_nonzero(oc) == 5
+
+
 # --- P12: binary16 rounding against numpy ------------------------------------
+def test_f16_bit_converters_exhaustive():
+    # every binary16 bit pattern: its value matches numpy's reading of the
+    # same bits, and the value converts back to the same pattern (NaNs to a
+    # NaN pattern); signed zeros, subnormals and infinities included
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.f16_bits_to_double(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    back = oracle.double_to_f16_bits(got[~nan])
+    assert np.array_equal(back, bits[~nan])
+    nb = oracle.double_to_f16_bits(np.array([np.nan, -np.nan]))
+    assert np.all(np.isnan(nb.view(np.float16)))
+    sub = bits[(bits & 0x7C00) == 0]                         # zeros and subnormals
+    assert sub.size == 2048
+    assert np.array_equal(oracle.double_to_f16_bits(oracle.f16_bits_to_double(sub)), sub)
+
+
 def test_f16_round_all_values_and_midpoints():
     allh = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
     finite = allh[np.isfinite(allh)].astype(np.float64)
@@ -283,6 +324,43 @@ def test_decode_tracks_fp64_recurrence_within_f16_noise():
 
 
 # --- P13 / P14: partial windows and batch independence ------------------------
+def test_decode_fp64_step_reading():
+    # The other reading of the per-token requantization: each step in fp64,
+    # rounded straight to binary16.  With dt = 0 the state stays put and y is
+    # C.S + D x; one step from a binary16 state equals numpy's own binary16
+    # rounding of the fp64 update; over T steps it stays within T half-ulps
+    # of the unrounded recurrence; and it differs from the binary32 contract
+    # only where the binary32 stage moved a value across a binary16 rounding
+    # boundary (one ulp at most after one step).
+    T, B, H, P, N, G = 16, 2, 4, 8, 16, 2
+    x, dt, A, Bm, Cm, D, s0 = _decode_inputs(27, T, B, H, P, N, G)
+    g = np.arange(H) // (H // G)
+    bits = s0.view(np.uint16).copy()
+    y0 = oracle.decode_f16state_fp64(x, np.zeros_like(dt), A, Bm, Cm, D, bits)
+    assert np.array_equal(bits, s0.view(np.uint16))
+    ref0 = np.einsum("tbhn,bhpn->tbhp", Cm[:, :, g].astype(np.float64), s0.astype(np.float64)) \
+        + D[None, None, :, None].astype(np.float64) * x
+    assert rel(y0, ref0) < 1e-13
+    b1 = s0.view(np.uint16).copy()
+    oracle.decode_f16state_fp64(x[:1], dt[:1], A, Bm[:1], Cm[:1], D, b1)
+    d = dt[0].astype(np.float64)[:, :, None, None]
+    a = np.exp(d * A.astype(np.float64)[None, :, None, None])
+    upd = a * s0.astype(np.float64) + d * x[0].astype(np.float64)[..., None] * Bm[0][:, g].astype(np.float64)[:, :, None, :]
+    assert np.array_equal(b1, upd.astype(np.float16).view(np.uint16))
+    b32 = s0.view(np.uint16).copy()
+    oracle.decode_f16state(x[:1], dt[:1], A, Bm[:1], Cm[:1], D, b32)
+    diff = np.abs(b1.view(np.float16).astype(np.float64) - b32.view(np.float16).astype(np.float64))
+    ulp = np.spacing(np.abs(b1.view(np.float16))).astype(np.float64)
+    assert np.mean(b1 == b32) > 0.99 and np.all(diff <= ulp)
+    bT = s0.view(np.uint16).copy()
+    yT = oracle.decode_f16state_fp64(x, dt, A, Bm, Cm, D, bT)
+    yr, hr = oracle.ssd_scan(np.transpose(x, (1, 0, 2, 3)), np.transpose(dt, (1, 0, 2)), A,
+                             np.transpose(Bm, (1, 0, 2, 3)), np.transpose(Cm, (1, 0, 2, 3)), D,
+                             h0=s0.astype(np.float64))
+    assert rel(bT.view(np.float16).astype(np.float64), hr) < T * 2.0 ** -11
+    assert rel(np.transpose(yT, (1, 0, 2, 3)), yr) < T * 2.0 ** -11
+
+
 def test_partial_window_isolation_and_batch_independence():
     x, dt, A, Bm, Cm, D = rand_inputs(26, 3, 80, 4, 4, 8, 2)
     lens = [80, 53, 1]
