@@ -36,12 +36,17 @@ MFMA_F16_PEAK = 2500.0     # TFLOP/s dense f16
 # fp32 VALU issue without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_layer_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "mamba_ssd_scan_amd", "csrc", "window.hip")
+# the window kernel's sources: the kernel, its argument block and the helpers it includes
+KERNEL_SOURCES = [os.path.join(ROOT, "mamba_ssd_scan_amd", "csrc", n)
+                  for n in ("ssd_scan.hip", "ssd_scan.h", "gfx950_ops.h", "common.h")]
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

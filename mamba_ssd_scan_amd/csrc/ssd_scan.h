@@ -1,0 +1,39 @@
+// Arguments of the streamed window scan (ssd_scan.hip) and its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace m2 {
+
+struct ScanArgs {
+  int B, L, H, G, Q, nchunks;
+  const _Float16* x;   // x rows: token stride xstride elements
+  const _Float16* Bm;  // B rows: token stride gstride elements
+  const _Float16* Cm;  // C rows: token stride gstride elements
+  int xstride, gstride;
+  const _Float16* dt;
+  long long dtld;      // dt rows: token stride in elements
+  const float* A;
+  const float* D;
+  const float* state_in;
+  float* state_out;
+  const int* seqlens;
+  const int* cu;       // packed layout: row offsets (B+1), else null
+  int T;               // packed layout: rows of the per-token tensors
+  int xpk;             // x, B, C rows follow the packed rows (else padded b * L + t)
+  _Float16* y;
+  unsigned* ctrl;      // claim counters, done counter, generation, error
+  unsigned long long* flags;   // per item: decay bits << 32 | generation tag | 1 once published
+  float* agg;          // per item: segment aggregate state (private tile layout)
+  int nseg;            // segments per sequence
+  int cps;             // chunks per segment
+  int tree_lg;         // log2 of the radix of the segment tree
+  int dt_sp;
+  const float* dt_bias;
+};
+
+// Launches the scan for binary16 x, B, C and dt, N = 128, P = 64 (the
+// caller checks those); the workspace pointers (ctrl, flags, agg) follow the
+// window workspace layout.  a.nseg = 0 lets the launch choose the segments.
+hipError_t launch_ssd_scan(const ScanArgs& a, int cus, hipStream_t st);
+
+}  // namespace m2

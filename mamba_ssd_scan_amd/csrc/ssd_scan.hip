@@ -1,0 +1,705 @@
+// Whole-window Mamba-2 scan in its chunked state-space-dual form, with the
+// binary16 inputs streamed from HBM into LDS by buffer loads that write LDS
+// directly, two 32-token steps ahead of the step being computed.
+//
+// The method is Mamba-2 / structured state-space duality (Dao and Gu 2024,
+// listed under "References" on page "Mamb2_8B_FP4_Recall_SQ3.25").  For one
+// head, with log-decays la_t = dt_t * A_h and their running sum S_t from the
+// start of a chunk, the recurrence S <- e^{la_t} S + dt_t x_t B_t^T,
+// y_t = S C_t + D x_t is evaluated step by step (32 tokens), with the state
+// H entering the step:
+//   y_t   = sum_{s<=t in step} (C_t.B_s) e^{S_t-S_s} dt_s x_s          (diagonal)
+//         + e^{S_t - S_step} C_t . H                                  (readout)
+//         + D x_t
+//   H    <- e^{S_end - S_step} H + sum_s e^{S_end-S_s} dt_s x_s B_s^T  (state update)
+// Only differences S_t - S_s with s <= t are exponentiated, so every factor
+// is <= 1.
+//
+// Work split: one workgroup of eight waves per (segment, sequence, group,
+// block of four heads of the group); wave = (head, half of the head dim).
+// The recurrence is separable over p, so each half of a head is an
+// independent scan whose 32 x N share of the state stays in registers as
+// 16x16 fp32 MFMA tiles of S^T[n, p].  The four heads share the group's B
+// and C rows in LDS.  A segment is a run of consecutive chunks: inside it the
+// state passes from step to step in registers; segments hand their
+// aggregates over through an indexed tree in the workspace (local-state pass,
+// hand-off, output pass, as in the other window kernel).
+//
+// Streaming.  Every 32-token step occupies one of three LDS slots: the
+// wave's own x rows (32 x 64 bytes) and the group's B and C rows (32 x 256
+// bytes each).  Each wave issues its x rows and an eighth of B and C as
+// 16-byte-per-lane buffer loads that write LDS directly (no registers, no
+// staging arithmetic), two steps ahead; one workgroup barrier per step makes
+// a slot visible once every wave's loads into it have landed.  The three
+// slots are distinct LDS objects addressed only with compile-time slot
+// choices, so the compiler's wait for an LDS-writing load covers exactly
+// that slot's loads and leaves the next slot's loads in flight.  The x tile
+// is weighted for the state update after its transposed read, in registers.
+//
+// LDS layouts (16-byte units swizzled by row, so that the row reads of B and
+// C, the transposed reads of B and x, and the row reads of x reach distinct
+// banks): x row t, unit k at t*64 + 16*(k ^ xsw(t)); B/C row s, unit k at
+// s*256 + 16*(k ^ bsw(s)).  The buffer loads put lane l's 16 bytes at
+// slot + 16*l, so each lane loads the global unit that the swizzle maps
+// there.
+#include "common.h"
+#include "gfx950_ops.h"
+#include "ssd_scan.h"
+#include "../../include/mamba2ssd.h"
+
+namespace m2 {
+
+namespace ps {
+constexpr int TS = 32;       // tokens per step
+constexpr int N = 128;       // state size
+constexpr int P = 64;        // head dim
+constexpr int KH = 4;        // heads per workgroup
+constexpr int NT = N / 16;   // state tiles along n
+constexpr int KM = N / 32;   // 32-wide k-steps over n
+constexpr int MAXJ = 8;      // steps per chunk at most (chunk 256)
+constexpr unsigned kSpinLimit = 1u << 22;
+
+// control block of the workspace: eight claim counters and the done counter /
+// generation / error word, each on its own 128-byte line
+constexpr int kCtrlStride = 32;
+constexpr int kCtrlDone = 8 * kCtrlStride;
+constexpr int kCtrlGen = 9 * kCtrlStride;
+constexpr int kCtrlErr = 10 * kCtrlStride;
+
+// PH head-dim columns per wave: 32 (eight waves, two per SIMD, 256
+// registers each) or 64 (four waves, one per SIMD, 512 registers each).
+template <int PH> struct W {
+  static constexpr int WPH = P / PH;             // waves per head
+  static constexpr int NWV = KH * WPH;           // waves per workgroup
+  static constexpr int NTH = 64 * NWV;
+  static constexpr int PT = PH / 16;             // state tiles along p
+  static constexpr int XU = PH / 8;              // 16-byte units per x row
+  static constexpr int XI = TS * PH * 2 / 1024;  // x loads (1 KB each) per wave and step
+  static constexpr int BI = 8 / NWV;             // B (and C) loads per wave and step
+  // x row t, 16-byte unit k -> physical unit (rows of 64 or 128 bytes)
+  static __device__ __forceinline__ int xsw(int t) {
+    if constexpr (PH == 32) return (2 * ((t >> 2) & 1)) ^ ((t >> 3) & 1);
+    else return (2 * ((t >> 1) & 3)) ^ ((t >> 3) & 1);
+  }
+  // half offset of unit k of row r
+  static __device__ __forceinline__ int xo(int r, int k) { return r * PH + 8 * (k ^ xsw(r)); }
+  struct alignas(16) Slot {
+    _Float16 x[NWV][TS * PH];   // per wave: 32 tokens x PH columns
+    _Float16 b[TS * N];         // 32 tokens x 256 bytes
+    _Float16 c[TS * N];
+  };
+};
+
+__device__ __forceinline__ int bsw(int s) { return ((s & 3) << 2) | ((s >> 2) & 3); }
+__device__ __forceinline__ int bo(int r, int k) { return r * N + 8 * (k ^ bsw(r)); }
+
+// first state column of the 4-row group j of state tile nt: lane group j of
+// k-step m reads n = 8 j + 32 m .. + 7, tiles 2m and 2m+1 hold its two halves
+__device__ __forceinline__ int ncol(int nt, int j) { return 8 * j + 32 * (nt >> 1) + 4 * (nt & 1); }
+
+// Buffer descriptor words in scalar registers (wave-uniform p and bytes) for
+// the loads below; loads past `bytes` return zero.
+__device__ __forceinline__ u4 rsrc_words(const void* p, unsigned bytes) {
+  const unsigned long long v = (unsigned long long)p;
+  return u4{(unsigned)__builtin_amdgcn_readfirstlane((unsigned)v),
+            (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32)),
+            (unsigned)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// LDS byte address of a workgroup-shared location
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)__builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// 16 bytes per lane from the buffer at byte offset voff straight into LDS:
+// lane l's bytes land at lds + 16 l.  Written as an asm statement so that the
+// compiler does not track these loads: it would otherwise make some LDS reads
+// wait for every LDS-writing load in flight, draining the prefetch.  The
+// waits for them are explicit (vm_wait, before the barrier that publishes a
+// slot); the load has no register result, so nothing is written to a
+// register while it is in flight.
+__device__ __forceinline__ void dma16(u4 r, unsigned lds, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// 4 bytes per lane into LDS (lane l's bytes land at lds + 4 l); as dma16.
+__device__ __forceinline__ void dma4(u4 r, unsigned lds, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// Wait until at most n of this wave's vector memory operations are
+// outstanding (they complete in issue order); n outside 0..15 waits for all.
+__device__ __forceinline__ void vm_wait(int n) {
+#define M2_VMW(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+  switch (n) {
+    M2_VMW(1) M2_VMW(2) M2_VMW(3) M2_VMW(4) M2_VMW(5) M2_VMW(6) M2_VMW(7) M2_VMW(8) M2_VMW(9) M2_VMW(10)
+    M2_VMW(11) M2_VMW(12) M2_VMW(13) M2_VMW(14) M2_VMW(15)
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+#undef M2_VMW
+}
+
+// Workgroup barrier for the slots.  No fence: a workgroup release fence would
+// make the compiler wait for every LDS-writing buffer load in flight.  The
+// empty asm statements keep the compiler from moving LDS accesses across it;
+// the caller has already waited for what must be visible.
+__device__ __forceinline__ void slot_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads and writes are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace ps
+
+template <int PH>
+__global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
+  using namespace ps;
+  using Wd = W<PH>;
+  using Slot = typename Wd::Slot;
+  constexpr int NWV = Wd::NWV, NTH = Wd::NTH, PT = Wd::PT, WPH = Wd::WPH;
+  __shared__ Slot r0, r1, r2;
+  __shared__ float Sx[NWV][256];     // per wave: running log2-decay from the chunk start (inclusive)
+  __shared__ float Dx[NWV][256];     // per wave: the chunk's dt
+  __shared__ _Float16 dtr[2][256 * 8];    // a chunk's dt rows as read (8 elements per token from the aligned base), two chunks
+  __shared__ unsigned sh_ticket, sh_gen;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, q = lane >> 4;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hpg = a.H / a.G;
+  const int nhb = (hpg + KH - 1) / KH;
+  const int BG = a.B * a.G;
+  const int HV = WPH * a.H;   // hand-off items per sequence and segment: (head, wave of the head)
+  const int BHV = a.B * HV;
+
+  // ---- claim a workgroup item: the XCD's own (sequence, group) partition first, segment-major
+  if (tid == 0) {
+    sh_gen = __hip_atomic_load(&a.ctrl[kCtrlGen], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned x0 = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u;   // HW_REG_XCC_ID
+    for (int k = 0; k < 8; ++k) {
+      const unsigned px = (x0 + k) & 7u;
+      const int npairs = BG > (int)px ? (BG - (int)px + 7) / 8 : 0;
+      const unsigned n = (unsigned)(npairs * nhb * a.nseg);
+      if (n == 0) continue;
+      unsigned* cnt = &a.ctrl[px * kCtrlStride];
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+      const unsigned t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t < n) {
+        const int per_c = npairs * nhb;
+        const int cc = (int)t / per_c, rem = (int)t - cc * per_c;
+        const int gid = (int)px + 8 * (rem / nhb);
+        sh_ticket = (unsigned)((cc * BG + gid) * nhb + rem % nhb);
+        break;
+      }
+    }
+  }
+  // zero the slots: rows past a sequence's end are never loaded, and their
+  // (unused) values must be finite
+  {
+    constexpr int SLOT16 = (int)(sizeof(Slot) / 16);
+    u4* z0 = reinterpret_cast<u4*>(&r0);
+    u4* z1 = reinterpret_cast<u4*>(&r1);
+    u4* z2 = reinterpret_cast<u4*>(&r2);
+    for (int i = tid; i < SLOT16; i += NTH) {
+      z0[i] = u4{0u, 0u, 0u, 0u};
+      z1[i] = u4{0u, 0u, 0u, 0u};
+      z2[i] = u4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+  const unsigned ticket = __builtin_amdgcn_readfirstlane(sh_ticket);
+  const unsigned gen = __builtin_amdgcn_readfirstlane(sh_gen);
+  const unsigned tag = (gen & 0x3fffffffu) << 2;
+  const int hblk = (int)(ticket % (unsigned)nhb);
+  const int sg = (int)(ticket / (unsigned)nhb) / BG;   // segment (= chunk when nseg > 1)
+  const int gid = (int)(ticket / (unsigned)nhb) - sg * BG;
+  const int b = gid / a.G, g = gid - b * a.G;
+  const int hin = hblk * KH + wid / WPH;
+  const bool live = hin < hpg;                  // waves past the group's last head only load B and C
+  const int h = g * hpg + (live ? hin : 0);
+  const int half = wid % WPH;
+  const int hb = b * a.H + h;
+  const int bhv = b * HV + WPH * h + half;
+  const unsigned item = (unsigned)(sg * BHV + bhv);
+  const SeqRows span = seq_rows(a.seqlens, a.cu, b, a.L, a.T);
+  const int len = __builtin_amdgcn_readfirstlane(span.len);
+  const int ubase = __builtin_amdgcn_readfirstlane((int)span.base);
+  const size_t xbase = a.xpk ? (size_t)ubase : (size_t)b * a.L;
+  const int c0 = sg * a.cps;                                    // first chunk of the segment
+  const int c1 = min(c0 + a.cps, a.nchunks);                    // one past its last chunk
+  const bool last = sg + 1 == a.nseg;
+  // wave-uniform scalars (a value still pending from a load before the step
+  // loops would make the compiler wait for all memory operations inside them)
+  const float Ah = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.A[h] * kLog2e)));
+  const float Dh = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.D[h])));
+
+  // buffer views of this sequence (the range ends at its last token)
+  constexpr unsigned ES = 2;
+  const unsigned xrow = (unsigned)a.xstride * ES;
+  const unsigned grow = (unsigned)a.gstride * ES;
+  const unsigned yrow = (unsigned)(a.H * P) * ES;
+  const unsigned xspan = len > 0 && live ? (unsigned)(len - 1) * xrow + PH * ES : 0u;
+  const unsigned yspan = len > 0 && live ? (unsigned)(len - 1) * yrow + PH * ES : 0u;
+  const unsigned gspan = len > 0 ? (unsigned)(len - 1) * grow + N * ES : 0u;
+  const u4 rx = rsrc_words(a.x + xbase * a.xstride + (size_t)h * P + PH * half, xspan);
+  const u4 rb = rsrc_words(a.Bm + xbase * a.gstride + (size_t)g * N, gspan);
+  const rsrc_t rc = mkr(a.Cm + xbase * a.gstride + (size_t)g * N, gspan);
+  const u4 rc4 = rsrc_words(a.Cm + xbase * a.gstride + (size_t)g * N, gspan);
+  const rsrc_t ry = mkr(a.y + ((size_t)ubase * a.H + h) * P + PH * half, yspan);
+  // dt of the block's heads: token t's row starts sh0 + t dtld elements past
+  // a 4-byte aligned base (dt needs only element alignment, any row stride)
+  const int h0 = g * hpg + hblk * KH;
+  const _Float16* const dt0 = a.dt + (size_t)ubase * a.dtld + h0;
+  const int sh0 = (int)(((size_t)dt0 >> 1) & 1);
+  const u4 rdt = rsrc_words(dt0 - sh0, len > 0 ? ((unsigned)(sh0 + (len - 1) * a.dtld + (a.H - h0)) * ES + 3u) & ~3u : 0u);
+  float* const Sw = Sx[wid];
+  float* const Dw = Dx[wid];
+
+  // steps of chunk c that hold tokens of this sequence
+  auto steps_of = [&](int c) { return (min(max(len - c * a.Q, 0), a.Q) + TS - 1) / TS; };
+  // every step of the segment, in order
+  const int ncv = min(max((len - c0 * a.Q + a.Q - 1) / a.Q, 0), c1 - c0);   // chunks with tokens
+
+  // ---- loads of one step into a slot (this wave's share) ----------------------
+  // (DX + DBC loads per wave and step; the explicit waits count them)
+  constexpr int DX = Wd::XI, DBC = Wd::BI;
+  auto issue = [&](Slot& sl, int tok0, bool with_c) {
+    const unsigned t0 = (unsigned)tok0;
+    constexpr int XU = Wd::XU;
+#pragma unroll
+    for (int i = 0; i < DX; ++i) {
+      const int row = (64 / XU) * i + lane / XU, pk = lane % XU;
+      dma16(rx, lds_addr(&sl.x[wid][512 * i]), (t0 + row) * xrow + 16u * (unsigned)(pk ^ Wd::xsw(row)));
+    }
+#pragma unroll
+    for (int i = 0; i < DBC; ++i) {
+      const int blk = wid * DBC + i;
+      const int row = 4 * blk + (lane >> 4), pk = lane & 15;
+      const unsigned go = (t0 + row) * grow + 16u * (unsigned)(pk ^ bsw(row));
+      dma16(rb, lds_addr(&sl.b[512 * blk]), go);
+      if (with_c) dma16(rc4, lds_addr(&sl.c[512 * blk]), go);
+    }
+  };
+
+  // ---- per chunk: dt and the running log2-decay (4 tokens per lane) ----------
+  // A chunk's dt of the block's four heads goes into LDS with the step loads,
+  // one chunk ahead (two buffers): per token the 16 aligned bytes from the
+  // dword that holds head h0, four lanes per token (the four heads lie at
+  // elements sh .. sh + 3 of them, sh the row's misalignment); each wave
+  // then scans its own head.
+  constexpr int DTI = 256 / 16 / NWV;    // dt loads per wave for a chunk of up to 256 tokens
+  auto dt_sh = [&](int tok) { return (unsigned)(sh0 + tok * a.dtld); };   // element offset of a token's row
+  const float dtbl = a.dt_sp && a.dt_bias
+                         ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.dt_bias[h])))
+                         : 0.f;
+  auto issue_dt = [&](int cc) {
+#pragma unroll
+    for (int i = 0; i < DTI; ++i) {
+      const int li = wid * DTI + i;
+      const int t = 16 * li + (lane >> 2);   // tokens past the chunk load rows of the next one (unused)
+      dma4(rdt, lds_addr(&dtr[cc & 1][128 * li]), (dt_sh(cc * a.Q + t) & ~1u) * ES + 4u * (unsigned)(lane & 3));
+    }
+  };
+  // dt and the running log2-decay of chunk cc (its dt in LDS); a raw dt goes
+  // through the softplus, and tokens past the sequence keep dt = 0 (the state
+  // passes through them unchanged)
+  auto scan_dt = [&](int cc) {
+    const _Float16* dc = dtr[cc & 1];
+    const int hw = wid / WPH;              // this wave's head in the block
+    float d[4], v[4], run = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * lane + e;
+      float u = (float)dc[8 * i + (int)(dt_sh(cc * a.Q + i) & 1u) + hw];
+      if (a.dt_sp) u = dt_softplus_fast(u, dtbl);
+      if (i >= a.Q || cc * a.Q + i >= len) u = 0.f;
+      d[e] = u;
+      run += u * Ah;
+      v[e] = run;
+    }
+    float pre = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float u = __shfl_up(pre, off, 64);
+      if (lane >= off) pre += u;
+    }
+    pre -= run;   // exclusive prefix of the lane totals
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * lane + e;
+      if (i < a.Q) {
+        Sw[i] = v[e] + pre;
+        Dw[i] = d[e];
+      }
+    }
+  };
+
+  // ---- one 32-token step of the output pass ---------------------------------------
+  // R: the state entering the step (S^T tiles), advanced to its end when
+  // `advance`; y of the step is stored
+  f4 R[NT][PT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) R[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // x rows s = 4q..4q+3 and 16+4q..+3, column p = 16 pt + lr (transposed reads)
+  auto x_frag = [&](const _Float16* xs, int pt) -> h8 {
+    const int k = 2 * pt + ((lr & 3) >> 1), o = 4 * (lr & 1);
+    const int ra0 = 4 * q + (lr >> 2), ra1 = 16 + 4 * q + (lr >> 2);
+    return cat(tr4(&xs[Wd::xo(ra0, k) + o]), tr4(&xs[Wd::xo(ra1, k) + o]));
+  };
+  // acc[nt][pt] += sum_s B[s, n] w_s x[s, p] over a slot's 32 tokens, with the
+  // per-token weights w of the lane's tokens (4q..4q+3, 16+4q..16+4q+3)
+  auto state_mfma = [&](const Slot& sl, const h8 (&xa)[PT], const float (&w)[8], f4 (&acc)[NT][PT])
+      __attribute__((always_inline)) {
+    h8 xw[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xw[pt][e] = (_Float16)__builtin_fmaf((float)xa[pt][e], w[e], 0.f);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int k = (lr & 3) + 4 * (nt >> 1), o = 4 * (nt & 1);
+      const int rb0 = 4 * q + (lr >> 2), rb1 = 16 + 4 * q + (lr >> 2);
+      const h8 bt = cat(tr4(&sl.b[bo(rb0, k) + o]), tr4(&sl.b[bo(rb1, k) + o]));
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(bt, xw[pt], acc[nt][pt]);
+    }
+  };
+  // weights dt_s 2^{Sref - S_s} of the lane's tokens of the step at i0
+  auto weights = [&](int i0, float Sref, float (&w)[8]) {
+    const f4 S0 = *reinterpret_cast<const f4*>(&Sw[i0 + 4 * q]);
+    const f4 S1 = *reinterpret_cast<const f4*>(&Sw[i0 + 16 + 4 * q]);
+    const f4 d0 = *reinterpret_cast<const f4*>(&Dw[i0 + 4 * q]);
+    const f4 d1 = *reinterpret_cast<const f4*>(&Dw[i0 + 16 + 4 * q]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = d0[i] * ex2(Sref - S0[i]);
+      w[4 + i] = d1[i] * ex2(Sref - S1[i]);
+    }
+  };
+
+  auto step = [&](const Slot& sl, int i0, int tok0, bool advance) __attribute__((always_inline)) {
+    const _Float16* xs = sl.x[wid];
+    const float Sj_start = i0 ? Sw[i0 - 1] : 0.f;
+    const float Sj_end = Sw[i0 + TS - 1];
+    // C fragments: rows t = 16 T + lr, n = 8 q + 32 m .. + 7
+    h8 cf[2][KM];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int m = 0; m < KM; ++m) cf[T][m] = *reinterpret_cast<const h8*>(&sl.c[bo(16 * T + lr, q + 4 * m)]);
+    // decay-masked C.B^T: rows s (4 per lane) x column t (one per lane), per t-tile
+    h8 mf[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int tl = 16 * T + lr;
+      const float St = Sw[i0 + tl];
+      f4 mb[2];
+#pragma unroll
+      for (int S = 0; S < 2; ++S) {
+        mb[S] = f4{0.f, 0.f, 0.f, 0.f};
+        if (S <= T) {
+#pragma unroll
+          for (int m = 0; m < KM; ++m)
+            mb[S] = mfma16(*reinterpret_cast<const h8*>(&sl.b[bo(16 * S + lr, q + 4 * m)]), cf[T][m], mb[S]);
+          const f4 Ss = *reinterpret_cast<const f4*>(&Sw[i0 + 16 * S + 4 * q]);
+          const f4 ds = *reinterpret_cast<const f4*>(&Dw[i0 + 16 * S + 4 * q]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // the exponent is clamped so that the masked entries (s > t) stay
+            // finite; off-diagonal tiles (S < T) hold only s < t
+            const float v = mb[S][i] * ds[i] * ex2(fminf(St - Ss[i], 0.f));
+            mb[S][i] = (S < T || 4 * q + i <= lr) ? v : 0.f;
+          }
+        }
+      }
+      mf[T] = h8{(_Float16)mb[0][0], (_Float16)mb[0][1], (_Float16)mb[0][2], (_Float16)mb[0][3],
+                 (_Float16)mb[1][0], (_Float16)mb[1][1], (_Float16)mb[1][2], (_Float16)mb[1][3]};
+    }
+    float sc[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) sc[T] = ex2(Sw[i0 + 16 * T + lr] - Sj_start);
+    h8 xa[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) xa[pt] = x_frag(xs, pt);
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      // readout operand: the state rows p of this p-tile as binary16
+      h8 ra[KM];
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        const f4 s0 = R[2 * m][pt], s1 = R[2 * m + 1][pt];
+        ra[m] = h8{(_Float16)s0[0], (_Float16)s0[1], (_Float16)s0[2], (_Float16)s0[3],
+                   (_Float16)s1[0], (_Float16)s1[1], (_Float16)s1[2], (_Float16)s1[3]};
+      }
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const int tl = 16 * T + lr;
+        const f4 yd = mfma16(xa[pt], mf[T], f4{0.f, 0.f, 0.f, 0.f});
+        f4 yr = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KM; ++m) yr = mfma16(ra[m], cf[T][m], yr);
+        const int p0 = 16 * pt + 4 * q;
+        const h4 xr = *reinterpret_cast<const h4*>(&xs[Wd::xo(tl, 2 * pt + (q >> 1)) + 4 * (q & 1)]);
+        h4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)(__builtin_fmaf(sc[T], yr[i], yd[i]) + Dh * (float)xr[i]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, hv), ry,
+                                              (unsigned)(tok0 + tl) * yrow + (unsigned)p0 * ES, 0, 0);
+      }
+    }
+    if (advance) {
+      // R <- e^{S_end - S_start} R + sum_s w_s B_s x_s, w_s = dt_s e^{S_end - S_s}
+      const float dec = ex2(Sj_end - Sj_start);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
+      float w[8];
+      weights(i0, Sj_end, w);
+      state_mfma(sl, xa, w, R);
+    }
+  };
+
+  // ---- streaming over a segment's steps, three slots in rotation -----------------
+  // Steps are numbered over the segment (chunk c0 + k / J, step k % J).
+  const int J = a.Q / TS;                       // steps per full chunk
+  auto tok_of = [&](int k) { return (c0 + k / J) * a.Q + (k % J) * TS; };
+  int nsteps = 0;                               // steps with tokens
+  if (ncv > 0) nsteps = (ncv - 1) * J + steps_of(c0 + ncv - 1);
+  // The pass over the segment: the loads of its first chunk's dt and of its
+  // first two steps are already in flight (with_c: x, B and C, else x and B);
+  // per step k the loads of step k + 2 (and, at a chunk's first step, of the
+  // next chunk's dt), then body(k, slot), then the barrier that publishes
+  // step k + 1.  At a chunk boundary each wave scans the next chunk's dt
+  // after that barrier (the scan overwrites only the wave's own arrays).
+  // Explicit waits: before the barrier that publishes step k + 1, this
+  // wave's loads of step k + 1 must have landed.  Vector memory operations
+  // complete in issue order, so it waits until no more are outstanding than
+  // were issued after them: the stores of steps k - 1 and k (stores_per_step
+  // each, when this wave stores) and the loads of step k + 2.  Operations the
+  // count leaves out (dt loads, hand-off traffic) only make it wait longer.
+  auto pass = [&](bool with_c, int stores_per_step, auto&& body) __attribute__((always_inline)) {
+    const int D = DX + DBC * (with_c ? 2 : 1);
+    if (nsteps > 0) vm_wait(nsteps > 1 ? D : 0);   // the dt and step 0's loads; step 1's may stay in flight
+    slot_barrier();
+    if (ncv > 0) scan_dt(c0);
+    auto one = [&](int k, const Slot& sl, Slot& nx) __attribute__((always_inline)) {
+      const int kc = k % J, cc = c0 + k / J;
+      if (kc == 0 && cc + 1 < c0 + ncv) issue_dt(cc + 1);
+      const bool more = k + 2 < nsteps;
+      if (more) issue(nx, tok_of(k + 2), with_c);
+      body(k, sl);
+      if (k + 1 < nsteps) vm_wait((k > 0 ? stores_per_step : 0) + (more ? D : 0) + stores_per_step);
+      slot_barrier();
+      if (k + 1 < nsteps && (k + 1) % J == 0) scan_dt(cc + 1);
+    };
+    for (int k = 0; k < nsteps; k += 3) {
+      one(k, r0, r2);
+      if (k + 1 >= nsteps) break;
+      one(k + 1, r1, r0);
+      if (k + 2 >= nsteps) break;
+      one(k + 2, r2, r1);
+    }
+  };
+  // the first loads of a pass
+  auto prologue = [&](bool with_c) {
+    if (ncv > 0) issue_dt(c0);
+    if (nsteps > 0) issue(r0, tok_of(0), with_c);
+    if (nsteps > 1) issue(r1, tok_of(1), with_c);
+  };
+
+  // ---- phase 1: the segment's local state (every segment but the last) ----------
+  // acc is kept relative to the end of the current chunk: it is decayed over
+  // each new chunk before that chunk's tokens are added.
+  float segdec = 1.f;                           // decay over the segment
+  f4 acc[NT][PT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
+  if (!last) {
+    prologue(false);
+    pass(false, 0, [&](int k, const Slot& sl) __attribute__((always_inline)) {
+      const int kc = k % J, i0 = kc * TS;
+      const int cc = c0 + k / J;
+      const float Send = Sw[min(a.Q, len - cc * a.Q) - 1];   // dt = 0 past the end: S constant there
+      if (kc == 0) {
+        const float dec = ex2(Send);
+        segdec *= dec;
+        if (k > 0) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[nt][pt] *= dec;
+        }
+      }
+      if (live) {
+        h8 xa[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) xa[pt] = x_frag(sl.x[wid], pt);
+        float w[8];
+        weights(i0, Send, w);
+        state_mfma(sl, xa, w, acc);
+      }
+    });
+  }
+  // the output pass's first loads, in flight during the hand-off
+  prologue(true);
+
+  // ---- phase 2: carry-in over an indexed tree of segments (radix r = 2^lg) --------
+  // With i = sg + 1 and block(i) = r^(number of trailing zero base-r digits of
+  // i), segment sg publishes the aggregate of segments (i - block(i), i]
+  // (1-based), and its carry-in is the initial state advanced through the
+  // aggregates that tile [1, i-1], taken newest first, n_1 = i-1,
+  // n_{k+1} = n_k - block(n_k):
+  //   carry = F(n_1) + D(n_1) F(n_2) + D(n_1) D(n_2) F(n_3) + ... + (prod D) h0
+  // (F: aggregate state, D: its decay).  The first (r-1) log_r(block(i)) of
+  // them cover (i - block(i), i-1]: once they are folded in, the running sum
+  // combined with the local state is this segment's own aggregate.  A segment
+  // waits only on earlier ones (claimed before it), and the order of the sums
+  // is fixed, so results do not depend on timing.
+  constexpr unsigned kStBytes = (unsigned)(N * PH) * 4u;
+  auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * 4u; };
+  auto node_item = [&](int j) -> unsigned { return (unsigned)((j - 1) * BHV + bhv); };   // j: 1-based segment
+  if (live) {
+    const int i = sg + 1;
+    const int lg = a.tree_lg;
+    const int t = ((1 << lg) - 1) * (__builtin_ctz((unsigned)i) / lg);   // aggregates inside this segment's block
+    float scale = 1.f;                                                    // product of the decays folded in
+    int nodes = 0, my_node = 0;
+    for (int n = i - 1; n > 0; n -= 1 << (lg * (__builtin_ctz((unsigned)n) / lg)), ++nodes)
+      if (lane == nodes) my_node = n;
+    // wait until aggregates k0 .. k1-1 are published (one flag per lane, all
+    // polled together); the flag word also holds the aggregate's decay
+    float my_dec = 1.f;
+    auto wait_group = [&](int k0, int k1) {
+      const bool mine = lane >= k0 && lane < k1;
+      const unsigned it = mine ? node_item(my_node) : 0u;
+      unsigned spins = 0;
+      while (true) {
+        bool ready = true;
+        if (mine) {
+          const unsigned long long f = __hip_atomic_load(&a.flags[it], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ready = (unsigned)f == (tag | 1u);
+          my_dec = __uint_as_float((unsigned)(f >> 32));
+        }
+        if (__ballot(!ready) == 0) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          if (lane == 0) __hip_atomic_fetch_or(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      // compiler-only fence: the aggregate loads stay after the poll
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    auto fold = [&](int k) {
+      const int n = __builtin_amdgcn_readlane(my_node, k);
+      const rsrc_t r = mkr(a.agg + (size_t)node_item(n) * (N * PH), kStBytes);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const f4 v = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, v[e], R[nt][pt][e]);
+        }
+      scale *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
+    };
+    const int tb = t < nodes ? t : nodes;
+    if (tb > 0) {
+      wait_group(0, tb);
+      for (int k = 0; k < tb; ++k) fold(k);
+    }
+    if (!last) {
+      // own aggregate: (segdec R + local, segdec scale)
+      const rsrc_t r = mkr(a.agg + (size_t)item * (N * PH), kStBytes);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          f4 v = acc[nt][pt];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(segdec, R[nt][pt][k], v[k]);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
+        }
+      __builtin_amdgcn_s_waitcnt(0);
+      // compiler-only fence: no data store moves past the flag store
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      const unsigned long long f =
+          ((unsigned long long)__float_as_uint(segdec * scale) << 32) | (unsigned long long)(tag | 1u);
+      if (lane == 0) __hip_atomic_store(&a.flags[item], f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (nodes > tb) {
+      wait_group(tb, nodes);
+      for (int k = tb; k < nodes; ++k) fold(k);
+    }
+    if (a.state_in) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const int p = PH * half + 16 * pt + lr, n = ncol(nt, q);
+          const f4 h0v = *reinterpret_cast<const f4*>(a.state_in + ((size_t)hb * P + p) * N + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, h0v[e], R[nt][pt][e]);
+        }
+    }
+  }
+
+  // ---- phase 3: outputs; R runs from the carry-in through the segment ---------------
+  const bool want_state = last && a.state_out != nullptr;
+  pass(true, live ? 2 * PT : 0, [&](int k, const Slot& sl) __attribute__((always_inline)) {
+    if (live) step(sl, (k % J) * TS, tok_of(k), k + 1 < nsteps || want_state);
+  });
+  if (want_state && live) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const int p = PH * half + 16 * pt + lr, n = ncol(nt, q);
+        *reinterpret_cast<f4*>(a.state_out + ((size_t)hb * P + p) * N + n) = R[nt][pt];
+      }
+  }
+
+  // ---- retire -------------------------------------------------------------------
+  if (tid == 0) {
+    const unsigned total = (unsigned)(a.nseg * BG * nhb);
+    const unsigned done = __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == total - 1) {
+      for (int k = 0; k < 8; ++k) __hip_atomic_store(&a.ctrl[k * kCtrlStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl[kCtrlDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl[kCtrlGen], gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Launch of the streamed scan (binary16 I/O, N = 128, P = 64 are the
+// caller's to check).  Segments: as many runs of consecutive chunks per
+// sequence as keep every CU busy with one workgroup; inside a segment the
+// state passes from step to step in registers, segment boundaries go
+// through the hand-off tree.
+hipError_t launch_ssd_scan(const ScanArgs& in, int cus, hipStream_t st) {
+  using namespace ps;
+  ScanArgs a = in;
+  const int hpg = a.H / a.G;
+  const long long slots = (long long)a.B * a.G * ((hpg + KH - 1) / KH);   // workgroups per segment index
+  int nseg = a.nseg > 0 ? a.nseg : (int)(cus / slots);
+  nseg = nseg < 1 ? 1 : (nseg > a.nchunks ? a.nchunks : nseg);
+  a.cps = (a.nchunks + nseg - 1) / nseg;
+  a.nseg = (a.nchunks + a.cps - 1) / a.cps;
+  const long long wgs = (long long)a.nseg * slots;
+  // every workgroup resident at once: the chain of dependent publishes is the
+  // critical path (radix 8); otherwise aggregate traffic matters more (radix 4)
+  a.tree_lg = wgs <= cus ? 3 : 2;
+  ssd_scan_kernel<32><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace m2

@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "gfx950_ops.h"
+#include "ssd_scan.h"
 #include "../../include/mamba2ssd.h"
 
 namespace m2 {
@@ -1136,6 +1137,7 @@ int norm_parts_per_head() { return kNormParts; }
 hipError_t launch_exact_window_f32(const mamba2_dims& d, const mamba2_window_io& io_, const float* x, const float* Bm,
                                    const float* Cm, long long xld, long long gld, int xpk, hipStream_t st);
 
+
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t ctrl, flags, agg, convx, blo, total;
@@ -1253,6 +1255,16 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     // binary32 I/O: the exact token-sequential form in binary32 (the chunked
     // form's MFMA operands are binary16 and would round binary32 inputs)
     e = launch_exact_window_f32(d, io_, a.x, a.Bm, a.Cm, a.xstride, a.gstride, d.conv_width == 4 ? 0 : 1, st);
+  } else if (d.dstate == 128 && a.Blo == nullptr) {
+    // binary16 x, B, C at N = 128: the streamed scan
+    ScanArgs sa;
+    sa.B = a.B; sa.L = a.L; sa.H = a.H; sa.G = a.G; sa.Q = a.Q; sa.nchunks = a.nchunks;
+    sa.x = a.x; sa.Bm = a.Bm; sa.Cm = a.Cm; sa.xstride = a.xstride; sa.gstride = a.gstride;
+    sa.dt = a.dt; sa.dtld = a.dtld; sa.A = a.A; sa.D = a.D;
+    sa.state_in = a.state_in; sa.state_out = a.state_out; sa.seqlens = a.seqlens; sa.cu = a.cu; sa.T = a.T;
+    sa.xpk = a.xpk; sa.y = a.y; sa.ctrl = a.ctrl; sa.flags = a.flags; sa.agg = a.agg;
+    sa.nseg = a.nseg; sa.cps = 0; sa.tree_lg = 3; sa.dt_sp = a.dt_sp; sa.dt_bias = a.dt_bias;
+    e = launch_ssd_scan(sa, device_cus(), st);
   } else {
     const bool blo = a.Blo != nullptr;   // only binary16 conv output carries a remainder
     switch (d.dstate) {

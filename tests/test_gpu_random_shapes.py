@@ -69,7 +69,14 @@ def test_window_random_configuration(seed):
                         segments=c["segments"], dt_softplus=int(c["raw"]))
     ws = m2.alloc_workspace(dims, DEV)
     kw = dict(dt_softplus=True, dt_bias=to_dev(inp["dt_bias"])) if c["raw"] else {}
-    window_checked(to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=to_dev(inp["x"]),
+    dt = to_dev(inp["dt"])
+    if "dt_cols" in c:
+        # dt as columns [off, off + H) of wider rows (width H + extra)
+        off, extra = c["dt_cols"]
+        wide = torch.zeros((B, L, H + extra), dtype=dt.dtype, device=DEV)
+        wide[:, :, off:off + H] = dt
+        dt = wide[:, :, off:off + H]
+    window_checked(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=to_dev(inp["x"]),
                         B=to_dev(inp["B"]), C=to_dev(inp["C"]), state_in=to_dev(h0) if h0 is not None else None,
                         state_out=hT, seqlens=torch.tensor(c["lens"], dtype=torch.int32, device=DEV),
                         chunk=c["chunk"], segments=c["segments"], **kw)
@@ -98,3 +105,18 @@ def test_window_one_token_cancelling_factor_f32():
 @pytest.mark.parametrize("seed", [400, 401, 402, 403])
 def test_window_random_configuration_more(seed):
     test_window_random_configuration(seed)
+
+
+@pytest.mark.parametrize("H,G,off,extra", [(12, 4, 1, 3), (4, 4, 1, 2), (8, 8, 3, 6), (16, 2, 1, 1)])
+def test_window_dt_column_slice(H, G, off, extra):
+    # dt read in place from wider rows at an odd element offset, with odd and
+    # even row strides and groups of 1, 2 or 3 heads (blocks of heads that
+    # start at odd head indices)
+    c = dict(B=2, L=300, H=H, G=G, N=128, chunk=64, segments=2, lens=[300, 177], raw=True, h0=True,
+             dtype=np.float16, dt_cols=(off, extra))
+    seed = 500 + H + G + off + extra
+    EDGES[seed] = c
+    try:
+        test_window_random_configuration(seed)
+    finally:
+        del EDGES[seed]
