@@ -318,10 +318,11 @@ int32_t mamba2_decode_step(const mamba2_dims* dims, const mamba2_decode_io* io, 
  *         state (B,H,P,N) resident type, read and updated IN PLACE;
  *         z (B, H*P) io and norm_w (H*P) f32 when norm_group > 0;
  *         y (B, H*P) io.
+ *   dims.batch * dims.ngroups at most 16384 (MAMBA2_EUNSUPPORTED beyond).
  *   ws, ws_bytes: workspace of at least mamba2_mixer_decode_workspace_bytes()
  *         bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE; every
- *         call leaves it ready for the next one on the same stream (calls that
- *         may overlap must not share it).
+ *         call leaves it ready for the next one on the same stream, whatever
+ *         the next call's batch (calls that may overlap must not share it).
  * Errors: EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP. */
 typedef struct mamba2_mixer_decode_io {
     const void* xBC;

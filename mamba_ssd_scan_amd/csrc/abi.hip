@@ -19,6 +19,7 @@ hipError_t window_take_error(void* ws, unsigned* flags, hipStream_t st);
 hipError_t launch_window(const mamba2_dims& d, const mamba2_window_io& io, void* ws, hipStream_t st);
 hipError_t launch_requant_window(const mamba2_dims& d, const mamba2_window_io& io, hipStream_t st);
 size_t mixer_decode_workspace_bytes(const mamba2_dims& d);
+size_t mixer_decode_max_counters();
 size_t scan_grad_workspace_bytes(const mamba2_dims& d);
 hipError_t launch_scan_grad(const mamba2_dims& d, const mamba2_scan_grad_io& io, void* ws, hipStream_t st);
 hipError_t launch_mixer_decode(const mamba2_dims& d, const mamba2_mixer_decode_io& io, void* ws, hipStream_t st);
@@ -307,6 +308,8 @@ static int32_t check_mixer_decode(const mamba2_dims* d) {
   // the norm finish stages two partial sums per head in LDS (1024 slots)
   if (d->norm_group > 0 && d->nheads > 512) return MAMBA2_EUNSUPPORTED;
   if ((int64_t)d->batch * d->nheads > ((int64_t)1 << 31) - 1) return MAMBA2_EUNSUPPORTED;
+  // one arrival counter per (sequence, group) in the workspace's fixed region
+  if ((int64_t)d->batch * d->ngroups > (int64_t)m2::mixer_decode_max_counters()) return MAMBA2_EUNSUPPORTED;
   return MAMBA2_OK;
 }
 

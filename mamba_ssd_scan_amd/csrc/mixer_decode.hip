@@ -254,8 +254,10 @@ __global__ __launch_bounds__(256) void mixer_decode_kernel(const MixDecArgs<IO> 
 }
 
 // ---------------------------------------------------------------------------
-// Workspace: the (sequence, group) arrival counters (self-resetting) and the
-// norm's partial sums.
+// Workspace: the (sequence, group) arrival counters (self-resetting) in a
+// region of fixed size at its start, then the norm's partial sums.  The fixed
+// region keeps every counter clear of the partial sums of any call, whatever
+// its batch, so a workspace can serve calls of different sizes in turn.
 hipError_t launch_gated_norm_tokens(int io_f16, void* y, const float* normsum, const float* nw, int ntok, int H,
                                     int group, float eps, hipStream_t st);
 int norm_parts_per_head();
@@ -263,11 +265,13 @@ int norm_parts_per_head();
 struct MixDecWs {
   size_t cnt_grp, normsum, total;
 };
+constexpr size_t kMixDecCounters = 16384;   // (sequence, group) counters at most
+size_t mixer_decode_max_counters() { return kMixDecCounters; }
 static MixDecWs mixdec_ws(const mamba2_dims& d) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   MixDecWs w;
   w.cnt_grp = 0;
-  w.normsum = up((size_t)d.batch * d.ngroups * 4);
+  w.normsum = kMixDecCounters * 4;
   w.total = up(w.normsum + (d.norm_group > 0 ? (size_t)d.batch * d.nheads * 2 * 4 : 0));
   return w;
 }

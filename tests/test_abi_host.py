@@ -269,11 +269,13 @@ def test_mixer_decode_validation_codes():
         assert lib.mamba2_mixer_decode_workspace_bytes(ctypes.byref(dims(**kw)), ctypes.byref(n)) == code, kw
     d3 = m2.make_dims(64, 1, H, P, N, G, 256, conv_width=0)
     assert lib.mamba2_mixer_decode_workspace_bytes(ctypes.byref(d3), ctypes.byref(n)) == -2   # needs the conv
-    # one arrival counter per (sequence, group); with the norm, the sums of g^2
-    # over each half of every head
+    # a fixed region of 16384 arrival counters (one per (sequence, group)),
+    # then, with the norm, the sums of g^2 over each half of every head
     up = lambda v: (v + 255) // 256 * 256
-    assert m2.mixer_decode_workspace_bytes(dims()) == up(up(64 * G * 4) + 64 * H * 2 * 4)
-    assert m2.mixer_decode_workspace_bytes(dims(norm_group=0)) == up(64 * G * 4)
+    assert m2.mixer_decode_workspace_bytes(dims()) == up(16384 * 4 + 64 * H * 2 * 4)
+    assert m2.mixer_decode_workspace_bytes(dims(norm_group=0)) == 16384 * 4
+    assert lib.mamba2_mixer_decode_workspace_bytes(ctypes.byref(dims(batch=2048)), ctypes.byref(n)) == 0
+    assert lib.mamba2_mixer_decode_workspace_bytes(ctypes.byref(dims(batch=2049)), ctypes.byref(n)) == -2
     # more than 256 norm groups per token
     assert lib.mamba2_mixer_decode_workspace_bytes(ctypes.byref(m2.mixer_decode_dims(4, 512, 64, 128, 8, 64)),
                                                    ctypes.byref(n)) == -2
