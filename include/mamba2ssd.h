@@ -343,6 +343,26 @@ int32_t mamba2_mixer_decode_workspace_bytes(const mamba2_dims* dims, size_t* byt
 int32_t mamba2_mixer_decode_step(const mamba2_dims* dims, const mamba2_mixer_decode_io* io, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* The same one-token mixer step for callers that cannot allocate device
+ * memory or pass a workspace: code recorded under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Arguments, layouts,
+ * results and errors are those of mamba2_mixer_decode_step (the same kernels
+ * run), except that the workspace is a fixed array inside the library:
+ * mamba2_mixer_decode_noalloc_max_bytes() bytes per GPU, held by each GPU the
+ * library runs on until the process ends.  A request whose
+ * mamba2_mixer_decode_workspace_bytes() exceeds that size returns
+ * MAMBA2_EWORKSPACE before anything is enqueued (4 MiB: 4,032 sequences at
+ * H = 128 with the norm).  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks up that device's copy of the array (HIP runtime error ->
+ * MAMBA2_EHIP).  Every call on one GPU shares that GPU's array, which needs
+ * no clearing between calls (its arrival counters return to zero at the end
+ * of each call); calls that may overlap on one GPU (different streams) race
+ * and must be serialized by the caller.
+ * Errors: EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP. */
+size_t mamba2_mixer_decode_noalloc_max_bytes(void);
+int32_t mamba2_mixer_decode_step_noalloc(const mamba2_dims* dims, const mamba2_mixer_decode_io* io, void* stream);
+
 /* State load/store between f32 (B,H,P,N) and the resident state_dtype
  * (f16: round to nearest even, subnormals kept; f32: copy).  src and dst must
  * not overlap.  Errors: EINVAL, EUNSUPPORTED, EALIGN, EHIP. */

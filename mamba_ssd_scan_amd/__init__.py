@@ -17,6 +17,7 @@ __all__ = [
     "F16", "F32", "Dims", "Mamba2Error", "library_path", "load_library",
     "window_workspace_bytes", "alloc_workspace", "conv_scan_window", "window_take_error", "decode_step", "requant_window",
     "mixer_decode_workspace_bytes", "alloc_mixer_decode_workspace", "mixer_decode_step",
+    "mixer_decode_noalloc_max_bytes", "mixer_decode_step_noalloc",
     "scan_grad_workspace_bytes", "alloc_scan_grad_workspace", "scan_grad",
     "state_load", "state_store", "abi_version",
 ]
@@ -101,6 +102,10 @@ def load_library():
         lib.mamba2_mixer_decode_workspace_bytes.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
         lib.mamba2_mixer_decode_step.restype = ctypes.c_int32
         lib.mamba2_mixer_decode_step.argtypes = [dp, ctypes.POINTER(_MixerDecodeIO), vp, ctypes.c_size_t, vp]
+        lib.mamba2_mixer_decode_noalloc_max_bytes.restype = ctypes.c_size_t
+        lib.mamba2_mixer_decode_noalloc_max_bytes.argtypes = []
+        lib.mamba2_mixer_decode_step_noalloc.restype = ctypes.c_int32
+        lib.mamba2_mixer_decode_step_noalloc.argtypes = [dp, ctypes.POINTER(_MixerDecodeIO), vp]
         lib.mamba2_scan_grad_workspace_bytes.restype = ctypes.c_int32
         lib.mamba2_scan_grad_workspace_bytes.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
         lib.mamba2_scan_grad.restype = ctypes.c_int32
@@ -312,6 +317,26 @@ def mixer_decode_step(xBC, conv_w, conv_state, dt, A, D, state, y, workspace, *,
     _check("mamba2_mixer_decode_step",
            load_library().mamba2_mixer_decode_step(ctypes.byref(dims), ctypes.byref(io), _ptr(workspace),
                                                    workspace.numel(), _stream(xBC, stream)))
+
+
+def mixer_decode_noalloc_max_bytes() -> int:
+    """Size of the library's fixed workspace for mixer_decode_step_noalloc."""
+    return load_library().mamba2_mixer_decode_noalloc_max_bytes()
+
+
+def mixer_decode_step_noalloc(xBC, conv_w, conv_state, dt, A, D, state, y, *, conv_b=None, z=None, norm_w=None,
+                              ngroups, dstate, headdim=64, norm_group=0, norm_eps=1e-5, dt_softplus=False,
+                              dt_bias=None, stream=None):
+    """mixer_decode_step without a workspace argument: the library's fixed
+    per-GPU array serves as the workspace and nothing is allocated.  Calls
+    that may overlap on one GPU race.  See include/mamba2ssd.h."""
+    Bsz, H = dt.shape
+    sd = F16 if state.dtype == torch.float16 else F32
+    dims = mixer_decode_dims(Bsz, H, headdim, dstate, ngroups, norm_group, _io_dtype(xBC), sd, norm_eps, dt_softplus)
+    io = _MixerDecodeIO(_ptr(xBC), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                        _ptr(D), _ptr(state), _ptr(z), _ptr(norm_w), _ptr(y))
+    _check("mamba2_mixer_decode_step_noalloc",
+           load_library().mamba2_mixer_decode_step_noalloc(ctypes.byref(dims), ctypes.byref(io), _stream(xBC, stream)))
 
 
 def scan_grad_workspace_bytes(dims: Dims) -> int:

@@ -23,6 +23,8 @@ size_t mixer_decode_max_counters();
 size_t scan_grad_workspace_bytes(const mamba2_dims& d);
 hipError_t launch_scan_grad(const mamba2_dims& d, const mamba2_scan_grad_io& io, void* ws, hipStream_t st);
 hipError_t launch_mixer_decode(const mamba2_dims& d, const mamba2_mixer_decode_io& io, void* ws, hipStream_t st);
+hipError_t launch_mixer_decode_static(const mamba2_dims& d, const mamba2_mixer_decode_io& io, hipStream_t st);
+size_t mixer_decode_static_scratch_bytes();
 }  // namespace m2
 
 namespace {
@@ -370,6 +372,17 @@ int32_t mamba2_mixer_decode_step(const mamba2_dims* d, const mamba2_mixer_decode
   s = check_mixer_decode_args(d, io, ws, need);
   if (s != MAMBA2_OK) return s;
   return hip_status(m2::launch_mixer_decode(*d, *io, ws, (hipStream_t)stream));
+}
+
+size_t mamba2_mixer_decode_noalloc_max_bytes(void) { return m2::mixer_decode_static_scratch_bytes(); }
+
+int32_t mamba2_mixer_decode_step_noalloc(const mamba2_dims* d, const mamba2_mixer_decode_io* io, void* stream) {
+  int32_t s = check_mixer_decode(d);
+  if (s != MAMBA2_OK) return s;
+  s = check_mixer_decode_args(d, io, nullptr, 0);
+  if (s != MAMBA2_OK) return s;
+  if (m2::mixer_decode_workspace_bytes(*d) > m2::mixer_decode_static_scratch_bytes()) return MAMBA2_EWORKSPACE;
+  return hip_status(m2::launch_mixer_decode_static(*d, *io, (hipStream_t)stream));
 }
 
 // Validation for the scan's backward pass.

@@ -32,6 +32,8 @@
 // kernel, by the last head of each norm group, needs every head to wait for
 // its stores and an atomic before it retires; measured at 64 sequences that
 // costs more than the second launch.)
+#include <mutex>
+
 #include "state_io.h"
 #include "../../include/mamba2ssd.h"
 
@@ -329,6 +331,55 @@ static hipError_t launch_md_IO(const mamba2_dims& d, const mamba2_mixer_decode_i
 hipError_t launch_mixer_decode(const mamba2_dims& d, const mamba2_mixer_decode_io& io_, void* ws, hipStream_t st) {
   if (d.io_dtype == MAMBA2_F16) return launch_md_IO<_Float16>(d, io_, ws, st);
   return launch_md_IO<float>(d, io_, ws, st);
+}
+
+// ---------------------------------------------------------------------------
+// The step without a caller workspace, for callers that cannot allocate
+// (graph capture, serving loops): the same kernels take their workspace from
+// a fixed device array of this source file.  Each GPU holds its own copy of
+// the array for the life of the process; host code reaches it only through
+// the device address that hipGetSymbolAddress returns for the current device
+// (the array's name is a host-side stand-in, not a device address).
+//
+// The array starts zeroed when the code object is loaded.  The arrival
+// counters in it return to zero at the end of every call and the norm's
+// partial sums are written before they are read, so every call finds it
+// ready; calls that overlap on one GPU share it and race.
+constexpr size_t kStaticScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t mixer_decode_static_scratch_bytes() { return kStaticScratchBytes; }
+
+// Device address of the current device's scratch array, looked up once per
+// device with that device current.
+static hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_mixer_decode_static(const mamba2_dims& d, const mamba2_mixer_decode_io& io_, hipStream_t st) {
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_mixer_decode(d, io_, ws, st);
 }
 
 }  // namespace m2

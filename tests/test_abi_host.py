@@ -307,6 +307,49 @@ def test_window_take_error_validation_codes():
 
 
 @fake_pointers
+def test_mixer_decode_noalloc_validation_codes():
+    """The no-allocation step refuses on the host what the workspace form
+    refuses, plus requests whose workspace would exceed the fixed array."""
+    lib = m2.load_library()
+    MB = 1 << 36            # far enough apart that no batch below makes the ranges overlap
+    H, P, N, G = 128, 64, 128, 8
+    cap = m2.mixer_decode_noalloc_max_bytes()
+    assert cap == 4 << 20
+
+    def io(**over):
+        base = dict(xBC=FAKE, conv_w=FAKE + MB, conv_state=FAKE + 2 * MB, dt=FAKE + 3 * MB, A=FAKE + 4 * MB,
+                    D=FAKE + 4 * MB + 4096, state=FAKE + 8 * MB, z=FAKE + 5 * MB, norm_w=FAKE + 6 * MB,
+                    y=FAKE + 7 * MB)
+        base.update(over)
+        return m2._MixerDecodeIO(**base)
+
+    def call(i, batch=64, **kw):
+        d = m2.mixer_decode_dims(batch, H, P, N, G, **kw)
+        return lib.mamba2_mixer_decode_step_noalloc(ctypes.byref(d), ctypes.byref(i), None)
+
+    assert call(io(xBC=None), norm_group=8192) == -1
+    assert call(io(z=None), norm_group=8192) == -1
+    assert call(io(conv_w=FAKE + MB + 4), norm_group=8192) == -3
+    assert call(io(y=FAKE + 8 * MB + 4096), norm_group=8192) == -1
+    assert call(io(), norm_group=100) == -1
+    assert lib.mamba2_mixer_decode_step_noalloc(None, ctypes.byref(io()), None) == -1
+    d = m2.mixer_decode_dims(64, H, P, N, G, 8192)
+    assert lib.mamba2_mixer_decode_step_noalloc(ctypes.byref(d), None, None) == -1
+    # the largest batch whose workspace fits, and the first that does not
+    # (one group, so that the counter limit of 16384 (sequence, group) pairs
+    # is not what refuses the request)
+    per_seq = lambda b: m2.mixer_decode_workspace_bytes(m2.mixer_decode_dims(b, H, P, N, 1, 8192))
+    big = 1
+    while per_seq(big * 2) <= cap:
+        big *= 2
+    while per_seq(big + 1) <= cap:
+        big += 1
+    assert per_seq(big) <= cap < per_seq(big + 1) and big == 4032
+    d1 = m2.mixer_decode_dims(big + 1, H, P, N, 1, 8192)
+    assert lib.mamba2_mixer_decode_step_noalloc(ctypes.byref(d1), ctypes.byref(io()), None) == -4
+
+
+@fake_pointers
 def test_scan_grad_validation_codes():
     lib = m2.load_library()
     MB = 1 << 26
