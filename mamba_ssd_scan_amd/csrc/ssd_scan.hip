@@ -36,12 +36,16 @@
 // that slot's loads and leaves the next slot's loads in flight.  The x tile
 // is weighted for the state update after its transposed read, in registers.
 //
-// LDS layouts (16-byte units swizzled by row, so that the row reads of B and
-// C, the transposed reads of B and x, and the row reads of x reach distinct
-// banks): x row t, unit k at t*64 + 16*(k ^ xsw(t)); B/C row s, unit k at
-// s*256 + 16*(k ^ bsw(s)).  The buffer loads put lane l's 16 bytes at
-// slot + 16*l, so each lane loads the global unit that the swizzle maps
-// there.
+// LDS layouts (16-byte units swizzled by row): x row t, unit k at
+// t*64 + 16*(k ^ xsw(t)); B/C row s, unit k at s*256 + 16*(k ^ bsw(s)).  The
+// buffer loads put lane l's 16 bytes at slot + 16*l, so each lane loads the
+// global unit that the swizzle maps there.  The B/C swizzle is the linear map
+// over GF(2) that sends row bits 0..3 to units 3, 4, 8, 9: measured with the
+// LDS bank-conflict counter on gfx950, it keeps the 16-byte row reads of B
+// and C (lanes 16 rows x 4 units) free of conflicts, and gives the transposed
+// 8-byte reads of B (rows 4q + lane/4) their minimum, two lanes per bank
+// (32 lanes of 8 bytes against 16 distinct units).  The transposed reads of
+// the x tile are free of conflicts.
 #include "common.h"
 #include "gfx950_ops.h"
 #include "ssd_scan.h"
@@ -90,7 +94,9 @@ template <int PH> struct W {
   };
 };
 
-__device__ __forceinline__ int bsw(int s) { return ((s & 3) << 2) | ((s >> 2) & 3); }
+__device__ __forceinline__ int bsw(int s) {
+  return (3 * (s & 1)) ^ (4 * ((s >> 1) & 1)) ^ (8 * ((s >> 2) & 1)) ^ (9 * ((s >> 3) & 1));
+}
 __device__ __forceinline__ int bo(int r, int k) { return r * N + 8 * (k ^ bsw(r)); }
 
 // first state column of the 4-row group j of state tile nt: lane group j of
@@ -185,7 +191,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       const unsigned n = (unsigned)(npairs * nhb * a.nseg);
       if (n == 0) continue;
       unsigned* cnt = &a.ctrl[px * kCtrlStride];
-      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+      // (the XCD's own partition is claimed from at once; others are read first)
+      if (k > 0 && __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
       const unsigned t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (t < n) {
         const int per_c = npairs * nhb;
@@ -549,9 +556,6 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       }
     });
   }
-  // the output pass's first loads, in flight during the hand-off
-  prologue(true);
-
   // ---- phase 2: carry-in over an indexed tree of segments (radix r = 2^lg) --------
   // With i = sg + 1 and block(i) = r^(number of trailing zero base-r digits of
   // i), segment sg publishes the aggregate of segments (i - block(i), i]
@@ -564,17 +568,57 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // combined with the local state is this segment's own aggregate.  A segment
   // waits only on earlier ones (claimed before it), and the order of the sums
   // is fixed, so results do not depend on timing.
+  //
+  // A segment whose block is itself (i not a multiple of r) publishes its
+  // local aggregate at once, before the output pass's first loads are issued,
+  // and waits only for its own stores before it raises the flag; the others
+  // publish after their first folds.  Aggregates are read two at a time (the
+  // next one's loads in flight while the current one is added).
   constexpr unsigned kStBytes = (unsigned)(N * PH) * 4u;
   auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * 4u; };
   auto node_item = [&](int j) -> unsigned { return (unsigned)((j - 1) * BHV + bhv); };   // j: 1-based segment
+  const int si = sg + 1;
+  const int lg = a.tree_lg;
+  const int t_in = ((1 << lg) - 1) * (__builtin_ctz((unsigned)si) / lg);   // aggregates inside this segment's block
+  int nodes = 0, my_node = 0;
+  for (int n = si - 1; n > 0; n -= 1 << (lg * (__builtin_ctz((unsigned)n) / lg)), ++nodes)
+    if (lane == nodes) my_node = n;
+  const int tb = t_in < nodes ? t_in : nodes;
+  const bool early = !last && tb == 0;
+  float scale = 1.f;                            // product of the decays folded in
+  // own aggregate (segdec R + local, its decay segdec scale) into the workspace
+  auto publish_stores = [&]() __attribute__((always_inline)) {
+    const rsrc_t r = mkr(a.agg + (size_t)item * (N * PH), kStBytes);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        f4 v = acc[nt][pt];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(segdec, R[nt][pt][k], v[k]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
+      }
+  };
+  auto publish_flag = [&]() __attribute__((always_inline)) {
+    // compiler-only fence: no data store moves past the flag store
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const unsigned long long f =
+        ((unsigned long long)__float_as_uint(segdec * scale) << 32) | (unsigned long long)(tag | 1u);
+    if (lane == 0) __hip_atomic_store(&a.flags[item], f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (early && live) publish_stores();
+
+  // the output pass's first loads, in flight during the hand-off
+  prologue(true);
+  if (early && live) {
+    // the stores were issued before the prologue's loads and complete in
+    // order with them: wait until only those loads may be outstanding
+    constexpr int DP = DX + 2 * DBC;
+    vm_wait((ncv > 0 ? DTI : 0) + (nsteps > 0 ? DP : 0) + (nsteps > 1 ? DP : 0));
+    publish_flag();
+  }
+
   if (live) {
-    const int i = sg + 1;
-    const int lg = a.tree_lg;
-    const int t = ((1 << lg) - 1) * (__builtin_ctz((unsigned)i) / lg);   // aggregates inside this segment's block
-    float scale = 1.f;                                                    // product of the decays folded in
-    int nodes = 0, my_node = 0;
-    for (int n = i - 1; n > 0; n -= 1 << (lg * (__builtin_ctz((unsigned)n) / lg)), ++nodes)
-      if (lane == nodes) my_node = n;
     // wait until aggregates k0 .. k1-1 are published (one flag per lane, all
     // polled together); the flag word also holds the aggregate's decay
     float my_dec = 1.f;
@@ -599,46 +643,69 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       // compiler-only fence: the aggregate loads stay after the poll
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    auto fold = [&](int k) {
+    auto load_node = [&](int k, f4 (&buf)[NT][PT]) __attribute__((always_inline)) {
       const int n = __builtin_amdgcn_readlane(my_node, k);
       const rsrc_t r = mkr(a.agg + (size_t)node_item(n) * (N * PH), kStBytes);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const f4 v = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, v[e], R[nt][pt][e]);
-        }
-      scale *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
+        for (int pt = 0; pt < PT; ++pt)
+          buf[nt][pt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
     };
-    const int tb = t < nodes ? t : nodes;
-    if (tb > 0) {
-      wait_group(0, tb);
-      for (int k = 0; k < tb; ++k) fold(k);
-    }
-    if (!last) {
-      // own aggregate: (segdec R + local, segdec scale)
-      const rsrc_t r = mkr(a.agg + (size_t)item * (N * PH), kStBytes);
+    auto add_node = [&](int k, const f4 (&buf)[NT][PT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          f4 v = acc[nt][pt];
+        for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(segdec, R[nt][pt][k], v[k]);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
-        }
+          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, buf[nt][pt][e], R[nt][pt][e]);
+      scale *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
+    };
+    if (tb > 0) {
+      // (the local state is still live here: one aggregate at a time)
+      wait_group(0, tb);
+      for (int k = 0; k < tb; ++k) {
+        f4 b0[NT][PT];
+        load_node(k, b0);
+        add_node(k, b0);
+      }
+    }
+    if (!last && !early) {
+      publish_stores();
       __builtin_amdgcn_s_waitcnt(0);
-      // compiler-only fence: no data store moves past the flag store
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      const unsigned long long f =
-          ((unsigned long long)__float_as_uint(segdec * scale) << 32) | (unsigned long long)(tag | 1u);
-      if (lane == 0) __hip_atomic_store(&a.flags[item], f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      publish_flag();
     }
     if (nodes > tb) {
       wait_group(tb, nodes);
-      for (int k = tb; k < nodes; ++k) fold(k);
+      // Eight at most in straight-line code, two buffers: the next
+      // aggregate's loads are issued before the current one is added.  Loads
+      // are issued unconditionally (an index past the last repeats it,
+      // unused) and the code leaves as soon as the last one is added, so
+      // that every wait counts exactly the loads issued after the ones being
+      // added.  Deeper trees add the rest one at a time.
+      // (scheduling barriers keep each load group ahead of the additions
+      // that follow it)
+      const int kl = nodes - 1;
+      f4 b0[NT][PT], b1[NT][PT];
+      load_node(tb, b0);
+      load_node(min(tb + 1, kl), b1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        add_node(tb + j, b0);
+        if (tb + j + 1 > kl) break;
+        load_node(min(tb + j + 2, kl), b0);
+        __builtin_amdgcn_sched_barrier(0);
+        add_node(tb + j + 1, b1);
+        if (tb + j + 2 > kl) break;
+        load_node(min(tb + j + 3, kl), b1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int k = tb + 8; k < nodes; ++k) {
+        f4 bk[NT][PT];
+        load_node(k, bk);
+        add_node(k, bk);
+      }
     }
     if (a.state_in) {
 #pragma unroll
