@@ -171,6 +171,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   __shared__ Slot r0, r1, r2;
   __shared__ float Sx[NWV][256];     // per wave: running log2-decay from the chunk start (inclusive)
   __shared__ float Dx[NWV][256];     // per wave: the chunk's dt
+  __shared__ float Wx[NWV][256];     // per wave: state-update weight of each token (see scan_dt)
+  __shared__ float Cx[NWV][256];     // per wave: readout scale of each token (output pass)
   __shared__ _Float16 dtr[2][256 * 8];    // a chunk's dt rows as read (8 elements per token from the aligned base), two chunks
   __shared__ unsigned sh_ticket, sh_gen;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, q = lane >> 4;
@@ -264,6 +266,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   const u4 rdt = rsrc_words(dt0 - sh0, len > 0 ? ((unsigned)(sh0 + (len - 1) * a.dtld + (a.H - h0)) * ES + 3u) & ~3u : 0u);
   float* const Sw = Sx[wid];
   float* const Dw = Dx[wid];
+  float* const Ww = Wx[wid];
+  float* const Cw = Cx[wid];
 
   // steps of chunk c that hold tokens of this sequence
   auto steps_of = [&](int c) { return (min(max(len - c * a.Q, 0), a.Q) + TS - 1) / TS; };
@@ -312,8 +316,14 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   };
   // dt and the running log2-decay of chunk cc (its dt in LDS); a raw dt goes
   // through the softplus, and tokens past the sequence keep dt = 0 (the state
-  // passes through them unchanged)
-  auto scan_dt = [&](int cc) {
+  // passes through them unchanged).  Per token i it also stores the weight
+  // of x_i in the state update, w_i = dt_i 2^{S_ref - S_i}, with S_ref the
+  // log2-decay at the end of i's 32-token step (output pass) or at the end of
+  // the chunk (local-state pass), and, for the output pass, the readout scale
+  // 2^{S_i - S_start} with S_start the log2-decay before i's step.  Both are
+  // at most 1: only differences S_a - S_b with a later than b are
+  // exponentiated.
+  auto scan_dt = [&](int cc, bool out_pass) {
     const _Float16* dc = dtr[cc & 1];
     const int hw = wid / WPH;              // this wave's head in the block
     float d[4], v[4], run = 0.f;
@@ -342,16 +352,26 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
         Dw[i] = d[e];
       }
     }
+    // (the wave's LDS accesses complete in order: the reads below see the
+    // stores above)
+    const int step0 = (4 * lane) & ~(TS - 1);
+    const float s_end = Sw[out_pass ? step0 + TS - 1 : min(a.Q, len - cc * a.Q) - 1];
+    const float s_start = step0 ? Sw[step0 - 1] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * lane + e;
+      if (i < a.Q) {
+        const float si = v[e] + pre;
+        Ww[i] = d[e] * ex2(s_end - si);
+        if (out_pass) Cw[i] = ex2(si - s_start);
+      }
+    }
   };
 
   // ---- one 32-token step of the output pass ---------------------------------------
   // R: the state entering the step (S^T tiles), advanced to its end when
   // `advance`; y of the step is stored
-  f4 R[NT][PT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) R[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 R[NT][PT];   // (set to zero before the hand-off: unused by the local-state pass)
 
   // x rows s = 4q..4q+3 and 16+4q..+3, column p = 16 pt + lr (transposed reads)
   auto x_frag = [&](const _Float16* xs, int pt) -> h8 {
@@ -361,117 +381,154 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   };
   // acc[nt][pt] += sum_s B[s, n] w_s x[s, p] over a slot's 32 tokens, with the
   // per-token weights w of the lane's tokens (4q..4q+3, 16+4q..16+4q+3)
-  auto state_mfma = [&](const Slot& sl, const h8 (&xa)[PT], const float (&w)[8], f4 (&acc)[NT][PT])
-      __attribute__((always_inline)) {
-    h8 xw[PT];
+  auto weigh_x = [&](const h8 (&xa)[PT], const float (&w)[8], h8 (&xw)[PT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
       for (int e = 0; e < 8; ++e) xw[pt][e] = (_Float16)__builtin_fmaf((float)xa[pt][e], w[e], 0.f);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int k = (lr & 3) + 4 * (nt >> 1), o = 4 * (nt & 1);
-      const int rb0 = 4 * q + (lr >> 2), rb1 = 16 + 4 * q + (lr >> 2);
-      const h8 bt = cat(tr4(&sl.b[bo(rb0, k) + o]), tr4(&sl.b[bo(rb1, k) + o]));
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(bt, xw[pt], acc[nt][pt]);
-    }
   };
-  // weights dt_s 2^{Sref - S_s} of the lane's tokens of the step at i0
-  auto weights = [&](int i0, float Sref, float (&w)[8]) {
-    const f4 S0 = *reinterpret_cast<const f4*>(&Sw[i0 + 4 * q]);
-    const f4 S1 = *reinterpret_cast<const f4*>(&Sw[i0 + 16 + 4 * q]);
-    const f4 d0 = *reinterpret_cast<const f4*>(&Dw[i0 + 4 * q]);
-    const f4 d1 = *reinterpret_cast<const f4*>(&Dw[i0 + 16 + 4 * q]);
+  // B^T fragments: rows n (tile nt), tokens s = 4q..4q+3 and 16+4q..+3 (transposed reads)
+  auto bt_frag = [&](const Slot& sl, int nt) -> h8 {
+    const int k = (lr & 3) + 4 * (nt >> 1), o = 4 * (nt & 1);
+    const int rb0 = 4 * q + (lr >> 2), rb1 = 16 + 4 * q + (lr >> 2);
+    return cat(tr4(&sl.b[bo(rb0, k) + o]), tr4(&sl.b[bo(rb1, k) + o]));
+  };
+
+  // state-update weights of the lane's tokens of the step at i0
+  auto weights = [&](int i0, float (&w)[8]) {
+    const f4 w0 = *reinterpret_cast<const f4*>(&Ww[i0 + 4 * q]);
+    const f4 w1 = *reinterpret_cast<const f4*>(&Ww[i0 + 16 + 4 * q]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      w[i] = d0[i] * ex2(Sref - S0[i]);
-      w[4 + i] = d1[i] * ex2(Sref - S1[i]);
+      w[i] = w0[i];
+      w[4 + i] = w1[i];
     }
   };
 
-  auto step = [&](const Slot& sl, int i0, int tok0, bool advance) __attribute__((always_inline)) {
+  // The step in stages, so that each stage's vector arithmetic can run under
+  // the previous stage's matrix products: (1) the C.B^T blocks while the
+  // state is converted to the readout operand; (2) the readout C.R while the
+  // state is decayed; (3) the state update while the decay mask is applied
+  // to C.B^T; (4) the masked product and the outputs.  The state always
+  // advances: after a pass's last step it is used only when it is the
+  // sequence's final state.  Scheduling barriers keep the stages in order.
+  auto step = [&](const Slot& sl, int i0, int tok0) __attribute__((always_inline)) {
     const _Float16* xs = sl.x[wid];
     const float Sj_start = i0 ? Sw[i0 - 1] : 0.f;
     const float Sj_end = Sw[i0 + TS - 1];
-    // C fragments: rows t = 16 T + lr, n = 8 q + 32 m .. + 7
-    h8 cf[2][KM];
+    // C rows t = 16 T + lr and B rows s = 16 S + lr, n = 8 q + 32 m .. + 7
+    h8 cf[2][KM], bf[2][KM];
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int m = 0; m < KM; ++m) cf[T][m] = *reinterpret_cast<const h8*>(&sl.c[bo(16 * T + lr, q + 4 * m)]);
-    // decay-masked C.B^T: rows s (4 per lane) x column t (one per lane), per t-tile
-    h8 mf[2];
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const int tl = 16 * T + lr;
-      const float St = Sw[i0 + tl];
-      f4 mb[2];
-#pragma unroll
-      for (int S = 0; S < 2; ++S) {
-        mb[S] = f4{0.f, 0.f, 0.f, 0.f};
-        if (S <= T) {
-#pragma unroll
-          for (int m = 0; m < KM; ++m)
-            mb[S] = mfma16(*reinterpret_cast<const h8*>(&sl.b[bo(16 * S + lr, q + 4 * m)]), cf[T][m], mb[S]);
-          const f4 Ss = *reinterpret_cast<const f4*>(&Sw[i0 + 16 * S + 4 * q]);
-          const f4 ds = *reinterpret_cast<const f4*>(&Dw[i0 + 16 * S + 4 * q]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // the exponent is clamped so that the masked entries (s > t) stay
-            // finite; off-diagonal tiles (S < T) hold only s < t
-            const float v = mb[S][i] * ds[i] * ex2(fminf(St - Ss[i], 0.f));
-            mb[S][i] = (S < T || 4 * q + i <= lr) ? v : 0.f;
-          }
-        }
+      for (int m = 0; m < KM; ++m) {
+        cf[T][m] = *reinterpret_cast<const h8*>(&sl.c[bo(16 * T + lr, q + 4 * m)]);
+        bf[T][m] = *reinterpret_cast<const h8*>(&sl.b[bo(16 * T + lr, q + 4 * m)]);
       }
-      mf[T] = h8{(_Float16)mb[0][0], (_Float16)mb[0][1], (_Float16)mb[0][2], (_Float16)mb[0][3],
-                 (_Float16)mb[1][0], (_Float16)mb[1][1], (_Float16)mb[1][2], (_Float16)mb[1][3]};
-    }
-    float sc[2];
-#pragma unroll
-    for (int T = 0; T < 2; ++T) sc[T] = ex2(Sw[i0 + 16 * T + lr] - Sj_start);
     h8 xa[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) xa[pt] = x_frag(xs, pt);
+    float w[8];
+    weights(i0, w);
+    // (1) readout operand: the state rows p as binary16; C.B^T blocks
+    // (s-tile, t-tile) = (0, 0), (0, 1), (1, 1): rows s (4 per lane) x column t
+    h8 ra[PT][KM];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-      // readout operand: the state rows p of this p-tile as binary16
-      h8 ra[KM];
+    for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
       for (int m = 0; m < KM; ++m) {
         const f4 s0 = R[2 * m][pt], s1 = R[2 * m + 1][pt];
-        ra[m] = h8{(_Float16)s0[0], (_Float16)s0[1], (_Float16)s0[2], (_Float16)s0[3],
-                   (_Float16)s1[0], (_Float16)s1[1], (_Float16)s1[2], (_Float16)s1[3]};
+        ra[pt][m] = h8{(_Float16)s0[0], (_Float16)s0[1], (_Float16)s0[2], (_Float16)s0[3],
+                       (_Float16)s1[0], (_Float16)s1[1], (_Float16)s1[2], (_Float16)s1[3]};
       }
+    f4 cb[3];
+#pragma unroll
+    for (int b = 0; b < 3; ++b) cb[b] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      cb[0] = mfma16(bf[0][m], cf[0][m], cb[0]);
+      cb[1] = mfma16(bf[0][m], cf[1][m], cb[1]);
+      cb[2] = mfma16(bf[1][m], cf[1][m], cb[2]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (2) readout C.R; the state decays over the step; B^T fragments and
+    // the weighted x for the update
+    h8 xw[PT];
+    weigh_x(xa, w, xw);
+    f4 yr[PT][2];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
-        const int tl = 16 * T + lr;
-        const f4 yd = mfma16(xa[pt], mf[T], f4{0.f, 0.f, 0.f, 0.f});
-        f4 yr = f4{0.f, 0.f, 0.f, 0.f};
+        yr[pt][T] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < KM; ++m) yr = mfma16(ra[m], cf[T][m], yr);
+        for (int m = 0; m < KM; ++m) yr[pt][T] = mfma16(ra[pt][m], cf[T][m], yr[pt][T]);
+      }
+    const float dec = ex2(Sj_end - Sj_start);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
+    __builtin_amdgcn_sched_barrier(0);
+    // (3) state update R += sum_s w_s B_s x_s; the decay mask on C.B^T
+    h8 bt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl, nt);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) R[nt][pt] = mfma16(bt[nt], xw[pt], R[nt][pt]);
+    h8 mf[2];
+    {
+      float Ss[2][4], ds[2][4];
+#pragma unroll
+      for (int S = 0; S < 2; ++S) {
+        const f4 sv = *reinterpret_cast<const f4*>(&Sw[i0 + 16 * S + 4 * q]);
+        const f4 dv = *reinterpret_cast<const f4*>(&Dw[i0 + 16 * S + 4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Ss[S][e] = sv[e];
+          ds[S][e] = dv[e];
+        }
+      }
+      float v[3][4];
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        const int S = b == 2 ? 1 : 0, T = b == 0 ? 0 : 1;
+        const float St = Sw[i0 + 16 * T + lr];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // the exponent is clamped so that the masked entries (s > t) stay
+          // finite; the off-diagonal block (s-tile 0, t-tile 1) holds only s < t
+          const float x = cb[b][e] * ds[S][e] * ex2(fminf(St - Ss[S][e], 0.f));
+          v[b][e] = (S < T || 4 * q + e <= lr) ? x : 0.f;
+        }
+      }
+      mf[0] = h8{(_Float16)v[0][0], (_Float16)v[0][1], (_Float16)v[0][2], (_Float16)v[0][3],
+                 (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+      mf[1] = h8{(_Float16)v[1][0], (_Float16)v[1][1], (_Float16)v[1][2], (_Float16)v[1][3],
+                 (_Float16)v[2][0], (_Float16)v[2][1], (_Float16)v[2][2], (_Float16)v[2][3]};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (4) masked product and the outputs y = sc C.R + (masked C.B^T) x + D x
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int tl = 16 * T + lr;
+      const float sc = Cw[i0 + tl];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const f4 yd = mfma16(xa[pt], mf[T], f4{0.f, 0.f, 0.f, 0.f});
         const int p0 = 16 * pt + 4 * q;
         const h4 xr = *reinterpret_cast<const h4*>(&xs[Wd::xo(tl, 2 * pt + (q >> 1)) + 4 * (q & 1)]);
         h4 hv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = (_Float16)(__builtin_fmaf(sc[T], yr[i], yd[i]) + Dh * (float)xr[i]);
+        for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(__builtin_fmaf(sc, yr[pt][T][e], yd[e]) + Dh * (float)xr[e]);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, hv), ry,
                                               (unsigned)(tok0 + tl) * yrow + (unsigned)p0 * ES, 0, 0);
       }
     }
-    if (advance) {
-      // R <- e^{S_end - S_start} R + sum_s w_s B_s x_s, w_s = dt_s e^{S_end - S_s}
-      const float dec = ex2(Sj_end - Sj_start);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
-      float w[8];
-      weights(i0, Sj_end, w);
-      state_mfma(sl, xa, w, R);
-    }
   };
+
 
   // ---- streaming over a segment's steps, three slots in rotation -----------------
   // Steps are numbered over the segment (chunk c0 + k / J, step k % J).
@@ -495,7 +552,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
     const int D = DX + DBC * (with_c ? 2 : 1);
     if (nsteps > 0) vm_wait(nsteps > 1 ? D : 0);   // the dt and step 0's loads; step 1's may stay in flight
     slot_barrier();
-    if (ncv > 0) scan_dt(c0);
+    if (ncv > 0) scan_dt(c0, with_c);
     auto one = [&](int k, const Slot& sl, Slot& nx) __attribute__((always_inline)) {
       const int kc = k % J, cc = c0 + k / J;
       if (kc == 0 && cc + 1 < c0 + ncv) issue_dt(cc + 1);
@@ -504,7 +561,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       body(k, sl);
       if (k + 1 < nsteps) vm_wait((k > 0 ? stores_per_step : 0) + (more ? D : 0) + stores_per_step);
       slot_barrier();
-      if (k + 1 < nsteps && (k + 1) % J == 0) scan_dt(cc + 1);
+      if (k + 1 < nsteps && (k + 1) % J == 0) scan_dt(cc + 1, with_c);
     };
     for (int k = 0; k < nsteps; k += 3) {
       one(k, r0, r2);
@@ -547,12 +604,20 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
         }
       }
       if (live) {
-        h8 xa[PT];
+        // every operand read before the products
+        h8 xa[PT], bt[NT], xw[PT];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) xa[pt] = x_frag(sl.x[wid], pt);
         float w[8];
-        weights(i0, Send, w);
-        state_mfma(sl, xa, w, acc);
+        weights(i0, w);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl, nt);
+        weigh_x(xa, w, xw);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(bt[nt], xw[pt], acc[nt][pt]);
       }
     });
   }
@@ -577,6 +642,10 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   constexpr unsigned kStBytes = (unsigned)(N * PH) * 4u;
   auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * 4u; };
   auto node_item = [&](int j) -> unsigned { return (unsigned)((j - 1) * BHV + bhv); };   // j: 1-based segment
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) R[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
   const int si = sg + 1;
   const int lg = a.tree_lg;
   const int t_in = ((1 << lg) - 1) * (__builtin_ctz((unsigned)si) / lg);   // aggregates inside this segment's block
@@ -723,7 +792,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // ---- phase 3: outputs; R runs from the carry-in through the segment ---------------
   const bool want_state = last && a.state_out != nullptr;
   pass(true, live ? 2 * PT : 0, [&](int k, const Slot& sl) __attribute__((always_inline)) {
-    if (live) step(sl, (k % J) * TS, tok_of(k), k + 1 < nsteps || want_state);
+    if (live) step(sl, (k % J) * TS, tok_of(k));
   });
   if (want_state && live) {
 #pragma unroll
