@@ -29,6 +29,8 @@ struct ScanArgs {
   int tree_lg;         // log2 of the radix of the segment tree
   int dt_sp;
   const float* dt_bias;
+  const _Float16* Blo;   // fused conv: B's binary16 remainder, rows of gn elements (else null)
+  int gn;
 };
 
 // Launches the scan for binary16 x, B, C and dt, N = 128, P = 64 (the

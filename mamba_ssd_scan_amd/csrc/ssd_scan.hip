@@ -87,10 +87,12 @@ template <int PH> struct W {
   }
   // half offset of unit k of row r
   static __device__ __forceinline__ int xo(int r, int k) { return r * PH + 8 * (k ^ xsw(r)); }
-  struct alignas(16) Slot {
+  // (with the binary16 remainder of B from the fused conv: its rows too)
+  template <bool BLO> struct alignas(16) Slot {
     _Float16 x[NWV][TS * PH];   // per wave: 32 tokens x PH columns
     _Float16 b[TS * N];         // 32 tokens x 256 bytes
     _Float16 c[TS * N];
+    _Float16 bl[BLO ? TS * N : 8];
   };
 };
 
@@ -162,17 +164,19 @@ __device__ __forceinline__ void slot_barrier() {
 
 }  // namespace ps
 
-template <int PH>
+template <int PH, bool BLO>
 __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   using namespace ps;
   using Wd = W<PH>;
-  using Slot = typename Wd::Slot;
+  using Slot = typename Wd::template Slot<BLO>;
   constexpr int NWV = Wd::NWV, NTH = Wd::NTH, PT = Wd::PT, WPH = Wd::WPH;
   __shared__ Slot r0, r1, r2;
   __shared__ float Sx[NWV][256];     // per wave: running log2-decay from the chunk start (inclusive)
   __shared__ float Dx[NWV][256];     // per wave: the chunk's dt
   __shared__ float Wx[NWV][256];     // per wave: state-update weight of each token (see scan_dt)
-  __shared__ float Cx[NWV][256];     // per wave: readout scale of each token (output pass)
+  // per wave: readout scale of each token (output pass); with the B
+  // remainder, whose rows take that room, the scales are computed per step
+  __shared__ float Cx[BLO ? 1 : NWV][256];
   __shared__ _Float16 dtr[2][256 * 8];    // a chunk's dt rows as read (8 elements per token from the aligned base), two chunks
   __shared__ unsigned sh_ticket, sh_gen;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, q = lane >> 4;
@@ -257,6 +261,9 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   const u4 rb = rsrc_words(a.Bm + xbase * a.gstride + (size_t)g * N, gspan);
   const rsrc_t rc = mkr(a.Cm + xbase * a.gstride + (size_t)g * N, gspan);
   const u4 rc4 = rsrc_words(a.Cm + xbase * a.gstride + (size_t)g * N, gspan);
+  const unsigned lrow = (unsigned)a.gn * ES;   // remainder rows of B (fused conv)
+  const u4 rbl = BLO ? rsrc_words(a.Blo + xbase * a.gn + (size_t)g * N, len > 0 ? (unsigned)(len - 1) * lrow + N * ES : 0u)
+                     : u4{0u, 0u, 0u, 0u};
   const rsrc_t ry = mkr(a.y + ((size_t)ubase * a.H + h) * P + PH * half, yspan);
   // dt of the block's heads: token t's row starts sh0 + t dtld elements past
   // a 4-byte aligned base (dt needs only element alignment, any row stride)
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   float* const Sw = Sx[wid];
   float* const Dw = Dx[wid];
   float* const Ww = Wx[wid];
-  float* const Cw = Cx[wid];
+  float* const Cw = Cx[BLO ? 0 : wid];
 
   // steps of chunk c that hold tokens of this sequence
   auto steps_of = [&](int c) { return (min(max(len - c * a.Q, 0), a.Q) + TS - 1) / TS; };
@@ -275,8 +282,9 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   const int ncv = min(max((len - c0 * a.Q + a.Q - 1) / a.Q, 0), c1 - c0);   // chunks with tokens
 
   // ---- loads of one step into a slot (this wave's share) ----------------------
-  // (DX + DBC loads per wave and step; the explicit waits count them)
+  // (DX + DBC per operand loads per wave and step; the explicit waits count them)
   constexpr int DX = Wd::XI, DBC = Wd::BI;
+  auto loads_per_step = [&](bool with_c) { return DX + DBC * ((with_c ? 2 : 1) + (BLO ? 1 : 0)); };
   auto issue = [&](Slot& sl, int tok0, bool with_c) {
     const unsigned t0 = (unsigned)tok0;
     constexpr int XU = Wd::XU;
@@ -292,6 +300,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       const unsigned go = (t0 + row) * grow + 16u * (unsigned)(pk ^ bsw(row));
       dma16(rb, lds_addr(&sl.b[512 * blk]), go);
       if (with_c) dma16(rc4, lds_addr(&sl.c[512 * blk]), go);
+      if constexpr (BLO) dma16(rbl, lds_addr(&sl.bl[512 * blk]), (t0 + row) * lrow + 16u * (unsigned)(pk ^ bsw(row)));
     }
   };
 
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       if (i < a.Q) {
         const float si = v[e] + pre;
         Ww[i] = d[e] * ex2(s_end - si);
-        if (out_pass) Cw[i] = ex2(si - s_start);
+        if (out_pass && !BLO) Cw[i] = ex2(si - s_start);
       }
     }
   };
@@ -388,10 +397,29 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       for (int e = 0; e < 8; ++e) xw[pt][e] = (_Float16)__builtin_fmaf((float)xa[pt][e], w[e], 0.f);
   };
   // B^T fragments: rows n (tile nt), tokens s = 4q..4q+3 and 16+4q..+3 (transposed reads)
-  auto bt_frag = [&](const Slot& sl, int nt) -> h8 {
+  auto bt_frag = [&](const _Float16* bs, int nt) -> h8 {
     const int k = (lr & 3) + 4 * (nt >> 1), o = 4 * (nt & 1);
     const int rb0 = 4 * q + (lr >> 2), rb1 = 16 + 4 * q + (lr >> 2);
-    return cat(tr4(&sl.b[bo(rb0, k) + o]), tr4(&sl.b[bo(rb1, k) + o]));
+    return cat(tr4(&bs[bo(rb0, k) + o]), tr4(&bs[bo(rb1, k) + o]));
+  };
+  // acc += B^T xw, with B as its binary16 high part plus remainder when the
+  // remainder is staged
+  auto update = [&](const Slot& sl, const h8 (&xw)[PT], f4 (&acc)[NT][PT]) __attribute__((always_inline)) {
+    h8 bt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl.b, nt);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(bt[nt], xw[pt], acc[nt][pt]);
+    if constexpr (BLO) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl.bl, nt);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(bt[nt], xw[pt], acc[nt][pt]);
+    }
   };
 
   // state-update weights of the lane's tokens of the step at i0
@@ -471,13 +499,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
     __builtin_amdgcn_sched_barrier(0);
     // (3) state update R += sum_s w_s B_s x_s; the decay mask on C.B^T
-    h8 bt[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl, nt);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) R[nt][pt] = mfma16(bt[nt], xw[pt], R[nt][pt]);
+    update(sl, xw, R);
     h8 mf[2];
     {
       float Ss[2][4], ds[2][4];
@@ -514,7 +536,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       const int tl = 16 * T + lr;
-      const float sc = Cw[i0 + tl];
+      const float sc = BLO ? ex2(Sw[i0 + tl] - Sj_start) : Cw[i0 + tl];
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
         const f4 yd = mfma16(xa[pt], mf[T], f4{0.f, 0.f, 0.f, 0.f});
@@ -549,7 +571,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // each, when this wave stores) and the loads of step k + 2.  Operations the
   // count leaves out (dt loads, hand-off traffic) only make it wait longer.
   auto pass = [&](bool with_c, int stores_per_step, auto&& body) __attribute__((always_inline)) {
-    const int D = DX + DBC * (with_c ? 2 : 1);
+    const int D = loads_per_step(with_c);
     if (nsteps > 0) vm_wait(nsteps > 1 ? D : 0);   // the dt and step 0's loads; step 1's may stay in flight
     slot_barrier();
     if (ncv > 0) scan_dt(c0, with_c);
@@ -605,19 +627,13 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       }
       if (live) {
         // every operand read before the products
-        h8 xa[PT], bt[NT], xw[PT];
+        h8 xa[PT], xw[PT];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) xa[pt] = x_frag(sl.x[wid], pt);
         float w[8];
         weights(i0, w);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl, nt);
         weigh_x(xa, w, xw);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = mfma16(bt[nt], xw[pt], acc[nt][pt]);
+        update(sl, xw, acc);
       }
     });
   }
@@ -682,7 +698,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   if (early && live) {
     // the stores were issued before the prologue's loads and complete in
     // order with them: wait until only those loads may be outstanding
-    constexpr int DP = DX + 2 * DBC;
+    const int DP = loads_per_step(true);
     vm_wait((ncv > 0 ? DTI : 0) + (nsteps > 0 ? DP : 0) + (nsteps > 1 ? DP : 0));
     publish_flag();
   }
@@ -834,7 +850,8 @@ hipError_t launch_ssd_scan(const ScanArgs& in, int cus, hipStream_t st) {
   // every workgroup resident at once: the chain of dependent publishes is the
   // critical path (radix 8); otherwise aggregate traffic matters more (radix 4)
   a.tree_lg = wgs <= cus ? 3 : 2;
-  ssd_scan_kernel<32><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
+  if (a.Blo) ssd_scan_kernel<32, true><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
+  else ssd_scan_kernel<32, false><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
   return hipGetLastError();
 }
 

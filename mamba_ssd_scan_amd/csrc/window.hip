@@ -1255,8 +1255,8 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     // binary32 I/O: the exact token-sequential form in binary32 (the chunked
     // form's MFMA operands are binary16 and would round binary32 inputs)
     e = launch_exact_window_f32(d, io_, a.x, a.Bm, a.Cm, a.xstride, a.gstride, d.conv_width == 4 ? 0 : 1, st);
-  } else if (d.dstate == 128 && a.Blo == nullptr) {
-    // binary16 x, B, C at N = 128: the streamed scan
+  } else if (d.dstate == 128) {
+    // binary16 x, B, C at N = 128 (from the fused conv: B with its remainder): the streamed scan
     ScanArgs sa;
     sa.B = a.B; sa.L = a.L; sa.H = a.H; sa.G = a.G; sa.Q = a.Q; sa.nchunks = a.nchunks;
     sa.x = a.x; sa.Bm = a.Bm; sa.Cm = a.Cm; sa.xstride = a.xstride; sa.gstride = a.gstride;
@@ -1264,6 +1264,7 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     sa.state_in = a.state_in; sa.state_out = a.state_out; sa.seqlens = a.seqlens; sa.cu = a.cu; sa.T = a.T;
     sa.xpk = a.xpk; sa.y = a.y; sa.ctrl = a.ctrl; sa.flags = a.flags; sa.agg = a.agg;
     sa.nseg = a.nseg; sa.cps = 0; sa.tree_lg = 3; sa.dt_sp = a.dt_sp; sa.dt_bias = a.dt_bias;
+    sa.Blo = a.Blo; sa.gn = a.gn;
     e = launch_ssd_scan(sa, device_cus(), st);
   } else {
     const bool blo = a.Blo != nullptr;   // only binary16 conv output carries a remainder
