@@ -33,8 +33,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_F16_PEAK = 2500.0     # TFLOP/s dense f16
-# fp32 VALU issue without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# fp32 VALU lane-operations: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz (a 64-wide
+# fp32 multiply issues in two clocks, which is also the published 157.3 TFLOP/s
+# fp32 vector rate counting an fma as two flops); no packed math
+VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_layer_traffic.txt")
 # the window kernel's sources: the kernel, its argument block and the helpers it includes
 KERNEL_SOURCES = [os.path.join(ROOT, "mamba_ssd_scan_amd", "csrc", n)
@@ -271,6 +273,108 @@ def cpu_baselines(inp, s, args):
     return out
 
 
+def time_mixer(torch, m2, synth, dev, stream, P, Q, calls=20):
+    """Microseconds per call of the mixer core (batch 4, L=2048: conv1d+SiLU,
+    scan, gated RMSNorm), inputs drawn on the device."""
+    # timing only (parity of this path is covered by the GPU tests); inputs are
+    # drawn on the device with the mixer workload's distributions
+    ms_ = synth.mixer_window()
+    MB_, ML_, MH_, MN_, MG_ = ms_.batch, ms_.seqlen, ms_.nheads, ms_.dstate, ms_.ngroups
+    Cd_ = MH_ * P + 2 * MG_ * MN_
+    gen = torch.Generator(device=dev).manual_seed(1004)
+    mx = {
+        "xBC": torch.randn(MB_, ML_, Cd_, device=dev, generator=gen).half(),
+        "conv_w": torch.randn(Cd_, 4, device=dev, generator=gen) * 0.5,
+        "conv_b": torch.zeros(Cd_, device=dev),
+        # dt as the layer window draws it: softplus(N(0,1) + log(expm1(dt0))),
+        # dt0 log-uniform on [1e-3, 1e-1], one per head
+        "dt": torch.nn.functional.softplus(
+            torch.randn(MB_, ML_, MH_, device=dev, generator=gen)
+            + torch.log(torch.expm1(torch.exp(torch.rand(MH_, device=dev, generator=gen) * float(np.log(100.0))
+                                              + float(np.log(1e-3)))))).half(),
+        "z": torch.randn(MB_, ML_, MH_ * P, device=dev, generator=gen).half(),
+        "norm_w": torch.ones(MH_ * P, device=dev),
+    }
+    mA = -torch.exp(torch.rand(MH_, device=dev, generator=gen) * float(np.log(16.0)))
+    mD = torch.randn(MH_, device=dev, generator=gen)
+    my = torch.empty(MB_, ML_, MH_ * P, dtype=torch.float16, device=dev)
+    mh = torch.empty(MB_, MH_, P, MN_, dtype=torch.float32, device=dev)
+    mcs = torch.empty(MB_, Cd_, 3, dtype=torch.float16, device=dev)
+    mdims = m2.make_dims(MB_, ML_, MH_, P, MN_, MG_, Q, conv_width=4, norm_group=MH_ * P)
+    mws = m2.alloc_workspace(mdims, dev)
+
+    def mstep():
+        m2.conv_scan_window(mx["dt"], mA, mD, my, mws, xBC=mx["xBC"], conv_w=mx["conv_w"], conv_b=mx["conv_b"],
+                            conv_state_out=mcs, state_out=mh, z=mx["z"], norm_w=mx["norm_w"], chunk=Q,
+                            norm_group=MH_ * P, ngroups=MG_, dstate=MN_, headdim=P, stream=stream)
+
+    for _ in range(3):
+        mstep()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(calls):
+        mstep()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    mix_us = ev0.elapsed_time(ev1) * 1e3 / calls
+    if m2.window_take_error(mws, stream=stream) != 0:
+        print("a segment hand-off gave up in the mixer calls: results invalid", file=sys.stderr)
+        sys.exit(1)
+    del mx, my, mh, mcs, mws
+    torch.cuda.empty_cache()
+    return mix_us, MB_, ML_, MH_, MN_, MG_
+
+
+def time_batched(torch, m2, dev, stream, L, H, P, N, G, Q, calls=20):
+    """Microseconds per call of the batched windows (8 sequences, seven of
+    2048 tokens and one of 1955), inputs drawn on the device with the layer
+    window's distributions; returns (us, lengths)."""
+    # timing only (parity of this workload is covered by the GPU tests); inputs
+    # are drawn on the device with the layer window's distributions
+    BB, blens = 8, [L] * 7 + [1955]
+    gen = torch.Generator(device=dev).manual_seed(1005)
+    bsets = []
+    for k in range(2):
+        dt0 = torch.exp(torch.rand(H, device=dev, generator=gen) * float(np.log(100.0)) + float(np.log(1e-3)))
+        bsets.append({
+            "x": torch.randn(BB, L, H, P, device=dev, generator=gen).half(),
+            "dt": torch.nn.functional.softplus(torch.randn(BB, L, H, device=dev, generator=gen)
+                                               + torch.log(torch.expm1(dt0))).half(),
+            "B": (torch.randn(BB, L, G, N, device=dev, generator=gen) / N ** 0.5).half(),
+            "C": (torch.randn(BB, L, G, N, device=dev, generator=gen) / N ** 0.5).half(),
+            "y": torch.empty(BB, L, H * P, dtype=torch.float16, device=dev),
+            "hT": torch.empty(BB, H, P, N, dtype=torch.float32, device=dev),
+        })
+    bA = -torch.exp(torch.rand(H, device=dev, generator=gen) * float(np.log(16.0)))
+    bD = torch.randn(H, device=dev, generator=gen)
+    bsl = torch.tensor(blens, dtype=torch.int32, device=dev)
+    bdims = m2.make_dims(BB, L, H, P, N, G, Q)
+    bws = m2.alloc_workspace(bdims, dev)
+
+    def bstep(k):
+        t = bsets[k % len(bsets)]
+        m2.conv_scan_window(t["dt"], bA, bD, t["y"], bws, x=t["x"], B=t["B"], C=t["C"], state_out=t["hT"],
+                            seqlens=bsl, chunk=Q, stream=stream)
+
+    for k in range(3):
+        bstep(k)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for k in range(calls):
+        bstep(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    bat_us = ev0.elapsed_time(ev1) * 1e3 / calls
+    if m2.window_take_error(bws, stream=stream) != 0:
+        print("a segment hand-off gave up in the batched calls: results invalid", file=sys.stderr)
+        sys.exit(1)
+    del bsets, bws
+    torch.cuda.empty_cache()
+    return bat_us, blens
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +386,9 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the layer window and print its fields (for kernel traces of that workload)")
+    ap.add_argument("--only", choices=["layer", "batched", "mixer"], default=None,
+                    help="time one workload alone (--steps calls after the warmup) and print its fields, for "
+                         "kernel traces and counters of that workload; layer is the same as --headline-only")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe)
@@ -301,6 +408,20 @@ def main():
     stream = torch.cuda.current_stream(dev)
     s = synth.layer_window()
     B, L, H, P, N, G, Q = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk
+    if args.only == "layer":
+        args.headline_only = True
+    elif args.only == "batched":
+        bus, blens = time_batched(torch, m2, dev, stream, L, H, P, N, G, Q, calls=args.steps)
+        bb = window_bytes(8, L, H, P, N, G, lens=blens)
+        print(json.dumps({"workload": "batched windows", "us": round(bus, 2), "calls": args.steps,
+                          "algorithmic_bytes": bb, "achieved_GBs": round(bb / (bus * 1e-6) / 1e9, 1)}), flush=True)
+        return
+    elif args.only == "mixer":
+        mus, MB_, ML_, MH_, MN_, MG_ = time_mixer(torch, m2, synth, dev, stream, P, Q, calls=args.steps)
+        mb = mixer_bytes(MB_, ML_, MH_, P, MN_, MG_)
+        print(json.dumps({"workload": "mixer core", "us": round(mus, 2), "calls": args.steps,
+                          "algorithmic_bytes": mb, "achieved_GBs": round(mb / (mus * 1e-6) / 1e9, 1)}), flush=True)
+        return
 
     # ---- inputs resident in HBM, rotated sets ---------------------------------
     sets = []
@@ -442,54 +563,8 @@ def main():
     del sets
     torch.cuda.empty_cache()
 
-    # ---- mixer core: conv1d+SiLU, scan, gated RMSNorm (batch 4, L=2048) --------
-    # timing only (parity of this path is covered by the GPU tests); inputs are
-    # drawn on the device with the mixer workload's distributions
-    ms_ = synth.mixer_window()
-    MB_, ML_, MH_, MN_, MG_ = ms_.batch, ms_.seqlen, ms_.nheads, ms_.dstate, ms_.ngroups
-    Cd_ = MH_ * P + 2 * MG_ * MN_
-    gen = torch.Generator(device=dev).manual_seed(1004)
-    mx = {
-        "xBC": torch.randn(MB_, ML_, Cd_, device=dev, generator=gen).half(),
-        "conv_w": torch.randn(Cd_, 4, device=dev, generator=gen) * 0.5,
-        "conv_b": torch.zeros(Cd_, device=dev),
-        # dt as the layer window draws it: softplus(N(0,1) + log(expm1(dt0))),
-        # dt0 log-uniform on [1e-3, 1e-1], one per head
-        "dt": torch.nn.functional.softplus(
-            torch.randn(MB_, ML_, MH_, device=dev, generator=gen)
-            + torch.log(torch.expm1(torch.exp(torch.rand(MH_, device=dev, generator=gen) * float(np.log(100.0))
-                                              + float(np.log(1e-3)))))).half(),
-        "z": torch.randn(MB_, ML_, MH_ * P, device=dev, generator=gen).half(),
-        "norm_w": torch.ones(MH_ * P, device=dev),
-    }
-    mA = -torch.exp(torch.rand(MH_, device=dev, generator=gen) * float(np.log(16.0)))
-    mD = torch.randn(MH_, device=dev, generator=gen)
-    my = torch.empty(MB_, ML_, MH_ * P, dtype=torch.float16, device=dev)
-    mh = torch.empty(MB_, MH_, P, MN_, dtype=torch.float32, device=dev)
-    mcs = torch.empty(MB_, Cd_, 3, dtype=torch.float16, device=dev)
-    mdims = m2.make_dims(MB_, ML_, MH_, P, MN_, MG_, Q, conv_width=4, norm_group=MH_ * P)
-    mws = m2.alloc_workspace(mdims, dev)
-
-    def mstep():
-        m2.conv_scan_window(mx["dt"], mA, mD, my, mws, xBC=mx["xBC"], conv_w=mx["conv_w"], conv_b=mx["conv_b"],
-                            conv_state_out=mcs, state_out=mh, z=mx["z"], norm_w=mx["norm_w"], chunk=Q,
-                            norm_group=MH_ * P, ngroups=MG_, dstate=MN_, headdim=P, stream=stream)
-
-    for _ in range(3):
-        mstep()
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(20):
-        mstep()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    mix_us = ev0.elapsed_time(ev1) * 1e3 / 20
-    if m2.window_take_error(mws, stream=stream) != 0:
-        print("a segment hand-off gave up in the mixer calls: results invalid", file=sys.stderr)
-        sys.exit(1)
+    mix_us, MB_, ML_, MH_, MN_, MG_ = time_mixer(torch, m2, synth, dev, stream, P, Q)
     mbytes = mixer_bytes(MB_, ML_, MH_, P, MN_, MG_)
-    del mx, my, mh, mcs, mws
-    torch.cuda.empty_cache()
 
     # ---- decode: 64 sequences, binary16 resident state ------------------------
     d = synth.DECODE
@@ -560,49 +635,8 @@ def main():
     md_us = ev0.elapsed_time(ev1) * 1e3 / T
     mdbytes = mixer_decode_bytes(DB, DH, DP, DN, DG)
 
-    # ---- batched windows: 8 sequences, seven of 2048 tokens and one of 1955 ----
-    # timing only (parity of this workload is covered by the GPU tests); inputs
-    # are drawn on the device with the layer window's distributions
-    BB, blens = 8, [L] * 7 + [1955]
-    gen = torch.Generator(device=dev).manual_seed(1005)
-    bsets = []
-    for k in range(2):
-        dt0 = torch.exp(torch.rand(H, device=dev, generator=gen) * float(np.log(100.0)) + float(np.log(1e-3)))
-        bsets.append({
-            "x": torch.randn(BB, L, H, P, device=dev, generator=gen).half(),
-            "dt": torch.nn.functional.softplus(torch.randn(BB, L, H, device=dev, generator=gen)
-                                               + torch.log(torch.expm1(dt0))).half(),
-            "B": (torch.randn(BB, L, G, N, device=dev, generator=gen) / N ** 0.5).half(),
-            "C": (torch.randn(BB, L, G, N, device=dev, generator=gen) / N ** 0.5).half(),
-            "y": torch.empty(BB, L, H * P, dtype=torch.float16, device=dev),
-            "hT": torch.empty(BB, H, P, N, dtype=torch.float32, device=dev),
-        })
-    bA = -torch.exp(torch.rand(H, device=dev, generator=gen) * float(np.log(16.0)))
-    bD = torch.randn(H, device=dev, generator=gen)
-    bsl = torch.tensor(blens, dtype=torch.int32, device=dev)
-    bdims = m2.make_dims(BB, L, H, P, N, G, Q)
-    bws = m2.alloc_workspace(bdims, dev)
-
-    def bstep(k):
-        t = bsets[k % len(bsets)]
-        m2.conv_scan_window(t["dt"], bA, bD, t["y"], bws, x=t["x"], B=t["B"], C=t["C"], state_out=t["hT"],
-                            seqlens=bsl, chunk=Q, stream=stream)
-
-    for k in range(3):
-        bstep(k)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for k in range(20):
-        bstep(k)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    bat_us = ev0.elapsed_time(ev1) * 1e3 / 20
-    if m2.window_take_error(bws, stream=stream) != 0:
-        print("a segment hand-off gave up in the batched calls: results invalid", file=sys.stderr)
-        sys.exit(1)
-    bbytes = window_bytes(BB, L, H, P, N, G, lens=blens)
-    del bsets, bws
-    torch.cuda.empty_cache()
+    bat_us, blens = time_batched(torch, m2, dev, stream, L, H, P, N, G, Q)
+    bbytes = window_bytes(8, L, H, P, N, G, lens=blens)
 
     # ---- CPU baseline: the oracle on bounded samples of each workload ----------
     cpu = cpu_baselines(inp, s, args) if not args.no_cpu_baseline else None
