@@ -171,12 +171,16 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   using Slot = typename Wd::template Slot<BLO>;
   constexpr int NWV = Wd::NWV, NTH = Wd::NTH, PT = Wd::PT, WPH = Wd::WPH;
   __shared__ Slot r0, r1, r2;
-  __shared__ float Sx[NWV][256];     // per wave: running log2-decay from the chunk start (inclusive)
-  __shared__ float Dx[NWV][256];     // per wave: the chunk's dt
-  __shared__ float Wx[NWV][256];     // per wave: state-update weight of each token (see scan_dt)
-  // per wave: readout scale of each token (output pass); with the B
-  // remainder, whose rows take that room, the scales are computed per step
-  __shared__ float Cx[BLO ? 1 : NWV][256];
+  // per head of the block (the two waves of a head write the same values):
+  __shared__ float Sx[KH][256];     // running log2-decay from the chunk start (inclusive)
+  __shared__ float Dx[KH][256];     // the chunk's dt
+  __shared__ float Wx[KH][256];     // state-update weight of each token (see scan_dt)
+  // readout scale of each token (output pass); with the B remainder, whose
+  // rows take that room, the scales are computed per step
+  __shared__ float Cx[BLO ? 1 : KH][256];
+  // the output steps' C.B^T blocks, each computed once per workgroup one step
+  // ahead (two buffers; lane l's four values of block b at [b][l])
+  __shared__ f4 cbs[2][3][64];
   __shared__ _Float16 dtr[2][256 * 8];    // a chunk's dt rows as read (8 elements per token from the aligned base), two chunks
   __shared__ unsigned sh_ticket, sh_gen;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, q = lane >> 4;
@@ -271,10 +275,10 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   const _Float16* const dt0 = a.dt + (size_t)ubase * a.dtld + h0;
   const int sh0 = (int)(((size_t)dt0 >> 1) & 1);
   const u4 rdt = rsrc_words(dt0 - sh0, len > 0 ? ((unsigned)(sh0 + (len - 1) * a.dtld + (a.H - h0)) * ES + 3u) & ~3u : 0u);
-  float* const Sw = Sx[wid];
-  float* const Dw = Dx[wid];
-  float* const Ww = Wx[wid];
-  float* const Cw = Cx[BLO ? 0 : wid];
+  float* const Sw = Sx[wid / WPH];
+  float* const Dw = Dx[wid / WPH];
+  float* const Ww = Wx[wid / WPH];
+  float* const Cw = Cx[BLO ? 0 : wid / WPH];
 
   // steps of chunk c that hold tokens of this sequence
   auto steps_of = [&](int c) { return (min(max(len - c * a.Q, 0), a.Q) + TS - 1) / TS; };
@@ -433,33 +437,50 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
     }
   };
 
-  // The step in stages, so that each stage's vector arithmetic can run under
-  // the previous stage's matrix products: (1) the C.B^T blocks while the
-  // state is converted to the readout operand; (2) the readout C.R while the
-  // state is decayed; (3) the state update while the decay mask is applied
-  // to C.B^T; (4) the masked product and the outputs.  The state always
-  // advances: after a pass's last step it is used only when it is the
-  // sequence's final state.  Scheduling barriers keep the stages in order.
-  auto step = [&](const Slot& sl, int i0, int tok0) __attribute__((always_inline)) {
+  // C.B^T block b of a step, (s-tile, t-tile) = (0, 0), (0, 1), (1, 1): rows
+  // s = 16 S + 4 q .. + 3 of column t = 16 T + lr per lane, into buffer buf
+  auto cb_block = [&](const Slot& sl, int b, int buf) __attribute__((always_inline)) {
+    const int S = b == 2 ? 1 : 0, T = b == 0 ? 0 : 1;
+    h8 bb[KM], cc[KM];
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      bb[m] = *reinterpret_cast<const h8*>(&sl.b[bo(16 * S + lr, q + 4 * m)]);
+      cc[m] = *reinterpret_cast<const h8*>(&sl.c[bo(16 * T + lr, q + 4 * m)]);
+    }
+    f4 acc1 = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < KM; ++m) acc1 = mfma16(bb[m], cc[m], acc1);
+    cbs[buf][b][lane] = acc1;
+  };
+
+  // The step in four stages, ordered so that the LDS, the vector ALU and the
+  // matrix cores overlap (every wave of the workgroup is in the same stage
+  // at once, right after the barrier that publishes the slot):
+  // (1) reads of the update's operands (x, B^T, weights), while the state is
+  //     converted to the readout operand and decayed over the step;
+  // (2) the state update R += sum_s w_s B_s x_s, with the reads of the C
+  //     rows issued between its products;
+  // (3) reads of the C.B^T blocks (computed during the previous step) and of
+  //     the outputs' per-token values, the readout C.R, and the decay mask
+  //     formed under it;
+  // (4) the masked product and the outputs.
+  // The state always advances: after a pass's last step it is used only
+  // when it is the sequence's final state.  Scheduling barriers keep the
+  // stages in order.
+  auto step = [&](const Slot& sl, int i0, int tok0, int cbuf) __attribute__((always_inline)) {
     const _Float16* xs = sl.x[wid];
     const float Sj_start = i0 ? Sw[i0 - 1] : 0.f;
     const float Sj_end = Sw[i0 + TS - 1];
-    // C rows t = 16 T + lr and B rows s = 16 S + lr, n = 8 q + 32 m .. + 7
-    h8 cf[2][KM], bf[2][KM];
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int m = 0; m < KM; ++m) {
-        cf[T][m] = *reinterpret_cast<const h8*>(&sl.c[bo(16 * T + lr, q + 4 * m)]);
-        bf[T][m] = *reinterpret_cast<const h8*>(&sl.b[bo(16 * T + lr, q + 4 * m)]);
-      }
+    // (1)
     h8 xa[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) xa[pt] = x_frag(xs, pt);
     float w[8];
     weights(i0, w);
-    // (1) readout operand: the state rows p as binary16; C.B^T blocks
-    // (s-tile, t-tile) = (0, 0), (0, 1), (1, 1): rows s (4 per lane) x column t
+    h8 bt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl.b, nt);
+    // readout operand: the state rows p as binary16; then the decay
     h8 ra[PT][KM];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
@@ -469,20 +490,57 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
         ra[pt][m] = h8{(_Float16)s0[0], (_Float16)s0[1], (_Float16)s0[2], (_Float16)s0[3],
                        (_Float16)s1[0], (_Float16)s1[1], (_Float16)s1[2], (_Float16)s1[3]};
       }
-    f4 cb[3];
+    const float dec = ex2(Sj_end - Sj_start);
 #pragma unroll
-    for (int b = 0; b < 3; ++b) cb[b] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      cb[0] = mfma16(bf[0][m], cf[0][m], cb[0]);
-      cb[1] = mfma16(bf[0][m], cf[1][m], cb[1]);
-      cb[2] = mfma16(bf[1][m], cf[1][m], cb[2]);
-    }
+      for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
     __builtin_amdgcn_sched_barrier(0);
-    // (2) readout C.R; the state decays over the step; B^T fragments and
-    // the weighted x for the update
+    // (2) C rows t = 16 T + lr, n = 8 q + 32 m .. + 7, read between the
+    // update's products
     h8 xw[PT];
     weigh_x(xa, w, xw);
+    h8 cf[2][KM];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) R[nt][pt] = mfma16(bt[nt], xw[pt], R[nt][pt]);
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int m = 0; m < KM; ++m) cf[T][m] = *reinterpret_cast<const h8*>(&sl.c[bo(16 * T + lr, q + 4 * m)]);
+#pragma unroll
+    for (int i = 0; i < 2 * KM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (BLO) {
+      // the remainder of B's binary16 rounding
+      h8 bl[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bl[nt] = bt_frag(sl.bl, nt);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) R[nt][pt] = mfma16(bl[nt], xw[pt], R[nt][pt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (3) the C.B^T blocks; per output column t = 16 T + lr: its log2-decay,
+    // readout scale and x rows (p = 16 pt + 4 q .. + 3); the readout C.R
+    f4 cb[3];
+#pragma unroll
+    for (int b = 0; b < 3; ++b) cb[b] = cbs[cbuf][b][lane];
+    float St[2], sc[2];
+    h4 xr[2][PT];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int tl = 16 * T + lr;
+      St[T] = Sw[i0 + tl];
+      if constexpr (!BLO) sc[T] = Cw[i0 + tl];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+        xr[T][pt] = *reinterpret_cast<const h4*>(&xs[Wd::xo(tl, 2 * pt + (q >> 1)) + 4 * (q & 1)]);
+    }
     f4 yr[PT][2];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
@@ -492,16 +550,24 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int m = 0; m < KM; ++m) yr[pt][T] = mfma16(ra[pt][m], cf[T][m], yr[pt][T]);
       }
-    const float dec = ex2(Sj_end - Sj_start);
+    // The mask entry of (s, t), s <= t, is dt_s 2^{S_t - S_s} C_t.B_s.  It
+    // factors as w_s 2^{S_t - S_end} with the update weight w_s = dt_s
+    // 2^{S_end - S_s} <= dt_s and 2^{S_t - S_end} >= 1, both finite while the
+    // step's decay stays within 2^-100; past that (rare) the entries are
+    // formed one by one, each exponent clamped so that the masked ones (s > t)
+    // stay finite.
+    float v[3][4];
+    if (__builtin_amdgcn_readfirstlane(Sj_start - Sj_end <= 100.f ? 1 : 0)) {
+      float u[2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int T = 0; T < 2; ++T) u[T] = ex2(St[T] - Sj_end);
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
-    __builtin_amdgcn_sched_barrier(0);
-    // (3) state update R += sum_s w_s B_s x_s; the decay mask on C.B^T
-    update(sl, xw, R);
-    h8 mf[2];
-    {
+      for (int b = 0; b < 3; ++b) {
+        const int S = b == 2 ? 1 : 0, T = b == 0 ? 0 : 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[b][e] = cb[b][e] * (w[4 * S + e] * u[T]);
+      }
+    } else {
       float Ss[2][4], ds[2][4];
 #pragma unroll
       for (int S = 0; S < 2; ++S) {
@@ -513,38 +579,41 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
           ds[S][e] = dv[e];
         }
       }
-      float v[3][4];
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
         const int S = b == 2 ? 1 : 0, T = b == 0 ? 0 : 1;
-        const float St = Sw[i0 + 16 * T + lr];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // the exponent is clamped so that the masked entries (s > t) stay
-          // finite; the off-diagonal block (s-tile 0, t-tile 1) holds only s < t
-          const float x = cb[b][e] * ds[S][e] * ex2(fminf(St - Ss[S][e], 0.f));
-          v[b][e] = (S < T || 4 * q + e <= lr) ? x : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) v[b][e] = cb[b][e] * ds[S][e] * ex2(fminf(St[T] - Ss[S][e], 0.f));
       }
-      mf[0] = h8{(_Float16)v[0][0], (_Float16)v[0][1], (_Float16)v[0][2], (_Float16)v[0][3],
-                 (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-      mf[1] = h8{(_Float16)v[1][0], (_Float16)v[1][1], (_Float16)v[1][2], (_Float16)v[1][3],
-                 (_Float16)v[2][0], (_Float16)v[2][1], (_Float16)v[2][2], (_Float16)v[2][3]};
+    }
+    // causal: the off-diagonal block (s-tile 0, t-tile 1) holds only s < t
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (b != 1 && 4 * q + e > lr) v[b][e] = 0.f;
+    h8 mf[2];
+    mf[0] = h8{(_Float16)v[0][0], (_Float16)v[0][1], (_Float16)v[0][2], (_Float16)v[0][3],
+               (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+    mf[1] = h8{(_Float16)v[1][0], (_Float16)v[1][1], (_Float16)v[1][2], (_Float16)v[1][3],
+               (_Float16)v[2][0], (_Float16)v[2][1], (_Float16)v[2][2], (_Float16)v[2][3]};
+    if constexpr (BLO) {
+#pragma unroll
+      for (int T = 0; T < 2; ++T) sc[T] = ex2(St[T] - Sj_start);
     }
     __builtin_amdgcn_sched_barrier(0);
     // (4) masked product and the outputs y = sc C.R + (masked C.B^T) x + D x
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       const int tl = 16 * T + lr;
-      const float sc = BLO ? ex2(Sw[i0 + tl] - Sj_start) : Cw[i0 + tl];
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
         const f4 yd = mfma16(xa[pt], mf[T], f4{0.f, 0.f, 0.f, 0.f});
         const int p0 = 16 * pt + 4 * q;
-        const h4 xr = *reinterpret_cast<const h4*>(&xs[Wd::xo(tl, 2 * pt + (q >> 1)) + 4 * (q & 1)]);
         h4 hv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(__builtin_fmaf(sc, yr[pt][T][e], yd[e]) + Dh * (float)xr[e]);
+        for (int e = 0; e < 4; ++e)
+          hv[e] = (_Float16)(__builtin_fmaf(sc[T], yr[pt][T][e], yd[e]) + Dh * (float)xr[T][pt][e]);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, hv), ry,
                                               (unsigned)(tok0 + tl) * yrow + (unsigned)p0 * ES, 0, 0);
       }
@@ -561,36 +630,49 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // The pass over the segment: the loads of its first chunk's dt and of its
   // first two steps are already in flight (with_c: x, B and C, else x and B);
   // per step k the loads of step k + 2 (and, at a chunk's first step, of the
-  // next chunk's dt), then body(k, slot), then the barrier that publishes
-  // step k + 1.  At a chunk boundary each wave scans the next chunk's dt
-  // after that barrier (the scan overwrites only the wave's own arrays).
-  // Explicit waits: before the barrier that publishes step k + 1, this
-  // wave's loads of step k + 1 must have landed.  Vector memory operations
-  // complete in issue order, so it waits until no more are outstanding than
-  // were issued after them: the stores of steps k - 1 and k (stores_per_step
-  // each, when this wave stores) and the loads of step k + 2.  Operations the
-  // count leaves out (dt loads, hand-off traffic) only make it wait longer.
+  // next chunk's dt), then body(k, slot of k, slot of k + 1), then the
+  // barrier that publishes step k + 1.  At a chunk boundary each wave scans
+  // the next chunk's dt after that barrier (the scan overwrites only its
+  // head's arrays, which no wave reads any more).
+  // Explicit waits: vector memory operations complete in issue order, so a
+  // wave waits until no more are outstanding than it issued after the ones
+  // that must have landed.  Before the barrier that publishes step k + 1:
+  // - local-state pass: the loads of step k + 1; issued after them were the
+  //   stores of steps k - 1 and k (stores_per_step each, when this wave
+  //   stores) and the loads of step k + 2;
+  // - output pass: the loads of step k + 2 as well, whose C.B^T blocks are
+  //   computed during step k + 1; issued after them were the stores of
+  //   step k.
+  // Operations the count leaves out (dt loads, hand-off traffic) only make it
+  // wait longer.  The output pass starts with the blocks of step 0, computed
+  // by waves 0-2 between two barriers; during step k, waves (k + 1 + w) mod 8
+  // = 0, 1, 2 compute block 0, 1, 2 of step k + 1.
   auto pass = [&](bool with_c, int stores_per_step, auto&& body) __attribute__((always_inline)) {
     const int D = loads_per_step(with_c);
-    if (nsteps > 0) vm_wait(nsteps > 1 ? D : 0);   // the dt and step 0's loads; step 1's may stay in flight
+    if (nsteps > 0) vm_wait(nsteps > 1 && !with_c ? D : 0);   // the dt and step 0's loads (output pass: step 1's too)
     slot_barrier();
     if (ncv > 0) scan_dt(c0, with_c);
-    auto one = [&](int k, const Slot& sl, Slot& nx) __attribute__((always_inline)) {
+    if (with_c && nsteps > 0) {
+      if (wid < 3) cb_block(r0, wid, 0);
+      slot_barrier();
+    }
+    auto one = [&](int k, const Slot& sl, Slot& nx, const Slot& nn) __attribute__((always_inline)) {
       const int kc = k % J, cc = c0 + k / J;
       if (kc == 0 && cc + 1 < c0 + ncv) issue_dt(cc + 1);
       const bool more = k + 2 < nsteps;
       if (more) issue(nx, tok_of(k + 2), with_c);
-      body(k, sl);
-      if (k + 1 < nsteps) vm_wait((k > 0 ? stores_per_step : 0) + (more ? D : 0) + stores_per_step);
+      body(k, sl, nn);
+      if (k + 1 < nsteps)
+        vm_wait(with_c ? stores_per_step : (k > 0 ? stores_per_step : 0) + (more ? D : 0) + stores_per_step);
       slot_barrier();
       if (k + 1 < nsteps && (k + 1) % J == 0) scan_dt(cc + 1, with_c);
     };
     for (int k = 0; k < nsteps; k += 3) {
-      one(k, r0, r2);
+      one(k, r0, r2, r1);
       if (k + 1 >= nsteps) break;
-      one(k + 1, r1, r0);
+      one(k + 1, r1, r0, r2);
       if (k + 2 >= nsteps) break;
-      one(k + 2, r2, r1);
+      one(k + 2, r2, r1, r0);
     }
   };
   // the first loads of a pass
@@ -611,7 +693,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
     for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
   if (!last) {
     prologue(false);
-    pass(false, 0, [&](int k, const Slot& sl) __attribute__((always_inline)) {
+    pass(false, 0, [&](int k, const Slot& sl, const Slot&) __attribute__((always_inline)) {
       const int kc = k % J, i0 = kc * TS;
       const int cc = c0 + k / J;
       const float Send = Sw[min(a.Q, len - cc * a.Q) - 1];   // dt = 0 past the end: S constant there
@@ -807,8 +889,10 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
 
   // ---- phase 3: outputs; R runs from the carry-in through the segment ---------------
   const bool want_state = last && a.state_out != nullptr;
-  pass(true, live ? 2 * PT : 0, [&](int k, const Slot& sl) __attribute__((always_inline)) {
-    if (live) step(sl, (k % J) * TS, tok_of(k));
+  pass(true, live ? 2 * PT : 0, [&](int k, const Slot& sl, const Slot& nsl) __attribute__((always_inline)) {
+    if (live) step(sl, (k % J) * TS, tok_of(k), k & 1);
+    const int blk = (wid + k + 1) & 7;
+    if (k + 1 < nsteps && blk < 3) cb_block(nsl, blk, (k + 1) & 1);
   });
   if (want_state && live) {
 #pragma unroll

@@ -121,6 +121,29 @@ def test_dt_zero_gives_skip_and_keeps_state():
     assert np.array_equal(hT2, h0)
 
 
+@pytest.mark.parametrize("segments", [0, 3])
+def test_window_steps_with_strong_decay(segments):
+    """Heads whose 32-token steps decay by more than 2^-100 (the scan then
+    forms the intra-step decay mask entry by entry), heads that straddle
+    that bound from step to step, and ordinary heads, in one window."""
+    inp = rand_window(61, 1, 900, 8, 128, 2)
+    rng = np.random.default_rng(62)
+    A = inp["A"].copy()
+    A[:4] = -16.0
+    inp["A"] = A
+    dt = inp["dt"].astype(np.float32)
+    # per-token log2 decay 16 dt log2(e): about 11.5 (heads 0, 1), and
+    # around 100 / 32 per token (heads 2, 3)
+    dt[..., 0:2] = 0.5 + 0.05 * rng.standard_normal(dt[..., 0:2].shape)
+    dt[..., 2:4] = 0.135 * np.exp(0.3 * rng.standard_normal(dt[..., 2:4].shape))
+    inp["dt"] = dt.astype(inp["dt"].dtype)
+    lg = -16.0 * math.log2(math.e) * inp["dt"].astype(np.float64)[0, :, 2:4]
+    steps = np.add.reduceat(lg, np.arange(0, 900, 32), axis=0)
+    assert (steps < -100).any() and (steps > -100).any()
+    h0 = np.random.default_rng(63).standard_normal((1, 8, 64, 128)).astype(np.float32)
+    check_window(f"strong decay, segments {segments}", inp, 256, seqlens=[900], state_in=h0, segments=segments)
+
+
 def test_split_window_carry_matches_unsplit():
     inp = rand_window(27, 1, 1024, 16, 128, 2)
     y, hT = run_window(inp, 256)
