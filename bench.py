@@ -174,25 +174,27 @@ def mixer_decode_bytes(B, H, P, N, G):
             + Cd * 4 * 4 + Cd * 4 + H * P * 4 + 2 * H * 4)
 
 
-def window_mfma_flops(L, H, P, N, Q=256, segments=8, step=32, half=32):
+def window_mfma_flops(L, H, P, N, Q=256, segments=8, step=32, half=32, heads_per_block=4):
     """f16 MFMA flops the window kernel issues for one sequence with a final
     state (16x16x32 instructions, 16384 flops each), for the chunks split into
     `segments` runs of consecutive chunks (the split the library picks for
     one layer window).  Per (half of a head) and 32-token step: the local-state
     pass, run on every segment but the last, takes N/16 x half/16
-    instructions; the output pass takes the causal C.B^T blocks (3 blocks x
-    N/32), the masked product (2 x half/16), the carry readout (2 x half/16 x
-    N/32) and the running-state update (N/16 x half/16) on every step but the
-    last step of each non-final segment."""
+    instructions; the output pass takes the masked product (2 x half/16), the
+    carry readout (2 x half/16 x N/32) and the running-state update
+    (N/16 x half/16) on every step, and a share of the causal C.B^T blocks
+    (3 blocks x N/32 per step), which one workgroup of heads_per_block heads
+    (two waves per head) computes once."""
     J = Q // step
     C = L // Q
     cps = -(-C // segments)
-    nseg = -(-C // cps)
     nt, pt, km = N // 16, half // 16, max(N // 32, 1)
+    waves = heads_per_block * (P // half)
     local = nt * pt * J * (C - cps)                      # all chunks outside the last segment
-    out = (3 * km + 2 * pt + 2 * pt * km) * J * C
-    upd = nt * pt * (J * C - (nseg - 1))
-    return H * (P // half) * (local + out + upd) * 16384
+    out = (2 * pt + 2 * pt * km) * J * C
+    upd = nt * pt * J * C
+    cb = 3 * km * J * C / waves
+    return H * (P // half) * (local + out + upd + cb) * 16384
 
 
 def _timed(fn, min_s=2.0, max_reps=20):
