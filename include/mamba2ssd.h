@@ -77,10 +77,16 @@ typedef struct mamba2_dims {
                             through the workspace.  Results agree up to
                             rounding for every k.                              */
     int32_t dt_softplus; /* 0: dt is given positive and used as is;
-                            1: dt is the raw pre-activation and every kernel
-                            uses dt_eff = (float) sp((double) dt +
-                            (double) dt_bias[h]), sp(v) = v for v > 20 and
-                            log1p(exp(v)) otherwise (no clamp)              */
+                            1: dt is the raw pre-activation, dt_eff =
+                            sp(dt + dt_bias[h]), sp(v) = v for v > 20 and
+                            log1p(exp(v)) otherwise (no clamp).  Decode, the
+                            one-token mixer, the requantized window, binary32
+                            windows and the backward evaluate it as
+                            (float) sp((double) dt + (double) dt_bias[h]);
+                            binary16 window scans evaluate it in binary32
+                            with the hardware exponential and logarithm
+                            (relative error below about 6e-5, within the
+                            window tolerance)                               */
     int32_t packed_tokens; /* window calls: 0 for the (B, L, ...) layout; T > 0
                             for packed variable-length windows: every
                             per-token tensor (x, B, C, xBC, dt, z, y) holds T
