@@ -23,6 +23,7 @@
 //    streaming pass over y and z;
 //  * gated_norm_kernel: the norm finish from per-head partial sums, for the
 //    one-token mixer step.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -1162,15 +1163,24 @@ static WsLayout ws_layout(const mamba2_dims& d) {
 
 size_t window_workspace_bytes(const mamba2_dims& d) { return ws_layout(d).total; }
 
-// compute units of the current device (cached per device)
-static int device_cus() {
-  static int cache[64];
+// current device (0 when it cannot be read), for the per-device caches below
+static int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] > 0) return cache[dev];
+  return hipGetDevice(&dev) == hipSuccess && dev >= 0 ? dev : 0;
+}
+constexpr int kMaxDevices = 64;
+
+// compute units of the current device (cached per device; threads that race
+// on a first query store the same value)
+static int device_cus() {
+  static std::atomic<int> cache[kMaxDevices];
+  const int dev = current_device();
+  if (dev >= kMaxDevices) return 256;
+  const int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  cache[dev] = n;
+  cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -1178,14 +1188,18 @@ template <typename IO, int N, bool BLO>
 static hipError_t launch_scan(const WinArgs<IO>& a, hipStream_t st) {
   const int hpg = a.H / a.G;
   const long long slots = (long long)a.B * a.G * ((hpg + wv::KH - 1) / wv::KH);   // workgroups per segment index
-  // Resident workgroups per CU (the state lives in registers, so usually one).
-  static int per_cu = 0;
+  // Resident workgroups per CU (the state lives in registers, so usually
+  // one), cached per device as device_cus() is.
+  static std::atomic<int> per_cu_cache[kMaxDevices];
+  const int dev = current_device();
+  int per_cu = dev < kMaxDevices ? per_cu_cache[dev].load(std::memory_order_relaxed) : 0;
   if (per_cu <= 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ssd_window_group_kernel<IO, N, BLO>, 64 * wv::NWV, 0) !=
             hipSuccess || n <= 0)
       n = 1;
     per_cu = n;
+    if (dev < kMaxDevices) per_cu_cache[dev].store(n, std::memory_order_relaxed);
   }
   const long long resident = (long long)device_cus() * per_cu;
   // Segments: as many consecutive-chunk runs per sequence as keep every
