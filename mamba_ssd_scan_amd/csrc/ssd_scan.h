@@ -27,6 +27,7 @@ struct ScanArgs {
   int nseg;            // segments per sequence
   int cps;             // chunks per segment
   int tree_lg;         // log2 of the radix of the segment tree
+  int pair;            // two segments: the second computes the first's local state itself (no hand-off)
   int dt_sp;
   const float* dt_bias;
   const _Float16* Blo;   // fused conv: B's binary16 remainder, rows of gn elements (else null)

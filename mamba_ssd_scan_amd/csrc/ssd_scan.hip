@@ -245,9 +245,10 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   const int len = __builtin_amdgcn_readfirstlane(span.len);
   const int ubase = __builtin_amdgcn_readfirstlane((int)span.base);
   const size_t xbase = a.xpk ? (size_t)ubase : (size_t)b * a.L;
-  const int c0 = sg * a.cps;                                    // first chunk of the segment
-  const int c1 = min(c0 + a.cps, a.nchunks);                    // one past its last chunk
+  int c0 = sg * a.cps;                                          // first chunk of the segment
+  int c1 = min(c0 + a.cps, a.nchunks);                          // one past its last chunk
   const bool last = sg + 1 == a.nseg;
+  const bool pair = a.pair != 0;
   // wave-uniform scalars (a value still pending from a load before the step
   // loops would make the compiler wait for all memory operations inside them)
   const float Ah = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.A[h] * kLog2e)));
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // steps of chunk c that hold tokens of this sequence
   auto steps_of = [&](int c) { return (min(max(len - c * a.Q, 0), a.Q) + TS - 1) / TS; };
   // every step of the segment, in order
-  const int ncv = min(max((len - c0 * a.Q + a.Q - 1) / a.Q, 0), c1 - c0);   // chunks with tokens
+  int ncv = min(max((len - c0 * a.Q + a.Q - 1) / a.Q, 0), c1 - c0);   // chunks with tokens
 
   // ---- loads of one step into a slot (this wave's share) ----------------------
   // (DX + DBC per operand loads per wave and step; the explicit waits count them)
@@ -684,14 +685,26 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
 
   // ---- phase 1: the segment's local state (every segment but the last) ----------
   // acc is kept relative to the end of the current chunk: it is decayed over
-  // each new chunk before that chunk's tokens are added.
+  // each new chunk before that chunk's tokens are added.  With two segments
+  // (pair) the first skips this pass and the second runs it over the first
+  // segment's chunks instead: its result, with the initial state, is the
+  // second segment's carry-in, and no hand-off is needed.  (A local-state
+  // step costs a third to a quarter of an output step, so the first segment
+  // gets the larger share of the chunks: see the launch.)
   float segdec = 1.f;                           // decay over the segment
   f4 acc[NT][PT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = f4{0.f, 0.f, 0.f, 0.f};
-  if (!last) {
+  const int own_c0 = c0, own_c1 = c1, own_ncv = ncv, own_nsteps = nsteps;
+  if (pair && last) {
+    c0 = 0;
+    c1 = a.cps;
+    ncv = min(max((len + a.Q - 1) / a.Q, 0), c1);
+    nsteps = ncv > 0 ? (ncv - 1) * J + steps_of(ncv - 1) : 0;
+  }
+  if (pair ? last : !last) {
     prologue(false);
     pass(false, 0, [&](int k, const Slot& sl, const Slot&) __attribute__((always_inline)) {
       const int kc = k % J, i0 = kc * TS;
@@ -719,6 +732,10 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       }
     });
   }
+  c0 = own_c0;
+  c1 = own_c1;
+  ncv = own_ncv;
+  nsteps = own_nsteps;
   // ---- phase 2: carry-in over an indexed tree of segments (radix r = 2^lg) --------
   // With i = sg + 1 and block(i) = r^(number of trailing zero base-r digits of
   // i), segment sg publishes the aggregate of segments (i - block(i), i]
@@ -748,11 +765,20 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   const int lg = a.tree_lg;
   const int t_in = ((1 << lg) - 1) * (__builtin_ctz((unsigned)si) / lg);   // aggregates inside this segment's block
   int nodes = 0, my_node = 0;
-  for (int n = si - 1; n > 0; n -= 1 << (lg * (__builtin_ctz((unsigned)n) / lg)), ++nodes)
-    if (lane == nodes) my_node = n;
+  if (!pair)
+    for (int n = si - 1; n > 0; n -= 1 << (lg * (__builtin_ctz((unsigned)n) / lg)), ++nodes)
+      if (lane == nodes) my_node = n;
   const int tb = t_in < nodes ? t_in : nodes;
-  const bool early = !last && tb == 0;
+  const bool early = !pair && !last && tb == 0;
   float scale = 1.f;                            // product of the decays folded in
+  if (pair && last) {
+    // the first segment's local state is the whole carry-in but for h0
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) R[nt][pt] = acc[nt][pt];
+    scale = segdec;
+  }
   // own aggregate (segdec R + local, its decay segdec scale) into the workspace
   auto publish_stores = [&]() __attribute__((always_inline)) {
     const rsrc_t r = mkr(a.agg + (size_t)item * (N * PH), kStBytes);
@@ -837,7 +863,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
         add_node(k, b0);
       }
     }
-    if (!last && !early) {
+    if (!pair && !last && !early) {
       publish_stores();
       __builtin_amdgcn_s_waitcnt(0);
       publish_flag();
@@ -930,6 +956,12 @@ hipError_t launch_ssd_scan(const ScanArgs& in, int cus, hipStream_t st) {
   nseg = nseg < 1 ? 1 : (nseg > a.nchunks ? a.nchunks : nseg);
   a.cps = (a.nchunks + nseg - 1) / nseg;
   a.nseg = (a.nchunks + a.cps - 1) / a.cps;
+  // Two segments: the second runs the first's local-state pass itself, so
+  // the first takes the larger share of the chunks (and leaves at least
+  // one): about 60 %, or 75 % with the B remainder, whose output steps cost
+  // more against its local-state steps (measured at 8 chunks: 5 and 6).
+  a.pair = a.nseg == 2;
+  if (a.pair) a.cps = min(a.Blo ? (3 * a.nchunks + 3) / 4 : (3 * a.nchunks + 4) / 5, a.nchunks - 1);
   const long long wgs = (long long)a.nseg * slots;
   // every workgroup resident at once: the chain of dependent publishes is the
   // critical path (radix 8); otherwise aggregate traffic matters more (radix 4)

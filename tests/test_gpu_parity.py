@@ -86,9 +86,11 @@ def test_many_chunks_carry_tree(B):
 
 @pytest.mark.parametrize("segments", [1, 2, 3, 9])
 def test_segments_of_consecutive_chunks(segments):
-    # 9 chunks of 128 tokens run as 1, 2, 3 or 9 segments (runs of 9, 5, 3 or 1
-    # chunks passing the state in registers); the lengths end inside the first
-    # chunk, inside a middle segment and at the window end
+    # 9 chunks of 128 tokens run as 1, 2, 3 or 9 segments (runs of 9, 6 + 3,
+    # 3 or 1 chunks passing the state in registers; with two segments the
+    # second computes the first one's local state itself, no hand-off); the
+    # lengths end inside the first chunk, inside an earlier segment and at
+    # the window end
     inp = rand_window(51 + segments, 3, 1100, 16, 128, 2)
     h0 = np.random.default_rng(52).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
     check_window(f"segments={segments}", inp, 128, seqlens=[1100, 700, 100], state_in=h0, segments=segments)
