@@ -71,11 +71,14 @@ typedef struct mamba2_dims {
     int32_t state_dtype; /* resident decode state: MAMBA2_F32 or MAMBA2_F16     */
     float norm_eps;      /* epsilon inside the RMSNorm square root              */
     int32_t segments;    /* window scan work split: 0 lets the library choose;
-                            k > 0 splits each sequence into min(k, chunks)
-                            runs of consecutive chunks.  Chunks inside a run
-                            pass the state on in registers; runs hand it over
-                            through the workspace.  Results agree up to
-                            rounding for every k.                              */
+                            k > 0 splits each sequence into up to min(k,
+                            chunks) runs of consecutive chunks.  Chunks
+                            inside a run pass the state on in registers;
+                            runs hand it over through the workspace, except
+                            that with two runs (binary16 I/O, dstate 128) the
+                            second computes the first's state itself and the
+                            first takes the larger share of the chunks.
+                            Results agree up to rounding for every k.       */
     int32_t dt_softplus; /* 0: dt is given positive and used as is;
                             1: dt is the raw pre-activation, dt_eff =
                             sp(dt + dt_bias[h]), sp(v) = v for v > 20 and
