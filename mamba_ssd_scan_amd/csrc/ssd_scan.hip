@@ -455,16 +455,18 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   };
 
   // The step in four stages, ordered so that the LDS, the vector ALU and the
-  // matrix cores overlap (every wave of the workgroup is in the same stage
-  // at once, right after the barrier that publishes the slot):
-  // (1) reads of the update's operands (x, B^T, weights), while the state is
-  //     converted to the readout operand and decayed over the step;
-  // (2) the state update R += sum_s w_s B_s x_s, with the reads of the C
-  //     rows issued between its products;
-  // (3) reads of the C.B^T blocks (computed during the previous step) and of
-  //     the outputs' per-token values, the readout C.R, and the decay mask
-  //     formed under it;
+  // matrix cores overlap:
+  // (1) reads of the C rows while the state is converted to the readout
+  //     operand;
+  // (2) the readout C.R, with the state decayed over the step and the
+  //     update's operands (x, B^T, weights) read under its products;
+  // (3) the state update R += sum_s w_s B_s x_s, with the reads of the C.B^T
+  //     blocks (computed during the previous step) and of the outputs'
+  //     per-token values, and the decay mask formed under it;
   // (4) the masked product and the outputs.
+  // (The readout operand dies with the readout, before the update's
+  // operands are read: fewer registers are live at once than with the
+  // update first.)
   // The state always advances: after a pass's last step it is used only
   // when it is the sequence's final state.  Scheduling barriers keep the
   // stages in order.
@@ -472,16 +474,13 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
     const _Float16* xs = sl.x[wid];
     const float Sj_start = i0 ? Sw[i0 - 1] : 0.f;
     const float Sj_end = Sw[i0 + TS - 1];
-    // (1)
-    h8 xa[PT];
+    // (1) C rows t = 16 T + lr, n = 8 q + 32 m .. + 7; the readout operand:
+    // the state rows p as binary16
+    h8 cf[2][KM];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) xa[pt] = x_frag(xs, pt);
-    float w[8];
-    weights(i0, w);
-    h8 bt[NT];
+    for (int T = 0; T < 2; ++T)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl.b, nt);
-    // readout operand: the state rows p as binary16; then the decay
+      for (int m = 0; m < KM; ++m) cf[T][m] = *reinterpret_cast<const h8*>(&sl.c[bo(16 * T + lr, q + 4 * m)]);
     h8 ra[PT][KM];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
@@ -491,30 +490,41 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
         ra[pt][m] = h8{(_Float16)s0[0], (_Float16)s0[1], (_Float16)s0[2], (_Float16)s0[3],
                        (_Float16)s1[0], (_Float16)s1[1], (_Float16)s1[2], (_Float16)s1[3]};
       }
+    __builtin_amdgcn_sched_barrier(0);
+    // (2) the readout C.R while the state decays over the step; the update's
+    // operands (x, B^T, weights) read
+    f4 yr[PT][2];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        yr[pt][T] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KM; ++m) yr[pt][T] = mfma16(ra[pt][m], cf[T][m], yr[pt][T]);
+      }
     const float dec = ex2(Sj_end - Sj_start);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) R[nt][pt] *= dec;
+    h8 xa[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) xa[pt] = x_frag(xs, pt);
+    float w[8];
+    weights(i0, w);
+    h8 bt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bt[nt] = bt_frag(sl.b, nt);
     __builtin_amdgcn_sched_barrier(0);
-    // (2) C rows t = 16 T + lr, n = 8 q + 32 m .. + 7, read between the
-    // update's products
+    // (3) the state update R += sum_s w_s B_s x_s; the C.B^T blocks and per
+    // output column t = 16 T + lr its log2-decay, readout scale and x rows
+    // (p = 16 pt + 4 q .. + 3); the decay mask formed under the products
     h8 xw[PT];
     weigh_x(xa, w, xw);
-    h8 cf[2][KM];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) R[nt][pt] = mfma16(bt[nt], xw[pt], R[nt][pt]);
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int m = 0; m < KM; ++m) cf[T][m] = *reinterpret_cast<const h8*>(&sl.c[bo(16 * T + lr, q + 4 * m)]);
-#pragma unroll
-    for (int i = 0; i < 2 * KM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
     if constexpr (BLO) {
       // the remainder of B's binary16 rounding
       h8 bl[NT];
@@ -525,9 +535,6 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) R[nt][pt] = mfma16(bl[nt], xw[pt], R[nt][pt]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // (3) the C.B^T blocks; per output column t = 16 T + lr: its log2-decay,
-    // readout scale and x rows (p = 16 pt + 4 q .. + 3); the readout C.R
     f4 cb[3];
 #pragma unroll
     for (int b = 0; b < 3; ++b) cb[b] = cbs[cbuf][b][lane];
@@ -542,15 +549,6 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       for (int pt = 0; pt < PT; ++pt)
         xr[T][pt] = *reinterpret_cast<const h4*>(&xs[Wd::xo(tl, 2 * pt + (q >> 1)) + 4 * (q & 1)]);
     }
-    f4 yr[PT][2];
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        yr[pt][T] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < KM; ++m) yr[pt][T] = mfma16(ra[pt][m], cf[T][m], yr[pt][T]);
-      }
     // The mask entry of (s, t), s <= t, is dt_s 2^{S_t - S_s} C_t.B_s.  It
     // factors as w_s 2^{S_t - S_end} with the update weight w_s = dt_s
     // 2^{S_end - S_s} <= dt_s and 2^{S_t - S_end} >= 1, both finite while the
