@@ -102,29 +102,30 @@ constexpr int kConvRB = 8;   // raw rows per batch; batch k+1 is loaded while ba
 template <typename IO> struct Raw8;
 template <> struct Raw8<_Float16> {
   h8 v;
-  __device__ __forceinline__ void load(const _Float16* p) { v = *reinterpret_cast<const h8*>(p); }
+  __device__ __forceinline__ void bload(rsrc_t r, unsigned off) {
+    v = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ __forceinline__ void bstore(rsrc_t r, unsigned off) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
+  }
   __device__ __forceinline__ void zero() { v = h8{}; }
   __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
   __device__ __forceinline__ void set(int e, float x) { v[e] = (_Float16)x; }
 };
 template <> struct Raw8<float> {
   f4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f4*>(p);
-    b = *reinterpret_cast<const f4*>(p + 4);
+  __device__ __forceinline__ void bload(rsrc_t r, unsigned off) {
+    a = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    b = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+  }
+  __device__ __forceinline__ void bstore(rsrc_t r, unsigned off) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, a), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, b), r, off + 16, 0, 0);
   }
   __device__ __forceinline__ void zero() { a = f4{}; b = f4{}; }
   __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
   __device__ __forceinline__ void set(int e, float x) { if (e < 4) a[e] = x; else b[e - 4] = x; }
 };
-template <typename IO> __device__ __forceinline__ void store_raw8(IO* p, const Raw8<IO>& r);
-template <> __device__ __forceinline__ void store_raw8(_Float16* p, const Raw8<_Float16>& r) {
-  *reinterpret_cast<h8*>(p) = r.v;
-}
-template <> __device__ __forceinline__ void store_raw8(float* p, const Raw8<float>& r) {
-  *reinterpret_cast<f4*>(p) = r.a;
-  *reinterpret_cast<f4*>(p + 4) = r.b;
-}
 
 template <typename IO>
 __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ xBC, const float* __restrict__ w,
@@ -133,26 +134,25 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
                                                         const int* __restrict__ cu, IO* __restrict__ out, int B,
                                                         int L, int T, int Cd, long long ld,
                                                         _Float16* __restrict__ blo, int bbeg, int gn) {
-  const int nch = Cd / 8, ntt = (L + kConvTT - 1) / kConvTT;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)B * ntt * nch) return;
-  const int cc = (int)(idx % nch);
-  const long long rest = idx / nch;
-  const int tt = (int)(rest % ntt), b = (int)(rest / ntt);
+  // a workgroup per (sequence, 32-token tile) and 256 groups of 8 channels:
+  // the tile's rows are wave-uniform
+  const int ntt = (L + kConvTT - 1) / kConvTT;
+  const int tt = (int)(blockIdx.x % (unsigned)ntt), b = (int)(blockIdx.x / (unsigned)ntt);
+  const int cc = (int)blockIdx.y * 256 + (int)threadIdx.x;
+  if (cc >= Cd / 8) return;
   const int c0 = cc * 8, t0 = tt * kConvTT;
   const SeqRows span = seq_rows(seqlens, cu, b, L, T);
   const int len = span.len;
-  // an empty sequence reads (and discards) row 0: its own first row may be
-  // the end of a packed tensor
-  const IO* src = xBC + (size_t)(len > 0 ? span.base : 0) * (size_t)ld + c0;
-  // Row t >= 0 of these channels, zero at or past the length.  The address is
-  // clamped into the sequence and the zero applied by a select, so the loads
-  // carry no branch and a whole batch is in flight at once.
-  const int tmax = len > 0 ? len - 1 : 0;
-  auto row = [&](int t, Raw8<IO>& v) {
-    v.load(src + (size_t)min(t, tmax) * (size_t)ld);
-    if (t >= len) v.zero();
-  };
+  constexpr unsigned ES = sizeof(IO);
+  const unsigned voff = (unsigned)c0 * ES;      // this lane's channels within a row
+  const unsigned rowb = (unsigned)Cd * ES;
+  const IO* const seq0 = xBC + (size_t)span.base * (size_t)ld;
+  // Row t >= 0 of these channels, through a buffer view of that row alone
+  // (address and range in scalar registers): the view is empty at or past
+  // the length, so those loads return zero without touching memory, and the
+  // loads carry no branch, select or per-lane address arithmetic.  A whole
+  // batch of rows is in flight at once.
+  auto row = [&](int t, Raw8<IO>& v) { v.bload(mkr(seq0 + (size_t)t * (size_t)ld, t < len ? rowb : 0u), voff); };
   Raw8<IO> h[3], cur[kConvRB], nxt[kConvRB];              // h: the 3 raw rows before the batch
   if (tt > 0) {
 #pragma unroll
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
     }
   };
   if (len == 0 && tt == 0) put_state(h[0], h[1], h[2]);
-  IO* dst = out + (size_t)b * L * Cd + c0;
+  IO* const dst = out + (size_t)b * L * Cd;
   const bool lo_here = blo != nullptr && c0 >= bbeg && c0 < bbeg + gn;
 #pragma unroll
   for (int kb = 0; kb < kConvTT / kConvRB; ++kb) {
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
         uo[e] = u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
         o.set(e, uo[e]);
       }
-      store_raw8(dst + (size_t)t * Cd, o);
+      o.bstore(mkr(dst + (size_t)t * Cd, rowb), voff);
       if constexpr (sizeof(IO) == 2) {
         // B's channels also leave what their binary16 copy drops, for the
         // scan's state contraction
@@ -225,7 +225,8 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(const IO* __restrict__ x
           h8 lo;
 #pragma unroll
           for (int e = 0; e < 8; ++e) lo[e] = (_Float16)(uo[e] - (float)o.v[e]);
-          *reinterpret_cast<h8*>(blo + ((size_t)b * L + t) * gn + (c0 - bbeg)) = lo;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, lo), mkr(blo + ((size_t)b * L + t) * gn, (unsigned)gn * 2u),
+                                                 (unsigned)(c0 - bbeg) * 2u, 0, 0);
         }
       }
       if (t == len - 1) put_state(r1, r2, cur[k]);
@@ -1244,8 +1245,8 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     const int cd = d.nheads * kP + 2 * d.ngroups * d.dstate;
     IO* xc = (IO*)(base + wl.convx);
     _Float16* blo = sizeof(IO) == 2 ? (_Float16*)(base + wl.blo) : nullptr;
-    const long long threads = (long long)d.batch * ((d.seqlen + kConvTT - 1) / kConvTT) * (cd / 8);
-    conv_silu_kernel<IO><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(
+    const dim3 cgrid((unsigned)(d.batch * ((d.seqlen + kConvTT - 1) / kConvTT)), (unsigned)((cd / 8 + 255) / 256));
+    conv_silu_kernel<IO><<<cgrid, 256, 0, st>>>(
         (const IO*)io_.xBC, io_.conv_w, io_.conv_b, (const IO*)io_.conv_state_in, (IO*)io_.conv_state_out,
         io_.seqlens, io_.cu_seqlens, xc, d.batch, d.seqlen, d.packed_tokens, cd,
         io_.xBC_ld > 0 ? io_.xBC_ld : (long long)cd, blo, d.nheads * kP, d.ngroups * d.dstate);
