@@ -646,7 +646,9 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // wait longer.  The output pass starts with the blocks of step 0, computed
   // by waves 0-2 between two barriers; during step k, waves (k + 1 + w) mod 8
   // = 0, 1, 2 compute block 0, 1, 2 of step k + 1.
-  auto pass = [&](bool with_c, int stores_per_step, auto&& body) __attribute__((always_inline)) {
+  // The start of a pass, which needs only its prologue's loads: the first
+  // chunk's dt scan and (output pass) the C.B^T blocks of step 0.
+  auto pass_head = [&](bool with_c) __attribute__((always_inline)) {
     const int D = loads_per_step(with_c);
     if (nsteps > 0) vm_wait(nsteps > 1 && !with_c ? D : 0);   // the dt and step 0's loads (output pass: step 1's too)
     slot_barrier();
@@ -655,6 +657,9 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       if (wid < 3) cb_block(r0, wid, 0);
       slot_barrier();
     }
+  };
+  auto pass_steps = [&](bool with_c, int stores_per_step, auto&& body) __attribute__((always_inline)) {
+    const int D = loads_per_step(with_c);
     auto one = [&](int k, const Slot& sl, Slot& nx, const Slot& nn) __attribute__((always_inline)) {
       const int kc = k % J, cc = c0 + k / J;
       if (kc == 0 && cc + 1 < c0 + ncv) issue_dt(cc + 1);
@@ -673,6 +678,10 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       if (k + 2 >= nsteps) break;
       one(k + 2, r2, r1, r0);
     }
+  };
+  auto pass = [&](bool with_c, int stores_per_step, auto&& body) __attribute__((always_inline)) {
+    pass_head(with_c);
+    pass_steps(with_c, stores_per_step, body);
   };
   // the first loads of a pass
   auto prologue = [&](bool with_c) {
@@ -808,6 +817,11 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
     vm_wait((ncv > 0 ? DTI : 0) + (nsteps > 0 ? DP : 0) + (nsteps > 1 ? DP : 0));
     publish_flag();
   }
+  // The output pass's start (its first chunk's dt scan and step 0's C.B^T
+  // blocks) needs no carry-in: unless this segment publishes after its first
+  // folds, it runs now, while the aggregates it waits for are published.
+  const bool late_publish = !pair && !last && !early;
+  if (!late_publish) pass_head(true);
 
   if (live) {
     // wait until aggregates k0 .. k1-1 are published (one flag per lane, all
@@ -913,7 +927,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
 
   // ---- phase 3: outputs; R runs from the carry-in through the segment ---------------
   const bool want_state = last && a.state_out != nullptr;
-  pass(true, live ? 2 * PT : 0, [&](int k, const Slot& sl, const Slot& nsl) __attribute__((always_inline)) {
+  if (late_publish) pass_head(true);
+  pass_steps(true, live ? 2 * PT : 0, [&](int k, const Slot& sl, const Slot& nsl) __attribute__((always_inline)) {
     if (live) step(sl, (k % J) * TS, tok_of(k), k & 1);
     const int blk = (wid + k + 1) & 7;
     if (k + 1 < nsteps && blk < 3) cb_block(nsl, blk, (k + 1) & 1);
