@@ -96,6 +96,20 @@ def test_segments_of_consecutive_chunks(segments):
     check_window(f"segments={segments}", inp, 128, seqlens=[1100, 700, 100], state_in=h0, segments=segments)
 
 
+def test_streamed_scan_more_workgroups_than_compute_units():
+    # The binary16 N = 128 scan with 8 sequences of 5 chunks as 5 segments
+    # each: 320 workgroups, more than the compute units, so the hand-off takes
+    # the radix-4 tree and a segment may wait on one that is not resident at
+    # the same time (it waits only on segments claimed before it).  Lengths
+    # end inside every segment, at one token and at zero.
+    inp = rand_window(71, 8, 640, 32, 128, 8)
+    lens = [640, 600, 1, 129, 384, 640, 257, 0]
+    h0 = np.random.default_rng(72).standard_normal((8, 32, 64, 128)).astype(np.float32) * 0.3
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 8 * 8 * 5 > cus
+    check_window("more workgroups than compute units", inp, 128, seqlens=lens, state_in=h0, segments=5)
+
+
 def test_ragged_batch_with_initial_state():
     inp = rand_window(21, 3, 700, 16, 128, 2)
     h0 = np.random.default_rng(22).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
