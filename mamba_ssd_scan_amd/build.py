@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmamba2ssd.so")
-SOURCES = ["abi.hip", "decode.hip", "grad.hip", "mixer_decode.hip", "requant.hip", "ssd_scan.hip", "window.hip"]
+SOURCES = ["abi.hip", "colscan.hip", "decode.hip", "grad.hip", "mixer_decode.hip", "requant.hip", "ssd_scan.hip", "window.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 ops are kept out of the generated code

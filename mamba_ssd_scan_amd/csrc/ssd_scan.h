@@ -39,4 +39,10 @@ struct ScanArgs {
 // window workspace layout.  a.nseg = 0 lets the launch choose the segments.
 hipError_t launch_ssd_scan(const ScanArgs& a, int cus, hipStream_t st);
 
+// Launches the column scan (colscan.hip): one workgroup per (sequence, head,
+// half of the head dim) over the whole sequence, the state split over n
+// between its waves; no workspace.  Same argument contract as
+// launch_ssd_scan without the B remainder (a.Blo must be null).
+hipError_t launch_ssd_colscan(const ScanArgs& a, hipStream_t st);
+
 }  // namespace m2

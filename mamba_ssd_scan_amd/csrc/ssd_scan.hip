@@ -105,63 +105,6 @@ __device__ __forceinline__ int bo(int r, int k) { return r * N + 8 * (k ^ bsw(r)
 // k-step m reads n = 8 j + 32 m .. + 7, tiles 2m and 2m+1 hold its two halves
 __device__ __forceinline__ int ncol(int nt, int j) { return 8 * j + 32 * (nt >> 1) + 4 * (nt & 1); }
 
-// Buffer descriptor words in scalar registers (wave-uniform p and bytes) for
-// the loads below; loads past `bytes` return zero.
-__device__ __forceinline__ u4 rsrc_words(const void* p, unsigned bytes) {
-  const unsigned long long v = (unsigned long long)p;
-  return u4{(unsigned)__builtin_amdgcn_readfirstlane((unsigned)v),
-            (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32)),
-            (unsigned)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
-}
-
-// LDS byte address of a workgroup-shared location
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)__builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p);
-}
-
-// 16 bytes per lane from the buffer at byte offset voff straight into LDS:
-// lane l's bytes land at lds + 16 l.  Written as an asm statement so that the
-// compiler does not track these loads: it would otherwise make some LDS reads
-// wait for every LDS-writing load in flight, draining the prefetch.  The
-// waits for them are explicit (vm_wait, before the barrier that publishes a
-// slot); the load has no register result, so nothing is written to a
-// register while it is in flight.
-__device__ __forceinline__ void dma16(u4 r, unsigned lds, unsigned voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-
-// 4 bytes per lane into LDS (lane l's bytes land at lds + 4 l); as dma16.
-__device__ __forceinline__ void dma4(u4 r, unsigned lds, unsigned voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-
-// Wait until at most n of this wave's vector memory operations are
-// outstanding (they complete in issue order); n outside 0..15 waits for all.
-__device__ __forceinline__ void vm_wait(int n) {
-#define M2_VMW(k) \
-  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
-  switch (n) {
-    M2_VMW(1) M2_VMW(2) M2_VMW(3) M2_VMW(4) M2_VMW(5) M2_VMW(6) M2_VMW(7) M2_VMW(8) M2_VMW(9) M2_VMW(10)
-    M2_VMW(11) M2_VMW(12) M2_VMW(13) M2_VMW(14) M2_VMW(15)
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-#undef M2_VMW
-}
-
-// Workgroup barrier for the slots.  No fence: a workgroup release fence would
-// make the compiler wait for every LDS-writing buffer load in flight.  The
-// empty asm statements keep the compiler from moving LDS accesses across it;
-// the caller has already waited for what must be visible.
-__device__ __forceinline__ void slot_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads and writes are done
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 }  // namespace ps
 
 template <int PH, bool BLO>

@@ -1280,7 +1280,16 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     sa.xpk = a.xpk; sa.y = a.y; sa.ctrl = a.ctrl; sa.flags = a.flags; sa.agg = a.agg;
     sa.nseg = a.nseg; sa.cps = 0; sa.tree_lg = 3; sa.dt_sp = a.dt_sp; sa.dt_bias = a.dt_bias;
     sa.Blo = a.Blo; sa.gn = a.gn;
-    e = launch_ssd_scan(sa, device_cus(), st);
+    // One round of column-scan workgroups (2 x heads x sequences at most
+    // one per compute unit) over short windows: the segmented scan would run
+    // too few workgroups there (one chunk), or a hand-off between short
+    // segments.  Measured on the 8B layer shape at batch 1: 16 us against
+    // 27 us at L = 256, 27 against 35 us at L = 512, and 49 against 44 us at
+    // L = 1024, where the segmented scan's larger steps win.  Callers that
+    // ask for a segment count get the segmented scan.
+    const int cus = device_cus();
+    if (a.Blo == nullptr && d.segments == 0 && 2LL * a.B * a.H <= cus && a.L <= 512) e = launch_ssd_colscan(sa, st);
+    else e = launch_ssd_scan(sa, cus, st);
   } else {
     const bool blo = a.Blo != nullptr;   // only binary16 conv output carries a remainder
     switch (d.dstate) {

@@ -174,6 +174,64 @@ def test_split_window_carry_matches_unsplit():
         assert ey <= Y_TOL and es <= S_TOL
 
 
+# ---------------------------------------------------------------------------
+# Short windows of one round of (sequence, head, half) workgroups run the
+# column scan (the state split over n between a workgroup's waves, one
+# workgroup per sequence and half head); these cases take that path.
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_short_window_full_heads_column_scan(chunk):
+    # one 8B-shape window of 512 tokens, every head, with an initial state;
+    # and a ragged length with canaries past it
+    inp = rand_window(91 + chunk, 1, 512, 128, 128, 8)
+    h0 = np.random.default_rng(92).standard_normal((1, 128, 64, 128)).astype(np.float32) * 0.3
+    check_window(f"column scan L=512 chunk {chunk}", inp, chunk, state_in=h0)
+    check_window(f"column scan L=437 of 512 chunk {chunk}", inp, chunk, seqlens=[437], state_in=h0)
+
+
+def test_short_windows_column_scan_ragged_zero_and_one_token():
+    inp = rand_window(93, 3, 300, 16, 128, 2)
+    h0 = np.random.default_rng(94).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
+    check_window("column scan ragged", inp, 64, seqlens=[300, 1, 0], state_in=h0)
+    y, hT = run_window(inp, 64, seqlens=[300, 1, 0], state_in=h0, y_fill=3.0)
+    assert np.array_equal(hT[2], h0[2]) and np.all(y[2] == np.float16(3.0))
+
+
+def test_short_window_column_scan_raw_dt_and_packed():
+    s = synth.WindowShape(2, 500, 16, 64, 128, 2, 256, np.float16, "wide")
+    inp = synth.window_inputs(s, 95, raw_dt=True)
+    h0 = np.random.default_rng(96).standard_normal((2, 16, 64, 128)).astype(np.float32) * 0.3
+    check_window("column scan raw dt", inp, 128, seqlens=[500, 263], state_in=h0)
+    lens = [500, 263]
+    yp, hT = run_window_packed(inp, lens, 128, state_in=h0)
+    T = sum(lens)
+    assert np.all(yp[T:] == np.float16(12345.0))       # nothing past the packed rows
+    y = unpack_rows(yp[:T], lens, 500).reshape(len(lens), 500, 16, 64)
+    yr, hr = oracle_window(inp, lens, h0)
+    ey = max(slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)), np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2)
+             for b, n in enumerate(lens))
+    es = slice_err(hT, hr, 2)
+    say(f"[column scan packed] y {ey:.3e} state {es:.3e}")
+    assert ey <= Y_TOL and es <= S_TOL
+
+
+def test_short_window_column_scan_strong_decay():
+    # steps decaying by more than 2^-100 take the entry-by-entry mask factors
+    inp = rand_window(97, 1, 480, 8, 128, 2)
+    A = inp["A"].copy()
+    A[:4] = -16.0
+    inp["A"] = A
+    dt = inp["dt"].astype(np.float32)
+    rng = np.random.default_rng(98)
+    dt[..., 0:2] = 0.5 + 0.05 * rng.standard_normal(dt[..., 0:2].shape)
+    dt[..., 2:4] = 0.135 * np.exp(0.3 * rng.standard_normal(dt[..., 2:4].shape))
+    inp["dt"] = dt.astype(inp["dt"].dtype)
+    lg = -16.0 * math.log2(math.e) * inp["dt"].astype(np.float64)[0, :, 2:4]
+    steps = np.add.reduceat(lg, np.arange(0, 480, 32), axis=0)
+    assert (steps < -100).any() and (steps > -100).any()
+    h0 = np.random.default_rng(99).standard_normal((1, 8, 64, 128)).astype(np.float32)
+    check_window("column scan strong decay", inp, 256, seqlens=[480], state_in=h0)
+
+
 def test_layer_window_full_size():
     s = synth.layer_window()
     check_window("layer L=2048", synth.window_inputs(s, 1001), s.chunk)
