@@ -46,6 +46,8 @@
 // 8-byte reads of B (rows 4q + lane/4) their minimum, two lanes per bank
 // (32 lanes of 8 bytes against 16 distinct units).  The transposed reads of
 // the x tile are free of conflicts.
+#include <stddef.h>
+
 #include "common.h"
 #include "gfx950_ops.h"
 #include "ssd_scan.h"
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   using Wd = W<PH>;
   using Slot = typename Wd::template Slot<BLO>;
   constexpr int NWV = Wd::NWV, NTH = Wd::NTH, PT = Wd::PT, WPH = Wd::WPH;
-  __shared__ Slot r0, r1, r2;
+  __shared__ Slot rs[3];
   // per head of the block (the two waves of a head write the same values):
   __shared__ float Sx[KH][256];     // running log2-decay from the chunk start (inclusive)
   __shared__ float Dx[KH][256];     // the chunk's dt
@@ -160,14 +162,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // (unused) values must be finite
   {
     constexpr int SLOT16 = (int)(sizeof(Slot) / 16);
-    u4* z0 = reinterpret_cast<u4*>(&r0);
-    u4* z1 = reinterpret_cast<u4*>(&r1);
-    u4* z2 = reinterpret_cast<u4*>(&r2);
-    for (int i = tid; i < SLOT16; i += NTH) {
-      z0[i] = u4{0u, 0u, 0u, 0u};
-      z1[i] = u4{0u, 0u, 0u, 0u};
-      z2[i] = u4{0u, 0u, 0u, 0u};
-    }
+    u4* z = reinterpret_cast<u4*>(&rs[0]);
+    for (int i = tid; i < 3 * SLOT16; i += NTH) z[i] = u4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
   const unsigned ticket = __builtin_amdgcn_readfirstlane(sh_ticket);
@@ -207,7 +203,6 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   const unsigned gspan = len > 0 ? (unsigned)(len - 1) * grow + N * ES : 0u;
   const u4 rx = rsrc_words(a.x + xbase * a.xstride + (size_t)h * P + PH * half, xspan);
   const u4 rb = rsrc_words(a.Bm + xbase * a.gstride + (size_t)g * N, gspan);
-  const rsrc_t rc = mkr(a.Cm + xbase * a.gstride + (size_t)g * N, gspan);
   const u4 rc4 = rsrc_words(a.Cm + xbase * a.gstride + (size_t)g * N, gspan);
   const unsigned lrow = (unsigned)a.gn * ES;   // remainder rows of B (fused conv)
   const u4 rbl = BLO ? rsrc_words(a.Blo + xbase * a.gn + (size_t)g * N, len > 0 ? (unsigned)(len - 1) * lrow + N * ES : 0u)
@@ -233,22 +228,30 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // (DX + DBC per operand loads per wave and step; the explicit waits count them)
   constexpr int DX = Wd::XI, DBC = Wd::BI;
   auto loads_per_step = [&](bool with_c) { return DX + DBC * ((with_c ? 2 : 1) + (BLO ? 1 : 0)); };
-  auto issue = [&](Slot& sl, int tok0, bool with_c) {
+  // (a slot's LDS byte address from the slots' base: the slot index of a
+  // step is a runtime value)
+  const unsigned lds_rs = lds_addr(&rs[0]);
+  const unsigned lds_dtr = lds_addr(&dtr[0][0]);
+  constexpr unsigned kSlotB = (unsigned)sizeof(Slot);
+  constexpr unsigned kOx = (unsigned)offsetof(Slot, x), kOb = (unsigned)offsetof(Slot, b),
+                     kOc = (unsigned)offsetof(Slot, c), kObl = (unsigned)offsetof(Slot, bl);
+  auto issue = [&](int si, int tok0, bool with_c) {
     const unsigned t0 = (unsigned)tok0;
+    const unsigned base = lds_rs + (unsigned)si * kSlotB;
     constexpr int XU = Wd::XU;
 #pragma unroll
     for (int i = 0; i < DX; ++i) {
       const int row = (64 / XU) * i + lane / XU, pk = lane % XU;
-      dma16(rx, lds_addr(&sl.x[wid][512 * i]), (t0 + row) * xrow + 16u * (unsigned)(pk ^ Wd::xsw(row)));
+      dma16(rx, base + kOx + (unsigned)(2 * (TS * PH * wid + 512 * i)), (t0 + row) * xrow + 16u * (unsigned)(pk ^ Wd::xsw(row)));
     }
 #pragma unroll
     for (int i = 0; i < DBC; ++i) {
       const int blk = wid * DBC + i;
       const int row = 4 * blk + (lane >> 4), pk = lane & 15;
       const unsigned go = (t0 + row) * grow + 16u * (unsigned)(pk ^ bsw(row));
-      dma16(rb, lds_addr(&sl.b[512 * blk]), go);
-      if (with_c) dma16(rc4, lds_addr(&sl.c[512 * blk]), go);
-      if constexpr (BLO) dma16(rbl, lds_addr(&sl.bl[512 * blk]), (t0 + row) * lrow + 16u * (unsigned)(pk ^ bsw(row)));
+      dma16(rb, base + kOb + 1024u * (unsigned)blk, go);
+      if (with_c) dma16(rc4, base + kOc + 1024u * (unsigned)blk, go);
+      if constexpr (BLO) dma16(rbl, base + kObl + 1024u * (unsigned)blk, (t0 + row) * lrow + 16u * (unsigned)(pk ^ bsw(row)));
     }
   };
 
@@ -268,7 +271,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
     for (int i = 0; i < DTI; ++i) {
       const int li = wid * DTI + i;
       const int t = 16 * li + (lane >> 2);   // tokens past the chunk load rows of the next one (unused)
-      dma4(rdt, lds_addr(&dtr[cc & 1][128 * li]), (dt_sh(cc * a.Q + t) & ~1u) * ES + 4u * (unsigned)(lane & 3));
+      dma4(rdt, lds_dtr + (unsigned)(cc & 1) * (unsigned)sizeof(dtr[0]) + 256u * (unsigned)li,
+           (dt_sh(cc * a.Q + t) & ~1u) * ES + 4u * (unsigned)(lane & 3));
     }
   };
   // dt and the running log2-decay of chunk cc (its dt in LDS); a raw dt goes
@@ -566,7 +570,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // ---- streaming over a segment's steps, three slots in rotation -----------------
   // Steps are numbered over the segment (chunk c0 + k / J, step k % J).
   const int J = a.Q / TS;                       // steps per full chunk
-  auto tok_of = [&](int k) { return (c0 + k / J) * a.Q + (k % J) * TS; };
+  const int lgJ = __builtin_ctz((unsigned)J);   // J = 2, 4 or 8
+  auto tok_of = [&](int k) { return (c0 + (k >> lgJ)) * a.Q + (k & (J - 1)) * TS; };
   int nsteps = 0;                               // steps with tokens
   if (ncv > 0) nsteps = (ncv - 1) * J + steps_of(c0 + ncv - 1);
   // The pass over the segment: the loads of its first chunk's dt and of its
@@ -597,30 +602,25 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
     slot_barrier();
     if (ncv > 0) scan_dt(c0, with_c);
     if (with_c && nsteps > 0) {
-      if (wid < 3) cb_block(r0, wid, 0);
+      if (wid < 3) cb_block(rs[0], wid, 0);
       slot_barrier();
     }
   };
   auto pass_steps = [&](bool with_c, int stores_per_step, auto&& body) __attribute__((always_inline)) {
     const int D = loads_per_step(with_c);
-    auto one = [&](int k, const Slot& sl, Slot& nx, const Slot& nn) __attribute__((always_inline)) {
-      const int kc = k % J, cc = c0 + k / J;
+    auto one = [&](int k, int si) __attribute__((always_inline)) {
+      const int kc = k & (J - 1), cc = c0 + (k >> lgJ);
+      const int nn = si == 2 ? 0 : si + 1, nx = si == 0 ? 2 : si - 1;   // slots of steps k + 1, k + 2
       if (kc == 0 && cc + 1 < c0 + ncv) issue_dt(cc + 1);
       const bool more = k + 2 < nsteps;
       if (more) issue(nx, tok_of(k + 2), with_c);
-      body(k, sl, nn);
+      body(k, rs[si], rs[nn]);
       if (k + 1 < nsteps)
         vm_wait(with_c ? stores_per_step : (k > 0 ? stores_per_step : 0) + (more ? D : 0) + stores_per_step);
       slot_barrier();
-      if (k + 1 < nsteps && (k + 1) % J == 0) scan_dt(cc + 1, with_c);
+      if (k + 1 < nsteps && kc == J - 1) scan_dt(cc + 1, with_c);
     };
-    for (int k = 0; k < nsteps; k += 3) {
-      one(k, r0, r2, r1);
-      if (k + 1 >= nsteps) break;
-      one(k + 1, r1, r0, r2);
-      if (k + 2 >= nsteps) break;
-      one(k + 2, r2, r1, r0);
-    }
+    for (int k = 0, si = 0; k < nsteps; ++k, si = si == 2 ? 0 : si + 1) one(k, si);
   };
   auto pass = [&](bool with_c, int stores_per_step, auto&& body) __attribute__((always_inline)) {
     pass_head(with_c);
@@ -629,8 +629,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // the first loads of a pass
   auto prologue = [&](bool with_c) {
     if (ncv > 0) issue_dt(c0);
-    if (nsteps > 0) issue(r0, tok_of(0), with_c);
-    if (nsteps > 1) issue(r1, tok_of(1), with_c);
+    if (nsteps > 0) issue(0, tok_of(0), with_c);
+    if (nsteps > 1) issue(1, tok_of(1), with_c);
   };
 
   // ---- phase 1: the segment's local state (every segment but the last) ----------
@@ -657,8 +657,8 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   if (pair ? last : !last) {
     prologue(false);
     pass(false, 0, [&](int k, const Slot& sl, const Slot&) __attribute__((always_inline)) {
-      const int kc = k % J, i0 = kc * TS;
-      const int cc = c0 + k / J;
+      const int kc = k & (J - 1), i0 = kc * TS;
+      const int cc = c0 + (k >> lgJ);
       const float Send = Sw[min(a.Q, len - cc * a.Q) - 1];   // dt = 0 past the end: S constant there
       if (kc == 0) {
         const float dec = ex2(Send);
@@ -872,7 +872,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   const bool want_state = last && a.state_out != nullptr;
   if (late_publish) pass_head(true);
   pass_steps(true, live ? 2 * PT : 0, [&](int k, const Slot& sl, const Slot& nsl) __attribute__((always_inline)) {
-    if (live) step(sl, (k % J) * TS, tok_of(k), k & 1);
+    if (live) step(sl, (k & (J - 1)) * TS, tok_of(k), k & 1);
     const int blk = (wid + k + 1) & 7;
     if (k + 1 < nsteps && blk < 3) cb_block(nsl, blk, (k + 1) & 1);
   });
