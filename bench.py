@@ -377,6 +377,48 @@ def time_batched(torch, m2, dev, stream, L, H, P, N, G, Q, calls=20):
     return bat_us, blens
 
 
+def time_short(torch, m2, dev, stream, H, P, N, G, Q, L=512, calls=50):
+    """Microseconds per call of one short window at the layer shape (batch 1,
+    L = 512, final state), inputs drawn on the device with the layer window's
+    distributions and rotated over four sets (the short-window path)."""
+    # timing only (parity of this shape is covered by the GPU tests)
+    gen = torch.Generator(device=dev).manual_seed(1007)
+    ssets = []
+    for k in range(4):
+        dt0 = torch.exp(torch.rand(H, device=dev, generator=gen) * float(np.log(100.0)) + float(np.log(1e-3)))
+        ssets.append({
+            "x": torch.randn(1, L, H, P, device=dev, generator=gen).half(),
+            "dt": torch.nn.functional.softplus(torch.randn(1, L, H, device=dev, generator=gen)
+                                               + torch.log(torch.expm1(dt0))).half(),
+            "B": (torch.randn(1, L, G, N, device=dev, generator=gen) / N ** 0.5).half(),
+            "C": (torch.randn(1, L, G, N, device=dev, generator=gen) / N ** 0.5).half(),
+            "y": torch.empty(1, L, H * P, dtype=torch.float16, device=dev),
+            "hT": torch.empty(1, H, P, N, dtype=torch.float32, device=dev),
+        })
+    sA = -torch.exp(torch.rand(H, device=dev, generator=gen) * float(np.log(16.0)))
+    sD = torch.randn(H, device=dev, generator=gen)
+    sws = m2.alloc_workspace(m2.make_dims(1, L, H, P, N, G, Q), dev)
+
+    def sstep(k):
+        t = ssets[k % len(ssets)]
+        m2.conv_scan_window(t["dt"], sA, sD, t["y"], sws, x=t["x"], B=t["B"], C=t["C"], state_out=t["hT"],
+                            chunk=Q, stream=stream)
+
+    for k in range(5):
+        sstep(k)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for k in range(calls):
+        sstep(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / calls
+    del ssets, sws
+    torch.cuda.empty_cache()
+    return us, L
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,7 +430,7 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the layer window and print its fields (for kernel traces of that workload)")
-    ap.add_argument("--only", choices=["layer", "batched", "mixer"], default=None,
+    ap.add_argument("--only", choices=["layer", "batched", "mixer", "short"], default=None,
                     help="time one workload alone (--steps calls after the warmup) and print its fields, for "
                          "kernel traces and counters of that workload; layer is the same as --headline-only")
     args = ap.parse_args()
@@ -417,6 +459,12 @@ def main():
         bb = window_bytes(8, L, H, P, N, G, lens=blens)
         print(json.dumps({"workload": "batched windows", "us": round(bus, 2), "calls": args.steps,
                           "algorithmic_bytes": bb, "achieved_GBs": round(bb / (bus * 1e-6) / 1e9, 1)}), flush=True)
+        return
+    elif args.only == "short":
+        sus, SL_ = time_short(torch, m2, dev, stream, H, P, N, G, Q, calls=args.steps)
+        sb = window_bytes(1, SL_, H, P, N, G)
+        print(json.dumps({"workload": "short window", "us": round(sus, 2), "calls": args.steps,
+                          "algorithmic_bytes": sb, "achieved_GBs": round(sb / (sus * 1e-6) / 1e9, 1)}), flush=True)
         return
     elif args.only == "mixer":
         mus, MB_, ML_, MH_, MN_, MG_ = time_mixer(torch, m2, synth, dev, stream, P, Q, calls=args.steps)
@@ -639,6 +687,8 @@ def main():
 
     bat_us, blens = time_batched(torch, m2, dev, stream, L, H, P, N, G, Q)
     bbytes = window_bytes(8, L, H, P, N, G, lens=blens)
+    sh_us, SL_ = time_short(torch, m2, dev, stream, H, P, N, G, Q)
+    shbytes = window_bytes(1, SL_, H, P, N, G)
 
     # ---- CPU baseline: the oracle on bounded samples of each workload ----------
     cpu = cpu_baselines(inp, s, args) if not args.no_cpu_baseline else None
@@ -682,6 +732,10 @@ def main():
                     "tokens_per_s": round(sum(blens) / (bat_us * 1e-6), 1), "algorithmic_bytes": bbytes,
                     "achieved_GBs": round(bbytes / (bat_us * 1e-6) / 1e9, 1),
                     "frac": round(bbytes / (bat_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "short_window": {"workload": "one window of 512 tokens at the layer shape, final state (column scan)",
+                         "us": round(sh_us, 2), "tokens_per_s": round(SL_ / (sh_us * 1e-6), 1),
+                         "algorithmic_bytes": shbytes, "achieved_GBs": round(shbytes / (sh_us * 1e-6) / 1e9, 1),
+                         "frac": round(shbytes / (sh_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "requant_window": {"workload": "layer window, state requantized to binary16 after every token",
                            "us": round(rq_us, 2), "tokens_per_s": round(B * L / (rq_us * 1e-6), 1),
                            "state_updates_per_s": round(rq_updates / (rq_us * 1e-6), 1),
