@@ -78,6 +78,11 @@ typedef struct mamba2_dims {
                             that with two runs (binary16 I/O, dstate 128) the
                             second computes the first's state itself and the
                             first takes the larger share of the chunks.
+                            With 0, binary16 windows at dstate 128 of at
+                            most 512 tokens whose 2 x heads x batch fits one
+                            workgroup per compute unit run unsplit, each
+                            workgroup a whole sequence for half a head with
+                            the state split over dstate between its waves.
                             Results agree up to rounding for every k.       */
     int32_t dt_softplus; /* 0: dt is given positive and used as is;
                             1: dt is the raw pre-activation, dt_eff =
