@@ -188,6 +188,16 @@ def test_short_window_full_heads_column_scan(chunk):
     check_window(f"column scan L=437 of 512 chunk {chunk}", inp, chunk, seqlens=[437], state_in=h0)
 
 
+def test_column_scan_routing_boundary():
+    # 512 tokens run the column scan, 513 the segmented scan (two runs of
+    # 256-token chunks); both against the oracle at the full head count
+    inp = rand_window(100, 1, 513, 128, 128, 8)
+    h0 = np.random.default_rng(101).standard_normal((1, 128, 64, 128)).astype(np.float32) * 0.3
+    short = {k: (v[:, :512] if v.ndim > 1 else v) for k, v in inp.items()}
+    check_window("L=512 (column scan)", short, 256, state_in=h0)
+    check_window("L=513 (segmented scan)", inp, 256, state_in=h0)
+
+
 def test_short_windows_column_scan_ragged_zero_and_one_token():
     inp = rand_window(93, 3, 300, 16, 128, 2)
     h0 = np.random.default_rng(94).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
