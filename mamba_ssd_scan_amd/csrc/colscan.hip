@@ -272,15 +272,17 @@ __global__ __launch_bounds__(cs::NTH) void ssd_colscan_kernel(ScanArgs a) {
                                           (unsigned)(tok0 + fin_t) * yrow + (unsigned)(4 * fin_p), 0, 0);
   };
 
-  // ---- the step, software-pipelined over two steps --------------------------------
-  // Step k's front half (after the barrier that publishes its rows): its LDS
-  // reads, the readout of the state entering it and its quarter's C.B^T
+  // ---- the step in two halves -------------------------------------------------------
+  // The front half (after the barrier that publishes the step's rows): its
+  // LDS reads, the readout of the state entering it and its quarter's C.B^T
   // blocks (MFMA), the mask factors of its diagonal product, and the state
-  // update.  Its back half runs in step k + 1, under step k + 1's reads and
-  // products: the masked C.B^T as binary16, the diagonal product (MFMA) on
-  // top of the scaled readout, and this wave's shares of y written to LDS
-  // (t = 16 T + lr, p = 16 pq + 4 q + e), summed by finish in step k + 2.
-  // Carried from the front half to the back half:
+  // update.  The back half: the masked C.B^T as binary16, the diagonal
+  // product (MFMA) on top of the scaled readout, and this wave's shares of
+  // y written to LDS (t = 16 T + lr, p = 16 pq + 4 q + e), summed by finish
+  // in the next step.  (Running the back half under the next step's reads
+  // and products measured about 5 % slower: the values carried across the
+  // barrier cost register moves every step.)
+  // Passed from the front half to the back half:
   h8 c_xa;            // x^T of the step (the diagonal's A operand)
   f4 c_gb[3];         // C.B^T blocks (s-tile, t-tile) = (0,0), (0,1), (1,1)
   f4 c_yr[2];         // readout C.H of t-tiles 0, 1
@@ -413,12 +415,12 @@ __global__ __launch_bounds__(cs::NTH) void ssd_colscan_kernel(ScanArgs a) {
 
   // ---- streaming over the steps, DEPTH + 1 slots in rotation ---------------------
   // Per step k: the loads of step k + DEPTH (and at a chunk's first step the
-  // next chunk's dt), step k - 2's outputs summed and stored, step k's front
-  // half with step k - 1's back half under it, then the barrier that
-  // publishes step k + 1's rows and step k - 1's shares.  Explicit waits:
-  // vector memory operations complete in issue order, so before that
-  // barrier a wave waits until no more are outstanding than it issued after
-  // step k + 1's loads (per step: its dt loads, its loads, its store).
+  // next chunk's dt), step k - 1's outputs summed and stored, step k, then
+  // the barrier that publishes step k + 1's rows and step k's shares.
+  // Explicit waits: vector memory operations complete in issue order, so
+  // before that barrier a wave waits until no more are outstanding than it
+  // issued after step k + 1's loads (per step: its dt loads, its loads, its
+  // store).
   static_assert(DEPTH == 2, "the wait count below is written for loads two steps ahead");
   if (nch > 0) issue_dt(0);
   if (nsteps > 0) issue(0, 0);
@@ -434,13 +436,13 @@ __global__ __launch_bounds__(cs::NTH) void ssd_colscan_kernel(ScanArgs a) {
     if (ndt) issue_dt(c + 1);
     const bool more = k + 2 < nsteps;
     if (more) issue(si == 0 ? 2 : si - 1, (k + 2) * TS);
-    if (k >= 2) finish(k & 1, (k - 2) * TS);
+    if (k >= 1) finish((k - 1) & 1, (k - 1) * TS);
     auto rest = front(slots[si], kc * TS);
-    if (k >= 1) back((k - 1) & 1);
     rest(H);
+    back(k & 1);
     // issued after step k + 1's loads (in step k - 1): that step's store,
     // then this step's dt loads, loads and store
-    if (k + 1 < nsteps) vm_wait((k >= 3 ? 1 : 0) + (ndt ? DT : 0) + (more ? DL : 0) + (k >= 2 ? 1 : 0));
+    if (k + 1 < nsteps) vm_wait((k >= 2 ? 1 : 0) + (ndt ? DT : 0) + (more ? DL : 0) + (k >= 1 ? 1 : 0));
     slot_barrier();
     si = si == 2 ? 0 : si + 1;
     if (++kc == J) {
@@ -449,13 +451,8 @@ __global__ __launch_bounds__(cs::NTH) void ssd_colscan_kernel(ScanArgs a) {
       if (k + 1 < nsteps) scan_dt(c);
     }
   }
-  // the last two steps' outputs
-  if (nsteps > 1) finish(nsteps & 1, (nsteps - 2) * TS);
-  if (nsteps > 0) {
-    back((nsteps - 1) & 1);
-    slot_barrier();
-    finish((nsteps - 1) & 1, (nsteps - 1) * TS);
-  }
+  // the last step's outputs
+  if (nsteps > 0) finish((nsteps - 1) & 1, (nsteps - 1) * TS);
 
   if (a.state_out) {
 #pragma unroll
