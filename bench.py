@@ -542,6 +542,24 @@ def main():
         torch.cuda.synchronize()
         rep_us.append(ev0.elapsed_time(ev1) / 50 * 1e3)
 
+    # the same calls without a final state (scoring windows discard it; the
+    # segment hand-off then carries binary16 aggregates)
+    def step_ns(k):
+        t = sets[k % len(sets)]
+        m2.conv_scan_window(t["dt"], t["A"], t["D"], t["y"], ws, x=t["x"], B=t["B"], C=t["C"], chunk=Q, stream=stream)
+
+    for k in range(10):
+        step_ns(k)
+    ns_us = []
+    for r in range(3):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for k in range(50):
+            step_ns(k)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ns_us.append(ev0.elapsed_time(ev1) / 50 * 1e3)
+
     # single-call latency (one launch, synchronized)
     lat = []
     for k in range(20):
@@ -720,6 +738,8 @@ def main():
         "window_latency_us": round(lat_us, 2),
         "window_repeats_us": {"median": round(float(np.median(rep_us)), 2), "min": round(float(np.min(rep_us)), 2),
                               "sd": round(float(np.std(rep_us)), 2), "repeats": len(rep_us), "calls_each": 50},
+        "window_no_final_state_us": {"median": round(float(np.median(ns_us)), 2), "min": round(float(np.min(ns_us)), 2),
+                                     "calls_each": 50, "algorithmic_bytes": wbytes - B * H * P * N * 4},
         "window_algorithmic_bytes": wbytes,
         "window_mfma_tflops": round(mflops / (ms * 1e-3) / 1e12, 1),
         "window_mfma_frac": round(mflops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK, 4),

@@ -47,6 +47,7 @@
 // (32 lanes of 8 bytes against 16 distinct units).  The transposed reads of
 // the x tile are free of conflicts.
 #include <stddef.h>
+#include <type_traits>
 
 #include "common.h"
 #include "gfx950_ops.h"
@@ -109,7 +110,7 @@ __device__ __forceinline__ int ncol(int nt, int j) { return 8 * j + 32 * (nt >> 
 
 }  // namespace ps
 
-template <int PH, bool BLO>
+template <int PH, bool BLO, bool A16>
 __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   using namespace ps;
   using Wd = W<PH>;
@@ -704,8 +705,18 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // and waits only for its own stores before it raises the flag; the others
   // publish after their first folds.  Aggregates are read two at a time (the
   // next one's loads in flight while the current one is added).
-  constexpr unsigned kStBytes = (unsigned)(N * PH) * 4u;
-  auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * 4u; };
+  // A16 (no final state asked for): an aggregate is stored as binary16,
+  // scaled by a power of two chosen from the wave's largest magnitude so
+  // that it lies in [2^14, 2^15), with the inverse scale after its 16 tiles
+  // (8 KB per item instead of 16 KB: half the publish stores and fold
+  // loads).  Only the readouts then see the aggregates, and a readout takes
+  // the state as binary16 anyway; a final state would carry their rounding
+  // (up to 2^-11 of its largest entry per aggregate), so calls that ask for
+  // one keep the binary32 aggregates.
+  constexpr unsigned ESZ = A16 ? 2u : 4u;
+  constexpr unsigned kStBytes = (unsigned)(N * PH) * ESZ + (A16 ? 4u : 0u);
+  constexpr unsigned kScaleOff = (unsigned)(N * PH) * 2u;
+  auto st_off = [&](int nt, int pt) -> unsigned { return (unsigned)((nt * PT + pt) * 256 + lane * 4) * ESZ; };
   auto node_item = [&](int j) -> unsigned { return (unsigned)((j - 1) * BHV + bhv); };   // j: 1-based segment
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -732,15 +743,46 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
   // own aggregate (segdec R + local, its decay segdec scale) into the workspace
   auto publish_stores = [&]() __attribute__((always_inline)) {
     const rsrc_t r = mkr(a.agg + (size_t)item * (N * PH), kStBytes);
+    if constexpr (A16) {
+      f4 v[NT][PT];
+      float m = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        f4 v = acc[nt][pt];
+        for (int pt = 0; pt < PT; ++pt) {
+          v[nt][pt] = acc[nt][pt];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(segdec, R[nt][pt][k], v[k]);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
-      }
+          for (int k = 0; k < 4; ++k) {
+            v[nt][pt][k] = __builtin_fmaf(segdec, R[nt][pt][k], v[nt][pt][k]);
+            m = fmaxf(m, fabsf(v[nt][pt][k]));
+          }
+        }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      // biased exponent eb of the largest magnitude, clamped so that the
+      // scale 2^(141 - eb) and its inverse are normal binary32 numbers
+      const unsigned eb = min(max((__float_as_uint(m) >> 23) & 0xffu, 15u), 254u);
+      const float sc = __uint_as_float((268u - eb) << 23), inv = __uint_as_float((eb - 14u) << 23);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const h4 hv = h4{(_Float16)(v[nt][pt][0] * sc), (_Float16)(v[nt][pt][1] * sc),
+                           (_Float16)(v[nt][pt][2] * sc), (_Float16)(v[nt][pt][3] * sc)};
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, hv), r, st_off(nt, pt), 0, kSc1);
+        }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(inv), r, kScaleOff, 0, kSc1);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          f4 v = acc[nt][pt];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(segdec, R[nt][pt][k], v[k]);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, st_off(nt, pt), 0, kSc1);
+        }
+    }
   };
   auto publish_flag = [&]() __attribute__((always_inline)) {
     // compiler-only fence: no data store moves past the flag store
@@ -791,29 +833,42 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       // compiler-only fence: the aggregate loads stay after the poll
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
-    auto load_node = [&](int k, f4 (&buf)[NT][PT]) __attribute__((always_inline)) {
+    // an aggregate's tiles (and with A16 its inverse scale: one load group)
+    using Tile = typename std::conditional<A16, h4, f4>::type;
+    struct Node {
+      Tile t[NT][PT];
+      float inv;
+    };
+    auto load_node = [&](int k, Node& buf) __attribute__((always_inline)) {
       const int n = __builtin_amdgcn_readlane(my_node, k);
       const rsrc_t r = mkr(a.agg + (size_t)node_item(n) * (N * PH), kStBytes);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-          buf[nt][pt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
+        for (int pt = 0; pt < PT; ++pt) {
+          if constexpr (A16)
+            buf.t[nt][pt] = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, st_off(nt, pt), 0, kSc1));
+          else
+            buf.t[nt][pt] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, st_off(nt, pt), 0, kSc1));
+        }
+      if constexpr (A16) buf.inv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, kScaleOff, 0, kSc1));
     };
-    auto add_node = [&](int k, const f4 (&buf)[NT][PT]) __attribute__((always_inline)) {
+    auto add_node = [&](int k, const Node& buf) __attribute__((always_inline)) {
+      float f = scale;
+      if constexpr (A16) f *= __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, buf.inv)));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(scale, buf[nt][pt][e], R[nt][pt][e]);
+          for (int e = 0; e < 4; ++e) R[nt][pt][e] = __builtin_fmaf(f, (float)buf.t[nt][pt][e], R[nt][pt][e]);
       scale *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dec), k));
     };
     if (tb > 0) {
       // (the local state is still live here: one aggregate at a time)
       wait_group(0, tb);
       for (int k = 0; k < tb; ++k) {
-        f4 b0[NT][PT];
+        Node b0;
         load_node(k, b0);
         add_node(k, b0);
       }
@@ -834,7 +889,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
       // (scheduling barriers keep each load group ahead of the additions
       // that follow it)
       const int kl = nodes - 1;
-      f4 b0[NT][PT], b1[NT][PT];
+      Node b0, b1;
       load_node(tb, b0);
       load_node(min(tb + 1, kl), b1);
       __builtin_amdgcn_sched_barrier(0);
@@ -850,7 +905,7 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       for (int k = tb + 8; k < nodes; ++k) {
-        f4 bk[NT][PT];
+        Node bk;
         load_node(k, bk);
         add_node(k, bk);
       }
@@ -922,8 +977,15 @@ hipError_t launch_ssd_scan(const ScanArgs& in, int cus, hipStream_t st) {
   // every workgroup resident at once: the chain of dependent publishes is the
   // critical path (radix 8); otherwise aggregate traffic matters more (radix 4)
   a.tree_lg = wgs <= cus ? 3 : 2;
-  if (a.Blo) ssd_scan_kernel<32, true><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
-  else ssd_scan_kernel<32, false><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
+  // binary16 aggregates when no final state is asked for (see the kernel)
+  const bool a16 = a.state_out == nullptr;
+  if (a.Blo) {
+    if (a16) ssd_scan_kernel<32, true, true><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
+    else ssd_scan_kernel<32, true, false><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
+  } else {
+    if (a16) ssd_scan_kernel<32, false, true><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
+    else ssd_scan_kernel<32, false, false><<<(unsigned)wgs, W<32>::NTH, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

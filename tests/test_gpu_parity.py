@@ -110,6 +110,42 @@ def test_streamed_scan_more_workgroups_than_compute_units():
     check_window("more workgroups than compute units", inp, 128, seqlens=lens, state_in=h0, segments=5)
 
 
+# Calls that ask for no final state hand segment aggregates over as scaled
+# binary16 (only the readouts see them); y against the oracle.
+def check_window_y_only(name, inp, chunk, seqlens=None, state_in=None, segments=0):
+    say(f"[window, no final state] {name}: shape x{inp['x'].shape} chunk {chunk} segments {segments}")
+    y, _ = run_window(inp, chunk, seqlens=seqlens, state_in=state_in, want_state=False, y_fill=12345.0,
+                      segments=segments)
+    yr, _ = oracle_window(inp, seqlens, state_in)
+    ey = 0.0
+    for b in range(y.shape[0]):
+        n = seqlens[b] if seqlens is not None else y.shape[1]
+        if n > 0:
+            ey = max(ey, slice_err(np.transpose(y[b:b + 1, :n], (0, 2, 1, 3)),
+                                   np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2))
+        assert np.all(y[b, n:] == np.float16(12345.0))
+    say(f"[window, no final state] {name}: y err {ey:.3e}")
+    assert ey <= Y_TOL
+
+
+def test_windows_without_final_state():
+    s = synth.layer_window()
+    check_window_y_only("layer L=2048", synth.window_inputs(s, 1001), s.chunk)
+    # a two-level tree (nine segments) and a three-level one (more workgroups
+    # than compute units: radix 4, late publishers re-rounding combined
+    # aggregates), with initial states and ragged lengths
+    inp = rand_window(54, 3, 1100, 16, 128, 2)
+    h0 = np.random.default_rng(55).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
+    check_window_y_only("segments=9", inp, 128, seqlens=[1100, 700, 100], state_in=h0, segments=9)
+    inp = rand_window(71, 8, 640, 32, 128, 8)
+    lens = [640, 600, 1, 129, 384, 640, 257, 0]
+    h0 = np.random.default_rng(72).standard_normal((8, 32, 64, 128)).astype(np.float32) * 0.3
+    check_window_y_only("more workgroups than compute units", inp, 128, seqlens=lens, state_in=h0, segments=5)
+    s2 = synth.WindowShape(2, 600, 8, 64, 128, 2, 256, np.float16, "wide")
+    inp = synth.window_inputs(s2, 81, raw_dt=True)
+    check_window_y_only("raw dt", inp, 256, seqlens=[600, 411], segments=3)
+
+
 def test_ragged_batch_with_initial_state():
     inp = rand_window(21, 3, 700, 16, 128, 2)
     h0 = np.random.default_rng(22).standard_normal((3, 16, 64, 128)).astype(np.float32) * 0.5
