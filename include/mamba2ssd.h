@@ -132,7 +132,11 @@ typedef struct mamba2_dims {
  *             dt_bias (H) f32 or NULL (zero) is added before the softplus)
  *   A, D (H) f32
  *   state_in  (B,H,P,N) f32 or NULL (zero initial state)
- *   state_out (B,H,P,N) f32 or NULL: state after token seqlens[b]-1
+ *   state_out (B,H,P,N) f32 or NULL: state after token seqlens[b]-1.
+ *             With NULL (binary16 I/O, dstate 128), segments of a sequence
+ *             hand their aggregate states over as binary16 scaled by a
+ *             power of two, which only the readouts of y see (y within the
+ *             same tolerance); with a state_out they stay binary32.
  *   seqlens   device int32 (B) or NULL (all L); each value is clamped to
  *             [0, L].  Rows t >= seqlens[b] of y are not written.
  *   cu_seqlens device int32 (B+1), packed layout only (dims.packed_tokens
