@@ -21,7 +21,10 @@
 // segments and no hand-off between workgroups: x is read from HBM once, y is
 // written once.  When the batch is small this gives 2 x heads x sequences
 // workgroups (256 for one 8B-shape sequence), where splitting by heads alone
-// would leave most compute units idle.
+// would leave most compute units idle.  A wave's share of the state is a
+// quarter of the segmented scan's, so per output its steps cost more (their
+// barrier, LDS round trips and share sums are not amortized): the library
+// routes only short windows here.
 //
 // Per wave and step: readout 2 MFMAs, its quarter's C.B^T blocks 3, the
 // masked diagonal product 2, the state update 2 (16x16x32 f16, fp32
