@@ -79,7 +79,7 @@ typedef struct mamba2_dims {
                             second computes the first's state itself and the
                             first takes the larger share of the chunks.
                             With 0, binary16 windows at dstate 128 of at
-                            most 512 tokens whose 2 x heads x batch fits one
+                            most 768 tokens whose 2 x heads x batch fits one
                             workgroup per compute unit run unsplit, each
                             workgroup a whole sequence for half a head with
                             the state split over dstate between its waves.

@@ -34,6 +34,8 @@
 namespace m2 {
 
 constexpr int kP = 64;                     // head dim
+// longest window the column scan takes (see the launch of the binary16 scan)
+constexpr int kColscanMaxL = 768;
 constexpr unsigned kSpinLimit = 1u << 22;  // bounded waits: an error flag instead of a hang
 constexpr int kNormParts = 2;              // partial sums of g^2 per (token, head) handed to the norm finish
 
@@ -1283,12 +1285,13 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
     // One round of column-scan workgroups (2 x heads x sequences at most
     // one per compute unit) over short windows: the segmented scan would run
     // too few workgroups there (one chunk), or a hand-off between short
-    // segments.  Measured on the 8B layer shape at batch 1: 16 us against
-    // 27 us at L = 256, 27 against 35 us at L = 512, and 49 against 44 us at
-    // L = 1024, where the segmented scan's larger steps win.  Callers that
-    // ask for a segment count get the segmented scan.
+    // segments.  Measured on the 8B layer shape at batch 1 (column against
+    // segmented): 16 against 27 us at L = 256, 26 against 35 us at 512, 36
+    // against 40 us at 768, 41 against 40 us at 896, where the segmented
+    // scan's larger steps begin to win.  Callers that ask for a segment
+    // count get the segmented scan.
     const int cus = device_cus();
-    if (a.Blo == nullptr && d.segments == 0 && 2LL * a.B * a.H <= cus && a.L <= 512) e = launch_ssd_colscan(sa, st);
+    if (a.Blo == nullptr && d.segments == 0 && 2LL * a.B * a.H <= cus && a.L <= kColscanMaxL) e = launch_ssd_colscan(sa, st);
     else e = launch_ssd_scan(sa, cus, st);
   } else {
     const bool blo = a.Blo != nullptr;   // only binary16 conv output carries a remainder

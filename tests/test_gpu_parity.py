@@ -225,13 +225,13 @@ def test_short_window_full_heads_column_scan(chunk):
 
 
 def test_column_scan_routing_boundary():
-    # 512 tokens run the column scan, 513 the segmented scan (two runs of
+    # 768 tokens run the column scan, 769 the segmented scan (four runs of
     # 256-token chunks); both against the oracle at the full head count
-    inp = rand_window(100, 1, 513, 128, 128, 8)
+    inp = rand_window(100, 1, 769, 128, 128, 8)
     h0 = np.random.default_rng(101).standard_normal((1, 128, 64, 128)).astype(np.float32) * 0.3
-    short = {k: (v[:, :512] if v.ndim > 1 else v) for k, v in inp.items()}
-    check_window("L=512 (column scan)", short, 256, state_in=h0)
-    check_window("L=513 (segmented scan)", inp, 256, state_in=h0)
+    short = {k: (v[:, :768] if v.ndim > 1 else v) for k, v in inp.items()}
+    check_window("L=768 (column scan)", short, 256, state_in=h0)
+    check_window("L=769 (segmented scan)", inp, 256, state_in=h0)
 
 
 def test_short_windows_column_scan_ragged_zero_and_one_token():
