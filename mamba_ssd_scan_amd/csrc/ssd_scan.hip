@@ -932,13 +932,26 @@ __global__ __launch_bounds__(ps::W<PH>::NTH) void ssd_scan_kernel(ScanArgs a) {
     if (k + 1 < nsteps && blk < 3) cb_block(nsl, blk, (k + 1) & 1);
   });
   if (want_state && live) {
+    // Staged through the slots (every wave has passed the pass's last
+    // barrier, so none reads them any more) so that each store writes two
+    // whole 512-byte state rows: per wave and p tile, 16 rows of N floats,
+    // rows SR floats apart so that the tile writes of 16 rows fall on
+    // distinct banks.  A wave reads back only what it wrote itself (its LDS
+    // accesses complete in order).
+    constexpr int SR = N + 4;
+    static_assert(NWV * 16 * SR * sizeof(float) <= 3 * sizeof(Slot), "staging fits the slots");
+    float* const stg = reinterpret_cast<float*>(&rs[0]) + wid * (16 * SR);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int pt = 0; pt < PT; ++pt) {
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        const int p = PH * half + 16 * pt + lr, n = ncol(nt, q);
-        *reinterpret_cast<f4*>(a.state_out + ((size_t)hb * P + p) * N + n) = R[nt][pt];
+      for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f4*>(&stg[lr * SR + ncol(nt, q)]) = R[nt][pt];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 2 * i + (lane >> 5), c = 4 * (lane & 31);
+        const f4 v = *reinterpret_cast<const f4*>(&stg[row * SR + c]);
+        *reinterpret_cast<f4*>(a.state_out + ((size_t)hb * P + PH * half + 16 * pt + row) * N + c) = v;
       }
+    }
   }
 
   // ---- retire -------------------------------------------------------------------
