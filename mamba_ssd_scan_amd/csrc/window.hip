@@ -1246,7 +1246,11 @@ static hipError_t launch_IO(const mamba2_dims& d, const mamba2_window_io& io_, v
   if (d.conv_width == 4) {
     const int cd = d.nheads * kP + 2 * d.ngroups * d.dstate;
     IO* xc = (IO*)(base + wl.convx);
-    _Float16* blo = sizeof(IO) == 2 ? (_Float16*)(base + wl.blo) : nullptr;
+    // B's binary16 remainder keeps a final state within its tolerance (the
+    // conv output is rounded to binary16 before the scan); without a final
+    // state only y sees the state, through binary16 readouts, and the
+    // remainder is neither written nor read
+    _Float16* blo = sizeof(IO) == 2 && io_.state_out != nullptr ? (_Float16*)(base + wl.blo) : nullptr;
     const dim3 cgrid((unsigned)(d.batch * ((d.seqlen + kConvTT - 1) / kConvTT)), (unsigned)((cd / 8 + 255) / 256));
     conv_silu_kernel<IO><<<cgrid, 256, 0, st>>>(
         (const IO*)io_.xBC, io_.conv_w, io_.conv_b, (const IO*)io_.conv_state_in, (IO*)io_.conv_state_out,

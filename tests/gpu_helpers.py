@@ -94,13 +94,13 @@ def projection_rows(xbc, lead, tail):
 
 
 def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=None, state_in=None,
-              want_conv_state=True, segments=0, xbc_in_rows=None):
+              want_conv_state=True, segments=0, xbc_in_rows=None, want_state=True):
     xBC = to_dev(inp["xBC"])
     if xbc_in_rows is not None:
         xBC = projection_rows(xBC, *xbc_in_rows)
     Bsz, L, Cn = inp["xBC"].shape
     y = torch.empty((Bsz, L, H * P), dtype=xBC.dtype, device=DEV)
-    hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=DEV)
+    hT = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=DEV) if want_state else None
     cso = torch.empty((Bsz, Cn, 3), dtype=xBC.dtype, device=DEV) if want_conv_state else None
     csi = to_dev(conv_state_in) if conv_state_in is not None else None
     h0 = to_dev(np.asarray(state_in, np.float32)) if state_in is not None else None
@@ -116,7 +116,8 @@ def run_mixer(inp, H, P, G, N, chunk, norm_group, seqlens=None, conv_state_in=No
                         chunk=chunk, norm_group=norm_group, ngroups=G, dstate=N, headdim=P, segments=segments,
                         **raw_dt_args(inp))
     torch.cuda.synchronize()
-    return y.cpu().numpy(), hT.cpu().numpy(), (cso.cpu().numpy() if want_conv_state else None)
+    return (y.cpu().numpy(), hT.cpu().numpy() if want_state else None,
+            cso.cpu().numpy() if want_conv_state else None)
 
 
 def pack_rows(a, lens):

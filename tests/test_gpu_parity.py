@@ -787,14 +787,18 @@ def test_mixer_core_full_size_sampled():
     H, P, G, N = s.nheads, s.headdim, s.ngroups, s.dstate
     say("[mixer] full size B=4 L=2048")
     y, hT, _ = run_mixer(inp, H, P, G, N, s.chunk, H * P, want_conv_state=False)
+    # without a final state (the conv writes no binary16 remainder of B, the
+    # scan takes B as binary16 alone)
+    y_ns, _, _ = run_mixer(inp, H, P, G, N, s.chunk, H * P, want_conv_state=False, want_state=False)
     for b in range(s.batch):
         sub = {k: (v[b:b + 1] if (v.ndim > 1 and k in ("xBC", "dt", "z")) else v) for k, v in inp.items()}
         out_r, h_r, _ = oracle.mixer_core(sub["xBC"], inp["conv_w"], inp["conv_b"], sub["dt"], inp["A"], inp["D"],
                                           sub["z"], inp["norm_w"], H, P, G, N, H * P)
         e = slice_err(y[b][None], out_r[0][None], 1)
         es = slice_err(hT[b:b + 1], h_r, 2)
-        say(f"[mixer] seq {b}: out {e:.3e} state {es:.3e}")
-        assert e <= Y_TOL and es <= S_TOL
+        e_ns = slice_err(y_ns[b][None], out_r[0][None], 1)
+        say(f"[mixer] seq {b}: out {e:.3e} state {es:.3e}; without a final state: out {e_ns:.3e}")
+        assert e <= Y_TOL and es <= S_TOL and e_ns <= Y_TOL
 
 
 # ---- decode --------------------------------------------------------------------
