@@ -135,8 +135,11 @@ typedef struct mamba2_dims {
  *   state_out (B,H,P,N) f32 or NULL: state after token seqlens[b]-1.
  *             With NULL (binary16 I/O, dstate 128), segments of a sequence
  *             hand their aggregate states over as binary16 scaled by a
- *             power of two, which only the readouts of y see (y within the
- *             same tolerance); with a state_out they stay binary32.
+ *             power of two, and with the fused conv B enters the scan as
+ *             its binary16 value alone (no remainder): only the readouts of
+ *             y see the state then (y within the same tolerance).  With a
+ *             state_out the aggregates stay binary32 and B keeps its
+ *             binary16 remainder, so the final state meets its own.
  *   seqlens   device int32 (B) or NULL (all L); each value is clamped to
  *             [0, L].  Rows t >= seqlens[b] of y are not written.
  *   cu_seqlens device int32 (B+1), packed layout only (dims.packed_tokens
