@@ -144,6 +144,26 @@ def test_windows_without_final_state():
     s2 = synth.WindowShape(2, 600, 8, 64, 128, 2, 256, np.float16, "wide")
     inp = synth.window_inputs(s2, 81, raw_dt=True)
     check_window_y_only("raw dt", inp, 256, seqlens=[600, 411], segments=3)
+    # packed rows, three segments, no final state
+    lens = [600, 411, 0, 257, 1]
+    inp = rand_window(86, len(lens), 600, 8, 128, 2)
+    h0 = np.random.default_rng(87).standard_normal((len(lens), 8, 64, 128)).astype(np.float32) * 0.3
+    x, dt, Bm, Cm = (to_dev(pack_rows(inp[k], lens)) for k in ("x", "dt", "B", "C"))
+    T = dt.shape[0]
+    y = torch.full((T + 16, 8 * 64), 12345.0, dtype=x.dtype, device=DEV)
+    dims = m2.make_dims(len(lens), 600, 8, 64, 128, 2, 256, packed_tokens=T)
+    ws = m2.alloc_workspace(dims, DEV)
+    window_checked(dt, to_dev(inp["A"]), to_dev(inp["D"]), y, ws, x=x, B=Bm, C=Cm, state_in=to_dev(h0),
+                   chunk=256, segments=3, cu_seqlens=to_dev(cu_of(lens)), max_seqlen=600)
+    torch.cuda.synchronize()
+    yp = y.cpu().numpy()
+    assert np.all(yp[T:] == np.float16(12345.0))
+    yu = unpack_rows(yp[:T], lens, 600).reshape(len(lens), 600, 8, 64)
+    yr, _ = oracle_window(inp, lens, h0)
+    ey = max(slice_err(np.transpose(yu[b:b + 1, :n], (0, 2, 1, 3)), np.transpose(yr[b:b + 1, :n], (0, 2, 1, 3)), 2)
+             for b, n in enumerate(lens) if n > 0)
+    say(f"[window, no final state] packed: y err {ey:.3e}")
+    assert ey <= Y_TOL
 
 
 def test_ragged_batch_with_initial_state():
